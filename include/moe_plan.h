@@ -1,0 +1,266 @@
+/*
+ * moe_plan -- expert-parallel dispatch planning for one MoE layer on MI355X.
+ *
+ * C ABI of the HIP library load_balance_planning_amd/libmoe_plan.so.
+ *
+ * The path turns a layer's gate logits into an expert-parallel dispatch plan:
+ *   moe_plan_route     top-k gating + load histograms
+ *   moe_plan_hist      the histograms alone, from a given top-k
+ *   moe_plan_plan      hot-expert replication + token re-routing
+ *   moe_plan_dispatch  dispatch layout + bf16 row gather
+ * EP ranks and NVLink domains ("nodes") are logical partitions on one GPU:
+ *   source rank of token t   src(t)  = t / (T/R)     (contiguous token blocks)
+ *   domain of rank r          dom(r)  = r / G         (contiguous rank blocks)
+ *   main rank of expert e     main(e) = e / (E/R)     (contiguous expert blocks)
+ *
+ * Sources:
+ *   [TopoEP]   "TopoEP: Topology-Aware Load Balancing for Expert-Parallel MoE
+ *              Training": routing matrix (section 4.1, Eq. 3), domain demand
+ *              (Eq. 4), constraints C1-C5 (section 4.2), two-stage solver
+ *              (section 4.3, Eqs. 9 and 10, Fig. 9), device-resident plan that
+ *              drives dispatch (sections 3.1 and 5).
+ *   [Coupling] "Expert Coupling in MoE Pretraining": within-layer expert
+ *              co-selection counts, layer-to-layer routing counts.
+ *
+ * Conventions for every call
+ *   - Pointers named in the structs are HIP device pointers unless stated.
+ *     The caller allocates and owns every input and output buffer; sizes are
+ *     fixed by the configuration (moe_plan_query reports them).  Layouts are
+ *     dense row-major int32 / float32 / uint16 (bf16 bit patterns).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  The compute
+ *     calls only enqueue work: they never allocate, never synchronise and
+ *     never copy to the host.  One handle serves one stream at a time; calls
+ *     on one stream run in order.
+ *   - Argument and configuration errors return a negative code synchronously
+ *     and enqueue nothing.  A data-dependent error (a NaN gate logit) sets a
+ *     device status word that moe_plan_status reads.
+ *   - Every output is fully overwritten on each call; unused entries of the
+ *     instance arrays are -1.  Results are deterministic: the same inputs give
+ *     the same bytes on every run.
+ */
+#ifndef MOE_PLAN_H
+#define MOE_PLAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size or inconsistent configuration */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but beyond this build's limits (see moe_plan_create) */
+  MOE_ERR_HIP = -3,         /* a HIP runtime call failed */
+  MOE_ERR_NONFINITE = -4,   /* status flag: a gate logit was NaN */
+  MOE_ERR_INTERNAL = -5     /* status flag: an internal consistency check failed on the device */
+};
+
+/* Status-word bits reported by moe_plan_status. */
+#define MOE_STATUS_NAN_LOGIT 1
+#define MOE_STATUS_PLAN_CHECK 2
+
+typedef struct moe_plan* moe_plan_t;
+
+/*
+ * Layer configuration.
+ *   T  tokens of all ranks (multiple of R; 0 allowed)
+ *   E  routed experts (multiple of R);  k  top-k (1 <= k <= E)
+ *   R  logical EP ranks;  G  ranks per NVLink domain (R multiple of G), M = R/G domains
+ *   H  hidden size in bf16 elements per token row
+ *   replica_budget  B: extra expert instances per layer over all ranks; domain d
+ *                   may add B_d = B/M (+1 for d < B mod M)
+ *   slots_per_rank  N_slot replica slots per rank [TopoEP C3]; <= 0 derives
+ *                   ceil(ceil(B/M)/G)
+ *   expert_bytes    ||W_e|| in bytes; < 0 derives 9*H*H/4 (three H x 3H/8 bf16
+ *                   matrices: 9 MiB at H = 2048, the [TopoEP] Fig. 3 example)
+ *   token_bytes     S_tok in bytes; <= 0 derives 2*H (one bf16 row)
+ *   max_refine_iters  cap on intra-node refinement iterations per domain;
+ *                   <= 0 derives 4096
+ */
+typedef struct {
+  int32_t T, E, k, R, G, H;
+  int32_t replica_budget;
+  int32_t slots_per_rank;
+  int64_t expert_bytes;
+  int64_t token_bytes;
+  int32_t max_refine_iters;
+} moe_plan_config;
+
+/* Element counts of every caller-owned buffer for a configuration. */
+typedef struct {
+  int64_t topk;          /* T*k      topk_idx, topk_val, slot_inst, slot_rank, perm, slot_pos */
+  int64_t omega;         /* R*E      omega */
+  int64_t experts;       /* E        expert_count */
+  int64_t pair;          /* E*E      cooc, trans */
+  int64_t tiles;         /* NT = R * ceil((T/R)/64) token tiles of up to 64 tokens of one source */
+  int64_t tile_words;    /* NT*E     tile_mask (uint64) and tile_base (int32) */
+  int64_t inst_cap;      /* E+B      inst_expert, inst_rank, inst_load */
+  int64_t quota;         /* R*(E+B)  quota */
+  int64_t inst_offset;   /* E+B+1 */
+  int64_t rank_offset;   /* R+1 */
+  int64_t dispatch_elems;/* T*k*H    bf16 elements of the dispatch buffer */
+  int64_t n_slot;        /* derived N_slot */
+  int64_t expert_bytes;  /* derived ||W_e|| */
+  int64_t token_bytes;   /* derived S_tok */
+  int64_t max_refine_iters;
+  int64_t workspace_bytes; /* device memory the handle owns */
+} moe_plan_sizes;
+
+/*
+ * Outputs of moe_plan_route / moe_plan_hist.
+ *   topk_idx   int32 [T][k]: the k experts of each token, largest logit first;
+ *              equal logits order by lower expert index; -0.0 equals +0.0.
+ *   topk_val   float [T][k] (nullable): bit copy of the selected logits.
+ *   expert_count int32 [E]: assignments per expert.
+ *   omega      int32 [R][E]: routing matrix, assignments of source rank s that
+ *              select expert e [TopoEP Eq. 3].
+ *   cooc       int32 [E][E] (nullable): tokens selecting both a and b, a != b;
+ *              zero diagonal [Coupling, within-layer co-selection].
+ *   trans      int32 [E][E] (nullable; written only when prev_topk is given):
+ *              tokens selecting a in the previous layer and b in this one
+ *              [Coupling, cross-layer routing].
+ *   tile_mask  uint64 [NT][E]: bit j of tile_mask[x][e] is set when the j-th
+ *              token of tile x selects e.  Tile x = s*C + c covers tokens
+ *              s*T/R + 64c ... of source s (C = ceil((T/R)/64)).
+ *   tile_base  int32 [NT][E]: assignments of e in all earlier tiles
+ *              (exclusive prefix over tiles in token order).
+ * tile_mask and tile_base carry the stable per-(source, expert) token order
+ * from the histogram step to moe_plan_plan; treat them as opaque.
+ */
+typedef struct {
+  int32_t* topk_idx;
+  float* topk_val;
+  int32_t* expert_count;
+  int32_t* omega;
+  int32_t* cooc;
+  int32_t* trans;
+  uint64_t* tile_mask;
+  int32_t* tile_base;
+} moe_route_out;
+
+/*
+ * Outputs of moe_plan_plan.
+ *   n_inst       int32 [1]: number of expert instances (E + replicas).
+ *   inst_expert, inst_rank, inst_load  int32 [E+B]: instance i is an instance
+ *                of expert inst_expert[i] on rank inst_rank[i] executing
+ *                inst_load[i] assignments (U[e][r]).  Instances are
+ *                rank-major; on each rank its main experts (ascending) come
+ *                first, then its replicas (ascending expert).  Entries from
+ *                n_inst on are -1.
+ *   rank_load    int32 [R]: L_r, assignments executed on rank r [TopoEP 4.2].
+ *   quota        int32 [R][E+B]: q[s][i], assignments of source s run on
+ *                instance i (zero for i >= n_inst).
+ *   slot_inst    int32 [T*k]: instance of slot t*k+j.
+ *   slot_rank    int32 [T*k]: position of the slot inside its instance's
+ *                segment of the dispatch buffer (stable: slot order).
+ */
+typedef struct {
+  int32_t* n_inst;
+  int32_t* inst_expert;
+  int32_t* inst_rank;
+  int32_t* inst_load;
+  int32_t* rank_load;
+  int32_t* quota;
+  int32_t* slot_inst;
+  int32_t* slot_rank;
+} moe_plan_out;
+
+/*
+ * Outputs of moe_plan_dispatch.
+ *   perm         int32 [T*k]: slot id (t*k+j) at each dispatch row.
+ *   slot_pos     int32 [T*k]: dispatch row of each slot (inverse of perm).
+ *   inst_offset  int32 [E+B+1]: first dispatch row of each instance; entry
+ *                n_inst is T*k; later entries are -1.
+ *   rank_offset  int32 [R+1]: first dispatch row of each rank; entry R is T*k.
+ *   dispatch     uint16 [T*k][H]: bf16 rows, dispatch[pos] = hidden[perm[pos]/k].
+ */
+typedef struct {
+  int32_t* perm;
+  int32_t* slot_pos;
+  int32_t* inst_offset;
+  int32_t* rank_offset;
+  uint16_t* dispatch;
+} moe_dispatch_out;
+
+/* Buffer sizes for a configuration (host only, no GPU work).  Returns
+ * MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED as moe_plan_create would. */
+int moe_plan_query(const moe_plan_config* cfg, moe_plan_sizes* sizes);
+
+/*
+ * Validate cfg, bind the current HIP device and allocate the handle's
+ * workspace (it may synchronise).  Limits of this build: E <= 2048, k <= 32,
+ * R <= 256, G <= 64, B <= 1024, E/R + N_slot <= 1024, T*k < 2^31, H >= 1.
+ * On success *out is a new handle; on error *out is NULL.
+ */
+int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out);
+
+/*
+ * Top-k gating and histograms of one layer.  logits: float [T][E] (device).
+ * prev_topk: int32 [T][k] of the previous layer (nullable); out->trans is
+ * written only when both prev_topk and out->trans are non-null.  Required
+ * outputs: topk_idx, expert_count, omega, tile_mask, tile_base.
+ * Sources: [TopoEP] section 2.1 (top-k gating) and Eq. 3; [Coupling].
+ */
+int moe_plan_route(moe_plan_t h, const float* logits, const int32_t* prev_topk,
+                   const moe_route_out* out, void* stream);
+
+/*
+ * The histogram half of moe_plan_route from a given top-k: topk_idx int32
+ * [T][k] (device, each row k distinct experts in [0, E)).  Writes
+ * expert_count, omega, tile_mask, tile_base and the nullable cooc / trans of
+ * out; out->topk_idx and out->topk_val are ignored.
+ */
+int moe_plan_hist(moe_plan_t h, const int32_t* topk_idx, const int32_t* prev_topk,
+                  const moe_route_out* out, void* stream);
+
+/*
+ * Replica placement and token re-routing [TopoEP section 4.3]:
+ *   D[d][e] = sum of omega over the sources of domain d (Eq. 4);
+ *   stage 1 (inter-node placement): per domain, experts whose main instance is
+ *     elsewhere with benefit b = 2*D*S_tok - ||W_e|| > 0 (Eq. 9), in
+ *     descending b (ties: lower e), each to the rank of the domain with the
+ *     fewest replicas and a free slot (ties: lower rank), within B_d;
+ *   stage-1 routing: each (s, e) demand to the instances of e in dom(s) if
+ *     any, else to all instances of e, split evenly (floor; the remainder one
+ *     each to the first instances in rank order);
+ *   stage 2 (intra-node refinement, Eq. 10): per domain, repeatedly move
+ *     delta = min(U[e][r_b], floor((L_b - L_t)/2)) >= 1 assignments from the
+ *     busiest rank r_b (ties: lower rank) to a rank r_t of the domain that
+ *     hosts e or has a free slot, choosing the largest delta, then the lowest
+ *     L_t, then an existing instance before a new replica, then lower e,
+ *     then lower r_t; at most max_refine_iters moves per domain;
+ *   quotas: per expert, demands omega[s][e] are matched to the instance loads
+ *     in three passes -- the source's own rank, its domain, anywhere -- each
+ *     pass sources ascending, instances in rank order;
+ *   slot instances: the p-th slot (token order) of source s and expert e goes
+ *     to the first instance whose running quota sum exceeds p.
+ * route: the outputs of moe_plan_route / moe_plan_hist for this layer
+ * (topk_idx, omega, tile_mask, tile_base are read).
+ */
+int moe_plan_plan(moe_plan_t h, const moe_route_out* route, const moe_plan_out* out, void* stream);
+
+/*
+ * Dispatch layout and bf16 gather [TopoEP section 5: the plan stays on the
+ * device and the receive counts are derived there].  The slots are laid out
+ * as a stable counting sort by instance: slot_pos = inst_offset[slot_inst] +
+ * slot_rank, with inst_offset / rank_offset exclusive prefix sums of the
+ * instance / rank loads.  hidden: uint16 [T][H] bf16 rows (device).  Reads
+ * plan->n_inst, inst_rank, inst_load, slot_inst, slot_rank.
+ */
+int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const uint16_t* hidden,
+                      const moe_dispatch_out* out, void* stream);
+
+/*
+ * Synchronise the handle's last stream, copy the device status word to
+ * *host_flags (MOE_STATUS_* bits, 0 when clean) and clear it.
+ */
+int moe_plan_status(moe_plan_t h, int32_t* host_flags);
+
+/* Free the handle's workspace (synchronises the device).  NULL is a no-op. */
+void moe_plan_destroy(moe_plan_t h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_PLAN_H */

@@ -1,0 +1,151 @@
+"""CPU oracle of the MoE dispatch-planning path -- TEST INFRASTRUCTURE ONLY.
+
+A ctypes wrapper around oracle/libmoe_oracle.so (plain single-threaded C++).
+Only tests/, the smoke check and the benchmark's CPU-baseline leg may use it.
+The product library never imports it and shares no code with it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+class OracleCfg(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("R", ctypes.c_int32), ("G", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("B", ctypes.c_int32), ("n_slot", ctypes.c_int32),
+                ("W", ctypes.c_int64), ("S", ctypes.c_int64), ("max_iters", ctypes.c_int32)]
+
+
+def _p(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def lib(path: str | None = None):
+    global _LIB
+    if path is not None:
+        return _setup(ctypes.CDLL(path))
+    if _LIB is None:
+        alt = os.environ.get("MOE_ORACLE_LIB")  # a mutant build, used by the pin self-test
+        if alt:
+            _LIB = _setup(ctypes.CDLL(alt))
+            return _LIB
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _LIB = _setup(ctypes.CDLL(_build.LIB))
+    return _LIB
+
+
+def _setup(l):
+    vp = ctypes.c_void_p
+    l.oracle_params.argtypes = [vp, vp]
+    l.oracle_domain_budget.argtypes = [vp, vp]
+    l.oracle_route.argtypes = [vp] * 9
+    l.oracle_plan.argtypes = [vp] * 12 + [ctypes.c_int32, vp]
+    l.oracle_dispatch.argtypes = [vp, ctypes.c_int32] + [vp] * 9
+    for f in (l.oracle_params, l.oracle_domain_budget, l.oracle_route, l.oracle_plan, l.oracle_dispatch):
+        f.restype = ctypes.c_int
+    return l
+
+
+def make_cfg(T, E, k, R, G, H, B, n_slot=0, W=-1, S=0, max_iters=0) -> OracleCfg:
+    return OracleCfg(T, E, k, R, G, H, B, n_slot, W, S, max_iters)
+
+
+def params(cfg: OracleCfg, l=None) -> dict:
+    l = l or lib()
+    out = np.zeros(8, dtype=np.int64)
+    rc = l.oracle_params(ctypes.byref(cfg), _p(out))
+    if rc != 0:
+        raise ValueError("invalid oracle configuration (%d)" % rc)
+    M = int(out[0])
+    bd = np.zeros(M, dtype=np.int32)
+    l.oracle_domain_budget(ctypes.byref(cfg), _p(bd))
+    return dict(M=M, Tr=int(out[1]), Er=int(out[2]), n_slot=int(out[3]), S=int(out[4]), W=int(out[5]),
+                max_iters=int(out[6]), B=int(out[7]), Bd=bd)
+
+
+def route(cfg: OracleCfg, logits: np.ndarray, prev_topk: np.ndarray | None = None,
+          want_cooc: bool = True, l=None) -> dict:
+    l = l or lib()
+    T, E, k, R = cfg.T, cfg.E, cfg.k, cfg.R
+    logits = np.ascontiguousarray(logits, dtype=np.float32).reshape(T, E)
+    out = dict(topk_idx=np.zeros((T, k), np.int32), topk_val=np.zeros((T, k), np.float32),
+               count=np.zeros(E, np.int32), omega=np.zeros((R, E), np.int32))
+    out["cooc"] = np.zeros((E, E), np.int32) if want_cooc else None
+    if prev_topk is not None:
+        prev_topk = np.ascontiguousarray(prev_topk, dtype=np.int32).reshape(T, k)
+        out["trans"] = np.zeros((E, E), np.int32)
+    else:
+        out["trans"] = None
+    rc = l.oracle_route(ctypes.byref(cfg), _p(logits), _p(prev_topk), _p(out["topk_idx"]), _p(out["topk_val"]),
+                        _p(out["count"]), _p(out["omega"]), _p(out["cooc"]), _p(out["trans"]))
+    out["status"] = rc
+    if rc not in (0, -4):
+        raise ValueError("oracle_route failed (%d)" % rc)
+    return out
+
+
+def plan(cfg: OracleCfg, omega: np.ndarray, topk_idx: np.ndarray, trace_cap: int = 0, l=None) -> dict:
+    l = l or lib()
+    T, E, k, R, B = cfg.T, cfg.E, cfg.k, cfg.R, cfg.B
+    cap = E + B
+    omega = np.ascontiguousarray(omega, dtype=np.int32).reshape(R, E)
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32).reshape(T, k)
+    out = dict(n_inst=np.zeros(1, np.int32), inst_expert=np.zeros(cap, np.int32),
+               inst_rank=np.zeros(cap, np.int32), inst_load=np.zeros(cap, np.int32),
+               rank_load=np.zeros(R, np.int32), quota=np.zeros((R, cap), np.int32),
+               slot_inst=np.zeros(T * k, np.int32), rank_load_stage1=np.zeros(R, np.int32))
+    trace = np.zeros((max(trace_cap, 1), 7), np.int32)
+    ntr = np.zeros(1, np.int32)
+    rc = l.oracle_plan(ctypes.byref(cfg), _p(omega), _p(topk_idx), _p(out["n_inst"]), _p(out["inst_expert"]),
+                       _p(out["inst_rank"]), _p(out["inst_load"]), _p(out["rank_load"]), _p(out["quota"]),
+                       _p(out["slot_inst"]), _p(out["rank_load_stage1"]),
+                       _p(trace) if trace_cap > 0 else None, trace_cap, _p(ntr))
+    if rc != 0:
+        raise ValueError("oracle_plan failed (%d)" % rc)
+    out["n_iters"] = int(ntr[0])
+    out["trace"] = trace[:min(int(ntr[0]), trace_cap)] if trace_cap > 0 else None
+    return out
+
+
+def dispatch(cfg: OracleCfg, n_inst: int, inst_rank: np.ndarray, slot_inst: np.ndarray,
+             hidden: np.ndarray | None, l=None) -> dict:
+    l = l or lib()
+    T, k, R, H, cap = cfg.T, cfg.k, cfg.R, cfg.H, cfg.E + cfg.B
+    N = T * k
+    inst_rank = np.ascontiguousarray(inst_rank, dtype=np.int32)
+    slot_inst = np.ascontiguousarray(slot_inst, dtype=np.int32).reshape(N)
+    out = dict(perm=np.zeros(N, np.int32), slot_pos=np.zeros(N, np.int32),
+               inst_offset=np.zeros(cap + 1, np.int32), rank_offset=np.zeros(R + 1, np.int32),
+               slot_rank=np.zeros(N, np.int32))
+    disp = None
+    if hidden is not None:
+        hidden = np.ascontiguousarray(hidden, dtype=np.uint16).reshape(T, H)
+        disp = np.zeros((N, H), np.uint16)
+    rc = l.oracle_dispatch(ctypes.byref(cfg), int(n_inst), _p(inst_rank), _p(slot_inst), _p(hidden),
+                           _p(out["perm"]), _p(out["slot_pos"]), _p(out["inst_offset"]), _p(out["rank_offset"]),
+                           _p(out["slot_rank"]), _p(disp))
+    if rc != 0:
+        raise ValueError("oracle_dispatch failed (%d)" % rc)
+    out["dispatch"] = disp
+    return out
+
+
+def run_all(cfg: OracleCfg, logits: np.ndarray, hidden: np.ndarray | None,
+            prev_topk: np.ndarray | None = None, want_cooc: bool = True, l=None) -> dict:
+    """route -> plan -> dispatch for one layer; returns every output in one dict."""
+    r = route(cfg, logits, prev_topk, want_cooc, l=l)
+    p = plan(cfg, r["omega"], r["topk_idx"], l=l)
+    d = dispatch(cfg, int(p["n_inst"][0]), p["inst_rank"], p["slot_inst"], hidden, l=l)
+    out = {}
+    out.update(r)
+    out.update(p)
+    out.update(d)
+    return out

@@ -1,0 +1,73 @@
+/*
+ * CPU oracle for the MoE dispatch-planning path -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded C++ implementation of what the path
+ * computes, used to check the HIP library output byte for byte.  Only the
+ * tests, the smoke check and the benchmark's CPU-baseline leg may load it;
+ * the product path never calls it and shares no code with it.
+ *
+ * Sources (cited by page title and section / equation):
+ *   [TopoEP]  "TopoEP: Topology-Aware Load Balancing for Expert-Parallel MoE
+ *             Training" -- routing matrix (Eq. 3), domain demand (Eq. 4),
+ *             constraints C1-C5 (section 4.2), two-stage solver (section 4.3,
+ *             Eqs. 9 and 10, Fig. 9).
+ *   [Coupling] "Expert Coupling in MoE Pretraining" -- within-layer expert
+ *             co-selection counts and layer-to-layer routing counts.
+ *
+ * Every function returns 0 on success or a negative status:
+ *   -1 invalid argument / configuration, -4 a NaN gate logit,
+ *   -5 an internal consistency check failed.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t T;          /* tokens of all ranks, contiguous blocks of T/R per source rank */
+  int32_t E;          /* routed experts; main(e) = e / (E/R) */
+  int32_t k;          /* top-k */
+  int32_t R;          /* EP ranks */
+  int32_t G;          /* ranks per NVLink domain; dom(r) = r / G */
+  int32_t H;          /* hidden size (bf16 elements per token row) */
+  int32_t B;          /* replica budget: extra instances per layer, all domains together */
+  int32_t n_slot;     /* replica slots per rank; <= 0 derives ceil(ceil(B/M)/G) */
+  int64_t W;          /* expert parameter bytes; < 0 derives 9*H*H/4 */
+  int64_t S;          /* bytes of one routed activation; <= 0 derives 2*H */
+  int32_t max_iters;  /* intra-node refinement iterations per domain; <= 0 derives 4096 */
+} oracle_cfg;
+
+/* Derived parameters: out[0..7] = M, T_r, E_r, n_slot, S, W, max_iters, B (as given). */
+int oracle_params(const oracle_cfg* c, int64_t* out);
+/* Per-domain replica budget B_d for d in [0, M). */
+int oracle_domain_budget(const oracle_cfg* c, int32_t* out_bd);
+
+/* Top-k selection plus histograms.  prev_topk / trans and cooc may be NULL. */
+int oracle_route(const oracle_cfg* c, const float* logits, const int32_t* prev_topk,
+                 int32_t* topk_idx, float* topk_val, int32_t* count, int32_t* omega,
+                 int32_t* cooc, int32_t* trans);
+
+/* Two-stage replica placement, token routing, quotas and per-slot instances.
+ * rank_load_stage1 (R entries), trace (trace_cap records of 7 int32) and
+ * n_trace may be NULL.  A trace record is
+ * {domain, iteration, r_busy, expert, r_target, delta, created_replica}. */
+int oracle_plan(const oracle_cfg* c, const int32_t* omega, const int32_t* topk_idx,
+                int32_t* n_inst, int32_t* inst_expert, int32_t* inst_rank, int32_t* inst_load,
+                int32_t* rank_load, int32_t* quota, int32_t* slot_inst,
+                int32_t* rank_load_stage1, int32_t* trace, int32_t trace_cap, int32_t* n_trace);
+
+/* Stable counting-sort layout of the slots by instance, then the row copy.
+ * slot_rank (T*k) receives each slot's position inside its instance segment.
+ * dispatch may be NULL (layout only). */
+int oracle_dispatch(const oracle_cfg* c, int32_t n_inst, const int32_t* inst_rank,
+                    const int32_t* slot_inst, const uint16_t* hidden,
+                    int32_t* perm, int32_t* slot_pos, int32_t* inst_offset, int32_t* rank_offset,
+                    int32_t* slot_rank, uint16_t* dispatch);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,74 @@
+"""Self-test of the oracle pins: plant plausible mistakes in copies of the
+oracle source, build each on the CPU, and check that the pin suite rejects
+every one of them.  The mistakes are the kind a reader might make when
+restating the pages: a dropped factor, a flipped tie-break, a swapped index,
+a wrong default.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as obuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.cpp")
+
+# (name, exact text in the oracle, replacement)
+MUTANTS = [
+    ("topk order reversed", "topk_idx[t * k + j] = order[j];", "topk_idx[t * k + j] = order[k - 1 - j];"),
+    ("topk ascending", "return row[a] > row[b]; });", "return row[a] < row[b]; });"),
+    ("cooc diagonal kept", "if (a != b) cooc[(int64_t)a * E + b] += 1;", "cooc[(int64_t)a * E + b] += 1;"),
+    ("trans transposed", "trans[(int64_t)a * E + b] += 1;", "trans[(int64_t)b * E + a] += 1;"),
+    ("omega interleaved sources", "omega[src_of(d, t) * E + e] += 1;", "omega[(t % R) * E + e] += 1;"),
+    ("Eq. 9 factor 2 dropped", "int64_t b = 2 * D[m * E + e] * d.S - d.W;", "int64_t b = D[m * E + e] * d.S - d.W;"),
+    ("Eq. 9 local experts", "if (dom_of(c, main_of(d, e)) == m) continue;", "if (dom_of(c, main_of(d, e)) != m) continue;"),
+    ("stage 1 ascending benefit", "if (a.first != b.first) return a.first > b.first;",
+     "if (a.first != b.first) return a.first < b.first;"),
+    ("stage 1 ties to higher rank", "if (best < 0 || nrep[r] < nrep[best]) best = r;",
+     "if (best < 0 || nrep[r] <= nrep[best]) best = r;"),
+    ("even split remainder to the last", "Uer(e, sel[i]) += w / m + (i < w % m ? 1 : 0);",
+     "Uer(e, sel[i]) += w / m + (i >= m - w % m ? 1 : 0);"),
+    ("routing ignores the source domain", "if (X(e, r) && dom_of(c, r) == dom_of(c, s)) sel.push_back(r);",
+     "if (X(e, r) && r == s) sel.push_back(r);"),
+    ("Eq. 10 without the half gap", "int64_t delta = std::min(Uer(e, rb), (L[rb] - L[rt]) / 2);",
+     "int64_t delta = std::min(Uer(e, rb), (L[rb] - L[rt]));"),
+    ("busiest rank ties to higher rank", "if (L[r] > L[rb]) rb = r;", "if (L[r] >= L[rb]) rb = r;"),
+    ("refinement prefers the busier target", "else if (L[rt] != blt) better = L[rt] < blt;",
+     "else if (L[rt] != blt) better = L[rt] > blt;"),
+    ("refinement prefers new replicas", "else if (is_new != bnew) better = is_new < bnew;",
+     "else if (is_new != bnew) better = is_new > bnew;"),
+    ("refinement ignores the slot limit", "if (is_new && !(nrep[rt] < d.n_slot && rep_dom[m] < Bd)) continue;",
+     "if (is_new && !(rep_dom[m] < Bd)) continue;"),
+    ("replicas listed before mains", "      if (main_of(d, e) == r) inst_of[e * R + r] = n++;\n    for (int64_t e = 0; e < E; ++e)\n      if (X(e, r) && main_of(d, e) != r) inst_of[e * R + r] = n++;",
+     "      if (X(e, r) && main_of(d, e) != r) inst_of[e * R + r] = n++;\n    for (int64_t e = 0; e < E; ++e)\n      if (main_of(d, e) == r) inst_of[e * R + r] = n++;"),
+    ("quota without the same-rank pass", "bool ok = pass == 0 ? (r == s) :", "bool ok = pass == 0 ? (dom_of(c, r) == dom_of(c, s)) :"),
+    ("quota without the same-domain pass", ": pass == 1 ? (dom_of(c, r) == dom_of(c, s)) : true;", ": pass == 1 ? true : true;"),
+    ("slot walk off by one", "if (run > p) chosen = i;", "if (run >= p) chosen = i;"),
+    ("dispatch order not stable", "[&](int32_t a, int32_t b) { return slot_inst[a] < slot_inst[b]; });",
+     "[&](int32_t a, int32_t b) { return slot_inst[a] != slot_inst[b] ? slot_inst[a] < slot_inst[b] : a > b; });"),
+    ("budget remainder to high domains", "return c->B / d.M + (dom < c->B % d.M ? 1 : 0);",
+     "return c->B / d.M + (dom >= d.M - c->B % d.M ? 1 : 0);"),
+    ("slots per rank rounded down", "d.n_slot = c->n_slot > 0 ? c->n_slot : (per_dom + c->G - 1) / c->G;",
+     "d.n_slot = c->n_slot > 0 ? c->n_slot : per_dom / c->G;"),
+    ("expert bytes halved", "d.W = c->W >= 0 ? c->W : 9LL * c->H * c->H / 4;", "d.W = c->W >= 0 ? c->W : 9LL * c->H * c->H / 8;"),
+    ("token bytes one byte per element", "d.S = c->S > 0 ? c->S : 2LL * c->H;", "d.S = c->S > 0 ? c->S : 1LL * c->H;"),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, "mutation site not found: " + name
+    src = tmp_path / "moe_oracle.cpp"
+    src.write_text(text.replace(old, new))
+    lib = obuild.build(out=str(tmp_path / "libmutant.so"), src=str(src))
+    env = dict(os.environ, MOE_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, "the pins accept the mutant '%s'" % name
