@@ -59,6 +59,7 @@ enum {
 /* Status-word bits reported by moe_plan_status. */
 #define MOE_STATUS_NAN_LOGIT 1
 #define MOE_STATUS_PLAN_CHECK 2
+#define MOE_STATUS_BAD_TOPK 4   /* a top-k entry out of [0, E) or repeated within a token */
 
 typedef struct moe_plan* moe_plan_t;
 
@@ -209,7 +210,9 @@ int moe_plan_route(moe_plan_t h, const float* logits, const int32_t* prev_topk,
  * The histogram half of moe_plan_route from a given top-k: topk_idx int32
  * [T][k] (device, each row k distinct experts in [0, E)).  Writes
  * expert_count, omega, tile_mask, tile_base and the nullable cooc / trans of
- * out; out->topk_idx and out->topk_val are ignored.
+ * out; out->topk_idx and out->topk_val are ignored.  moe_plan_plan reads the
+ * top-k through its route argument, so hand it a moe_route_out whose
+ * topk_idx points at this same top-k.
  */
 int moe_plan_hist(moe_plan_t h, const int32_t* topk_idx, const int32_t* prev_topk,
                   const moe_route_out* out, void* stream);

@@ -1,0 +1,284 @@
+"""MI355X-native expert-parallel dispatch planning for MoE layers.
+
+A thin ctypes binding of the C ABI in include/moe_plan.h (library
+load_balance_planning_amd/libmoe_plan.so, HIP kernels for gfx950).  The
+functions named like the C entry points only marshal arguments; every step of
+the path runs in the library's kernels.  `Layer` is a convenience wrapper that
+allocates the caller-owned buffers as torch tensors on the current HIP device
+and runs the calls on torch's current stream -- PyTorch is used for device
+memory and streams only.
+
+There is no CPU fallback: importing this package without the built library
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+from . import build as _build
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_HIP = -3
+MOE_ERR_NONFINITE = -4
+MOE_ERR_INTERNAL = -5
+MOE_STATUS_NAN_LOGIT = 1
+MOE_STATUS_PLAN_CHECK = 2
+MOE_STATUS_BAD_TOPK = 4
+
+_ERRORS = {MOE_ERR_INVALID_ARG: "invalid argument", MOE_ERR_UNSUPPORTED: "unsupported configuration",
+           MOE_ERR_HIP: "HIP runtime error", MOE_ERR_NONFINITE: "non-finite gate logit",
+           MOE_ERR_INTERNAL: "internal error"}
+
+
+class MoePlanError(RuntimeError):
+    def __init__(self, call: str, code: int):
+        super().__init__("%s failed: %s (%d)" % (call, _ERRORS.get(code, "error"), code))
+        self.code = code
+
+
+class moe_plan_config(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("R", ctypes.c_int32),
+                ("G", ctypes.c_int32), ("H", ctypes.c_int32), ("replica_budget", ctypes.c_int32),
+                ("slots_per_rank", ctypes.c_int32), ("expert_bytes", ctypes.c_int64),
+                ("token_bytes", ctypes.c_int64), ("max_refine_iters", ctypes.c_int32)]
+
+
+class moe_plan_sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "topk", "omega", "experts", "pair", "tiles", "tile_words", "inst_cap", "quota", "inst_offset",
+        "rank_offset", "dispatch_elems", "n_slot", "expert_bytes", "token_bytes", "max_refine_iters",
+        "workspace_bytes")]
+
+
+class moe_route_out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "topk_idx", "topk_val", "expert_count", "omega", "cooc", "trans", "tile_mask", "tile_base")]
+
+
+class moe_plan_out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "n_inst", "inst_expert", "inst_rank", "inst_load", "rank_load", "quota", "slot_inst", "slot_rank")]
+
+
+class moe_dispatch_out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("perm", "slot_pos", "inst_offset", "rank_offset", "dispatch")]
+
+
+EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
+           "moe_plan_dispatch", "moe_plan_status", "moe_plan_destroy")
+
+_LIB = None
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def lib():
+    """The loaded HIP library (built in-tree on first use if it is not there yet)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        l = ctypes.CDLL(_build.LIB)
+        vp = ctypes.c_void_p
+        l.moe_plan_query.argtypes = [vp, vp]
+        l.moe_plan_create.argtypes = [vp, vp]
+        l.moe_plan_route.argtypes = [vp, vp, vp, vp, vp]
+        l.moe_plan_hist.argtypes = [vp, vp, vp, vp, vp]
+        l.moe_plan_plan.argtypes = [vp, vp, vp, vp]
+        l.moe_plan_dispatch.argtypes = [vp, vp, vp, vp, vp]
+        l.moe_plan_status.argtypes = [vp, vp]
+        l.moe_plan_destroy.argtypes = [vp]
+        l.moe_plan_destroy.restype = None
+        for n in EXPORTS[:-1]:
+            getattr(l, n).restype = ctypes.c_int
+        _LIB = l
+    return _LIB
+
+
+def _check(call: str, rc: int):
+    if rc != MOE_OK:
+        raise MoePlanError(call, rc)
+
+
+# ---- entry points, same names as the C ABI ---------------------------------
+
+def moe_plan_query(cfg: moe_plan_config) -> moe_plan_sizes:
+    sz = moe_plan_sizes()
+    _check("moe_plan_query", lib().moe_plan_query(ctypes.byref(cfg), ctypes.byref(sz)))
+    return sz
+
+
+def moe_plan_create(cfg: moe_plan_config) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check("moe_plan_create", lib().moe_plan_create(ctypes.byref(cfg), ctypes.byref(h)))
+    return h
+
+
+def moe_plan_route(h, logits: int, prev_topk: int | None, out: moe_route_out, stream: int):
+    _check("moe_plan_route", lib().moe_plan_route(h, logits, prev_topk, ctypes.byref(out), stream))
+
+
+def moe_plan_hist(h, topk_idx: int, prev_topk: int | None, out: moe_route_out, stream: int):
+    _check("moe_plan_hist", lib().moe_plan_hist(h, topk_idx, prev_topk, ctypes.byref(out), stream))
+
+
+def moe_plan_plan(h, route: moe_route_out, out: moe_plan_out, stream: int):
+    _check("moe_plan_plan", lib().moe_plan_plan(h, ctypes.byref(route), ctypes.byref(out), stream))
+
+
+def moe_plan_dispatch(h, plan: moe_plan_out, hidden: int, out: moe_dispatch_out, stream: int):
+    _check("moe_plan_dispatch", lib().moe_plan_dispatch(h, ctypes.byref(plan), hidden, ctypes.byref(out), stream))
+
+
+def moe_plan_status(h) -> int:
+    flags = ctypes.c_int32(0)
+    _check("moe_plan_status", lib().moe_plan_status(h, ctypes.byref(flags)))
+    return flags.value
+
+
+def moe_plan_destroy(h):
+    lib().moe_plan_destroy(h)
+
+
+# ---- torch-owned buffers ----------------------------------------------------
+
+def make_config(T, E, k, R, G, H, B, slots_per_rank=0, expert_bytes=-1, token_bytes=0,
+                max_refine_iters=0) -> moe_plan_config:
+    return moe_plan_config(T, E, k, R, G, H, B, slots_per_rank, expert_bytes, token_bytes, max_refine_iters)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class RouteBuffers:
+    topk_idx: object
+    topk_val: object
+    expert_count: object
+    omega: object
+    cooc: object
+    trans: object
+    tile_mask: object
+    tile_base: object
+
+    def struct(self) -> moe_route_out:
+        return moe_route_out(*(_ptr(getattr(self, n)) for n, _ in moe_route_out._fields_))
+
+
+@dataclass
+class PlanBuffers:
+    n_inst: object
+    inst_expert: object
+    inst_rank: object
+    inst_load: object
+    rank_load: object
+    quota: object
+    slot_inst: object
+    slot_rank: object
+
+    def struct(self) -> moe_plan_out:
+        return moe_plan_out(*(_ptr(getattr(self, n)) for n, _ in moe_plan_out._fields_))
+
+
+@dataclass
+class DispatchBuffers:
+    perm: object
+    slot_pos: object
+    inst_offset: object
+    rank_offset: object
+    dispatch: object
+
+    def struct(self) -> moe_dispatch_out:
+        return moe_dispatch_out(*(_ptr(getattr(self, n)) for n, _ in moe_dispatch_out._fields_))
+
+
+class Layer:
+    """One MoE layer's planner: a handle plus torch-allocated output buffers."""
+
+    def __init__(self, cfg: moe_plan_config, device=None, cooc: bool = True, trans: bool = False,
+                 topk_val: bool = True):
+        import torch
+        if not torch.cuda.is_available():
+            raise RuntimeError("load_balance_planning_amd needs a HIP device")
+        self.torch = torch
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.cfg = cfg
+        self.sizes = moe_plan_query(cfg)
+        with torch.cuda.device(self.device):
+            self.handle = moe_plan_create(cfg)
+        sz, dev, i32 = self.sizes, self.device, torch.int32
+        T, E, k, R, H = cfg.T, cfg.E, cfg.k, cfg.R, cfg.H
+        e = lambda n, dt=i32: torch.empty(int(n), dtype=dt, device=dev)
+        self.route_out = RouteBuffers(
+            topk_idx=e(sz.topk).view(T, k), topk_val=e(sz.topk, torch.float32).view(T, k) if topk_val else None,
+            expert_count=e(E), omega=e(sz.omega).view(R, E),
+            cooc=e(sz.pair).view(E, E) if cooc else None, trans=e(sz.pair).view(E, E) if trans else None,
+            tile_mask=e(sz.tile_words, torch.int64), tile_base=e(sz.tile_words))
+        self.plan_out = PlanBuffers(
+            n_inst=e(1), inst_expert=e(sz.inst_cap), inst_rank=e(sz.inst_cap), inst_load=e(sz.inst_cap),
+            rank_load=e(R), quota=e(sz.quota).view(R, sz.inst_cap), slot_inst=e(sz.topk), slot_rank=e(sz.topk))
+        self.dispatch_out = DispatchBuffers(
+            perm=e(sz.topk), slot_pos=e(sz.topk), inst_offset=e(sz.inst_offset), rank_offset=e(sz.rank_offset),
+            dispatch=e(sz.dispatch_elems, torch.int16).view(T * k, H))
+        self._route_s = self.route_out.struct()
+        self._plan_s = self.plan_out.struct()
+        self._disp_s = self.dispatch_out.struct()
+
+    def _stream(self, stream=None) -> int:
+        s = self.torch.cuda.current_stream(self.device) if stream is None else stream
+        return s.cuda_stream
+
+    def route(self, logits, prev_topk=None, stream=None):
+        self._check_tensor(logits, (self.cfg.T, self.cfg.E), self.torch.float32)
+        if prev_topk is not None:
+            self._check_tensor(prev_topk, (self.cfg.T, self.cfg.k), self.torch.int32)
+        moe_plan_route(self.handle, _ptr(logits), _ptr(prev_topk), self._route_s, self._stream(stream))
+        return self.route_out
+
+    def hist(self, topk_idx, prev_topk=None, stream=None):
+        self._check_tensor(topk_idx, (self.cfg.T, self.cfg.k), self.torch.int32)
+        if prev_topk is not None:
+            self._check_tensor(prev_topk, (self.cfg.T, self.cfg.k), self.torch.int32)
+        # moe_plan_plan reads the top-k through the route struct: keep it pointing at this top-k.
+        if topk_idx.data_ptr() != self.route_out.topk_idx.data_ptr():
+            self.route_out.topk_idx.copy_(topk_idx)
+        moe_plan_hist(self.handle, _ptr(topk_idx), _ptr(prev_topk), self._route_s, self._stream(stream))
+        return self.route_out
+
+    def plan(self, stream=None):
+        moe_plan_plan(self.handle, self._route_s, self._plan_s, self._stream(stream))
+        return self.plan_out
+
+    def dispatch(self, hidden, stream=None):
+        self._check_tensor(hidden, (self.cfg.T, self.cfg.H), None)
+        if hidden.element_size() != 2:
+            raise TypeError("hidden must be a 16-bit (bf16) tensor")
+        moe_plan_dispatch(self.handle, self._plan_s, _ptr(hidden), self._disp_s, self._stream(stream))
+        return self.dispatch_out
+
+    def status(self) -> int:
+        return moe_plan_status(self.handle)
+
+    def _check_tensor(self, t, shape, dtype):
+        if tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != self.device:
+            raise ValueError("expected a contiguous %s tensor of shape %s on %s" % (dtype, shape, self.device))
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError("expected dtype %s, got %s" % (dtype, t.dtype))
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            moe_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

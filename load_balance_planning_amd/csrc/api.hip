@@ -1,0 +1,220 @@
+// C ABI of the moe_plan library: validation, workspace ownership and the
+// launch sequence of each call.  See include/moe_plan.h for the contract.
+#include <new>
+
+#include "internal.h"
+
+struct moe_plan {
+  moe::Dims d;
+  moe_plan_config cfg;
+  int device;
+  moe::Workspace ws;
+  void* ws_base;
+  size_t ws_bytes;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kMaxLds = 160 * 1024;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+  size_t status, prev_mask, demand, einst_off, einst_list, qrep, colpre, total;
+};
+
+WsLayout ws_layout(const moe::Dims& d) {
+  WsLayout l;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes > 0 ? bytes : 1); return at; };
+  l.status = take(sizeof(int32_t));
+  l.prev_mask = take(sizeof(uint64_t) * (size_t)d.NT * d.E);
+  l.demand = take(sizeof(int64_t) * (size_t)d.M * d.E);
+  l.einst_off = take(sizeof(int32_t) * (size_t)(d.E + 1));
+  l.einst_list = take(sizeof(int32_t) * (size_t)d.cap);
+  l.qrep = take(sizeof(int32_t) * (size_t)d.cap * d.R);
+  l.colpre = take(sizeof(int32_t) * (size_t)d.cap * d.R);
+  l.total = o;
+  return l;
+}
+
+// Validates the configuration and derives every dimension the kernels use.
+int derive(const moe_plan_config* c, moe::Dims* d) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->E < 1 || c->k < 1 || c->k > c->E || c->R < 1 || c->G < 1 || c->H < 1 ||
+      c->replica_budget < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->R % c->G != 0 || c->T % c->R != 0 || c->E % c->R != 0) return MOE_ERR_INVALID_ARG;
+  if (c->E > moe::kMaxE || c->k > moe::kMaxK || c->R > moe::kMaxR || c->G > moe::kMaxG ||
+      c->replica_budget > moe::kMaxB)
+    return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)c->T * c->k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (c->token_bytes > ((int64_t)1 << 30) || c->expert_bytes > ((int64_t)1 << 62)) return MOE_ERR_UNSUPPORTED;
+  moe::Dims x;
+  x.T = c->T; x.E = c->E; x.k = c->k; x.R = c->R; x.G = c->G; x.H = c->H; x.B = c->replica_budget;
+  x.M = c->R / c->G;
+  x.Tr = c->T / c->R;
+  x.Er = c->E / c->R;
+  x.C = (x.Tr + moe::kTile - 1) / moe::kTile;
+  x.NT = x.R * x.C;
+  x.cap = x.E + x.B;
+  const int per_dom = (x.B + x.M - 1) / x.M;
+  x.n_slot = c->slots_per_rank > 0 ? c->slots_per_rank : (per_dom + x.G - 1) / x.G;
+  if (x.n_slot > x.B) x.n_slot = x.B;  // more slots than replicas can never be used
+  x.max_iters = c->max_refine_iters > 0 ? c->max_refine_iters : 4096;
+  x.S = c->token_bytes > 0 ? c->token_bytes : 2LL * c->H;
+  x.W = c->expert_bytes >= 0 ? c->expert_bytes : 9LL * c->H * c->H / 4;
+  if (x.Er + x.n_slot > 1024) return MOE_ERR_UNSUPPORTED;
+  if (moe::plan_lds_bytes(x) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+  *d = x;
+  return MOE_OK;
+}
+
+int bind(moe_plan_t h) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+  if (cur != h->device && hipSetDevice(h->device) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" int moe_plan_query(const moe_plan_config* cfg, moe_plan_sizes* sz) {
+  moe::Dims d;
+  const int rc = derive(cfg, &d);
+  if (rc != MOE_OK) return rc;
+  if (!sz) return MOE_ERR_INVALID_ARG;
+  sz->topk = (int64_t)d.T * d.k;
+  sz->omega = (int64_t)d.R * d.E;
+  sz->experts = d.E;
+  sz->pair = (int64_t)d.E * d.E;
+  sz->tiles = d.NT;
+  sz->tile_words = (int64_t)d.NT * d.E;
+  sz->inst_cap = d.cap;
+  sz->quota = (int64_t)d.R * d.cap;
+  sz->inst_offset = d.cap + 1;
+  sz->rank_offset = d.R + 1;
+  sz->dispatch_elems = (int64_t)d.T * d.k * d.H;
+  sz->n_slot = d.n_slot;
+  sz->expert_bytes = d.W;
+  sz->token_bytes = d.S;
+  sz->max_refine_iters = d.max_iters;
+  sz->workspace_bytes = (int64_t)ws_layout(d).total;
+  return MOE_OK;
+}
+
+extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  moe::Dims d;
+  const int rc = derive(cfg, &d);
+  if (rc != MOE_OK) return rc;
+  moe_plan* h = new (std::nothrow) moe_plan();
+  if (!h) return MOE_ERR_INTERNAL;
+  h->d = d;
+  h->cfg = *cfg;
+  if (hipGetDevice(&h->device) != hipSuccess) { delete h; return MOE_ERR_HIP; }
+  const WsLayout l = ws_layout(d);
+  if (hipMalloc(&h->ws_base, l.total) != hipSuccess) { delete h; return MOE_ERR_HIP; }
+  h->ws_bytes = l.total;
+  char* b = static_cast<char*>(h->ws_base);
+  h->ws.status = reinterpret_cast<int32_t*>(b + l.status);
+  h->ws.prev_mask = reinterpret_cast<uint64_t*>(b + l.prev_mask);
+  h->ws.demand = reinterpret_cast<int64_t*>(b + l.demand);
+  h->ws.einst_off = reinterpret_cast<int32_t*>(b + l.einst_off);
+  h->ws.einst_list = reinterpret_cast<int32_t*>(b + l.einst_list);
+  h->ws.qrep = reinterpret_cast<int32_t*>(b + l.qrep);
+  h->ws.colpre = reinterpret_cast<int32_t*>(b + l.colpre);
+  if (hipMemset(h->ws_base, 0, l.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(h->ws_base);
+    delete h;
+    return MOE_ERR_HIP;
+  }
+  *out = h;
+  return MOE_OK;
+}
+
+extern "C" int moe_plan_route(moe_plan_t h, const float* logits, const int32_t* prev_topk, const moe_route_out* out,
+                              void* stream) {
+  if (!h || !out || !out->expert_count || !out->omega) return MOE_ERR_INVALID_ARG;
+  const moe::Dims& d = h->d;
+  if (d.T > 0 && (!logits || !out->topk_idx || !out->tile_mask || !out->tile_base)) return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t* prev = (prev_topk && out->trans) ? prev_topk : nullptr;
+  hipError_t e = moe::launch_route_topk(d, logits, prev, out->topk_idx, out->topk_val, out->tile_mask,
+                                        h->ws.prev_mask, h->ws.status, st);
+  if (e == hipSuccess) e = moe::launch_scan(d, out->tile_mask, out->tile_base, out->omega, out->expert_count, st);
+  if (e == hipSuccess) e = moe::launch_pairs(d, out->tile_mask, h->ws.prev_mask, out->cooc, prev ? out->trans : nullptr, st);
+  return hip_rc(e);
+}
+
+extern "C" int moe_plan_hist(moe_plan_t h, const int32_t* topk_idx, const int32_t* prev_topk, const moe_route_out* out,
+                             void* stream) {
+  if (!h || !out || !out->expert_count || !out->omega) return MOE_ERR_INVALID_ARG;
+  const moe::Dims& d = h->d;
+  if (d.T > 0 && (!topk_idx || !out->tile_mask || !out->tile_base)) return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t* prev = (prev_topk && out->trans) ? prev_topk : nullptr;
+  hipError_t e = moe::launch_build_masks(d, topk_idx, prev, out->tile_mask, h->ws.prev_mask, h->ws.status, st);
+  if (e == hipSuccess) e = moe::launch_scan(d, out->tile_mask, out->tile_base, out->omega, out->expert_count, st);
+  if (e == hipSuccess) e = moe::launch_pairs(d, out->tile_mask, h->ws.prev_mask, out->cooc, prev ? out->trans : nullptr, st);
+  return hip_rc(e);
+}
+
+extern "C" int moe_plan_plan(moe_plan_t h, const moe_route_out* route, const moe_plan_out* out, void* stream) {
+  if (!h || !route || !out || !route->omega) return MOE_ERR_INVALID_ARG;
+  const moe::Dims& d = h->d;
+  if (d.T > 0 && (!route->topk_idx || !route->tile_mask || !route->tile_base || !out->slot_inst || !out->slot_rank))
+    return MOE_ERR_INVALID_ARG;
+  if (!out->n_inst || !out->inst_expert || !out->inst_rank || !out->inst_load || !out->rank_load || !out->quota)
+    return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_plan(d, route->omega, *out, h->ws, st);
+  if (e == hipSuccess) e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *out, h->ws, st);
+  return hip_rc(e);
+}
+
+extern "C" int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const uint16_t* hidden,
+                                 const moe_dispatch_out* out, void* stream) {
+  if (!h || !plan || !out || !plan->n_inst || !plan->inst_rank || !plan->inst_load || !out->inst_offset ||
+      !out->rank_offset)
+    return MOE_ERR_INVALID_ARG;
+  const moe::Dims& d = h->d;
+  if (d.T > 0 && (!plan->slot_inst || !plan->slot_rank || !hidden || !out->perm || !out->slot_pos || !out->dispatch))
+    return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_offsets(d, plan->n_inst, plan->inst_rank, plan->inst_load, out->inst_offset,
+                                     out->rank_offset, h->ws.status, st);
+  if (e == hipSuccess)
+    e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, out->inst_offset, hidden, out->perm, out->slot_pos,
+                           out->dispatch, h->ws.status, st);
+  return hip_rc(e);
+}
+
+extern "C" int moe_plan_status(moe_plan_t h, int32_t* host_flags) {
+  if (!h || !host_flags) return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, h->ws.status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+  if (hipMemset(h->ws.status, 0, sizeof(v)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return MOE_ERR_HIP;
+  *host_flags = v;
+  return MOE_OK;
+}
+
+extern "C" void moe_plan_destroy(moe_plan_t h) {
+  if (!h) return;
+  if (bind(h) == MOE_OK) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(h->ws_base);
+  }
+  delete h;
+}

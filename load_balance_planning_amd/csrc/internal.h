@@ -1,0 +1,67 @@
+// Internal declarations of the moe_plan HIP library (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_plan.h"
+
+namespace moe {
+
+// Limits of this build (checked by moe_plan_create).
+constexpr int kMaxE = 2048;
+constexpr int kMaxK = 32;
+constexpr int kMaxR = 256;
+constexpr int kMaxG = 64;
+constexpr int kMaxB = 1024;
+constexpr int kTile = 64;  // tokens per tile: one bit per token in a 64-bit presence mask
+
+// Everything a kernel needs to know about the layer, derived once at create time.
+struct Dims {
+  int32_t T, E, k, R, G, H, B;
+  int32_t M;        // domains
+  int32_t Tr;       // tokens per source rank
+  int32_t Er;       // experts per rank (main instances)
+  int32_t C;        // tiles per source rank
+  int32_t NT;       // tiles
+  int32_t cap;      // instance capacity E + B
+  int32_t n_slot;   // replica slots per rank
+  int32_t max_iters;
+  int64_t S, W;     // token bytes, expert bytes
+};
+
+// Device workspace owned by a handle.
+struct Workspace {
+  int32_t* status;      // [1]   MOE_STATUS_* bits
+  uint64_t* prev_mask;  // [NT][E] presence masks of the previous layer's top-k
+  int64_t* demand;      // [M][E] domain demand D (Eq. 4)
+  int32_t* einst_off;   // [E+1] per-expert instance lists (rank order) ...
+  int32_t* einst_list;  // [cap] ... instance ids
+  int32_t* qrep;        // [cap][R] quotas of instances of replicated experts
+  int32_t* colpre;      // [cap][R] exclusive prefix of qrep over sources
+};
+
+// Launchers (all asynchronous on `st`).
+hipError_t launch_route_topk(const Dims& d, const float* logits, const int32_t* prev_topk, int32_t* topk_idx,
+                             float* topk_val, uint64_t* tile_mask, uint64_t* prev_mask, int32_t* status,
+                             hipStream_t st);
+hipError_t launch_build_masks(const Dims& d, const int32_t* topk_idx, const int32_t* prev_topk,
+                              uint64_t* tile_mask, uint64_t* prev_mask, int32_t* status, hipStream_t st);
+hipError_t launch_scan(const Dims& d, const uint64_t* tile_mask, int32_t* tile_base, int32_t* omega,
+                       int32_t* count, hipStream_t st);
+hipError_t launch_pairs(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc,
+                        int32_t* trans, hipStream_t st);
+hipError_t launch_plan(const Dims& d, const int32_t* omega, const moe_plan_out& out, const Workspace& ws,
+                       hipStream_t st);
+hipError_t launch_assign(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
+                         const int32_t* tile_base, const moe_plan_out& out, const Workspace& ws, hipStream_t st);
+hipError_t launch_offsets(const Dims& d, const int32_t* n_inst, const int32_t* inst_rank, const int32_t* inst_load,
+                          int32_t* inst_offset, int32_t* rank_offset, int32_t* status, hipStream_t st);
+hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t* slot_rank,
+                         const int32_t* inst_offset, const uint16_t* hidden, int32_t* perm, int32_t* slot_pos,
+                         uint16_t* dispatch, int32_t* status, hipStream_t st);
+
+// LDS bytes the plan kernel needs for these dimensions.
+size_t plan_lds_bytes(const Dims& d);
+
+}  // namespace moe

@@ -1,0 +1,62 @@
+"""The C ABI library loads (no GPU needed) and exports every entry point include/*.h declares;
+the host-only size query follows the header's contract."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:int|void)\s+(moe_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_path():
+    assert set(declared_functions()) >= {"moe_plan_create", "moe_plan_route", "moe_plan_plan", "moe_plan_dispatch"}
+
+
+def test_library_exports_every_declared_symbol():
+    import load_balance_planning_amd as m
+    lib = m.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", m.lib_path()], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared_functions()) <= exported
+    assert set(m.EXPORTS) == set(declared_functions())
+
+
+def test_query_sizes_and_validation():
+    import load_balance_planning_amd as m
+    s = m.moe_plan_query(m.make_config(32768, 256, 8, 64, 8, 7168, 32))
+    assert (s.topk, s.omega, s.pair, s.tiles, s.inst_cap, s.quota) == (262144, 16384, 65536, 512, 288, 64 * 288)
+    assert s.dispatch_elems == 32768 * 8 * 7168 and s.n_slot == 1
+    assert s.token_bytes == 2 * 7168 and s.expert_bytes == 9 * 7168 * 7168 // 4
+    s = m.moe_plan_query(m.make_config(16384, 128, 8, 8, 4, 2048, 16))
+    assert s.n_slot == 2 and s.tiles == 8 * 32
+    s = m.moe_plan_query(m.make_config(800, 256, 8, 8, 8, 13, 4))   # 100 tokens per rank: 2 tiles each
+    assert s.tiles == 16
+    bad = [m.make_config(100, 8, 2, 3, 1, 16, 0),      # T % R
+           m.make_config(96, 9, 2, 3, 2, 16, 0),       # R % G
+           m.make_config(96, 8, 9, 4, 2, 16, 0),       # k > E
+           m.make_config(96, 8, 2, 4, 2, 0, 0),        # H
+           m.make_config(96, 8, 2, 4, 2, 16, -1)]      # B
+    for c in bad:
+        with pytest.raises(m.MoePlanError) as ei:
+            m.moe_plan_query(c)
+        assert ei.value.code == m.MOE_ERR_INVALID_ARG
+    for c in [m.make_config(1024, 4096, 2, 4, 2, 16, 0), m.make_config(1024, 64, 33, 4, 2, 16, 0),
+              m.make_config(1024, 512, 2, 512, 2, 16, 0)]:
+        with pytest.raises(m.MoePlanError) as ei:
+            m.moe_plan_query(c)
+        assert ei.value.code == m.MOE_ERR_UNSUPPORTED
