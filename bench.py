@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE dispatch-planning path on one MI355X.
+
+A step is one pass of the whole path -- moe_plan_route -> moe_plan_plan ->
+moe_plan_dispatch -- over every layer of the workload, inputs resident in
+HBM.  Prints ONE JSON line:
+  value       routed token-slots per second (T*k*L / step time)
+  roofline    the dominant kernel (the bf16 gather of moe_plan_dispatch):
+              algorithmic bytes per launch / its mean duration (HIP events on
+              the stream it runs on) against the 8 TB/s HBM peak
+  chain       the same for the whole step (algorithmic bytes of every call)
+  cpu_baseline  the CPU oracle on one core over a bounded sample
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "deepseek_v3_layer"
+GATHER_PMC = os.path.join(ROOT, "profiles", "gather_deepseek_v3_layer_pmc.txt")
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes each call must move per layer (the dense alternatives it avoids are not counted)."""
+    T, E, k, R, H, B = w.T, w.E, w.k, w.R, w.H, w.B
+    cap = E + B
+    tiles = R * ((T // R + 63) // 64)
+    route = (T * E * 4                 # logits read
+             + T * k * 4 * 2           # top-k indices and values written
+             + tiles * E * 8 * 2       # presence masks written, re-read by the scan
+             + tiles * E * 4           # tile prefix written
+             + (R * E + E) * 4         # routing matrix and expert counts
+             + E * E * 4 * (2 if w.L > 1 else 1))  # co-selection (+ transitions)
+    plan = (R * E * 4                  # routing matrix read
+            + R * cap * 4              # quotas written
+            + T * k * 4                # top-k re-read
+            + tiles * E * 12           # masks and prefix re-read
+            + T * k * 4 * 2)           # slot instance and in-instance rank written
+    dispatch = (T * H * 2              # hidden rows read once
+                + T * k * H * 2        # dispatch rows written
+                + T * k * 4 * 4)       # slot instance/rank read, slot position and permutation written
+    return dict(route=route, plan=plan, dispatch=dispatch, total=(route + plan + dispatch) * w.L)
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def gather_traffic(w):
+    """HBM bytes per gather launch from the committed rocprofv3 counter runs, if they still
+    describe the current kernel source (else None)."""
+    if w.name != DEFAULT_WORKLOAD or not os.path.exists(GATHER_PMC):
+        return None
+    text = open(GATHER_PMC).read()
+    m = re.search(r"source_sha256_16:\s*(\w+)", text)
+    src = os.path.join(ROOT, "load_balance_planning_amd", "csrc", "dispatch.hip")
+    if not m or m.group(1) != source_hash(src):
+        return None
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    return float(t.group(1)) if t else None
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle, single-threaded on one core, on whole layers of the workload until the
+    time budget is spent (at least one layer)."""
+    import oracle
+    orig = os.sched_getaffinity(0)
+    core = min(orig)
+    os.sched_setaffinity(0, {core})
+    try:
+        cfg = oracle.make_cfg(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
+        hidden = synth.hidden(w)
+        layers = synth.all_logits(w)
+        l = oracle.lib()
+        done, t0 = 0, time.perf_counter()
+        elapsed = 0.0
+        while True:
+            lg = layers[done % w.L]
+            t1 = time.perf_counter()
+            oracle.run_all(cfg, lg, hidden, l=l)
+            elapsed += time.perf_counter() - t1
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    finally:
+        os.sched_setaffinity(0, orig)
+    slots = w.T * w.k * done
+    return {"value": slots / elapsed, "unit": "token-slots/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full layer(s) of %s (route+plan+dispatch incl. the bf16 row copy), %.1f s on core %d"
+                      % (done, w.name, elapsed, core)}
+
+
+def run_gpu(w, steps: int, warmup: int) -> dict:
+    import torch
+    import load_balance_planning_amd as mp
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
+    hidden = torch.from_numpy(synth.hidden(w).view(np.int16)).to(dev)
+    logits = [torch.from_numpy(lg).to(dev) for lg in synth.all_logits(w)]
+    layers = [mp.Layer(cfg, device=dev, cooc=True, trans=(l > 0)) for l in range(w.L)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        for l, layer in enumerate(layers):
+            prev = layers[l - 1].route_out.topk_idx if l > 0 else None
+            if ev is not None:
+                ev[l][0].record(stream)
+            layer.route(logits[l], prev)
+            if ev is not None:
+                ev[l][1].record(stream)
+            layer.plan()
+            if ev is not None:
+                ev[l][2].record(stream)
+            layer.dispatch(hidden)
+            if ev is not None:
+                ev[l][3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    for layer in layers:
+        if layer.status() != 0:
+            raise RuntimeError("device status word set during warm-up")
+    # Timed region: exactly `steps` steps, synchronised on both sides.
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    # Per-call durations from events around each call, in a second timed pass of the same steps.
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(w.L)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    per = {"route": [], "plan": [], "dispatch": []}
+    for s in range(steps):
+        for l in range(w.L):
+            e = evs[s][l]
+            per["route"].append(e[0].elapsed_time(e[1]))
+            per["plan"].append(e[1].elapsed_time(e[2]))
+            per["dispatch"].append(e[2].elapsed_time(e[3]))
+    status = [layer.status() for layer in layers]
+    for layer in layers:
+        layer.close()
+    return dict(ms_total=ms_total, per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
+                per_call_ms_min={k: float(np.min(v)) for k, v in per.items()}, status=status,
+                device=torch.cuda.get_device_name(dev))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=synth.WORKLOAD_ORDER)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the planning path runs its logical EP ranks on a single device. "
+              "Run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    w = synth.WORKLOADS[args.workload]
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
+    g = run_gpu(w, args.steps, args.warmup)
+    ms_per_step = g["ms_total"] / args.steps
+    slots = w.T * w.k * w.L
+    value = slots / (ms_per_step / 1e3)
+    ab = algorithmic_bytes(w)
+    disp_ms = g["per_call_ms"]["dispatch"]
+    achieved = ab["dispatch"] / (disp_ms / 1e3) / 1e9
+    traffic = gather_traffic(w)
+    chain_gbs = ab["total"] / (ms_per_step / 1e3) / 1e9
+    out = {
+        "metric": "routed token-slots/sec for route+plan+dispatch; gather HBM GB/s vs peak",
+        "value": value, "unit": "token-slots/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "R": w.R, "G": w.G, "H": w.H,
+                   "replica_budget": w.B, "layers": w.L, "zipf_s": w.zipf_s, "beta": w.beta,
+                   "couple_p": w.couple_p, "seed": w.seed},
+        "roofline": {"bound": "hbm", "kernel": "gather (moe_plan_dispatch)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": ab["dispatch"],
+                     "launch_ms": disp_ms},
+        "chain": {"algorithmic_bytes_per_step": ab["total"], "achieved": chain_gbs, "peak": HBM_PEAK_GBS,
+                  "unit": "GB/s", "frac": chain_gbs / HBM_PEAK_GBS},
+        "per_call_us": {k: v * 1e3 for k, v in g["per_call_ms"].items()},
+        "per_call_us_min": {k: v * 1e3 for k, v in g["per_call_ms_min"].items()},
+        "cpu_baseline": cpu,
+        "device": g["device"],
+    }
+    if any(g["status"]):
+        out["status_flags"] = g["status"]
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
