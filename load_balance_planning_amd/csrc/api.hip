@@ -21,7 +21,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t status, prev_mask, demand, einst_off, einst_list, qrep, colpre, total;
+  size_t status, prev_mask, demand, einst_off, einst_list, rlist, colpre, total;
 };
 
 WsLayout ws_layout(const moe::Dims& d) {
@@ -30,10 +30,10 @@ WsLayout ws_layout(const moe::Dims& d) {
   auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes > 0 ? bytes : 1); return at; };
   l.status = take(sizeof(int32_t));
   l.prev_mask = take(sizeof(uint64_t) * (size_t)d.NT * d.E);
-  l.demand = take(sizeof(int64_t) * (size_t)d.M * d.E);
+  l.demand = take(sizeof(int32_t) * (size_t)d.M * d.E);
   l.einst_off = take(sizeof(int32_t) * (size_t)(d.E + 1));
   l.einst_list = take(sizeof(int32_t) * (size_t)d.cap);
-  l.qrep = take(sizeof(int32_t) * (size_t)d.cap * d.R);
+  l.rlist = take(sizeof(int32_t) * (size_t)(d.E + 1));
   l.colpre = take(sizeof(int32_t) * (size_t)d.cap * d.R);
   l.total = o;
   return l;
@@ -66,7 +66,7 @@ int derive(const moe_plan_config* c, moe::Dims* d) {
   x.S = c->token_bytes > 0 ? c->token_bytes : 2LL * c->H;
   x.W = c->expert_bytes >= 0 ? c->expert_bytes : 9LL * c->H * c->H / 4;
   if (x.Er + x.n_slot > 1024) return MOE_ERR_UNSUPPORTED;
-  if (moe::plan_lds_bytes(x) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+  if (moe::plan_lds_bytes(x) > kMaxLds || moe::scan_lds_bytes(x) > kMaxLds) return MOE_ERR_UNSUPPORTED;
   *d = x;
   return MOE_OK;
 }
@@ -123,10 +123,10 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   char* b = static_cast<char*>(h->ws_base);
   h->ws.status = reinterpret_cast<int32_t*>(b + l.status);
   h->ws.prev_mask = reinterpret_cast<uint64_t*>(b + l.prev_mask);
-  h->ws.demand = reinterpret_cast<int64_t*>(b + l.demand);
+  h->ws.demand = reinterpret_cast<int32_t*>(b + l.demand);
   h->ws.einst_off = reinterpret_cast<int32_t*>(b + l.einst_off);
   h->ws.einst_list = reinterpret_cast<int32_t*>(b + l.einst_list);
-  h->ws.qrep = reinterpret_cast<int32_t*>(b + l.qrep);
+  h->ws.rlist = reinterpret_cast<int32_t*>(b + l.rlist);
   h->ws.colpre = reinterpret_cast<int32_t*>(b + l.colpre);
   if (hipMemset(h->ws_base, 0, l.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->ws_base);

@@ -9,7 +9,8 @@
 // The copy is source-ordered: each hidden row is read from HBM once and
 // written to its k dispatch rows, so HBM traffic is T*H*2 bytes read plus
 // T*k*H*2 bytes written -- a destination-ordered gather would read each row
-// k times.  Stores are non-temporal: the dispatch buffer is not re-read here.
+// k times (and measured slower on MI355X).  Plain stores: on MI355X they beat
+// non-temporal ones for this write pattern.
 #include "internal.h"
 
 namespace moe {
@@ -116,12 +117,7 @@ __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* 
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
         const int c = base + tid + u * 256;
-        if (c < vpr) {
-          __builtin_nontemporal_store(v[u].x, &dst[c].x);
-          __builtin_nontemporal_store(v[u].y, &dst[c].y);
-          __builtin_nontemporal_store(v[u].z, &dst[c].z);
-          __builtin_nontemporal_store(v[u].w, &dst[c].w);
-        }
+        if (c < vpr) dst[c] = v[u];
       }
     }
   }

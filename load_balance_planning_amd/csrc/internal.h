@@ -34,11 +34,11 @@ struct Dims {
 struct Workspace {
   int32_t* status;      // [1]   MOE_STATUS_* bits
   uint64_t* prev_mask;  // [NT][E] presence masks of the previous layer's top-k
-  int64_t* demand;      // [M][E] domain demand D (Eq. 4)
+  int32_t* demand;      // [M][E] domain demand D (Eq. 4) when it does not fit in LDS
   int32_t* einst_off;   // [E+1] per-expert instance lists (rank order) ...
   int32_t* einst_list;  // [cap] ... instance ids
-  int32_t* qrep;        // [cap][R] quotas of instances of replicated experts
-  int32_t* colpre;      // [cap][R] exclusive prefix of qrep over sources
+  int32_t* rlist;       // [E+1] experts with more than one instance; entry E is their count
+  int32_t* colpre;      // [cap][R] exclusive prefix of each instance's quotas over sources
 };
 
 // Launchers (all asynchronous on `st`).
@@ -61,7 +61,8 @@ hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t*
                          const int32_t* inst_offset, const uint16_t* hidden, int32_t* perm, int32_t* slot_pos,
                          uint16_t* dispatch, int32_t* status, hipStream_t st);
 
-// LDS bytes the plan kernel needs for these dimensions.
+// LDS bytes the plan and scan kernels need for these dimensions.
 size_t plan_lds_bytes(const Dims& d);
+size_t scan_lds_bytes(const Dims& d);
 
 }  // namespace moe

@@ -1,26 +1,41 @@
 // Replica placement, token re-routing, quotas and per-slot instances on gfx950.
 //
 // [TopoEP] section 4.3 (two-stage solver, Eqs. 9 and 10) with the quota and
-// slot rules documented in moe_plan.h.  The solver runs in one workgroup of
-// 16 waves with its whole state in LDS: the domains are independent in both
-// stages, so wave w plans domains w, w+16, ...; each stage-2 iteration is a
-// wave-wide argmin over packed candidate keys followed by one update, the
-// one-update-per-iteration rule of the page.  All arithmetic is integer and
-// every selection has a total order, so the plan is bitwise reproducible.
+// slot rules documented in moe_plan.h.  Three kernels:
+//   plan_kernel    one workgroup of 16 waves holding the solver state in LDS.
+//                  The domains are independent in both stages, so wave w plans
+//                  domains w, w+16, ...; each refinement iteration is a
+//                  wave-wide argmin over packed candidate keys followed by one
+//                  update -- the page's one-update-per-iteration rule.
+//   quota_kernel   one workgroup per replicated expert computes its three-pass
+//                  transport in closed form (interval overlaps of cumulative
+//                  demand and capacity); the other workgroups copy the routing
+//                  matrix into the quota columns of single-instance experts.
+//   assign_kernel  one thread per slot: stable rank inside its (source,
+//                  expert) pair from the tile masks, then instance and position.
+// All arithmetic is integer and every selection has a total order, so the plan
+// is bitwise reproducible.
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kTransportWaves = 8;  // waves with LDS scratch for the per-expert quota transport
+// Dynamic LDS of the plan kernel; the solver helpers index it by the offsets
+// of PlanLayout so that every access compiles to an LDS instruction.
+extern __shared__ int32_t plan_lds[];
 
-// Offsets (in int32 units) of the plan kernel's LDS arrays.
+constexpr int kPlanThreads = 512;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kDemandLdsMax = 16384;  // M*E int32 entries kept in LDS when they fit
+constexpr int kQuotaThreads = 256;     // >= kMaxR: one source (and one instance) per thread
+constexpr int kFillCells = 1024;       // quota cells per fill workgroup
+constexpr size_t kPlanLdsBudget = 160 * 1024;
+
+// Offsets (int32 units) of the plan kernel's LDS arrays.
 struct PlanLayout {
-  int L, nrep, inst_base, rep_dom, base_d, Umain, ereps, eoff, rlist, misc;
-  int rep_e, rep_r, rep_U, rep_inst, inst_e, inst_r, inst_u, wave_tot, scratch;
-  int scratch_per_wave;
+  int L, nrep, inst_base, rep_dom, Umain, eoff, rl, misc, hm, rep_e, rep_U, rep_id, wave_tot, D;
+  int RW;     // 64-bit words per host mask (ranks / 64, rounded up)
+  int NS;     // replica slots per rank held in LDS
   int total;
 };
 
@@ -30,39 +45,69 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-  lo = __shfl_xor(lo, m);
-  hi = __shfl_xor(hi, m);
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
   return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// Lexicographic minimum of (hi, lo) over the wave.
-__device__ __forceinline__ void wave_min_key(uint64_t& hi, uint32_t& lo) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint64_t oh = shfl_xor_u64(hi, m);
-    const uint32_t ol = (uint32_t)__shfl_xor((int)lo, m);
-    if (oh < hi || (oh == hi && ol < lo)) {
-      hi = oh;
-      lo = ol;
-    }
+// Maximum over the wave, returned in every lane.  Inside each 16-lane row a
+// DPP butterfly (quad swaps, half-row and row mirrors); the four row results
+// are then read out with readlane.  All 64 lanes must be active.
+__device__ __forceinline__ uint64_t wave_allmax_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(v); v = o > v ? o : v;
+  o = dpp_u64<0x4E>(v); v = o > v ? o : v;
+  o = dpp_u64<0x141>(v); v = o > v ? o : v;
+  o = dpp_u64<0x140>(v); v = o > v ? o : v;
+  uint64_t r = readlane_u64(v, 0);
+  o = readlane_u64(v, 16); r = o > r ? o : r;
+  o = readlane_u64(v, 32); r = o > r ? o : r;
+  o = readlane_u64(v, 48); r = o > r ? o : r;
+  return r;
+}
+
+// Lexicographic minimum of (hi, lo) over the wave, in every lane (branch-free).
+__device__ __forceinline__ void wave_allmin_key(uint64_t& hi, uint32_t& lo) {
+#define MOE_MIN_STEP(CTRL)                                              \
+  {                                                                     \
+    const uint64_t oh = dpp_u64<CTRL>(hi);                              \
+    const uint32_t ol = dpp_u32<CTRL>(lo);                              \
+    const bool take = (oh < hi) | ((oh == hi) & (ol < lo));             \
+    hi = take ? oh : hi;                                                \
+    lo = take ? ol : lo;                                                \
   }
+  MOE_MIN_STEP(0xB1)
+  MOE_MIN_STEP(0x4E)
+  MOE_MIN_STEP(0x141)
+  MOE_MIN_STEP(0x140)
+#undef MOE_MIN_STEP
+  uint64_t rh = readlane_u64(hi, 0);
+  uint32_t rl = (uint32_t)__builtin_amdgcn_readlane((int)lo, 0);
+#pragma unroll
+  for (int row = 1; row < 4; ++row) {
+    const uint64_t oh = readlane_u64(hi, row * 16);
+    const uint32_t ol = (uint32_t)__builtin_amdgcn_readlane((int)lo, row * 16);
+    const bool take = (oh < rh) | ((oh == rh) & (ol < rl));
+    rh = take ? oh : rh;
+    rl = take ? ol : rl;
+  }
+  hi = rh;
+  lo = rl;
 }
 
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int t = __shfl_up(v, off);
@@ -71,8 +116,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// In-place exclusive scan of a[0..n) in LDS by the whole workgroup; returns the total.
-// wave_tot: kPlanWaves + 1 ints of LDS.
+// In-place exclusive scan of a[0..n) in LDS by the whole plan workgroup; returns the total.
 __device__ int block_excl_scan(int* a, int n, int* wave_tot) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __syncthreads();
@@ -104,420 +148,568 @@ __device__ int block_excl_scan(int* a, int n, int* wave_tot) {
   return total;
 }
 
-__device__ __forceinline__ int64_t overlap(int64_t a0, int64_t a1, int64_t b0, int64_t b1) {
-  const int64_t lo = a0 > b0 ? a0 : b0, hi = a1 < b1 ? a1 : b1;
+__device__ __forceinline__ int overlap(int a0, int a1, int b0, int b1) {
+  const int lo = a0 > b0 ? a0 : b0, hi = a1 < b1 ? a1 : b1;
   return hi > lo ? hi - lo : 0;
 }
 
-__device__ __forceinline__ int domain_budget(const Dims& d, int m) {
+__device__ __forceinline__ int domain_budget(Dims d, int m) {
   return d.B / d.M + (m < d.B % d.M ? 1 : 0);
 }
 
+
+// Stage 1 of one domain with the candidate keys in registers: lane l holds
+// the keys of experts l, l+64, ... (at most 64*KMAX experts).
+template <int KMAX>
+__device__ __noinline__ void stage1_domain(Dims d, PlanLayout ly, int m, const int32_t* Dglobal) {
+  int32_t* nrep = plan_lds + ly.nrep;
+  int32_t* rep_e = plan_lds + ly.rep_e;
+  int32_t* rep_U = plan_lds + ly.rep_U;
+  int32_t* rep_dom = plan_lds + ly.rep_dom;
+  unsigned long long* hm = reinterpret_cast<unsigned long long*>(plan_lds + ly.hm);
+  const int RW = ly.RW, NS = ly.NS;
+  const int lane = threadIdx.x & 63;
+  const int E = d.E, G = d.G, Er = d.Er;
+  const int Bd = domain_budget(d, m);
+  uint64_t key[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = 0ull;
+    if (e < E) {
+      const int rm = e / Er;
+      const int64_t Dv = ly.D >= 0 ? plan_lds[ly.D + m * E + e] : Dglobal[m * E + e];
+      // Remote experts with positive benefit (Eq. 9); S > 0, so larger benefit
+      // is larger demand; ties to the lower expert.
+      if (rm / G != m && 2 * Dv * d.S - d.W > 0) key[i] = ((uint64_t)Dv << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+    }
+  }
+  int my_nrep = 0, placed = 0;
+  while (placed < Bd) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < KMAX; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_allmax_u64(best);
+    if (best == 0ull) break;
+    const int ebest = (int)(0xffffffffu - (uint32_t)best);
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) key[i] = key[i] == best ? 0ull : key[i];
+    // Least-occupied rank with a free slot, ties to the lower rank.
+    uint64_t rk = (lane < G && my_nrep < d.n_slot) ? ((uint64_t)(uint32_t)my_nrep << 32) | (uint32_t)lane : ~0ull;
+    uint32_t unused = 0;
+    wave_allmin_key(rk, unused);
+    if (rk == ~0ull) break;
+    if (lane == (int)(uint32_t)rk) {
+      const int r = m * G + lane;
+      rep_e[r * NS + my_nrep] = ebest;
+      rep_U[r * NS + my_nrep] = 0;
+      atomicOr(&hm[ebest * RW + (r >> 6)], 1ull << (r & 63));
+      my_nrep += 1;
+    }
+    placed += 1;
+  }
+  if (lane < G) nrep[m * G + lane] = my_nrep;
+  if (lane == 0) rep_dom[m] = placed;
+}
+
+// Max over aligned groups of GS lanes (GS <= 16) with DPP, in every lane.
+template <int GS>
+__device__ __forceinline__ uint64_t group_allmax_u64(uint64_t v) {
+  uint64_t o;
+  if (GS >= 2) { o = dpp_u64<0xB1>(v); v = o > v ? o : v; }
+  if (GS >= 4) { o = dpp_u64<0x4E>(v); v = o > v ? o : v; }
+  if (GS >= 8) { o = dpp_u64<0x141>(v); v = o > v ? o : v; }
+  if (GS >= 16) { o = dpp_u64<0x140>(v); v = o > v ? o : v; }
+  return v;
+}
+
+// Stage 2 of one domain for G <= GS <= 16.  The wave is 64/GS groups of GS
+// lanes; lane (g, t) stands for rank r0 + t of the domain and every group
+// keeps the same copy of the rank loads, so the busiest rank comes out of a
+// DPP max inside the group.  Lane (g, t) then evaluates the moves of hosted
+// entries c = g, g + 64/GS, ... of the busiest rank to target t: all
+// candidates of an iteration are evaluated at once and one wave-wide argmin
+// picks the move.  The winning key also carries the entry index, so the
+// update needs no search.
+template <int GS>
+__device__ __noinline__ void stage2_grouped(Dims d, PlanLayout ly, int m) {
+  constexpr int NG = 64 / GS;
+  int32_t* L = plan_lds + ly.L;
+  int32_t* nrep = plan_lds + ly.nrep;
+  int32_t* Umain = plan_lds + ly.Umain;
+  int32_t* rep_e = plan_lds + ly.rep_e;
+  int32_t* rep_U = plan_lds + ly.rep_U;
+  int32_t* rep_dom = plan_lds + ly.rep_dom;
+  unsigned long long* hm = reinterpret_cast<unsigned long long*>(plan_lds + ly.hm);
+  const int RW = ly.RW, NS = ly.NS;
+  const int lane = threadIdx.x & 63;
+  const int t = lane % GS, g = lane / GS;
+  const int G = d.G, Er = d.Er, E = d.E;
+  const int Bd = domain_budget(d, m);
+  const int r0 = m * G;
+  const bool in_dom = t < G;
+  const int r = r0 + (in_dom ? t : 0);
+  int Lr = in_dom ? L[r] : 0;
+  int nr = in_dom ? nrep[r] : 0;
+  int repdom = rep_dom[m];
+  const int hw = r >> 6;
+  const uint64_t hbit = 1ull << (r & 63);
+  for (int it = 0; it < d.max_iters; ++it) {
+    const uint64_t kb = group_allmax_u64<GS>(in_dom ? ((uint64_t)(uint32_t)Lr << 32) |
+                                                        (uint64_t)(0xffffffffu - (uint32_t)t) : 0ull);
+    const int lb = __builtin_amdgcn_readfirstlane((int)(0xffffffffu - (uint32_t)kb));
+    const int rb = r0 + lb;
+    const int Lb = __builtin_amdgcn_readfirstlane((int)(kb >> 32));
+    const int nh = Er + __builtin_amdgcn_readlane(nr, lb);
+    const int half = (Lb - Lr) >> 1;
+    const bool cand = in_dom && t != lb;
+    const bool can_add = nr < d.n_slot && repdom < Bd;
+    uint64_t best_hi = ~0ull;
+    uint32_t best_lo = ~0u;
+    for (int c = g; c < nh; c += NG) {
+      const bool is_main = c < Er;
+      const int jr = rb * NS + (is_main ? 0 : c - Er);
+      const int em = rb * Er + (is_main ? c : 0);
+      const int er = rep_e[jr];
+      const int Ur = rep_U[jr];
+      const int Um = Umain[em];
+      const int e = is_main ? em : er;
+      const int Ub = is_main ? Um : Ur;
+      const bool hosted = (hm[(e < E ? e : 0) * RW + hw] & hbit) != 0ull;
+      const int delta = Ub < half ? Ub : half;
+      const bool ok = cand & (Ub > 0) & (hosted | can_add) & (delta >= 1);
+      // Key: largest delta, lowest target load, existing instance first, lower e, lower r_t.
+      const uint64_t hi = ok ? ((uint64_t)(uint32_t)(0x7fffffff - delta) << 32) | (uint64_t)(uint32_t)Lr : ~0ull;
+      const uint32_t lo = ((uint32_t)(hosted ? 0 : 1) << 31) | ((uint32_t)e << 20) | ((uint32_t)r << 12) | (uint32_t)c;
+      const bool take = (hi < best_hi) | ((hi == best_hi) & (lo < best_lo));
+      best_hi = take ? hi : best_hi;
+      best_lo = take ? lo : best_lo;
+    }
+    wave_allmin_key(best_hi, best_lo);
+    if (best_hi == ~0ull) break;
+    const int delta = 0x7fffffff - (int)(uint32_t)(best_hi >> 32);
+    const bool is_new = (best_lo >> 31) != 0u;
+    const int e = (int)((best_lo >> 20) & 0x7ffu);
+    const int rt = (int)((best_lo >> 12) & 0xffu);
+    const int cb = (int)(best_lo & 0xfffu);
+    const int lt = rt - r0;
+    const int nrt = __builtin_amdgcn_readlane(nr, lt);
+    const bool main_t = e >= rt * Er && e < rt * Er + Er;
+    if (lane == 0) {
+      if (cb < Er) Umain[e] -= delta;
+      else rep_U[rb * NS + (cb - Er)] -= delta;
+      if (is_new) {
+        rep_e[rt * NS + nrt] = e;
+        rep_U[rt * NS + nrt] = delta;
+        nrep[rt] = nrt + 1;
+        atomicOr(&hm[e * RW + (rt >> 6)], 1ull << (rt & 63));
+      } else if (main_t) {
+        Umain[e] += delta;
+      }
+    }
+    if (!is_new && !main_t && lane < nrt && rep_e[rt * NS + lane] == e) rep_U[rt * NS + lane] += delta;
+    Lr += (in_dom && t == lt) ? delta : 0;
+    Lr -= (in_dom && t == lb) ? delta : 0;
+    nr += (in_dom && t == lt && is_new) ? 1 : 0;
+    repdom += is_new ? 1 : 0;
+    wave_sync();
+  }
+  if (g == 0 && in_dom) { L[r] = Lr; nrep[r] = nr; }
+  if (lane == 0) rep_dom[m] = repdom;
+}
+
+// Solver state in LDS:
+//   hm[e][w]        64-bit words of the set of ranks hosting an instance of e
+//   rep_e/rep_U[r][j] expert and load of replica slot j < nrep[r] of rank r
+//   Umain[e]        load of e's main instance;  L[r] rank loads
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout ly, const int32_t* __restrict__ omega,
                                                             moe_plan_out out, Workspace ws) {
-  extern __shared__ int32_t lds[];
+  int32_t* lds = plan_lds;
   int32_t* L = lds + ly.L;
   int32_t* nrep = lds + ly.nrep;
   int32_t* inst_base = lds + ly.inst_base;
   int32_t* rep_dom = lds + ly.rep_dom;
-  int32_t* base_d = lds + ly.base_d;
   int32_t* Umain = lds + ly.Umain;
-  int32_t* ereps = lds + ly.ereps;
   int32_t* eoff = lds + ly.eoff;
-  int32_t* rlist = lds + ly.rlist;
-  int32_t* misc = lds + ly.misc;  // [0] n_inst, [1] replicated experts, [2] check flag
+  int32_t* rl = lds + ly.rl;
+  int32_t* misc = lds + ly.misc;  // [1] experts replicated in stage 1, [2] replicated at the end
+  unsigned long long* hm = reinterpret_cast<unsigned long long*>(lds + ly.hm);
   int32_t* rep_e = lds + ly.rep_e;
-  int32_t* rep_r = lds + ly.rep_r;
   int32_t* rep_U = lds + ly.rep_U;
-  int32_t* rep_inst = lds + ly.rep_inst;
-  int32_t* inst_e = lds + ly.inst_e;
-  int32_t* inst_r = lds + ly.inst_r;
-  int32_t* inst_u = lds + ly.inst_u;
+  int32_t* rep_id = lds + ly.rep_id;
   int32_t* wave_tot = lds + ly.wave_tot;
+  int32_t* D = ly.D >= 0 ? lds + ly.D : ws.demand;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int E = d.E, R = d.R, G = d.G, M = d.M, Er = d.Er;
+  const int E = d.E, R = d.R, G = d.G, M = d.M, Er = d.Er, RW = ly.RW, NS = ly.NS;
+  auto host_bit = [&](int e, int r) -> bool { return (hm[e * RW + (r >> 6)] >> (r & 63)) & 1ull; };
+  // Slot of expert e among the replicas of rank r (-1 if none).
+  auto rep_slot = [&](int r, int e) -> int {
+    for (int j = 0; j < nrep[r]; ++j)
+      if (rep_e[r * NS + j] == e) return j;
+    return -1;
+  };
 
-  // ---- init ---------------------------------------------------------------
-  for (int e = tid; e < E; e += kPlanThreads) { Umain[e] = 0; ereps[e] = 0; }
-  for (int r = tid; r < R; r += kPlanThreads) nrep[r] = 0;
-  for (int m = tid; m < M; m += kPlanThreads) rep_dom[m] = 0;
-  if (tid == 0) {
-    int run = 0;
-    for (int m = 0; m < M; ++m) { base_d[m] = run; run += domain_budget(d, m); }
-    base_d[M] = run;
-    misc[0] = 0; misc[1] = 0; misc[2] = 0;
-  }
-  // Domain demand D[m][e] (Eq. 4), int64 in the workspace.
+  // ---- domain demand D[m][e] (Eq. 4), expert loads, main placement (C5) ----
   for (int idx = tid; idx < M * E; idx += kPlanThreads) {
     const int m = idx / E, e = idx - m * E;
-    int64_t sum = 0;
-    for (int g = 0; g < G; ++g) sum += omega[(int64_t)(m * G + g) * E + e];
-    ws.demand[idx] = sum;
+    const int32_t* o = omega + (int64_t)m * G * E + e;
+    int sum = 0;
+#pragma unroll 8
+    for (int g = 0; g < G; ++g) sum += o[(int64_t)g * E];
+    D[idx] = sum;
   }
+  for (int q = tid; q < E * RW; q += kPlanThreads) {
+    const int e = q / RW, w = q - e * RW;
+    const int rm = e / Er;
+    hm[q] = (rm >> 6) == w ? (1ull << (rm & 63)) : 0ull;
+  }
+  for (int r = tid; r < R; r += kPlanThreads) nrep[r] = 0;
+  if (tid == 0) { misc[0] = 0; misc[1] = 0; misc[2] = 0; misc[3] = 0; }
   __syncthreads();
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int cnt = 0;
+    for (int m = 0; m < M; ++m) cnt += D[m * E + e];
+    Umain[e] = cnt;  // every assignment on the main instance until replicas exist
+  }
 
   // ---- stage 1: inter-node placement (Eq. 9), one wave per domain ----------
   for (int m = wave; m < M; m += kPlanWaves) {
-    const int Bd = base_d[m + 1] - base_d[m];
-    uint32_t taken = 0;  // bit i: expert lane + 64 i already placed in this domain
-    while (rep_dom[m] < Bd) {
-      uint64_t best = 0ull;
-      for (int i = 0, e = lane; e < E; ++i, e += 64) {
-        if ((taken >> i) & 1u) continue;
-        if ((e / Er) / G == m) continue;
-        const int64_t D = ws.demand[(int64_t)m * E + e];
-        if (2 * D * d.S - d.W <= 0) continue;
-        // Largest benefit first; S > 0 so that is the largest demand; ties to the lower expert.
-        const uint64_t key = ((uint64_t)D << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
-        best = key > best ? key : best;
-      }
-      best = wave_max_u64(best);
-      if (best == 0ull) break;
-      const int ebest = (int)(0xffffffffu - (uint32_t)best);
-      if ((ebest & 63) == lane) taken |= 1u << (ebest >> 6);
-      int stop = 0;
-      if (lane == 0) {
-        int rbest = -1;  // least-occupied rank with a free slot, ties to the lower rank
-        for (int r = m * G; r < (m + 1) * G; ++r)
-          if (nrep[r] < d.n_slot && (rbest < 0 || nrep[r] < nrep[rbest])) rbest = r;
-        if (rbest < 0) {
-          stop = 1;
-        } else {
-          const int j = base_d[m] + rep_dom[m];
-          rep_e[j] = ebest; rep_r[j] = rbest; rep_U[j] = 0;
-          nrep[rbest] += 1;
-          rep_dom[m] += 1;
-          atomicAdd(&ereps[ebest], 1);
-        }
-      }
-      stop = __shfl(stop, 0);
-      wave_sync();
-      if (stop) break;
-    }
+    if (E <= 64 * 2) stage1_domain<2>(d, ly, m, ws.demand);
+    else if (E <= 64 * 4) stage1_domain<4>(d, ly, m, ws.demand);
+    else if (E <= 64 * 16) stage1_domain<16>(d, ly, m, ws.demand);
+    else stage1_domain<32>(d, ly, m, ws.demand);
   }
   __syncthreads();
 
-  // ---- stage-1 routing: even split over the selected instances -------------
-  for (int idx = tid; idx < R * E; idx += kPlanThreads) {
-    const int s = idx / E, e = idx - s * E;
-    const int w = omega[idx];
+  // ---- stage-1 routing --------------------------------------------------------
+  // Experts without replicas keep every assignment on the main instance.
+  // Replicated experts are routed per source: to the instance in the source's
+  // domain if there is one (at most one after stage 1), else split evenly over
+  // all instances in rank order.
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int n = 0;
+    for (int w = 0; w < RW; ++w) n += __popcll(hm[e * RW + w]);
+    if (n > 1) {
+      rl[atomicAdd(&misc[1], 1)] = e;
+      Umain[e] = 0;
+    }
+  }
+  __syncthreads();
+  const int nr1 = misc[1];
+  for (int idx = tid; idx < nr1 * R; idx += kPlanThreads) {
+    const int q = idx / R, s = idx - q * R;
+    const int e = rl[q];
+    const int w = omega[(int64_t)s * E + e];
     if (w == 0) continue;
-    const int ms = s / G, mm = (e / Er) / G;
-    if (ereps[e] == 0 || mm == ms) {
-      atomicAdd(&Umain[e], w);
-      continue;
-    }
+    const int ms = s / G, rm = e / Er;
     int local = -1;
-    for (int j = base_d[ms]; j < base_d[ms] + rep_dom[ms]; ++j)
-      if (rep_e[j] == e) local = j;
+    for (int r = ms * G; r < (ms + 1) * G; ++r)
+      if (host_bit(e, r)) { local = r; break; }
     if (local >= 0) {
-      atomicAdd(&rep_U[local], w);
+      if (local == rm) {
+        atomicAdd(&Umain[e], w);
+      } else {
+        const int j = rep_slot(local, e);
+        if (j >= 0) atomicAdd(&rep_U[local * NS + j], w);
+      }
       continue;
     }
-    // No instance in the source's domain: all instances of e, in rank order.
-    // After stage 1 each domain holds at most one instance of e and the
-    // domains are rank-ordered, so walking the domains visits them in order.
-    const int n = 1 + ereps[e];
+    int n = 0;
+    for (int ww = 0; ww < RW; ++ww) n += __popcll(hm[e * RW + ww]);
     int pos = 0;
-    for (int m = 0; m < M; ++m) {
-      int target = -2;
-      if (m == mm) {
-        target = -1;
-      } else {
-        for (int j = base_d[m]; j < base_d[m] + rep_dom[m]; ++j)
-          if (rep_e[j] == e) target = j;
+    for (int ww = 0; ww < RW; ++ww) {
+      unsigned long long bits = hm[e * RW + ww];
+      while (bits) {
+        const int r = ww * 64 + __ffsll((long long)bits) - 1;
+        bits &= bits - 1;
+        const int share = w / n + (pos < w % n ? 1 : 0);
+        ++pos;
+        if (share == 0) continue;
+        if (r == rm) {
+          atomicAdd(&Umain[e], share);
+        } else {
+          const int j = rep_slot(r, e);
+          if (j >= 0) atomicAdd(&rep_U[r * NS + j], share);
+        }
       }
-      if (target == -2) continue;
-      const int share = w / n + (pos < w % n ? 1 : 0);
-      ++pos;
-      if (share == 0) continue;
-      if (target == -1) atomicAdd(&Umain[e], share);
-      else atomicAdd(&rep_U[target], share);
     }
   }
   __syncthreads();
   for (int r = tid; r < R; r += kPlanThreads) {
     int sum = 0;
     for (int h = 0; h < Er; ++h) sum += Umain[r * Er + h];
-    const int m = r / G;
-    for (int j = base_d[m]; j < base_d[m] + rep_dom[m]; ++j)
-      if (rep_r[j] == r) sum += rep_U[j];
+    for (int j = 0; j < nrep[r]; ++j) sum += rep_U[r * NS + j];
     L[r] = sum;
   }
   __syncthreads();
 
   // ---- stage 2: intra-node refinement (Eq. 10), one wave per domain --------
+  // Lane l < G is rank r = m*G + l: it holds L_r and its replica count in
+  // registers, evaluates itself as the target of every expert hosted on the
+  // busiest rank, and applies its own side of the chosen move.
+  const bool grouped = G <= 16;
+  if (grouped) {
+    for (int m = wave; m < M; m += kPlanWaves) {
+      if (G <= 2) stage2_grouped<2>(d, ly, m);
+      else if (G <= 4) stage2_grouped<4>(d, ly, m);
+      else if (G <= 8) stage2_grouped<8>(d, ly, m);
+      else stage2_grouped<16>(d, ly, m);
+    }
+  } else
   for (int m = wave; m < M; m += kPlanWaves) {
-    const int Bd = base_d[m + 1] - base_d[m];
-    const int bj = base_d[m];
+    const int Bd = domain_budget(d, m);
     const int r0 = m * G;
+    const bool in_dom = lane < G;
+    const int r = r0 + (in_dom ? lane : 0);
+    int Lr = in_dom ? L[r] : 0;
+    int nr = in_dom ? nrep[r] : 0;
+    int repdom = rep_dom[m];
     for (int it = 0; it < d.max_iters; ++it) {
-      uint64_t kb = 0ull;
-      if (lane < G) kb = ((uint64_t)(uint32_t)L[r0 + lane] << 32) | (uint64_t)(0xffffffffu - (uint32_t)lane);
-      kb = wave_max_u64(kb);
-      const int rb = r0 + (int)(0xffffffffu - (uint32_t)kb);
+      const uint64_t kb = wave_allmax_u64(in_dom ? ((uint64_t)(uint32_t)Lr << 32) |
+                                                     (uint64_t)(0xffffffffu - (uint32_t)lane) : 0ull);
+      const int lb = (int)(0xffffffffu - (uint32_t)kb);
+      const int rb = r0 + lb;
       const int Lb = (int)(kb >> 32);
-      const int nh = Er + rep_dom[m];
+      const int nh = Er + __builtin_amdgcn_readlane(nr, lb);
       uint64_t best_hi = ~0ull;
       uint32_t best_lo = ~0u;
-      for (int cidx = lane; cidx < nh * G; cidx += 64) {
-        const int h = cidx / G, rt = r0 + (cidx - h * G);
-        if (rt == rb) continue;
-        int e, Ub;
-        if (h < Er) {
-          e = rb * Er + h;
-          Ub = Umain[e];
-        } else {
-          const int j = bj + (h - Er);
-          if (rep_r[j] != rb) continue;
-          e = rep_e[j];
-          Ub = rep_U[j];
-        }
-        if (Ub <= 0) continue;
-        bool hosted = (e / Er) == rt;
-        for (int j = bj; j < bj + rep_dom[m] && !hosted; ++j) hosted = rep_e[j] == e && rep_r[j] == rt;
-        if (!hosted && !(nrep[rt] < d.n_slot && rep_dom[m] < Bd)) continue;
-        const int Lt = L[rt];
-        const int half = (Lb - Lt) >> 1;
-        const int delta = Ub < half ? Ub : half;
-        if (delta < 1) continue;
-        // Key: largest delta, lowest target load, existing instance first, lower e, lower r_t.
-        const uint64_t hi = ((uint64_t)(uint32_t)(0x7fffffff - delta) << 32) | (uint64_t)(uint32_t)Lt;
-        const uint32_t lo = ((uint32_t)(hosted ? 0 : 1) << 31) | ((uint32_t)e << 16) | (uint32_t)rt;
-        if (hi < best_hi || (hi == best_hi && lo < best_lo)) {
-          best_hi = hi;
-          best_lo = lo;
+      if (in_dom && lane != lb) {
+        const int half = (Lb - Lr) >> 1;
+        const bool can_add = nr < d.n_slot && repdom < Bd;
+        for (int h = 0; h < nh; ++h) {
+          int e, Ub;
+          if (h < Er) {
+            e = rb * Er + h;
+            Ub = Umain[e];
+          } else {
+            e = rep_e[rb * NS + (h - Er)];
+            Ub = rep_U[rb * NS + (h - Er)];
+          }
+          if (Ub <= 0) continue;
+          const bool hosted = host_bit(e, r);
+          if (!hosted && !can_add) continue;
+          const int delta = Ub < half ? Ub : half;
+          if (delta < 1) continue;
+          // Key: largest delta, lowest target load, existing instance first, lower e, lower r_t.
+          const uint64_t hi = ((uint64_t)(uint32_t)(0x7fffffff - delta) << 32) | (uint64_t)(uint32_t)Lr;
+          const uint32_t lo = ((uint32_t)(hosted ? 0 : 1) << 31) | ((uint32_t)e << 16) | (uint32_t)r;
+          if (hi < best_hi || (hi == best_hi && lo < best_lo)) {
+            best_hi = hi;
+            best_lo = lo;
+          }
         }
       }
-      wave_min_key(best_hi, best_lo);
+      wave_allmin_key(best_hi, best_lo);
       if (best_hi == ~0ull) break;
-      if (lane == 0) {
-        const int delta = 0x7fffffff - (int)(uint32_t)(best_hi >> 32);
-        const bool is_new = (best_lo >> 31) != 0u;
-        const int e = (int)((best_lo >> 16) & 0x7fffu);
-        const int rt = (int)(best_lo & 0xffffu);
-        if ((e / Er) == rb) {
+      const int delta = 0x7fffffff - (int)(uint32_t)(best_hi >> 32);
+      const bool is_new = (best_lo >> 31) != 0u;
+      const int e = (int)((best_lo >> 16) & 0x7fffu);
+      const int rt = (int)(best_lo & 0xffffu);
+      if (in_dom && lane == lb) {
+        Lr -= delta;
+        if (e / Er == rb) {
           Umain[e] -= delta;
         } else {
-          for (int j = bj; j < bj + rep_dom[m]; ++j)
-            if (rep_e[j] == e && rep_r[j] == rb) rep_U[j] -= delta;
+          const int j = rep_slot(rb, e);
+          if (j >= 0) rep_U[rb * NS + j] -= delta;
         }
+      }
+      if (in_dom && r == rt) {
+        Lr += delta;
         if (is_new) {
-          const int j = bj + rep_dom[m];
-          rep_e[j] = e; rep_r[j] = rt; rep_U[j] = delta;
-          rep_dom[m] += 1;
-          nrep[rt] += 1;
-          atomicAdd(&ereps[e], 1);
-        } else if ((e / Er) == rt) {
+          rep_e[rt * NS + nr] = e;
+          rep_U[rt * NS + nr] = delta;
+          nr += 1;
+          nrep[rt] = nr;
+          atomicOr(&hm[e * RW + (rt >> 6)], 1ull << (rt & 63));
+        } else if (e / Er == rt) {
           Umain[e] += delta;
         } else {
-          for (int j = bj; j < bj + rep_dom[m]; ++j)
-            if (rep_e[j] == e && rep_r[j] == rt) rep_U[j] += delta;
+          const int j = rep_slot(rt, e);
+          if (j >= 0) rep_U[rt * NS + j] += delta;
         }
-        L[rb] -= delta;
-        L[rt] += delta;
       }
+      if (is_new) repdom += 1;
       wave_sync();
     }
+    if (in_dom) { L[r] = Lr; nrep[r] = nr; }
+    if (lane == 0) rep_dom[m] = repdom;
   }
   __syncthreads();
 
   // ---- instance table -------------------------------------------------------
-  for (int r = tid; r < R; r += kPlanThreads) inst_base[r] = Er + nrep[r];
+  for (int q = tid; q < R; q += kPlanThreads) inst_base[q] = Er + nrep[q];
   const int n_inst = block_excl_scan(inst_base, R, wave_tot);
-  if (tid == 0) { inst_base[R] = n_inst; misc[0] = n_inst; }
-  const int nregion = base_d[M];
-  for (int j = tid; j < nregion; j += kPlanThreads) {
-    int m = 0;
-    while (base_d[m + 1] <= j) ++m;
-    rep_inst[j] = -1;
-    if (j - base_d[m] >= rep_dom[m]) continue;
-    const int r = rep_r[j], e = rep_e[j];
-    int pos = 0;
-    for (int q = base_d[m]; q < base_d[m] + rep_dom[m]; ++q) pos += (rep_r[q] == r && rep_e[q] < e) ? 1 : 0;
-    const int id = inst_base[r] + Er + pos;
-    rep_inst[j] = id;
-    inst_e[id] = e; inst_r[id] = r; inst_u[id] = rep_U[j];
+  if (tid == 0) inst_base[R] = n_inst;
+  // Replicas of rank q: ids after its mains, ordered by expert.
+  for (int q = tid; q < R; q += kPlanThreads) {
+    const int n = nrep[q];
+    for (int j = 0; j < n; ++j) {
+      const int e = rep_e[q * NS + j];
+      int pos = 0;
+      for (int j2 = 0; j2 < n; ++j2) pos += rep_e[q * NS + j2] < e ? 1 : 0;
+      const int id = inst_base[q] + Er + pos;
+      rep_id[q * NS + j] = id;
+      out.inst_expert[id] = e; out.inst_rank[id] = q; out.inst_load[id] = rep_U[q * NS + j];
+    }
   }
   for (int e = tid; e < E; e += kPlanThreads) {
-    const int r = e / Er;
-    const int id = inst_base[r] + (e - r * Er);
-    inst_e[id] = e; inst_r[id] = r; inst_u[id] = Umain[e];
-    eoff[e] = 1 + ereps[e];
+    const int q = e / Er;
+    const int id = inst_base[q] + (e - q * Er);
+    out.inst_expert[id] = e; out.inst_rank[id] = q; out.inst_load[id] = Umain[e];
+    int n = 0;
+    for (int w = 0; w < RW; ++w) n += __popcll(hm[e * RW + w]);
+    eoff[e] = n;
   }
-  for (int r = tid; r < R; r += kPlanThreads) out.rank_load[r] = L[r];
+  for (int i = n_inst + tid; i < d.cap; i += kPlanThreads) {
+    out.inst_expert[i] = -1; out.inst_rank[i] = -1; out.inst_load[i] = -1;
+  }
+  for (int q = tid; q < R; q += kPlanThreads) out.rank_load[q] = L[q];
   if (tid == 0) out.n_inst[0] = n_inst;
-  __syncthreads();
-  for (int i = tid; i < d.cap; i += kPlanThreads) {
-    const bool live = i < n_inst;
-    out.inst_expert[i] = live ? inst_e[i] : -1;
-    out.inst_rank[i] = live ? inst_r[i] : -1;
-    out.inst_load[i] = live ? inst_u[i] : -1;
-    if (!live) inst_e[i] = -1;
-  }
   const int total_inst = block_excl_scan(eoff, E, wave_tot);
   if (tid == 0) eoff[E] = total_inst;
   __syncthreads();
   for (int e = tid; e <= E; e += kPlanThreads) ws.einst_off[e] = eoff[e];
-  // Per-expert instance lists in rank order.
+  // Per-expert instance lists in rank order (the set bits of the host mask),
+  // and the experts with more than one instance.
   for (int e = tid; e < E; e += kPlanThreads) {
     const int rm = e / Er;
-    int pos = 0;
-    if (ereps[e] > 0) {
-      for (int m = 0; m < M; ++m)
-        for (int j = base_d[m]; j < base_d[m] + rep_dom[m]; ++j) pos += (rep_e[j] == e && rep_r[j] < rm) ? 1 : 0;
-      const int q = atomicAdd(&misc[1], 1);
-      rlist[q] = e;
-    }
-    ws.einst_list[eoff[e] + pos] = inst_base[rm] + (e - rm * Er);
-  }
-  for (int j = tid; j < nregion; j += kPlanThreads) {
-    if (rep_inst[j] < 0) continue;
-    const int e = rep_e[j], r = rep_r[j];
-    int pos = (e / Er) < r ? 1 : 0;
-    for (int m = 0; m < M; ++m)
-      for (int q = base_d[m]; q < base_d[m] + rep_dom[m]; ++q) pos += (rep_e[q] == e && rep_r[q] < r) ? 1 : 0;
-    ws.einst_list[eoff[e] + pos] = rep_inst[j];
-  }
-  __syncthreads();
-
-  // ---- quotas of replicated experts: three-pass transport, one wave each ---
-  const int nrepl = misc[1];
-  if (wave < kTransportWaves) {
-    int32_t* sc = lds + ly.scratch + wave * ly.scratch_per_wave;
-    int32_t* dem = sc;           // [R]
-    int32_t* pfx = sc + R;       // [R]
-    int32_t* onr = sc + 2 * R;   // [R] list index of the instance on rank s, or -1
-    int32_t* caps = sc + 3 * R;  // [R] remaining capacity of list entry a
-    int32_t* cpfx = sc + 4 * R;  // [R]
-    int32_t* ilst = sc + 5 * R;  // [R] instance id of list entry a
-    int32_t* irank = sc + 6 * R; // [R] rank of list entry a
-    for (int q = wave; q < nrepl; q += kTransportWaves) {
-      const int e = rlist[q];
-      const int off = eoff[e], ne = eoff[e + 1] - eoff[e];
-      for (int a = lane; a < ne; a += 64) {
-        const int i = ws.einst_list[off + a];
-        ilst[a] = i; irank[a] = inst_r[i]; caps[a] = inst_u[i];
+    int pos = eoff[e];
+    if (eoff[e + 1] - pos > 1) ws.rlist[atomicAdd(&misc[2], 1)] = e;
+    for (int w = 0; w < RW; ++w) {
+      unsigned long long bits = hm[e * RW + w];
+      while (bits) {
+        const int q = w * 64 + __ffsll((long long)bits) - 1;
+        bits &= bits - 1;
+        const int j = q == rm ? 0 : rep_slot(q, e);
+        ws.einst_list[pos++] = q == rm ? inst_base[q] + (e - q * Er) : (j >= 0 ? rep_id[q * NS + j] : 0);
       }
-      for (int s = lane; s < R; s += 64) { onr[s] = -1; dem[s] = omega[(int64_t)s * E + e]; }
-      wave_sync();
-      for (int a = lane; a < ne; a += 64) onr[irank[a]] = a;
-      // Every access to qrep[.][s] below is made by the lane that owns source s.
-      for (int s = lane; s < R; s += 64)
-        for (int a = 0; a < ne; ++a) ws.qrep[(int64_t)ilst[a] * R + s] = 0;
-      wave_sync();
-      // Pass A: the instance on the source's own rank.
-      for (int s = lane; s < R; s += 64) {
-        const int a = onr[s];
-        if (a < 0) continue;
-        const int f = min(dem[s], caps[a]);
-        if (f <= 0) continue;
-        dem[s] -= f; caps[a] -= f;
-        ws.qrep[(int64_t)ilst[a] * R + s] += f;
-      }
-      wave_sync();
-      // Pass B: instances in the source's domain.  Sources ascending and
-      // instances in rank order: the greedy fill is the overlap of the two
-      // cumulative intervals, computed per domain.
-      for (int s = lane; s < R; s += 64) {
-        int run = 0;
-        for (int s2 = (s / G) * G; s2 < s; ++s2) run += dem[s2];
-        pfx[s] = run;
-      }
-      for (int a = lane; a < ne; a += 64) {
-        int run = 0;
-        for (int a2 = a - 1; a2 >= 0 && irank[a2] / G == irank[a] / G; --a2) run += caps[a2];
-        cpfx[a] = run;
-      }
-      wave_sync();
-      {
-        int newdem[4], newcap[4];
-        int u = 0;
-        for (int s = lane; s < R; s += 64, ++u) {
-          const int m = s / G;
-          int left = dem[s];
-          for (int a = 0; a < ne && left > 0; ++a) {
-            if (irank[a] / G != m) continue;
-            const int f = (int)overlap(pfx[s], pfx[s] + dem[s], cpfx[a], cpfx[a] + caps[a]);
-            if (f > 0) { ws.qrep[(int64_t)ilst[a] * R + s] += f; left -= f; }
-          }
-          newdem[u] = left;
-        }
-        u = 0;
-        for (int a = lane; a < ne; a += 64, ++u) {
-          const int m = irank[a] / G;
-          const int last = (m + 1) * G - 1;
-          const int dtot = pfx[last] + dem[last];
-          newcap[u] = caps[a] - (int)overlap(cpfx[a], cpfx[a] + caps[a], 0, dtot);
-        }
-        wave_sync();
-        u = 0;
-        for (int s = lane; s < R; s += 64, ++u) dem[s] = newdem[u];
-        u = 0;
-        for (int a = lane; a < ne; a += 64, ++u) caps[a] = newcap[u];
-        wave_sync();
-      }
-      // Pass C: all instances, all sources.
-      {
-        int carry = 0;
-        for (int s0 = 0; s0 < R; s0 += 64) {
-          const int s = s0 + lane;
-          const int v = s < R ? dem[s] : 0;
-          const int incl = wave_incl_scan(v);
-          if (s < R) pfx[s] = carry + incl - v;
-          carry += __shfl(incl, 63);
-        }
-        carry = 0;
-        for (int a0 = 0; a0 < ne; a0 += 64) {
-          const int a = a0 + lane;
-          const int v = a < ne ? caps[a] : 0;
-          const int incl = wave_incl_scan(v);
-          if (a < ne) cpfx[a] = carry + incl - v;
-          carry += __shfl(incl, 63);
-        }
-        wave_sync();
-        bool left_over = false;
-        for (int s = lane; s < R; s += 64) {
-          int left = dem[s];
-          for (int a = 0; a < ne && left > 0; ++a) {
-            const int f = (int)overlap(pfx[s], pfx[s] + dem[s], cpfx[a], cpfx[a] + caps[a]);
-            if (f > 0) { ws.qrep[(int64_t)ilst[a] * R + s] += f; left -= f; }
-          }
-          left_over |= left != 0;
-        }
-        if (left_over) misc[2] = 1;
-      }
-      wave_sync();
-      // Exclusive prefix of each instance's quotas over the sources.
-      for (int a = 0; a < ne; ++a) {
-        const int64_t base = (int64_t)ilst[a] * R;
-        int carry = 0;
-        for (int s0 = 0; s0 < R; s0 += 64) {
-          const int s = s0 + lane;
-          const int v = s < R ? ws.qrep[base + s] : 0;
-          const int incl = wave_incl_scan(v);
-          if (s < R) ws.colpre[base + s] = carry + incl - v;
-          carry += __shfl(incl, 63);
-        }
-      }
-      wave_sync();
     }
   }
   __syncthreads();
+  if (tid == 0) ws.rlist[E] = misc[2];
+}
 
-  // ---- dense quota matrix ----------------------------------------------------
-  const int cap = d.cap;
-  for (int64_t idx = tid; idx < (int64_t)R * cap; idx += kPlanThreads) {
-    const int s = (int)(idx / cap), i = (int)(idx - (int64_t)s * cap);
-    int q = 0;
-    if (i < n_inst) {
-      const int e = inst_e[i];
-      q = ereps[e] == 0 ? omega[(int64_t)s * E + e] : ws.qrep[(int64_t)i * R + s];
+// Exclusive scan over the quota workgroup (kQuotaThreads threads, one value each).
+__device__ int quota_block_excl_scan(int v, int* wtot) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+  __syncthreads();
+  return base + incl - v;
+}
+
+// Quotas.  Workgroups [0, n_transport): replicated expert rlist[b]; the rest
+// fill the columns of single-instance experts (all demand on the one instance)
+// and zero the unused columns.
+__global__ __launch_bounds__(kQuotaThreads) void quota_kernel(Dims d, const int32_t* __restrict__ omega,
+                                                              moe_plan_out out, Workspace ws, int n_transport) {
+  const int E = d.E, R = d.R, G = d.G, cap = d.cap;
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= n_transport) {
+    const int n = out.n_inst[0];
+    const int64_t c0 = (int64_t)(blockIdx.x - n_transport) * kFillCells;
+    for (int64_t c = c0 + tid; c < c0 + kFillCells && c < (int64_t)R * cap; c += kQuotaThreads) {
+      const int s = (int)(c / cap), i = (int)(c - (int64_t)s * cap);
+      if (i >= n) {
+        out.quota[c] = 0;
+      } else {
+        const int e = out.inst_expert[i];
+        if ((unsigned)e < (unsigned)E && ws.einst_off[e + 1] - ws.einst_off[e] == 1)
+          out.quota[c] = omega[(int64_t)s * E + e];
+      }
     }
-    out.quota[idx] = q;
+    return;
   }
-  if (tid == 0 && misc[2]) atomicOr(ws.status, MOE_STATUS_PLAN_CHECK);
+  const int q = blockIdx.x;
+  if (q >= ws.rlist[E]) return;
+  const int e = ws.rlist[q];
+  if ((unsigned)e >= (unsigned)E) return;
+  const int off = ws.einst_off[e], ne = ws.einst_off[e + 1] - off;
+  if (ne < 2 || ne > R || off < 0 || off + ne > cap) {
+    if (tid == 0) atomicOr(ws.status, MOE_STATUS_PLAN_CHECK);
+    return;
+  }
+  // Sources: one per thread.  Instances (rank order): one per thread.
+  __shared__ int dem0[kMaxR], fA[kMaxR], demA[kMaxR], pfxB[kMaxR], demB[kMaxR], pfxC[kMaxR], onr[kMaxR];
+  __shared__ int iid[kMaxR], irank[kMaxR], cap0[kMaxR], capA[kMaxR], cpfxB[kMaxR], capB[kMaxR], cpfxC[kMaxR];
+  __shared__ int wtot[kQuotaThreads / 64];
+  if (tid < R) { dem0[tid] = omega[(int64_t)tid * E + e]; onr[tid] = -1; }
+  if (tid < ne) {
+    int i = ws.einst_list[off + tid];
+    if ((unsigned)i >= (unsigned)cap) i = 0;  // cannot happen for a plan written by plan_kernel
+    int r = out.inst_rank[i];
+    if ((unsigned)r >= (unsigned)R) r = 0;
+    iid[tid] = i; irank[tid] = r; cap0[tid] = out.inst_load[i];
+  }
+  __syncthreads();
+  if (tid < ne) onr[irank[tid]] = tid;
+  __syncthreads();
+  // Pass A: the instance on the source's own rank.
+  if (tid < R) {
+    const int a = onr[tid];
+    const int f = a >= 0 ? min(dem0[tid], cap0[a]) : 0;
+    fA[tid] = f;
+    demA[tid] = dem0[tid] - f;
+  }
+  __syncthreads();
+  if (tid < ne) capA[tid] = cap0[tid] - fA[irank[tid]];
+  __syncthreads();
+  // Pass B: within each domain, sources ascending against instances in rank
+  // order: the greedy fill equals the overlap of the cumulative intervals.
+  if (tid < R) {
+    const int m = tid / G;
+    int run = 0;
+    for (int s2 = m * G; s2 < tid; ++s2) run += demA[s2];
+    pfxB[tid] = run;
+    int capd = 0;
+    for (int a = 0; a < ne; ++a) capd += (irank[a] / G == m) ? capA[a] : 0;
+    demB[tid] = demA[tid] - min(demA[tid], max(0, capd - run));
+  }
+  if (tid < ne) {
+    const int m = irank[tid] / G;
+    int run = 0;
+    for (int a2 = tid - 1; a2 >= 0 && irank[a2] / G == m; --a2) run += capA[a2];
+    cpfxB[tid] = run;
+    int demd = 0;
+    for (int s2 = m * G; s2 < (m + 1) * G; ++s2) demd += demA[s2];
+    capB[tid] = capA[tid] - overlap(run, run + capA[tid], 0, demd);
+  }
+  __syncthreads();
+  // Pass C: all sources against all instances.
+  const int pC = quota_block_excl_scan(tid < R ? demB[tid] : 0, wtot);
+  const int cC = quota_block_excl_scan(tid < ne ? capB[tid] : 0, wtot);
+  if (tid < R) pfxC[tid] = pC;
+  if (tid < ne) cpfxC[tid] = cC;
+  __syncthreads();
+  if (tid == 0) {
+    // Every remaining assignment must find a remaining slot.
+    const int dt = pfxC[R - 1] + demB[R - 1], ct = cpfxC[ne - 1] + capB[ne - 1];
+    if (dt != ct) atomicOr(ws.status, MOE_STATUS_PLAN_CHECK);
+  }
+  // Quota of (s, a) = the three passes' flows; column prefix over sources.
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int a = wave; a < ne; a += kQuotaThreads / 64) {
+    const int i = iid[a], ra = irank[a], ma = ra / G;
+    int carry = 0;
+    for (int s0 = 0; s0 < R; s0 += 64) {
+      const int s = s0 + lane;
+      int v = 0;
+      if (s < R) {
+        v = (ra == s ? fA[s] : 0) +
+            (ma == s / G ? overlap(pfxB[s], pfxB[s] + demA[s], cpfxB[a], cpfxB[a] + capA[a]) : 0) +
+            overlap(pfxC[s], pfxC[s] + demB[s], cpfxC[a], cpfxC[a] + capB[a]);
+        out.quota[(int64_t)s * cap + i] = v;
+      }
+      const int incl = wave_incl_scan(v);
+      if (s < R) ws.colpre[(int64_t)i * R + s] = carry + incl - v;
+      carry += __shfl(incl, 63);
+    }
+  }
 }
 
 // Instance and in-instance position of every slot.
@@ -570,27 +762,26 @@ PlanLayout plan_layout(const Dims& d) {
   PlanLayout ly;
   int o = 0;
   auto take = [&](int n) { const int at = o; o += (n + 3) & ~3; return at; };
+  ly.RW = (d.R + 63) / 64;
+  const int max_bd = (d.B + d.M - 1) / d.M;
+  ly.NS = d.n_slot < max_bd ? d.n_slot : max_bd;
+  if (ly.NS < 1) ly.NS = 1;
   ly.L = take(d.R);
   ly.nrep = take(d.R);
   ly.inst_base = take(d.R + 1);
   ly.rep_dom = take(d.M);
-  ly.base_d = take(d.M + 1);
   ly.Umain = take(d.E);
-  ly.ereps = take(d.E);
   ly.eoff = take(d.E + 1);
-  ly.rlist = take(d.E + 1);
+  ly.rl = take(d.E + 1);
   ly.misc = take(4);
-  const int nb = d.B > 0 ? d.B : 1;
-  ly.rep_e = take(nb);
-  ly.rep_r = take(nb);
-  ly.rep_U = take(nb);
-  ly.rep_inst = take(nb);
-  ly.inst_e = take(d.cap);
-  ly.inst_r = take(d.cap);
-  ly.inst_u = take(d.cap);
+  ly.hm = take(2 * d.E * ly.RW);
+  ly.rep_e = take(d.R * ly.NS);
+  ly.rep_U = take(d.R * ly.NS);
+  ly.rep_id = take(d.R * ly.NS);
   ly.wave_tot = take(kPlanWaves + 1);
-  ly.scratch_per_wave = 7 * d.R;
-  ly.scratch = take(kTransportWaves * ly.scratch_per_wave);
+  // The domain demand lives in LDS when it is small and still fits.
+  const bool d_fits = d.M * d.E <= kDemandLdsMax && (size_t)(o + d.M * d.E) * 4 <= kPlanLdsBudget;
+  ly.D = d_fits ? take(d.M * d.E) : -1;
   ly.total = o;
   return ly;
 }
@@ -609,6 +800,12 @@ hipError_t launch_plan(const Dims& d, const int32_t* omega, const moe_plan_out& 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, st, d, ly, omega, out, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_transport = d.B < d.E ? d.B : d.E;  // each replicated expert owns at least one replica
+  const int64_t n_fill = ((int64_t)d.R * d.cap + kFillCells - 1) / kFillCells;
+  hipLaunchKernelGGL(quota_kernel, dim3((unsigned)(n_transport + n_fill)), dim3(kQuotaThreads), 0, st, d, omega, out,
+                     ws, n_transport);
   return hipGetLastError();
 }
 
