@@ -1,13 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE dispatch-planning path on one MI355X.
 
-A step is one pass of the whole path -- moe_plan_route -> moe_plan_plan ->
-moe_plan_dispatch -- over every layer of the workload, inputs resident in
-HBM.  Prints ONE JSON line:
+A step is one pass of the whole path over every layer of the workload --
+moe_plan_step, i.e. route -> plan -> dispatch in one call per layer -- with
+the inputs resident in HBM.  Prints ONE JSON line:
   value       routed token-slots per second (T*k*L / step time)
-  roofline    the dominant kernel (the bf16 gather of moe_plan_dispatch):
-              algorithmic bytes per launch / its mean duration (HIP events on
-              the stream it runs on) against the 8 TB/s HBM peak
+  roofline    the dominant kernel (the bf16 gather, the one kernel of
+              moe_plan_dispatch): algorithmic bytes per launch / its mean
+              duration (HIP events around moe_plan_dispatch on the stream it
+              runs on, in a second pass of the same steps as three calls)
+              against the 8 TB/s HBM peak
   chain       the same for the whole step (algorithmic bytes of every call)
   cpu_baseline  the CPU oracle on one core over a bounded sample
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -116,20 +118,23 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     layers = [mp.Layer(cfg, device=dev, cooc=True, trans=(l > 0)) for l in range(w.L)]
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
+    def step():
+        # one pass of the whole path per layer: moe_plan_step (route + plan + dispatch in one call)
         for l, layer in enumerate(layers):
             prev = layers[l - 1].route_out.topk_idx if l > 0 else None
-            if ev is not None:
-                ev[l][0].record(stream)
+            layer.step(logits[l], hidden, prev)
+
+    def staged(ev):
+        # the same pass as three calls, with events around each call
+        for l, layer in enumerate(layers):
+            prev = layers[l - 1].route_out.topk_idx if l > 0 else None
+            ev[l][0].record(stream)
             layer.route(logits[l], prev)
-            if ev is not None:
-                ev[l][1].record(stream)
+            ev[l][1].record(stream)
             layer.plan()
-            if ev is not None:
-                ev[l][2].record(stream)
+            ev[l][2].record(stream)
             layer.dispatch(hidden)
-            if ev is not None:
-                ev[l][3].record(stream)
+            ev[l][3].record(stream)
 
     for _ in range(warmup):
         step()
@@ -151,7 +156,7 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(w.L)] for _ in range(steps)]
     torch.cuda.synchronize()
     for s in range(steps):
-        step(evs[s])
+        staged(evs[s])
     torch.cuda.synchronize()
     per = {"route": [], "plan": [], "dispatch": []}
     for s in range(steps):
@@ -168,6 +173,27 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
                 device=torch.cuda.get_device_name(dev))
 
 
+def copy_reference(nbytes: int, steps: int) -> dict:
+    """A plain device-to-device copy of nbytes (torch's copy kernel), the known-size reference
+    against which the HBM byte counters of the profiler are scaled."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms_per_copy": ms,
+            "GBps": 2 * nbytes / (ms / 1e3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,11 +202,16 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=synth.WORKLOAD_ORDER)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the path, time a plain copy of this many bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the planning path runs its logical EP ranks on a single device. "
               "Run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_bytes > 0:
+        print(json.dumps(copy_reference(args.copy_bytes, args.steps)), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
     g = run_gpu(w, args.steps, args.warmup)

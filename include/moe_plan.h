@@ -30,7 +30,10 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  The compute
  *     calls only enqueue work: they never allocate, never synchronise and
  *     never copy to the host.  One handle serves one stream at a time; calls
- *     on one stream run in order.
+ *     on one stream run in order.  The handle owns one more stream of default
+ *     priority: the pair counts (cooc, trans) are forked onto it after the
+ *     top-k and joined back into `stream` within the same call, so every
+ *     output is complete in `stream` order when the call's work ends.
  *   - Argument and configuration errors return a negative code synchronously
  *     and enqueue nothing.  A data-dependent error (a NaN gate logit) sets a
  *     device status word that moe_plan_status reads.
@@ -155,6 +158,11 @@ typedef struct {
  *   slot_inst    int32 [T*k]: instance of slot t*k+j.
  *   slot_rank    int32 [T*k]: position of the slot inside its instance's
  *                segment of the dispatch buffer (stable: slot order).
+ *   inst_offset  int32 [E+B+1]: first dispatch row of each instance (the
+ *                exclusive prefix of inst_load); entry n_inst is T*k, later
+ *                entries are -1.  These are the receive counts of the
+ *                dispatch, derived on the device [TopoEP section 5].
+ *   rank_offset  int32 [R+1]: first dispatch row of each rank; entry R is T*k.
  */
 typedef struct {
   int32_t* n_inst;
@@ -165,22 +173,19 @@ typedef struct {
   int32_t* quota;
   int32_t* slot_inst;
   int32_t* slot_rank;
+  int32_t* inst_offset;
+  int32_t* rank_offset;
 } moe_plan_out;
 
 /*
  * Outputs of moe_plan_dispatch.
  *   perm         int32 [T*k]: slot id (t*k+j) at each dispatch row.
  *   slot_pos     int32 [T*k]: dispatch row of each slot (inverse of perm).
- *   inst_offset  int32 [E+B+1]: first dispatch row of each instance; entry
- *                n_inst is T*k; later entries are -1.
- *   rank_offset  int32 [R+1]: first dispatch row of each rank; entry R is T*k.
  *   dispatch     uint16 [T*k][H]: bf16 rows, dispatch[pos] = hidden[perm[pos]/k].
  */
 typedef struct {
   int32_t* perm;
   int32_t* slot_pos;
-  int32_t* inst_offset;
-  int32_t* rank_offset;
   uint16_t* dispatch;
 } moe_dispatch_out;
 
@@ -237,7 +242,9 @@ int moe_plan_hist(moe_plan_t h, const int32_t* topk_idx, const int32_t* prev_top
  *     in three passes -- the source's own rank, its domain, anywhere -- each
  *     pass sources ascending, instances in rank order;
  *   slot instances: the p-th slot (token order) of source s and expert e goes
- *     to the first instance whose running quota sum exceeds p.
+ *     to the first instance whose running quota sum exceeds p;
+ *   dispatch offsets: exclusive prefix sums of the instance loads and of the
+ *     rank loads (instances are rank-major).
  * route: the outputs of moe_plan_route / moe_plan_hist for this layer
  * (topk_idx, omega, tile_mask, tile_base are read).
  */
@@ -247,12 +254,23 @@ int moe_plan_plan(moe_plan_t h, const moe_route_out* route, const moe_plan_out* 
  * Dispatch layout and bf16 gather [TopoEP section 5: the plan stays on the
  * device and the receive counts are derived there].  The slots are laid out
  * as a stable counting sort by instance: slot_pos = inst_offset[slot_inst] +
- * slot_rank, with inst_offset / rank_offset exclusive prefix sums of the
- * instance / rank loads.  hidden: uint16 [T][H] bf16 rows (device).  Reads
- * plan->n_inst, inst_rank, inst_load, slot_inst, slot_rank.
+ * slot_rank.  hidden: uint16 [T][H] bf16 rows (device).  Reads
+ * plan->slot_inst, slot_rank and inst_offset.
  */
 int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const uint16_t* hidden,
                       const moe_dispatch_out* out, void* stream);
+
+/*
+ * One whole pass of the path in a single call: moe_plan_route, then
+ * moe_plan_plan on its outputs, then moe_plan_dispatch -- the same outputs,
+ * bit for bit, as the three calls in order.  Inside the call the pair counts
+ * (route->cooc, route->trans) run on the handle's side stream, overlapping
+ * the plan, and are joined back into `stream` before the call's work ends.
+ * Sources: those of the three calls.
+ */
+int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* prev_topk, const uint16_t* hidden,
+                  const moe_route_out* route, const moe_plan_out* plan, const moe_dispatch_out* out,
+                  void* stream);
 
 /*
  * Synchronise the handle's last stream, copy the device status word to

@@ -61,15 +61,16 @@ class moe_route_out(ctypes.Structure):
 
 class moe_plan_out(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "n_inst", "inst_expert", "inst_rank", "inst_load", "rank_load", "quota", "slot_inst", "slot_rank")]
+        "n_inst", "inst_expert", "inst_rank", "inst_load", "rank_load", "quota", "slot_inst", "slot_rank",
+        "inst_offset", "rank_offset")]
 
 
 class moe_dispatch_out(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("perm", "slot_pos", "inst_offset", "rank_offset", "dispatch")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("perm", "slot_pos", "dispatch")]
 
 
 EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
-           "moe_plan_dispatch", "moe_plan_status", "moe_plan_destroy")
+           "moe_plan_dispatch", "moe_plan_step", "moe_plan_status", "moe_plan_destroy")
 
 _LIB = None
 
@@ -92,6 +93,7 @@ def lib():
         l.moe_plan_hist.argtypes = [vp, vp, vp, vp, vp]
         l.moe_plan_plan.argtypes = [vp, vp, vp, vp]
         l.moe_plan_dispatch.argtypes = [vp, vp, vp, vp, vp]
+        l.moe_plan_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         l.moe_plan_status.argtypes = [vp, vp]
         l.moe_plan_destroy.argtypes = [vp]
         l.moe_plan_destroy.restype = None
@@ -134,6 +136,12 @@ def moe_plan_plan(h, route: moe_route_out, out: moe_plan_out, stream: int):
 
 def moe_plan_dispatch(h, plan: moe_plan_out, hidden: int, out: moe_dispatch_out, stream: int):
     _check("moe_plan_dispatch", lib().moe_plan_dispatch(h, ctypes.byref(plan), hidden, ctypes.byref(out), stream))
+
+
+def moe_plan_step(h, logits: int, prev_topk, hidden: int, route: moe_route_out, plan: moe_plan_out,
+                  out: moe_dispatch_out, stream: int):
+    _check("moe_plan_step", lib().moe_plan_step(h, logits, prev_topk, hidden, ctypes.byref(route), ctypes.byref(plan),
+                                                ctypes.byref(out), stream))
 
 
 def moe_plan_status(h) -> int:
@@ -182,6 +190,8 @@ class PlanBuffers:
     quota: object
     slot_inst: object
     slot_rank: object
+    inst_offset: object
+    rank_offset: object
 
     def struct(self) -> moe_plan_out:
         return moe_plan_out(*(_ptr(getattr(self, n)) for n, _ in moe_plan_out._fields_))
@@ -191,8 +201,6 @@ class PlanBuffers:
 class DispatchBuffers:
     perm: object
     slot_pos: object
-    inst_offset: object
-    rank_offset: object
     dispatch: object
 
     def struct(self) -> moe_dispatch_out:
@@ -223,10 +231,10 @@ class Layer:
             tile_mask=e(sz.tile_words, torch.int64), tile_base=e(sz.tile_words))
         self.plan_out = PlanBuffers(
             n_inst=e(1), inst_expert=e(sz.inst_cap), inst_rank=e(sz.inst_cap), inst_load=e(sz.inst_cap),
-            rank_load=e(R), quota=e(sz.quota).view(R, sz.inst_cap), slot_inst=e(sz.topk), slot_rank=e(sz.topk))
+            rank_load=e(R), quota=e(sz.quota).view(R, sz.inst_cap), slot_inst=e(sz.topk), slot_rank=e(sz.topk),
+            inst_offset=e(sz.inst_offset), rank_offset=e(sz.rank_offset))
         self.dispatch_out = DispatchBuffers(
-            perm=e(sz.topk), slot_pos=e(sz.topk), inst_offset=e(sz.inst_offset), rank_offset=e(sz.rank_offset),
-            dispatch=e(sz.dispatch_elems, torch.int16).view(T * k, H))
+            perm=e(sz.topk), slot_pos=e(sz.topk), dispatch=e(sz.dispatch_elems, torch.int16).view(T * k, H))
         self._route_s = self.route_out.struct()
         self._plan_s = self.plan_out.struct()
         self._disp_s = self.dispatch_out.struct()
@@ -262,6 +270,18 @@ class Layer:
             raise TypeError("hidden must be a 16-bit (bf16) tensor")
         moe_plan_dispatch(self.handle, self._plan_s, _ptr(hidden), self._disp_s, self._stream(stream))
         return self.dispatch_out
+
+    def step(self, logits, hidden, prev_topk=None, stream=None):
+        """route + plan + dispatch in one call (moe_plan_step)."""
+        self._check_tensor(logits, (self.cfg.T, self.cfg.E), self.torch.float32)
+        self._check_tensor(hidden, (self.cfg.T, self.cfg.H), None)
+        if hidden.element_size() != 2:
+            raise TypeError("hidden must be a 16-bit (bf16) tensor")
+        if prev_topk is not None:
+            self._check_tensor(prev_topk, (self.cfg.T, self.cfg.k), self.torch.int32)
+        moe_plan_step(self.handle, _ptr(logits), _ptr(prev_topk), _ptr(hidden), self._route_s, self._plan_s,
+                      self._disp_s, self._stream(stream))
+        return self.route_out, self.plan_out, self.dispatch_out
 
     def status(self) -> int:
         return moe_plan_status(self.handle)

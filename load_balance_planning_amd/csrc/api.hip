@@ -11,6 +11,12 @@ struct moe_plan {
   moe::Workspace ws;
   void* ws_base;
   size_t ws_bytes;
+  // The pair counts (co-selection, transitions) depend only on the presence
+  // masks and nothing later on the path reads them, so they run on a side
+  // stream of the handle, forked after the top-k and joined back into the
+  // caller's stream at the end of the call.
+  hipStream_t side;
+  hipEvent_t fork, join, scan_done;
 };
 
 namespace {
@@ -21,7 +27,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t status, prev_mask, demand, einst_off, einst_list, rlist, colpre, total;
+  size_t status, prev_mask, demand, einst_off, einst_list, rlist, colpre, pair_part, omega_acc, total;
 };
 
 WsLayout ws_layout(const moe::Dims& d) {
@@ -35,6 +41,8 @@ WsLayout ws_layout(const moe::Dims& d) {
   l.einst_list = take(sizeof(int32_t) * (size_t)d.cap);
   l.rlist = take(sizeof(int32_t) * (size_t)(d.E + 1));
   l.colpre = take(sizeof(int32_t) * (size_t)d.cap * d.R);
+  l.pair_part = take(sizeof(int32_t) * moe::pair_part_words(d));
+  l.omega_acc = take(sizeof(int32_t) * (size_t)d.R * d.E);
   l.total = o;
   return l;
 }
@@ -128,7 +136,23 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   h->ws.einst_list = reinterpret_cast<int32_t*>(b + l.einst_list);
   h->ws.rlist = reinterpret_cast<int32_t*>(b + l.rlist);
   h->ws.colpre = reinterpret_cast<int32_t*>(b + l.colpre);
+  h->ws.pair_part = reinterpret_cast<int32_t*>(b + l.pair_part);
+  h->ws.omega_acc = reinterpret_cast<int32_t*>(b + l.omega_acc);
   if (hipMemset(h->ws_base, 0, l.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(h->ws_base);
+    delete h;
+    return MOE_ERR_HIP;
+  }
+  h->side = nullptr;
+  h->fork = h->join = h->scan_done = nullptr;
+  if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->scan_done, hipEventDisableTiming) != hipSuccess) {
+    if (h->scan_done) (void)hipEventDestroy(h->scan_done);
+    if (h->join) (void)hipEventDestroy(h->join);
+    if (h->fork) (void)hipEventDestroy(h->fork);
+    if (h->side) (void)hipStreamDestroy(h->side);
     (void)hipFree(h->ws_base);
     delete h;
     return MOE_ERR_HIP;
@@ -137,64 +161,135 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   return MOE_OK;
 }
 
+namespace {
+
+// Pair counts on the side stream: fork after the masks exist on `st`; the
+// caller joins (join_pairs) once everything else of the call is enqueued.
+hipError_t fork_pairs(moe_plan_t h, const moe_route_out* out, const int32_t* prev, hipStream_t st) {
+  if (!out->cooc && !(prev && out->trans)) return hipSuccess;
+  hipError_t e = hipEventRecord(h->fork, st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
+  if (e == hipSuccess)
+    e = moe::launch_pairs(h->d, out->tile_mask, h->ws.prev_mask, out->cooc, prev ? out->trans : nullptr,
+                          h->ws.pair_part, h->side);
+  if (e == hipSuccess) e = hipEventRecord(h->join, h->side);
+  return e;
+}
+
+hipError_t join_pairs(moe_plan_t h, const moe_route_out* out, const int32_t* prev, hipStream_t st) {
+  if (!out->cooc && !(prev && out->trans)) return hipSuccess;
+  return hipStreamWaitEvent(st, h->join, 0);
+}
+
+int check_route_out(const moe::Dims& d, const moe_route_out* out) {
+  if (!out || !out->expert_count || !out->omega) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!out->topk_idx || !out->tile_mask || !out->tile_base)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int check_plan_out(const moe::Dims& d, const moe_plan_out* out) {
+  if (!out || !out->n_inst || !out->inst_expert || !out->inst_rank || !out->inst_load || !out->rank_load ||
+      !out->quota || !out->inst_offset || !out->rank_offset)
+    return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!out->slot_inst || !out->slot_rank)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int check_dispatch_out(const moe::Dims& d, const moe_dispatch_out* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!out->perm || !out->slot_pos || !out->dispatch)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" int moe_plan_route(moe_plan_t h, const float* logits, const int32_t* prev_topk, const moe_route_out* out,
                               void* stream) {
-  if (!h || !out || !out->expert_count || !out->omega) return MOE_ERR_INVALID_ARG;
+  if (!h || check_route_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
-  if (d.T > 0 && (!logits || !out->topk_idx || !out->tile_mask || !out->tile_base)) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && !logits) return MOE_ERR_INVALID_ARG;
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* prev = (prev_topk && out->trans) ? prev_topk : nullptr;
   hipError_t e = moe::launch_route_topk(d, logits, prev, out->topk_idx, out->topk_val, out->tile_mask,
-                                        h->ws.prev_mask, h->ws.status, st);
+                                        h->ws.prev_mask, nullptr, h->ws.status, st);
+  if (e == hipSuccess) e = fork_pairs(h, out, prev, st);
   if (e == hipSuccess) e = moe::launch_scan(d, out->tile_mask, out->tile_base, out->omega, out->expert_count, st);
-  if (e == hipSuccess) e = moe::launch_pairs(d, out->tile_mask, h->ws.prev_mask, out->cooc, prev ? out->trans : nullptr, st);
+  if (e == hipSuccess) e = join_pairs(h, out, prev, st);
   return hip_rc(e);
 }
 
 extern "C" int moe_plan_hist(moe_plan_t h, const int32_t* topk_idx, const int32_t* prev_topk, const moe_route_out* out,
                              void* stream) {
-  if (!h || !out || !out->expert_count || !out->omega) return MOE_ERR_INVALID_ARG;
+  if (!h || check_route_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
-  if (d.T > 0 && (!topk_idx || !out->tile_mask || !out->tile_base)) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && !topk_idx) return MOE_ERR_INVALID_ARG;
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* prev = (prev_topk && out->trans) ? prev_topk : nullptr;
   hipError_t e = moe::launch_build_masks(d, topk_idx, prev, out->tile_mask, h->ws.prev_mask, h->ws.status, st);
+  if (e == hipSuccess) e = fork_pairs(h, out, prev, st);
   if (e == hipSuccess) e = moe::launch_scan(d, out->tile_mask, out->tile_base, out->omega, out->expert_count, st);
-  if (e == hipSuccess) e = moe::launch_pairs(d, out->tile_mask, h->ws.prev_mask, out->cooc, prev ? out->trans : nullptr, st);
+  if (e == hipSuccess) e = join_pairs(h, out, prev, st);
   return hip_rc(e);
 }
 
 extern "C" int moe_plan_plan(moe_plan_t h, const moe_route_out* route, const moe_plan_out* out, void* stream) {
-  if (!h || !route || !out || !route->omega) return MOE_ERR_INVALID_ARG;
+  if (!h || !route || !route->omega || check_plan_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
-  if (d.T > 0 && (!route->topk_idx || !route->tile_mask || !route->tile_base || !out->slot_inst || !out->slot_rank))
-    return MOE_ERR_INVALID_ARG;
-  if (!out->n_inst || !out->inst_expert || !out->inst_rank || !out->inst_load || !out->rank_load || !out->quota)
-    return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!route->topk_idx || !route->tile_mask || !route->tile_base)) return MOE_ERR_INVALID_ARG;
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = moe::launch_plan(d, route->omega, *out, h->ws, st);
+  hipError_t e = moe::launch_plan(d, route->omega, nullptr, nullptr, *out, h->ws, st);
   if (e == hipSuccess) e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *out, h->ws, st);
   return hip_rc(e);
 }
 
 extern "C" int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const uint16_t* hidden,
                                  const moe_dispatch_out* out, void* stream) {
-  if (!h || !plan || !out || !plan->n_inst || !plan->inst_rank || !plan->inst_load || !out->inst_offset ||
-      !out->rank_offset)
-    return MOE_ERR_INVALID_ARG;
+  if (!h || !plan || check_dispatch_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
-  if (d.T > 0 && (!plan->slot_inst || !plan->slot_rank || !hidden || !out->perm || !out->slot_pos || !out->dispatch))
-    return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!plan->slot_inst || !plan->slot_rank || !plan->inst_offset || !hidden)) return MOE_ERR_INVALID_ARG;
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = moe::launch_offsets(d, plan->n_inst, plan->inst_rank, plan->inst_load, out->inst_offset,
-                                     out->rank_offset, h->ws.status, st);
+  const hipError_t e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm,
+                                          out->slot_pos, out->dispatch, h->ws.status, st);
+  return hip_rc(e);
+}
+
+extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* prev_topk, const uint16_t* hidden,
+                             const moe_route_out* route, const moe_plan_out* plan, const moe_dispatch_out* out,
+                             void* stream) {
+  if (!h || check_route_out(h->d, route) != MOE_OK || check_plan_out(h->d, plan) != MOE_OK ||
+      check_dispatch_out(h->d, out) != MOE_OK)
+    return MOE_ERR_INVALID_ARG;
+  const moe::Dims& d = h->d;
+  if (d.T > 0 && (!logits || !hidden)) return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t* prev = (prev_topk && route->trans) ? prev_topk : nullptr;
+  const bool pairs = route->cooc || prev;
+  // Critical path on `st`: top-k (which also accumulates the routing matrix)
+  // -> plan -> quotas -> slot instances -> gather.  On the side stream,
+  // overlapping the plan: the tile prefix (needed from the slot instances on)
+  // and the pair counts (needed by nothing later).
+  hipError_t e = moe::launch_route_topk(d, logits, prev, route->topk_idx, route->topk_val, route->tile_mask,
+                                        h->ws.prev_mask, h->ws.omega_acc, h->ws.status, st);
+  if (e == hipSuccess) e = hipEventRecord(h->fork, st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
+  if (e == hipSuccess) e = moe::launch_scan(d, route->tile_mask, route->tile_base, nullptr, nullptr, h->side);
+  if (e == hipSuccess) e = hipEventRecord(h->scan_done, h->side);
+  if (e == hipSuccess && pairs)
+    e = moe::launch_pairs(d, route->tile_mask, h->ws.prev_mask, route->cooc, prev ? route->trans : nullptr,
+                          h->ws.pair_part, h->side);
+  if (e == hipSuccess && pairs) e = hipEventRecord(h->join, h->side);
+  if (e == hipSuccess) e = moe::launch_plan(d, route->omega, h->ws.omega_acc, route->expert_count, *plan, h->ws, st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(st, h->scan_done, 0);
+  if (e == hipSuccess) e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *plan, h->ws, st);
   if (e == hipSuccess)
-    e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, out->inst_offset, hidden, out->perm, out->slot_pos,
+    e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm, out->slot_pos,
                            out->dispatch, h->ws.status, st);
+  if (e == hipSuccess && pairs) e = hipStreamWaitEvent(st, h->join, 0);
   return hip_rc(e);
 }
 
@@ -214,6 +309,10 @@ extern "C" void moe_plan_destroy(moe_plan_t h) {
   if (!h) return;
   if (bind(h) == MOE_OK) {
     (void)hipDeviceSynchronize();
+    (void)hipEventDestroy(h->scan_done);
+    (void)hipEventDestroy(h->join);
+    (void)hipEventDestroy(h->fork);
+    (void)hipStreamDestroy(h->side);
     (void)hipFree(h->ws_base);
   }
   delete h;

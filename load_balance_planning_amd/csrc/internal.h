@@ -39,24 +39,30 @@ struct Workspace {
   int32_t* einst_list;  // [cap] ... instance ids
   int32_t* rlist;       // [E+1] experts with more than one instance; entry E is their count
   int32_t* colpre;      // [cap][R] exclusive prefix of each instance's quotas over sources
+  int32_t* pair_part;   // partial pair-count blocks of the tile splits (pair_part_words)
+  int32_t* omega_acc;   // [R][E] routing matrix accumulated by the top-k kernel (zero between calls)
 };
 
 // Launchers (all asynchronous on `st`).
+// omega_acc (nullable): also add each tile's per-expert counts to this [R][E]
+// accumulator (which must be zero on entry).
 hipError_t launch_route_topk(const Dims& d, const float* logits, const int32_t* prev_topk, int32_t* topk_idx,
-                             float* topk_val, uint64_t* tile_mask, uint64_t* prev_mask, int32_t* status,
-                             hipStream_t st);
+                             float* topk_val, uint64_t* tile_mask, uint64_t* prev_mask, int32_t* omega_acc,
+                             int32_t* status, hipStream_t st);
 hipError_t launch_build_masks(const Dims& d, const int32_t* topk_idx, const int32_t* prev_topk,
                               uint64_t* tile_mask, uint64_t* prev_mask, int32_t* status, hipStream_t st);
+// omega / count nullable: then only the tile prefix is written.
 hipError_t launch_scan(const Dims& d, const uint64_t* tile_mask, int32_t* tile_base, int32_t* omega,
                        int32_t* count, hipStream_t st);
 hipError_t launch_pairs(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc,
-                        int32_t* trans, hipStream_t st);
-hipError_t launch_plan(const Dims& d, const int32_t* omega, const moe_plan_out& out, const Workspace& ws,
-                       hipStream_t st);
+                        int32_t* trans, int32_t* part, hipStream_t st);
+// omega_acc (nullable): read the routing matrix from the workspace
+// accumulator instead, copy it to omega, write the expert counts to count_out
+// and clear the accumulator.
+hipError_t launch_plan(const Dims& d, int32_t* omega, int32_t* omega_acc, int32_t* count_out, const moe_plan_out& out,
+                       const Workspace& ws, hipStream_t st);
 hipError_t launch_assign(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
                          const int32_t* tile_base, const moe_plan_out& out, const Workspace& ws, hipStream_t st);
-hipError_t launch_offsets(const Dims& d, const int32_t* n_inst, const int32_t* inst_rank, const int32_t* inst_load,
-                          int32_t* inst_offset, int32_t* rank_offset, int32_t* status, hipStream_t st);
 hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t* slot_rank,
                          const int32_t* inst_offset, const uint16_t* hidden, int32_t* perm, int32_t* slot_pos,
                          uint16_t* dispatch, int32_t* status, hipStream_t st);
@@ -64,5 +70,7 @@ hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t*
 // LDS bytes the plan and scan kernels need for these dimensions.
 size_t plan_lds_bytes(const Dims& d);
 size_t scan_lds_bytes(const Dims& d);
+// Workspace words of the pair kernel.
+size_t pair_part_words(const Dims& d);
 
 }  // namespace moe

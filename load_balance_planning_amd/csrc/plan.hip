@@ -9,8 +9,9 @@
 //                  update -- the page's one-update-per-iteration rule.
 //   quota_kernel   one workgroup per replicated expert computes its three-pass
 //                  transport in closed form (interval overlaps of cumulative
-//                  demand and capacity); the other workgroups copy the routing
-//                  matrix into the quota columns of single-instance experts.
+//                  demand and capacity); other workgroups copy the routing
+//                  matrix into the quota columns of single-instance experts,
+//                  and one derives the dispatch offsets from the instance loads.
 //   assign_kernel  one thread per slot: stable rank inside its (source,
 //                  expert) pair from the tile masks, then instance and position.
 // All arithmetic is integer and every selection has a total order, so the plan
@@ -29,7 +30,7 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kDemandLdsMax = 16384;  // M*E int32 entries kept in LDS when they fit
 constexpr int kQuotaThreads = 256;     // >= kMaxR: one source (and one instance) per thread
 constexpr int kFillCells = 1024;       // quota cells per fill workgroup
-constexpr size_t kPlanLdsBudget = 160 * 1024;
+constexpr size_t kPlanLdsBudget = 160 * 1024 - 512;  // room for the static LDS copies of the dims
 
 // Offsets (int32 units) of the plan kernel's LDS arrays.
 struct PlanLayout {
@@ -38,6 +39,13 @@ struct PlanLayout {
   int NS;     // replica slots per rank held in LDS
   int total;
 };
+
+// The layer dimensions and the LDS layout, copied to LDS once per launch: the
+// solver helpers are separate functions (one variant per shape, so the
+// kernel's registers stay bounded), and reading these from LDS spares each
+// call the round trip through the stack that by-value structs would take.
+__shared__ Dims plan_dims;
+__shared__ PlanLayout plan_ly;
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -161,7 +169,9 @@ __device__ __forceinline__ int domain_budget(Dims d, int m) {
 // Stage 1 of one domain with the candidate keys in registers: lane l holds
 // the keys of experts l, l+64, ... (at most 64*KMAX experts).
 template <int KMAX>
-__device__ __noinline__ void stage1_domain(Dims d, PlanLayout ly, int m, const int32_t* Dglobal) {
+__device__ __noinline__ void stage1_domain(int m, const int32_t* Dglobal) {
+  const Dims d = plan_dims;
+  const PlanLayout ly = plan_ly;
   int32_t* nrep = plan_lds + ly.nrep;
   int32_t* rep_e = plan_lds + ly.rep_e;
   int32_t* rep_U = plan_lds + ly.rep_U;
@@ -232,7 +242,9 @@ __device__ __forceinline__ uint64_t group_allmax_u64(uint64_t v) {
 // picks the move.  The winning key also carries the entry index, so the
 // update needs no search.
 template <int GS>
-__device__ __noinline__ void stage2_grouped(Dims d, PlanLayout ly, int m) {
+__device__ __noinline__ void stage2_grouped(int m) {
+  const Dims d = plan_dims;
+  const PlanLayout ly = plan_ly;
   constexpr int NG = 64 / GS;
   int32_t* L = plan_lds + ly.L;
   int32_t* nrep = plan_lds + ly.nrep;
@@ -318,12 +330,175 @@ __device__ __noinline__ void stage2_grouped(Dims d, PlanLayout ly, int m) {
   if (lane == 0) rep_dom[m] = repdom;
 }
 
+// Max over aligned groups of GS lanes (GS <= 16) of 32-bit keys, in every lane.
+template <int GS>
+__device__ __forceinline__ uint32_t group_allmax_u32(uint32_t v) {
+  if (GS >= 2) v = max(v, dpp_u32<0xB1>(v));
+  if (GS >= 4) v = max(v, dpp_u32<0x4E>(v));
+  if (GS >= 8) v = max(v, dpp_u32<0x141>(v));
+  if (GS >= 16) v = max(v, dpp_u32<0x140>(v));
+  return v;
+}
+
+// Minimum of a 64-bit key over the wave, in every lane (branch-free).
+__device__ __forceinline__ uint64_t wave_allmin_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(v); v = o < v ? o : v;
+  o = dpp_u64<0x4E>(v); v = o < v ? o : v;
+  o = dpp_u64<0x141>(v); v = o < v ? o : v;
+  o = dpp_u64<0x140>(v); v = o < v ? o : v;
+  uint64_t r = readlane_u64(v, 0);
+  o = readlane_u64(v, 16); r = o < r ? o : r;
+  o = readlane_u64(v, 32); r = o < r ? o : r;
+  o = readlane_u64(v, 48); r = o < r ? o : r;
+  return r;
+}
+
+// Stage 2 of one domain with every hosted entry in registers (G <= GS <= 16,
+// at most J*64/GS entries -- mains plus replica slots -- per rank, every rank
+// load below 2^24).  Lane (g, t) stands for rank r0 + t and holds entries
+// c = g + (64/GS) j of that rank: eR[j] its expert (-1 for an empty slot) and
+// UR[j] its load U[e][r].  An iteration takes the busiest rank from a DPP max
+// of (L << 4 | 15 - t) inside the group, reads the busiest rank's entries
+// from the lanes of the group that hold them (one cross-lane read per
+// register), evaluates moving each of them to target t, and picks the move
+// with one wave-wide minimum of a 64-bit key
+//   (2^24 - 1 - delta) << 40 | L_t << 16 | new << 15 | e << 4 | t,
+// the same order as the LDS solver: largest delta, lowest target load,
+// existing instance first, lower expert, lower target rank.  The two lanes
+// involved update their registers; only the host bitmask lives in LDS.  The
+// state is written back at the end.
+template <int GS, int J>
+__device__ __noinline__ void stage2_regs(int m) {
+  const Dims d = plan_dims;
+  const PlanLayout ly = plan_ly;
+  constexpr int NG = 64 / GS;
+  int32_t* L = plan_lds + ly.L;
+  int32_t* nrep = plan_lds + ly.nrep;
+  int32_t* Umain = plan_lds + ly.Umain;
+  int32_t* rep_e = plan_lds + ly.rep_e;
+  int32_t* rep_U = plan_lds + ly.rep_U;
+  int32_t* rep_dom = plan_lds + ly.rep_dom;
+  unsigned long long* hm = reinterpret_cast<unsigned long long*>(plan_lds + ly.hm);
+  const int RW = ly.RW, NS = ly.NS;
+  const int lane = threadIdx.x & 63;
+  const int t = lane % GS, g = lane / GS;
+  const int G = d.G, Er = d.Er;
+  const int Bd = domain_budget(d, m);
+  const int r0 = m * G;
+  const bool in_dom = t < G;
+  const int r = r0 + (in_dom ? t : 0);
+  int Lr = in_dom ? L[r] : 0;
+  int nr = in_dom ? nrep[r] : 0;
+  int repdom = rep_dom[m];
+  const int hw = r >> 6;
+  const uint64_t hbit = 1ull << (r & 63);
+  int eR[J], UR[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = g + NG * j;
+    eR[j] = -1;
+    UR[j] = 0;
+    if (in_dom && c < Er) {
+      eR[j] = r * Er + c;
+      UR[j] = Umain[r * Er + c];
+    } else if (in_dom && c - Er < nr) {
+      eR[j] = rep_e[r * NS + (c - Er)];
+      UR[j] = rep_U[r * NS + (c - Er)];
+    }
+  }
+  for (int it = 0; it < d.max_iters; ++it) {
+    const uint32_t kb = group_allmax_u32<GS>(in_dom ? ((uint32_t)Lr << 4) | (uint32_t)(15 - t) : 0u);
+    const int lb = 15 - (int)(__builtin_amdgcn_readfirstlane(kb) & 15u);
+    const int Lb = (int)(__builtin_amdgcn_readfirstlane(kb) >> 4);
+    const int nh = Er + __builtin_amdgcn_readlane(nr, lb);
+    const int half = (Lb - Lr) >> 1;
+    const bool cand = in_dom && t != lb;
+    const bool can_add = nr < d.n_slot && repdom < Bd;
+    const int src = g * GS + lb;  // the lane of this group holding the busiest rank's entries
+    uint64_t best = ~0ull;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = g + NG * j;
+      const int eb = __shfl(eR[j], src);
+      const int Ub = __shfl(UR[j], src);
+      const bool exists = c < nh && eb >= 0;
+      const int es = exists ? eb : 0;
+      const bool hosted = (hm[es * RW + hw] & hbit) != 0ull;
+      const int delta = Ub < half ? Ub : half;
+      const bool ok = exists & cand & (Ub > 0) & (hosted | can_add) & (delta >= 1);
+      const uint64_t key = ((uint64_t)(0xffffffu - (uint32_t)delta) << 40) | ((uint64_t)(uint32_t)Lr << 16) |
+                           ((uint64_t)(hosted ? 0u : 1u) << 15) | ((uint64_t)(uint32_t)es << 4) | (uint64_t)t;
+      best = ok && key < best ? key : best;
+    }
+    best = wave_allmin_u64(best);
+    if (best == ~0ull) break;
+    const int delta = (int)(0xffffffu - (uint32_t)(best >> 40));
+    const bool is_new = ((best >> 15) & 1ull) != 0ull;
+    const int e = (int)((best >> 4) & 0x7ffull);
+    const int lt = (int)(best & 15ull);
+    const int rt = r0 + lt;
+    const int nrt = __builtin_amdgcn_readlane(nr, lt);
+    const int cn = Er + nrt;  // slot of a new replica on the target
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = g + NG * j;
+      const bool from = in_dom && t == lb && eR[j] == e;
+      const bool to_new = is_new && in_dom && t == lt && c == cn;
+      const bool to_old = !is_new && in_dom && t == lt && eR[j] == e;
+      UR[j] += ((to_new | to_old) ? delta : 0) - (from ? delta : 0);
+      UR[j] = to_new ? delta : UR[j];
+      eR[j] = to_new ? e : eR[j];
+    }
+    if (is_new && lane == 0) atomicOr(&hm[e * RW + (rt >> 6)], 1ull << (rt & 63));
+    Lr += (in_dom && t == lt) ? delta : 0;
+    Lr -= (in_dom && t == lb) ? delta : 0;
+    nr += (in_dom && t == lt && is_new) ? 1 : 0;
+    repdom += is_new ? 1 : 0;
+    wave_sync();
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = g + NG * j;
+    if (in_dom && c < Er) {
+      Umain[r * Er + c] = UR[j];
+    } else if (in_dom && c - Er < nr) {
+      rep_e[r * NS + (c - Er)] = eR[j];
+      rep_U[r * NS + (c - Er)] = UR[j];
+    }
+  }
+  if (g == 0 && in_dom) { L[r] = Lr; nrep[r] = nr; }
+  if (lane == 0) rep_dom[m] = repdom;
+}
+
+// Register-resident stage 2 when a rank's entries fit in 4 registers per lane
+// and the loads in the narrow key (the largest load of a domain never grows
+// during refinement), else the LDS version.
+template <int GS>
+__device__ void stage2_domain(const Dims& d, const PlanLayout& ly, int m) {
+  constexpr int NG = 64 / GS;
+  const int ent = d.Er + ly.NS;
+  const int lane = threadIdx.x & 63;
+  const int32_t* L = plan_lds + ly.L;
+  int lmax = lane < d.G ? L[m * d.G + lane] : 0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lmax = max(lmax, __shfl_xor(lmax, off));
+  const bool narrow = lmax < (1 << 24);
+  if (narrow && ent <= NG) stage2_regs<GS, 1>(m);
+  else if (narrow && ent <= 2 * NG) stage2_regs<GS, 2>(m);
+  else if (narrow && ent <= 4 * NG) stage2_regs<GS, 4>(m);
+  else stage2_grouped<GS>(m);
+}
+
 // Solver state in LDS:
 //   hm[e][w]        64-bit words of the set of ranks hosting an instance of e
 //   rep_e/rep_U[r][j] expert and load of replica slot j < nrep[r] of rank r
 //   Umain[e]        load of e's main instance;  L[r] rank loads
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout ly, const int32_t* __restrict__ omega,
-                                                            moe_plan_out out, Workspace ws) {
+// omega_acc (nullable): the routing matrix accumulated by the top-k kernel in
+// the workspace; it is then read from there, copied to omega (the route
+// output), summed into count_out and cleared for the next call.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout ly, int32_t* omega, int32_t* omega_acc,
+                                                            int32_t* count_out, moe_plan_out out, Workspace ws) {
   int32_t* lds = plan_lds;
   int32_t* L = lds + ly.L;
   int32_t* nrep = lds + ly.nrep;
@@ -341,6 +516,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
   int32_t* D = ly.D >= 0 ? lds + ly.D : ws.demand;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid == 0) {  // read by the solver helpers after the first barrier
+    plan_dims = d;
+    plan_ly = ly;
+  }
   const int E = d.E, R = d.R, G = d.G, M = d.M, Er = d.Er, RW = ly.RW, NS = ly.NS;
   auto host_bit = [&](int e, int r) -> bool { return (hm[e * RW + (r >> 6)] >> (r & 63)) & 1ull; };
   // Slot of expert e among the replicas of rank r (-1 if none).
@@ -351,13 +530,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
   };
 
   // ---- domain demand D[m][e] (Eq. 4), expert loads, main placement (C5) ----
-  for (int idx = tid; idx < M * E; idx += kPlanThreads) {
-    const int m = idx / E, e = idx - m * E;
-    const int32_t* o = omega + (int64_t)m * G * E + e;
-    int sum = 0;
+  if (omega_acc) {
+    for (int idx = tid; idx < M * E; idx += kPlanThreads) {
+      const int m = idx / E, e = idx - m * E;
+      const int64_t o = (int64_t)m * G * E + e;
+      int sum = 0;
+      for (int g = 0; g < G; ++g) {
+        const int v = omega_acc[o + (int64_t)g * E];
+        omega[o + (int64_t)g * E] = v;
+        omega_acc[o + (int64_t)g * E] = 0;
+        sum += v;
+      }
+      D[idx] = sum;
+    }
+  } else {
+    for (int idx = tid; idx < M * E; idx += kPlanThreads) {
+      const int m = idx / E, e = idx - m * E;
+      const int32_t* o = omega + (int64_t)m * G * E + e;
+      int sum = 0;
 #pragma unroll 8
-    for (int g = 0; g < G; ++g) sum += o[(int64_t)g * E];
-    D[idx] = sum;
+      for (int g = 0; g < G; ++g) sum += o[(int64_t)g * E];
+      D[idx] = sum;
+    }
   }
   for (int q = tid; q < E * RW; q += kPlanThreads) {
     const int e = q / RW, w = q - e * RW;
@@ -371,14 +565,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
     int cnt = 0;
     for (int m = 0; m < M; ++m) cnt += D[m * E + e];
     Umain[e] = cnt;  // every assignment on the main instance until replicas exist
+    if (count_out) count_out[e] = cnt;
   }
 
   // ---- stage 1: inter-node placement (Eq. 9), one wave per domain ----------
   for (int m = wave; m < M; m += kPlanWaves) {
-    if (E <= 64 * 2) stage1_domain<2>(d, ly, m, ws.demand);
-    else if (E <= 64 * 4) stage1_domain<4>(d, ly, m, ws.demand);
-    else if (E <= 64 * 16) stage1_domain<16>(d, ly, m, ws.demand);
-    else stage1_domain<32>(d, ly, m, ws.demand);
+    if (E <= 64 * 2) stage1_domain<2>(m, ws.demand);
+    else if (E <= 64 * 4) stage1_domain<4>(m, ws.demand);
+    else if (E <= 64 * 16) stage1_domain<16>(m, ws.demand);
+    else stage1_domain<32>(m, ws.demand);
   }
   __syncthreads();
 
@@ -451,10 +646,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
   const bool grouped = G <= 16;
   if (grouped) {
     for (int m = wave; m < M; m += kPlanWaves) {
-      if (G <= 2) stage2_grouped<2>(d, ly, m);
-      else if (G <= 4) stage2_grouped<4>(d, ly, m);
-      else if (G <= 8) stage2_grouped<8>(d, ly, m);
-      else stage2_grouped<16>(d, ly, m);
+      if (G <= 2) stage2_domain<2>(d, ly, m);
+      else if (G <= 4) stage2_domain<4>(d, ly, m);
+      else if (G <= 8) stage2_domain<8>(d, ly, m);
+      else stage2_domain<16>(d, ly, m);
     }
   } else
   for (int m = wave; m < M; m += kPlanWaves) {
@@ -603,13 +798,48 @@ __device__ int quota_block_excl_scan(int v, int* wtot) {
   return base + incl - v;
 }
 
-// Quotas.  Workgroups [0, n_transport): replicated expert rlist[b]; the rest
-// fill the columns of single-instance experts (all demand on the one instance)
-// and zero the unused columns.
+// Dispatch offsets: exclusive prefix of the instance loads (the receive
+// counts of every instance) and, since instances are rank-major, each rank's
+// first row.  One workgroup; thread j sums a contiguous run of instances.
+__device__ void offsets_block(const Dims& d, const moe_plan_out& out, int32_t* status) {
+  __shared__ int wtot_o[kQuotaThreads / 64];
+  const int tid = threadIdx.x;
+  int n = out.n_inst[0];
+  if (n < 0 || n > d.cap) {
+    if (tid == 0) atomicOr(status, MOE_STATUS_PLAN_CHECK);
+    n = 0;
+  }
+  const int per = (n + kQuotaThreads - 1) / kQuotaThreads;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int sum = 0;
+  for (int q = lo; q < hi; ++q) sum += out.inst_load[q];
+  const int before = quota_block_excl_scan(sum, wtot_o);
+  int total = 0;
+  for (int w = 0; w < kQuotaThreads / 64; ++w) total += wtot_o[w];
+  int run = before;
+  for (int q = lo; q < hi; ++q) {
+    out.inst_offset[q] = run;
+    const int r = out.inst_rank[q];
+    if ((unsigned)r < (unsigned)d.R && (q == 0 || out.inst_rank[q - 1] != r)) out.rank_offset[r] = run;
+    run += out.inst_load[q];
+  }
+  for (int i = n + tid; i <= d.cap; i += kQuotaThreads) out.inst_offset[i] = i == n ? total : -1;
+  if (tid == 0) out.rank_offset[d.R] = total;
+}
+
+// Quotas.  Workgroups [0, n_transport): replicated expert rlist[b]; then
+// n_fill workgroups fill the columns of single-instance experts (all demand
+// on the one instance) and zero the unused columns; the last workgroup
+// computes the dispatch offsets.
 __global__ __launch_bounds__(kQuotaThreads) void quota_kernel(Dims d, const int32_t* __restrict__ omega,
-                                                              moe_plan_out out, Workspace ws, int n_transport) {
+                                                              moe_plan_out out, Workspace ws, int n_transport,
+                                                              int n_fill) {
   const int E = d.E, R = d.R, G = d.G, cap = d.cap;
   const int tid = threadIdx.x;
+  if ((int)blockIdx.x == n_transport + n_fill) {
+    offsets_block(d, out, ws.status);
+    return;
+  }
   if ((int)blockIdx.x >= n_transport) {
     const int n = out.n_inst[0];
     const int64_t c0 = (int64_t)(blockIdx.x - n_transport) * kFillCells;
@@ -790,7 +1020,8 @@ PlanLayout plan_layout(const Dims& d) {
 
 size_t plan_lds_bytes(const Dims& d) { return sizeof(int32_t) * (size_t)plan_layout(d).total; }
 
-hipError_t launch_plan(const Dims& d, const int32_t* omega, const moe_plan_out& out, const Workspace& ws,
+hipError_t launch_plan(const Dims& d, int32_t* omega, int32_t* omega_acc, int32_t* count_out, const moe_plan_out& out,
+                       const Workspace& ws,
                        hipStream_t st) {
   const PlanLayout ly = plan_layout(d);
   const size_t lds = sizeof(int32_t) * (size_t)ly.total;
@@ -799,13 +1030,13 @@ hipError_t launch_plan(const Dims& d, const int32_t* omega, const moe_plan_out& 
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, st, d, ly, omega, out, ws);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, st, d, ly, omega, omega_acc, count_out, out, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_transport = d.B < d.E ? d.B : d.E;  // each replicated expert owns at least one replica
-  const int64_t n_fill = ((int64_t)d.R * d.cap + kFillCells - 1) / kFillCells;
-  hipLaunchKernelGGL(quota_kernel, dim3((unsigned)(n_transport + n_fill)), dim3(kQuotaThreads), 0, st, d, omega, out,
-                     ws, n_transport);
+  const int n_fill = (int)(((int64_t)d.R * d.cap + kFillCells - 1) / kFillCells);
+  hipLaunchKernelGGL(quota_kernel, dim3((unsigned)(n_transport + n_fill + 1)), dim3(kQuotaThreads), 0, st, d, omega,
+                     out, ws, n_transport, n_fill);
   return hipGetLastError();
 }
 

@@ -22,21 +22,9 @@
 namespace moe {
 namespace {
 
-// Total order of IEEE floats as unsigned integers, with -0.0 mapped onto +0.0.
-__device__ __forceinline__ uint32_t float_order_key(uint32_t u) {
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
+// Inverse of the order key u ^ (sign ? 0xffffffff : 0x80000000) of IEEE bits u.
 __device__ __forceinline__ uint32_t float_from_order_key(uint32_t k) {
   return (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
-}
-
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-  int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-  lo = __shfl(lo, src);
-  hi = __shfl(hi, src);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -78,30 +66,60 @@ __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
   return v;
 }
 
-// Exchange with lane (l ^ J) inside aligned groups: DPP for J < 4, else the
-// LDS crossbar.
+// Exchange with lane (l ^ J) of the same aligned group of 2J lanes, all
+// inside the DPP unit for J <= 8: quad permutes for J = 1, 2; for J = 4 a
+// row shift left or right by 4 (selected by bit 2 of the lane); for J = 8 a
+// row rotate by 8 (inside a row of 16 lanes that is l ^ 8).  J = 16 uses the
+// swizzle unit (xor mask mode), J = 32 the LDS crossbar.
 template <int J>
-__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v) {
-  if (J == 1) return dpp_u64<0xB1>(v);
-  if (J == 2) return dpp_u64<0x4E>(v);
-  return shfl_xor_u64(v, J);
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int lig) {
+  if (J == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);
+  if (J == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false);
+  if (J == 4) {
+    const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xf, 0xf, false);  // row_shl:4
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    return (lig & 4) ? dn : up;
+  }
+  if (J == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
+  if (J == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (16 << 10) | 0x1F);
+  return (uint32_t)__shfl_xor((int)v, J);
 }
 
-template <int P, int SIZE, int J>
-__device__ __forceinline__ uint64_t bitonic_step(uint64_t v, int lig) {
-  const uint64_t o = xor_lane_u64<J>(v);
-  const bool desc = (lig & SIZE) == 0;  // the last stage (SIZE = P) sorts every group descending
-  const bool lower = (lig & J) == 0;
-  const bool keep_max = lower == desc;
-  const uint64_t mx = o > v ? o : v, mn = o > v ? v : o;
-  return keep_max ? mx : mn;
+// Inclusive sum over the lanes 0..lig of each aligned group of P lanes: a DPP
+// row scan (row shifts by 1, 2, 4, 8, masked at group borders), then row
+// broadcasts for groups wider than a row.
+template <int P>
+__device__ __forceinline__ int group_incl_scan(int v, int lig) {
+  int o;
+  if (P >= 2) { o = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false); v += (lig & 15) >= 1 ? o : 0; }
+  if (P >= 4) { o = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false); v += (lig & 15) >= 2 ? o : 0; }
+  if (P >= 8) { o = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false); v += (lig & 15) >= 4 ? o : 0; }
+  if (P >= 16) { o = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false); v += (lig & 15) >= 8 ? o : 0; }
+  if (P >= 32) { o = __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); v += o; }  // row_bcast:15 into rows 1, 3
+  if (P >= 64) { o = __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); v += o; }  // row_bcast:31 into rows 2, 3
+  return v;
 }
 
-// Bitonic sort of one 64-bit key per lane over aligned groups of P lanes,
+// Value of the last lane of each aligned group of P lanes, in every lane.
+template <int P>
+__device__ __forceinline__ int group_last(int v) {
+  if (P == 64) return __builtin_amdgcn_readlane(v, 63);
+  return __builtin_amdgcn_ds_swizzle(v, ((0x1F & ~(P - 1)) << 0) | ((P - 1) << 5));
+}
+
+template <int SIZE, int J>
+__device__ __forceinline__ uint32_t bitonic_step_u32(uint32_t v, int lig) {
+  const uint32_t o = xor_lane_u32<J>(v, lig);
+  const bool desc = (lig & SIZE) == 0;  // in the last stage every lane sorts descending
+  const bool keep_max = ((lig & J) == 0) == desc;
+  return keep_max ? max(o, v) : min(o, v);
+}
+
+// Bitonic sort of one 32-bit key per lane over aligned groups of P lanes,
 // descending: afterwards lane l of a group holds the group's (l+1)-th largest.
 template <int P>
-__device__ __forceinline__ uint64_t group_sort_desc(uint64_t v, int lig) {
-#define MOE_BSTEP(S, J) if (P >= (S)) v = bitonic_step<P, ((S) >= P ? P : (S)), J>(v, lig);
+__device__ __forceinline__ uint32_t group_sort_desc_u32(uint32_t v, int lig) {
+#define MOE_BSTEP(S, J) if (P >= (S)) v = bitonic_step_u32<((S) >= P ? P : (S)), J>(v, lig);
   MOE_BSTEP(2, 1)
   MOE_BSTEP(4, 2) MOE_BSTEP(4, 1)
   MOE_BSTEP(8, 4) MOE_BSTEP(8, 2) MOE_BSTEP(8, 1)
@@ -112,30 +130,69 @@ __device__ __forceinline__ uint64_t group_sort_desc(uint64_t v, int lig) {
   return v;
 }
 
-// One workgroup per tile.  A group of P lanes handles one token; lane l holds
-// VPL logits as 64-bit keys
-//   high word: order key of the logit (-0.0 folded onto +0.0)
-//   low word : (0x7fffffff - e) << 1 | (logit is -0.0)
-// so the largest key is the largest logit with ties to the lower expert, and
-// the key alone gives back the expert and the exact logit bits.  Keys are
-// unique, so a descending sort of the candidates (below) gives the top-k in
-// order with ties already broken; lane j of the group writes choice j.
-// Workgroup size: one wave per token group of a 64-token tile, at most 1024
-// threads; 32 keys per lane need more than the 128 VGPRs a 1024-thread
-// workgroup allows, so those use 512.
+// Workgroup size of the top-k kernel: the waves walk the tile's tokens in
+// groups of P lanes, two tokens per group (the second one's row is
+// prefetched while the first is ranked), so a tile has 32P threads (at most
+// 1024); many waves per SIMD hide the latency of the cross-lane steps.  32
+// keys per lane need more than the 128 VGPRs a 1024-thread workgroup allows:
+// those take 512 threads.
 template <int P, int VPL>
 constexpr int topk_threads() {
-  return (P * 64 < 1024 ? P * 64 : 1024) / (VPL >= 32 ? 2 : 1);
+  return (P * 32 < 128 ? 128 : (P * 32 > 1024 ? 1024 : P * 32)) / (VPL >= 32 ? 2 : 1);
 }
 
+// Expert held in key slot v of lane l: 16-byte loads give lane l the experts
+// 4(l + P w) .. 4(l + P w) + 3 for w = v / 4; scalar loads give l + P v.
+template <int P, bool VEC4>
+__device__ __forceinline__ int slot_expert(int l, int v) {
+  return VEC4 ? 4 * (l + P * (v >> 2)) + (v & 3) : l + P * v;
+}
+
+// Issue the loads of one logit row for lane l of its group (raw IEEE bits);
+// slots past the row re-read its start (their keys are masked later).
+template <int P, int VPL, bool VEC4>
+__device__ __forceinline__ void load_logit_row(const float* __restrict__ row, int l, int E, uint32_t (&u)[VPL]) {
+  if (VEC4) {
+#pragma unroll
+    for (int w = 0; w < VPL / 4; ++w) {
+      const int e0 = slot_expert<P, VEC4>(l, 4 * w);
+      const float4 f = *reinterpret_cast<const float4*>(row + (e0 < E ? e0 : 0));
+      u[4 * w + 0] = __float_as_uint(f.x);
+      u[4 * w + 1] = __float_as_uint(f.y);
+      u[4 * w + 2] = __float_as_uint(f.z);
+      u[4 * w + 3] = __float_as_uint(f.w);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = slot_expert<P, VEC4>(l, v);
+      u[v] = __float_as_uint(row[e < E ? e : 0]);
+    }
+  }
+}
+
+// One workgroup per tile; a group of P lanes handles one token, lane l holding
+// VPL logits as 32-bit order keys (the IEEE total order as unsigned integers).
+// Selection:
+//   1. tau = the k-th largest of the P lane maxima.  k keys reach tau, so
+//      every key of the top-k does; the keys >= tau are the candidates.
+//   2. The candidates (about k + 2 on average when P >= 2k) are compacted to
+//      LDS as 64-bit keys (order key << 32 | (0x7fffffff - e) << 1), unique
+//      per expert, so a key's rank among them is its output position: larger
+//      logit first, equal logits to the lower expert.
+// -0.0 must rank equal to +0.0 (and keep its own bits), which 32-bit order keys
+// do not express, and more than P candidates do not fit the group: such tokens
+// take k rounds of a group max over 64-bit keys that fold -0.0 onto +0.0 and
+// keep the sign in bit 0.
 template <int P, int VPL, bool VEC4>
 __global__ __launch_bounds__((topk_threads<P, VPL>())) void route_topk_kernel(Dims d, const float* __restrict__ logits,
-                                                          const int32_t* __restrict__ prev_topk,
-                                                          int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_val,
-                                                          uint64_t* __restrict__ tile_mask,
-                                                          uint64_t* __restrict__ prev_mask,
-                                                          int32_t* __restrict__ status) {
+                                                                          const int32_t* __restrict__ prev_topk,
+                                                                          int32_t* __restrict__ topk_idx,
+                                                                          float* __restrict__ topk_val,
+                                                                          uint64_t* __restrict__ tile_mask,
+                                                                          uint64_t* __restrict__ prev_mask,
+                                                                          int32_t* __restrict__ omega_acc,
+                                                                          int32_t* __restrict__ status) {
   extern __shared__ unsigned long long smem_masks[];
   unsigned long long* smask = smem_masks;
   unsigned long long* pmask = smem_masks + d.E;
@@ -151,119 +208,101 @@ __global__ __launch_bounds__((topk_threads<P, VPL>())) void route_topk_kernel(Di
   }
   __syncthreads();
 
-  const int lane = tid % P;                  // lane inside the token group
-  const int grp_base = (tid & 63) - lane;     // wave lane of the group's first lane
-  uint64_t* cand_buf = reinterpret_cast<uint64_t*>(smem_masks + (want_prev ? 2 : 1) * d.E) + (tid & ~63);
+  const int lane = tid % P;                // lane inside the token group
+  const int grp_base = (tid & 63) - lane;  // wave lane of the group's first lane
+  const uint64_t grp_bits = (P == 64 ? ~0ull : ((1ull << P) - 1ull)) << grp_base;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem_masks + (want_prev ? 2 : 1) * d.E) + (tid & ~63) + grp_base;
   const int ngrp = nthr / P;
   bool bad = false;
-  for (int i = tid / P; i < nt; i += ngrp) {
+  const int i0 = tid / P;
+  uint32_t nxt[VPL];
+  load_logit_row<P, VPL, VEC4>(logits + (t0 + (i0 < nt ? i0 : nt - 1)) * d.E, lane, d.E, nxt);
+  for (int i = i0; i < nt; i += ngrp) {
     const int64_t t = t0 + i;
-    const float* row = logits + t * d.E;
-    uint64_t key[VPL];
-    if (VEC4) {
-      // lane l reads logits 4(l + P v) .. 4(l + P v) + 3 as one 16-byte load;
-      // every load is issued before any is used (out-of-range lanes re-read
-      // the row start and mask the keys).
-      float4 f4[VPL / 4];
+    uint32_t key[VPL];
+    {
+      uint32_t u[VPL];
 #pragma unroll
-      for (int v = 0; v < VPL / 4; ++v) {
-        const int e0 = 4 * (lane + P * v);
-        f4[v] = *reinterpret_cast<const float4*>(row + (e0 < d.E ? e0 : 0));
-      }
-#pragma unroll
-      for (int v = 0; v < VPL / 4; ++v) {
-        const int e0 = 4 * (lane + P * v);
-        const float4 f = f4[v];
-        const float fv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = e0 + q;
-          const uint32_t u = __float_as_uint(fv[q]);
-          bad |= (e < d.E) && ((u & 0x7fffffffu) > 0x7f800000u);
-          key[4 * v + q] = e < d.E ? ((uint64_t)float_order_key(u) << 32) |
-                                         (uint64_t)(((0x7fffffffu - (uint32_t)e) << 1) | (u == 0x80000000u ? 1u : 0u))
-                                   : 0ull;
-        }
-      }
-    } else {
-      uint32_t uv[VPL];
+      for (int v = 0; v < VPL; ++v) u[v] = nxt[v];
+      // prefetch the group's next token (the last one re-reads its own row)
+      const int in = i + ngrp < nt ? i + ngrp : i;
+      load_logit_row<P, VPL, VEC4>(logits + (t0 + in) * d.E, lane, d.E, nxt);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int e = lane + v * P;
-        uv[v] = __float_as_uint(row[e < d.E ? e : 0]);
-      }
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const int e = lane + v * P;
-        const uint32_t u = uv[v];
-        bad |= (e < d.E) && ((u & 0x7fffffffu) > 0x7f800000u);
-        key[v] = e < d.E ? ((uint64_t)float_order_key(u) << 32) |
-                               (uint64_t)(((0x7fffffffu - (uint32_t)e) << 1) | (u == 0x80000000u ? 1u : 0u))
-                         : 0ull;  // below every real key
+        // with 16-byte loads E is a multiple of 4: a vector is valid as a whole
+        const bool ok = VEC4 ? 4 * (lane + P * (v >> 2)) < d.E : slot_expert<P, VEC4>(lane, v) < d.E;
+        bad |= ok && __builtin_isnan(__uint_as_float(u[v]));
+        key[v] = ok ? (u[v] ^ ((uint32_t)((int32_t)u[v] >> 31) | 0x80000000u)) : 0u;  // 0: below every logit
       }
     }
-    // Threshold: the k-th largest of the group's lane maxima.  At least k
-    // keys reach it, so every top-k key does; the keys that reach it are the
-    // candidates.  When at most P keys qualify (the usual case) they are
-    // sorted once across the group's lanes; otherwise k rounds of group max.
-    uint64_t lmax = key[0];
+    uint32_t lmax = key[0];
 #pragma unroll
-    for (int v = 1; v < VPL; ++v) lmax = max_u64(lmax, key[v]);
+    for (int v = 1; v < VPL; ++v) lmax = max(lmax, key[v]);
     bool fast = d.k <= P;
-    int total = 0, before = 0, mine = 0;
     if (fast) {
-      const uint64_t sorted = group_sort_desc<P>(lmax, lane);
-      const uint64_t tau = shfl_u64(sorted, grp_base + d.k - 1);
+      const uint32_t tau = (uint32_t)__shfl((int)group_sort_desc_u32<P>(lmax, lane), grp_base + d.k - 1);
+      if ((__ballot(tau <= 0x80000000u) & grp_bits) != 0ull) {
+        // threshold at or below +0.0: a -0.0 (order key 0x7fffffff) may tie with a candidate
+        bool nz = false;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) nz |= key[v] == 0x7fffffffu;
+        fast = (__ballot(nz) & grp_bits) == 0ull;
+      }
+      int mine = 0;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) mine += key[v] >= tau ? 1 : 0;
-      int incl = mine;
-#pragma unroll
-      for (int off = 1; off < P; off <<= 1) {
-        const int o = __shfl_up(incl, off, P);
-        if (lane >= off) incl += o;
-      }
-      before = incl - mine;
-      total = __shfl(incl, grp_base + P - 1);
-      fast = total <= P;
+      const int incl = group_incl_scan<P>(mine, lane);
+      const int total = group_last<P>(incl);
+      fast = fast && total <= P;
       if (fast) {
-        uint64_t* buf = cand_buf + grp_base;
-        int w = before;
+        int w = incl - mine;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v)
-          if (key[v] >= tau) buf[w++] = key[v];
+        for (int v = 0; v < VPL; ++v) {
+          if (key[v] >= tau) {
+            const uint32_t e = (uint32_t)slot_expert<P, VEC4>(lane, v);
+            cand[w++] = ((uint64_t)key[v] << 32) | (uint64_t)((0x7fffffffu - e) << 1);
+          }
+        }
         wave_lds_sync();
-        uint64_t c = lane < total ? buf[lane] : 0ull;
-        wave_lds_sync();
-        c = group_sort_desc<P>(c, lane);
-        if (lane < d.k) {
-          const uint32_t lo = (uint32_t)c;
-          const int e = (int)(0x7fffffffu - (lo >> 1));
+        const uint64_t my = cand[lane < total ? lane : 0];
+        int rank = 0;
+        for (int j = 0; j < total; ++j) rank += cand[j] > my ? 1 : 0;
+        if (lane < total && rank < d.k) {
+          const int e = (int)(0x7fffffffu - ((uint32_t)my >> 1));
           if ((unsigned)e < (unsigned)d.E) {
-            const uint32_t u = (lo & 1u) ? 0x80000000u : float_from_order_key((uint32_t)(c >> 32));
-            topk_idx[t * d.k + lane] = e;
-            if (topk_val) topk_val[t * d.k + lane] = __uint_as_float(u);
+            topk_idx[t * d.k + rank] = e;
+            if (topk_val) topk_val[t * d.k + rank] = __uint_as_float(float_from_order_key((uint32_t)(my >> 32)));
             atomicOr(&smask[e], 1ull << i);
           } else {
             bad = true;
           }
         }
+        wave_lds_sync();
       }
     }
     if (!fast) {
-      for (int j = 0; j < d.k; ++j) {
-        uint64_t best = key[0];
+      uint64_t k64[VPL];
 #pragma unroll
-        for (int v = 1; v < VPL; ++v) best = max_u64(best, key[v]);
+      for (int v = 0; v < VPL; ++v) {
+        const uint32_t e = (uint32_t)slot_expert<P, VEC4>(lane, v);
+        const bool nz = key[v] == 0x7fffffffu;  // the order key of -0.0
+        const uint32_t hi = nz ? 0x80000000u : key[v];
+        k64[v] = key[v] == 0u ? 0ull : ((uint64_t)hi << 32) | (uint64_t)(((0x7fffffffu - e) << 1) | (nz ? 1u : 0u));
+      }
+      for (int j = 0; j < d.k; ++j) {
+        uint64_t best = k64[0];
+#pragma unroll
+        for (int v = 1; v < VPL; ++v) best = max_u64(best, k64[v]);
         best = group_max_u64<P>(best);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) key[v] = key[v] == best ? 0ull : key[v];
+        for (int v = 0; v < VPL; ++v) k64[v] = k64[v] == best ? 0ull : k64[v];
         if (lane == 0) {
           const uint32_t lo = (uint32_t)best;
           const int e = (int)(0x7fffffffu - (lo >> 1));
           if ((unsigned)e < (unsigned)d.E) {
-            const uint32_t u = (lo & 1u) ? 0x80000000u : float_from_order_key((uint32_t)(best >> 32));
+            const uint32_t ub = (lo & 1u) ? 0x80000000u : float_from_order_key((uint32_t)(best >> 32));
             topk_idx[t * d.k + j] = e;
-            if (topk_val) topk_val[t * d.k + j] = __uint_as_float(u);
+            if (topk_val) topk_val[t * d.k + j] = __uint_as_float(ub);
             atomicOr(&smask[e], 1ull << i);
           } else {
             bad = true;
@@ -287,8 +326,10 @@ __global__ __launch_bounds__((topk_threads<P, VPL>())) void route_topk_kernel(Di
   if (bad) atomicOr(status, MOE_STATUS_NAN_LOGIT);
   __syncthreads();
   for (int e = tid; e < d.E; e += nthr) {
-    tile_mask[(int64_t)x * d.E + e] = smask[e];
+    const unsigned long long mk = smask[e];
+    tile_mask[(int64_t)x * d.E + e] = mk;
     if (want_prev) prev_mask[(int64_t)x * d.E + e] = pmask[e];
+    if (omega_acc && mk != 0ull) atomicAdd(&omega_acc[(int64_t)s * d.E + e], __popcll(mk));  // Eq. 3
   }
 }
 
@@ -380,7 +421,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(Dims d, const uint64_t* __re
       run += v;
     }
     tot[src * kScanEB + l] = run;
-    if (blockIdx.x * kScanEB + l < d.E) omega[(int64_t)src * d.E + blockIdx.x * kScanEB + l] = run;
+    if (omega && blockIdx.x * kScanEB + l < d.E) omega[(int64_t)src * d.E + blockIdx.x * kScanEB + l] = run;
   }
   __syncthreads();
   if (threadIdx.x < kScanEB) {
@@ -390,7 +431,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(Dims d, const uint64_t* __re
       tot[src * kScanEB + el] = run;
       run += v;
     }
-    if (ok) count[e] = run;
+    if (ok && count) count[e] = run;
   }
   __syncthreads();
   for (int r = row; r < R * rps; r += kScanRows) {
@@ -410,86 +451,128 @@ __global__ __launch_bounds__(1024) void scan_kernel(Dims d, const uint64_t* __re
 
 // Pair counts as a binary product over tiles:
 //   out[a][b] = sum_x popcount(A[x][a] & B[x][b]).
-// A workgroup owns a 64 x PB block; its 16 waves split the tiles.  Each lane
-// holds A[x][a] for its own a; the PB masks B[x][b0..b0+PB) are wave-uniform
-// and come in through scalar loads, so one b costs two AND and two popcount
-// VALU operations for 64 experts a and 64 tokens.  Partial sums of the waves
-// meet in LDS.  The co-selection matrix is symmetric: only blocks touching
-// the upper triangle are computed, and each off-diagonal count is written
-// to both (a, b) and (b, a).  blockIdx.z + zbase: 0 co-selection (A = B =
+// Output blocks of 64 a x kPairB b.  Lane l of a wave holds A[x][a0 + l]; the
+// kPairB masks B[x][b0 ..] are wave-uniform and arrive through scalar loads,
+// so one b costs two AND and two popcount-accumulate VALU operations for 64
+// experts a and 64 tokens.  The tiles are split over `splits` workgroups per
+// block (and over the 4 waves of each) so that the launch fills the chip; the
+// waves meet in LDS and each workgroup stores its partial block, which
+// pair_reduce_kernel adds up in split order (with one split the block is
+// written directly).  The co-selection matrix is symmetric: blocks strictly
+// below the diagonal are skipped and each off-diagonal count is written to
+// (a, b) and (b, a).  Slice z (blockIdx.z + zbase): 0 co-selection (A = B =
 // this layer, zero diagonal), 1 transitions (A = previous layer, B = this layer).
-template <int PB>
-__global__ __launch_bounds__(1024) void pair_kernel(Dims d, const uint64_t* __restrict__ cur,
-                                                    const uint64_t* __restrict__ prev, int32_t* __restrict__ cooc,
-                                                    int32_t* __restrict__ trans, int zbase) {
-  __shared__ int32_t acc_s[64 * PB];
-  const bool is_trans = (int)blockIdx.z + zbase == 1;
+constexpr int kPairB = 16;
+constexpr int kPairThreads = 256;
+constexpr int kPairBlock = 64 * kPairB;
+
+// Write one finished 64 x kPairB block (co-selection: upper part mirrored).
+__device__ __forceinline__ void pair_store(const Dims& d, int32_t* __restrict__ out, bool is_trans, int a0, int b0,
+                                           int q, int v) {
+  const int al = q / kPairB, bl = q - al * kPairB;
+  const int aa = a0 + al, bb = b0 + bl;
+  if (aa >= d.E || bb >= d.E) return;
+  if (is_trans) {
+    out[(int64_t)aa * d.E + bb] = v;
+  } else if (aa == bb) {
+    out[(int64_t)aa * d.E + bb] = 0;
+  } else if (aa < bb) {
+    out[(int64_t)aa * d.E + bb] = v;
+    out[(int64_t)bb * d.E + aa] = v;
+  }
+}
+
+__global__ __launch_bounds__(kPairThreads) void pair_kernel(Dims d, const uint64_t* __restrict__ cur,
+                                                            const uint64_t* __restrict__ prev,
+                                                            int32_t* __restrict__ cooc, int32_t* __restrict__ trans,
+                                                            int32_t* __restrict__ part, int splits, int zbase) {
+  __shared__ int32_t acc_s[kPairBlock];
+  const int z = (int)blockIdx.z + zbase;
+  const bool is_trans = z == 1;
   const uint64_t* A = is_trans ? prev : cur;
-  int32_t* out = is_trans ? trans : cooc;
-  const int a0 = blockIdx.x * 64, b0 = blockIdx.y * PB;
-  if (!is_trans && b0 + PB - 1 < a0) return;  // strictly below the diagonal: written as mirrors
+  const int nb = (d.E + kPairB - 1) / kPairB;
+  const int blk = blockIdx.x;  // a-block * nb + b-block
+  const int a0 = (blk / nb) * 64, b0 = (blk % nb) * kPairB;
+  if (!is_trans && b0 + kPairB - 1 < a0) return;  // strictly below the diagonal: written as mirrors
+  const int split = blockIdx.y;
+  const int x0 = (int)((int64_t)d.NT * split / splits), x1 = (int)((int64_t)d.NT * (split + 1) / splits);
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nwave = blockDim.x >> 6;
-  for (int q = threadIdx.x; q < 64 * PB; q += blockDim.x) acc_s[q] = 0;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int q = threadIdx.x; q < kPairBlock; q += kPairThreads) acc_s[q] = 0;
   __syncthreads();
   const int a = a0 + lane;
   const bool a_ok = a < d.E;
-  int acc[PB];
+  uint32_t acc[kPairB];
 #pragma unroll
-  for (int bb = 0; bb < PB; ++bb) acc[bb] = 0;
-  constexpr int kBatch = 4;
-  for (int x0 = wave * kBatch; x0 < d.NT; x0 += nwave * kBatch) {
+  for (int bb = 0; bb < kPairB; ++bb) acc[bb] = 0;
+  constexpr int kBatch = 2;
+  constexpr int kWaves = kPairThreads / 64;
+  for (int xb = x0 + wave * kBatch; xb < x1; xb += kWaves * kBatch) {
     uint64_t am[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int x = x0 + u < d.NT ? x0 + u : d.NT - 1;
+      const bool in = xb + u < x1;
+      const int x = in ? xb + u : xb;
       am[u] = A[(int64_t)x * d.E + (a_ok ? a : 0)];
-      am[u] = (a_ok && x0 + u < d.NT) ? am[u] : 0ull;
+      am[u] = (a_ok && in) ? am[u] : 0ull;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int x = x0 + u < d.NT ? x0 + u : d.NT - 1;
+      const int x = xb + u < x1 ? xb + u : xb;
       const uint64_t* brow = cur + (int64_t)x * d.E;
       const uint32_t alo = (uint32_t)am[u], ahi = (uint32_t)(am[u] >> 32);
 #pragma unroll
-      for (int bb = 0; bb < PB; ++bb) {
+      for (int bb = 0; bb < kPairB; ++bb) {
         const uint64_t bv = brow[b0 + bb < d.E ? b0 + bb : 0];
         acc[bb] += __popc(alo & (uint32_t)bv) + __popc(ahi & (uint32_t)(bv >> 32));
       }
     }
   }
 #pragma unroll
-  for (int bb = 0; bb < PB; ++bb)
-    if (acc[bb] != 0) atomicAdd(&acc_s[lane * PB + bb], acc[bb]);
+  for (int bb = 0; bb < kPairB; ++bb)
+    if (acc[bb] != 0) atomicAdd(&acc_s[lane * kPairB + bb], (int)acc[bb]);
   __syncthreads();
-  for (int q = threadIdx.x; q < 64 * PB; q += blockDim.x) {
-    const int al = q / PB, bl = q - al * PB;
-    const int aa = a0 + al, bb = b0 + bl;
-    if (aa >= d.E || bb >= d.E) continue;
-    if (is_trans) {
-      out[(int64_t)aa * d.E + bb] = acc_s[q];
-    } else if (aa == bb) {
-      out[(int64_t)aa * d.E + bb] = 0;
-    } else if (aa < bb) {
-      out[(int64_t)aa * d.E + bb] = acc_s[q];
-      out[(int64_t)bb * d.E + aa] = acc_s[q];
-    }
+  if (splits > 1) {
+    int32_t* mine = part + ((int64_t)(z * gridDim.x + blk) * splits + split) * kPairBlock;
+    for (int q = threadIdx.x; q < kPairBlock; q += kPairThreads) mine[q] = acc_s[q];
+    return;
   }
+  int32_t* out = is_trans ? trans : cooc;
+  for (int q = threadIdx.x; q < kPairBlock; q += kPairThreads) pair_store(d, out, is_trans, a0, b0, q, acc_s[q]);
+}
+
+// Sum of the split partials of each block, in split order.
+__global__ __launch_bounds__(kPairThreads) void pair_reduce_kernel(Dims d, const int32_t* __restrict__ part,
+                                                                   int32_t* __restrict__ cooc,
+                                                                   int32_t* __restrict__ trans, int splits,
+                                                                   int zbase) {
+  const int z = (int)blockIdx.z + zbase;
+  const bool is_trans = z == 1;
+  const int nb = (d.E + kPairB - 1) / kPairB;
+  const int blk = blockIdx.x;
+  const int a0 = (blk / nb) * 64, b0 = (blk % nb) * kPairB;
+  if (!is_trans && b0 + kPairB - 1 < a0) return;
+  const int q = blockIdx.y * kPairThreads + threadIdx.x;
+  if (q >= kPairBlock) return;
+  const int32_t* all = part + (int64_t)(z * gridDim.x + blk) * splits * kPairBlock + q;
+  int sum = 0;
+  for (int sp = 0; sp < splits; ++sp) sum += all[(int64_t)sp * kPairBlock];
+  pair_store(d, is_trans ? trans : cooc, is_trans, a0, b0, q, sum);
 }
 
 template <int P, int VPL>
 hipError_t launch_topk_pv(const Dims& d, const float* logits, const int32_t* prev_topk, int32_t* topk_idx,
-                          float* topk_val, uint64_t* tile_mask, uint64_t* prev_mask, int32_t* status,
-                          hipStream_t st) {
+                          float* topk_val, uint64_t* tile_mask, uint64_t* prev_mask, int32_t* omega_acc,
+                          int32_t* status, hipStream_t st) {
   const int threads = topk_threads<P, VPL>();
   const size_t lds = sizeof(unsigned long long) * ((size_t)d.E * (prev_topk ? 2 : 1) + threads);
   const bool vec4 = (d.E % 4) == 0 && (VPL % 4) == 0 && ((uintptr_t)logits % 16) == 0;
   if (vec4) {
     hipLaunchKernelGGL((route_topk_kernel<P, VPL, true>), dim3(d.NT), dim3(threads), lds, st, d, logits, prev_topk,
-                       topk_idx, topk_val, tile_mask, prev_mask, status);
+                       topk_idx, topk_val, tile_mask, prev_mask, omega_acc, status);
   } else {
     hipLaunchKernelGGL((route_topk_kernel<P, VPL, false>), dim3(d.NT), dim3(threads), lds, st, d, logits, prev_topk,
-                       topk_idx, topk_val, tile_mask, prev_mask, status);
+                       topk_idx, topk_val, tile_mask, prev_mask, omega_acc, status);
   }
   return hipGetLastError();
 }
@@ -501,8 +584,8 @@ hipError_t launch_topk_pv(const Dims& d, const float* logits, const int32_t* pre
 // (the k-th largest lane maximum) rarely admits more than P candidates; VPL:
 // logits per lane rounded up to a power of two (>= 4).
 hipError_t launch_route_topk(const Dims& d, const float* logits, const int32_t* prev_topk, int32_t* topk_idx,
-                             float* topk_val, uint64_t* tile_mask, uint64_t* prev_mask, int32_t* status,
-                             hipStream_t st) {
+                             float* topk_val, uint64_t* tile_mask, uint64_t* prev_mask, int32_t* omega_acc,
+                             int32_t* status, hipStream_t st) {
   if (d.NT == 0) return hipSuccess;
   int P = 4;
   while (P < 64 && (P * 16 < d.E || P < 2 * d.k)) P *= 2;
@@ -510,8 +593,8 @@ hipError_t launch_route_topk(const Dims& d, const float* logits, const int32_t* 
   while (P * V < d.E) V *= 2;
 #define MOE_TOPK_CASE(P_, V_)                                                                             \
   if (P == (P_) && V == (V_))                                                                             \
-    return launch_topk_pv<P_, V_>(d, logits, prev_topk, topk_idx, topk_val, tile_mask, prev_mask, status, \
-                                  st);
+    return launch_topk_pv<P_, V_>(d, logits, prev_topk, topk_idx, topk_val, tile_mask, prev_mask, omega_acc, \
+                                  status, st);
   MOE_TOPK_CASE(4, 4)
   MOE_TOPK_CASE(4, 8)
   MOE_TOPK_CASE(4, 16)
@@ -559,15 +642,35 @@ hipError_t launch_scan(const Dims& d, const uint64_t* tile_mask, int32_t* tile_b
   return hipGetLastError();
 }
 
+// Tile splits of the pair kernel: enough workgroups to fill the chip (about
+// 1024), at least 8 tiles per workgroup.
+static int pair_splits(const Dims& d) {
+  const int na = (d.E + 63) / 64, nb = (d.E + kPairB - 1) / kPairB;
+  int s = 1024 / (na * nb);
+  if (s > d.NT / 8) s = d.NT / 8;
+  return s < 1 ? 1 : s;
+}
+
+size_t pair_part_words(const Dims& d) {
+  const int na = (d.E + 63) / 64, nb = (d.E + kPairB - 1) / kPairB;
+  const int sp = pair_splits(d);
+  return sp > 1 ? (size_t)2 * na * nb * sp * 64 * kPairB : 0;
+}
+
 hipError_t launch_pairs(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc,
-                        int32_t* trans, hipStream_t st) {
+                        int32_t* trans, int32_t* part, hipStream_t st) {
   if (!cooc && !trans) return hipSuccess;
   // slice 0 co-selection, slice 1 transitions; one launch covers the requested ones.
   const int nz = (cooc ? 1 : 0) + (trans ? 1 : 0);
   const int zbase = cooc ? 0 : 1;
-  const int na = (d.E + 63) / 64;
-  hipLaunchKernelGGL((pair_kernel<8>), dim3(na, (d.E + 7) / 8, nz), dim3(1024), 0, st, d, tile_mask, prev_mask, cooc,
-                     trans, zbase);
+  const int na = (d.E + 63) / 64, nb = (d.E + kPairB - 1) / kPairB;
+  const int sp = pair_splits(d);
+  hipLaunchKernelGGL(pair_kernel, dim3(na * nb, sp, nz), dim3(kPairThreads), 0, st, d, tile_mask, prev_mask, cooc,
+                     trans, part, sp, zbase);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp == 1) return e;
+  hipLaunchKernelGGL(pair_reduce_kernel, dim3(na * nb, kPairBlock / kPairThreads, nz), dim3(kPairThreads), 0, st, d,
+                     part, cooc, trans, sp, zbase);
   return hipGetLastError();
 }
 

@@ -43,25 +43,30 @@ def ocfg(c):
                            c.token_bytes, c.max_refine_iters)
 
 
-def gpu_layer(mp, cfg, logits=None, topk=None, hidden=None, prev_topk=None, trans=False, cooc=True):
-    """Run route (or hist) -> plan -> dispatch on the GPU; return host copies of every output."""
+def gpu_layer(mp, cfg, logits=None, topk=None, hidden=None, prev_topk=None, trans=False, cooc=True, fused=False):
+    """Run route (or hist) -> plan -> dispatch on the GPU -- as three calls, or as the single
+    moe_plan_step call when `fused` -- and return host copies of every output."""
     layer = mp.Layer(cfg, cooc=cooc, trans=trans)
     dev = layer.device
     prev = None if prev_topk is None else torch.from_numpy(np.ascontiguousarray(prev_topk, np.int32)).to(dev)
-    if logits is not None:
-        layer.route(torch.from_numpy(np.ascontiguousarray(logits)).to(dev), prev)
-    else:
-        layer.hist(torch.from_numpy(np.ascontiguousarray(topk, np.int32)).to(dev), prev)
-    layer.plan()
     hid = torch.from_numpy(np.ascontiguousarray(hidden).view(np.int16)).to(dev)
-    layer.dispatch(hid)
+    if fused:
+        assert logits is not None
+        layer.step(torch.from_numpy(np.ascontiguousarray(logits)).to(dev), hid, prev)
+    else:
+        if logits is not None:
+            layer.route(torch.from_numpy(np.ascontiguousarray(logits)).to(dev), prev)
+        else:
+            layer.hist(torch.from_numpy(np.ascontiguousarray(topk, np.int32)).to(dev), prev)
+        layer.plan()
+        layer.dispatch(hid)
     torch.cuda.synchronize()
     r, p, d = layer.route_out, layer.plan_out, layer.dispatch_out
     out = dict(topk_idx=npy(r.topk_idx), topk_val=npy(r.topk_val), count=npy(r.expert_count), omega=npy(r.omega),
                cooc=npy(r.cooc), trans=npy(r.trans), n_inst=npy(p.n_inst), inst_expert=npy(p.inst_expert),
                inst_rank=npy(p.inst_rank), inst_load=npy(p.inst_load), rank_load=npy(p.rank_load),
                quota=npy(p.quota), slot_inst=npy(p.slot_inst), slot_rank=npy(p.slot_rank), perm=npy(d.perm),
-               slot_pos=npy(d.slot_pos), inst_offset=npy(d.inst_offset), rank_offset=npy(d.rank_offset),
+               slot_pos=npy(d.slot_pos), inst_offset=npy(p.inst_offset), rank_offset=npy(p.rank_offset),
                dispatch=npy(d.dispatch).view(np.uint16))
     out["status"] = layer.status()
     layer.close()
@@ -120,9 +125,12 @@ def test_workload_full_size_parity(mp, name):
     prev = None
     for layer, lg in enumerate(synth.all_logits(w)):
         print("workload %s layer %d T=%d E=%d k=%d R=%d H=%d" % (name, layer, w.T, w.E, w.k, w.R, w.H), flush=True)
-        g = gpu_layer(mp, cfg, logits=lg, hidden=hidden, prev_topk=prev, trans=prev is not None)
         o = oracle_layer(cfg, logits=lg, hidden=hidden, prev_topk=prev)
+        g = gpu_layer(mp, cfg, logits=lg, hidden=hidden, prev_topk=prev, trans=prev is not None)
         compare(g, o, "%s layer %d" % (name, layer))
+        print("workload %s layer %d, single-call step" % (name, layer), flush=True)
+        g = gpu_layer(mp, cfg, logits=lg, hidden=hidden, prev_topk=prev, trans=prev is not None, fused=True)
+        compare(g, o, "%s layer %d (moe_plan_step)" % (name, layer))
         prev = o["topk_idx"]
 
 
@@ -198,7 +206,8 @@ def test_small_random_layers(mp, case):
     if case % 2 == 0:
         lg = inputs.random_logits(case, cfg.T, cfg.E, ties=(case % 4 == 0))
         prev = inputs.random_topk(case + 7, cfg.T, cfg.E, cfg.k) if cfg.T > 0 else None
-        got = gpu_layer(mp, cfg, logits=lg, hidden=hid, prev_topk=prev, trans=prev is not None)
+        # every other logits case goes through the single-call step
+        got = gpu_layer(mp, cfg, logits=lg, hidden=hid, prev_topk=prev, trans=prev is not None, fused=(case % 4 == 2))
         want = oracle_layer(cfg, logits=lg, hidden=hid, prev_topk=prev)
     else:
         topk = inputs.random_topk(case, cfg.T, cfg.E, cfg.k, skew=1.5)
