@@ -16,7 +16,8 @@ struct moe_plan {
   // stream of the handle, forked after the top-k and joined back into the
   // caller's stream at the end of the call.
   hipStream_t side;
-  hipEvent_t fork, join, scan_done;
+  hipEvent_t fork, join;
+  int acc_parity;  // which of the two routing-matrix accumulators the next moe_plan_step fills
 };
 
 namespace {
@@ -42,7 +43,7 @@ WsLayout ws_layout(const moe::Dims& d) {
   l.rlist = take(sizeof(int32_t) * (size_t)(d.E + 1));
   l.colpre = take(sizeof(int32_t) * (size_t)d.cap * d.R);
   l.pair_part = take(sizeof(int32_t) * moe::pair_part_words(d));
-  l.omega_acc = take(sizeof(int32_t) * (size_t)d.R * d.E);
+  l.omega_acc = take(sizeof(int32_t) * 2 * (size_t)d.R * d.E);
   l.total = o;
   return l;
 }
@@ -144,12 +145,11 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
     return MOE_ERR_HIP;
   }
   h->side = nullptr;
-  h->fork = h->join = h->scan_done = nullptr;
+  h->fork = h->join = nullptr;
+  h->acc_parity = 0;
   if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
       hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->scan_done, hipEventDisableTiming) != hipSuccess) {
-    if (h->scan_done) (void)hipEventDestroy(h->scan_done);
+      hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess) {
     if (h->join) (void)hipEventDestroy(h->join);
     if (h->fork) (void)hipEventDestroy(h->fork);
     if (h->side) (void)hipStreamDestroy(h->side);
@@ -240,7 +240,7 @@ extern "C" int moe_plan_plan(moe_plan_t h, const moe_route_out* route, const moe
   if (d.T > 0 && (!route->topk_idx || !route->tile_mask || !route->tile_base)) return MOE_ERR_INVALID_ARG;
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = moe::launch_plan(d, route->omega, nullptr, nullptr, *out, h->ws, st);
+  hipError_t e = moe::launch_plan(d, route->omega, nullptr, nullptr, nullptr, nullptr, nullptr, *out, h->ws, st);
   if (e == hipSuccess) e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *out, h->ws, st);
   return hip_rc(e);
 }
@@ -268,28 +268,28 @@ extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* p
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* prev = (prev_topk && route->trans) ? prev_topk : nullptr;
-  const bool pairs = route->cooc || prev;
-  // Critical path on `st`: top-k (which also accumulates the routing matrix)
-  // -> plan -> quotas -> slot instances -> gather.  On the side stream,
-  // overlapping the plan: the tile prefix (needed from the slot instances on)
-  // and the pair counts (needed by nothing later).
+  // On `st`: top-k (which also accumulates the routing matrix into one of the
+  // two workspace accumulators) -> plan (the solver reads that accumulator;
+  // workgroups on the CUs it leaves idle write the tile prefix, the routing
+  // matrix and counts outputs, and clear the other accumulator for the next
+  // call) -> quotas -> slot instances -> gather.  The pair counts, needed by
+  // nothing later, go to the side stream once the plan is enqueued, so that
+  // the fork does not delay it, and overlap the rest.
+  const int64_t re = (int64_t)d.R * d.E;
+  int32_t* acc = h->ws.omega_acc + (h->acc_parity ? re : 0);
+  int32_t* other = h->ws.omega_acc + (h->acc_parity ? 0 : re);
   hipError_t e = moe::launch_route_topk(d, logits, prev, route->topk_idx, route->topk_val, route->tile_mask,
-                                        h->ws.prev_mask, h->ws.omega_acc, h->ws.status, st);
-  if (e == hipSuccess) e = hipEventRecord(h->fork, st);
-  if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
-  if (e == hipSuccess) e = moe::launch_scan(d, route->tile_mask, route->tile_base, nullptr, nullptr, h->side);
-  if (e == hipSuccess) e = hipEventRecord(h->scan_done, h->side);
-  if (e == hipSuccess && pairs)
-    e = moe::launch_pairs(d, route->tile_mask, h->ws.prev_mask, route->cooc, prev ? route->trans : nullptr,
-                          h->ws.pair_part, h->side);
-  if (e == hipSuccess && pairs) e = hipEventRecord(h->join, h->side);
-  if (e == hipSuccess) e = moe::launch_plan(d, route->omega, h->ws.omega_acc, route->expert_count, *plan, h->ws, st);
-  if (e == hipSuccess) e = hipStreamWaitEvent(st, h->scan_done, 0);
+                                        h->ws.prev_mask, acc, h->ws.status, st);
+  if (e == hipSuccess)
+    e = moe::launch_plan(d, acc, route->tile_mask, route->tile_base, route->omega, route->expert_count, other, *plan,
+                         h->ws, st);
+  if (e == hipSuccess) h->acc_parity ^= 1;
+  if (e == hipSuccess) e = fork_pairs(h, route, prev, st);
   if (e == hipSuccess) e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *plan, h->ws, st);
   if (e == hipSuccess)
     e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm, out->slot_pos,
                            out->dispatch, h->ws.status, st);
-  if (e == hipSuccess && pairs) e = hipStreamWaitEvent(st, h->join, 0);
+  if (e == hipSuccess) e = join_pairs(h, route, prev, st);
   return hip_rc(e);
 }
 
@@ -309,7 +309,6 @@ extern "C" void moe_plan_destroy(moe_plan_t h) {
   if (!h) return;
   if (bind(h) == MOE_OK) {
     (void)hipDeviceSynchronize();
-    (void)hipEventDestroy(h->scan_done);
     (void)hipEventDestroy(h->join);
     (void)hipEventDestroy(h->fork);
     (void)hipStreamDestroy(h->side);

@@ -40,7 +40,8 @@ struct Workspace {
   int32_t* rlist;       // [E+1] experts with more than one instance; entry E is their count
   int32_t* colpre;      // [cap][R] exclusive prefix of each instance's quotas over sources
   int32_t* pair_part;   // partial pair-count blocks of the tile splits (pair_part_words)
-  int32_t* omega_acc;   // [R][E] routing matrix accumulated by the top-k kernel (zero between calls)
+  int32_t* omega_acc;   // [2][R][E] routing matrices accumulated by the top-k kernel in
+                        // alternate calls; the one not in use is zero
 };
 
 // Launchers (all asynchronous on `st`).
@@ -56,10 +57,13 @@ hipError_t launch_scan(const Dims& d, const uint64_t* tile_mask, int32_t* tile_b
                        int32_t* count, hipStream_t st);
 hipError_t launch_pairs(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc,
                         int32_t* trans, int32_t* part, hipStream_t st);
-// omega_acc (nullable): read the routing matrix from the workspace
-// accumulator instead, copy it to omega, write the expert counts to count_out
-// and clear the accumulator.
-hipError_t launch_plan(const Dims& d, int32_t* omega, int32_t* omega_acc, int32_t* count_out, const moe_plan_out& out,
+// Solver, quotas and dispatch offsets from the routing matrix omega.  When
+// scan_mask is given, extra workgroups of the solver launch also write the
+// tile prefix of those masks to scan_base, the routing matrix and expert
+// counts recomputed from the masks to scan_omega / scan_count, and zeros to
+// scan_zero (each nullable).
+hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan_mask, int32_t* scan_base,
+                       int32_t* scan_omega, int32_t* scan_count, int32_t* scan_zero, const moe_plan_out& out,
                        const Workspace& ws, hipStream_t st);
 hipError_t launch_assign(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
                          const int32_t* tile_base, const moe_plan_out& out, const Workspace& ws, hipStream_t st);

@@ -16,7 +16,10 @@
 //                  expert) pair from the tile masks, then instance and position.
 // All arithmetic is integer and every selection has a total order, so the plan
 // is bitwise reproducible.
+#include <algorithm>
+
 #include "internal.h"
+#include "tile_scan.h"
 
 namespace moe {
 namespace {
@@ -494,11 +497,29 @@ __device__ void stage2_domain(const Dims& d, const PlanLayout& ly, int m) {
 //   hm[e][w]        64-bit words of the set of ranks hosting an instance of e
 //   rep_e/rep_U[r][j] expert and load of replica slot j < nrep[r] of rank r
 //   Umain[e]        load of e's main instance;  L[r] rank loads
-// omega_acc (nullable): the routing matrix accumulated by the top-k kernel in
-// the workspace; it is then read from there, copied to omega (the route
-// output), summed into count_out and cleared for the next call.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout ly, int32_t* omega, int32_t* omega_acc,
-                                                            int32_t* count_out, moe_plan_out out, Workspace ws) {
+// Workgroup 0 is the solver; it reads the routing matrix from omega.
+// Workgroups 1.. (when scan_mask is given) run on the CUs the solver leaves
+// idle: for kScanEB experts each, the tile prefix of the presence masks into
+// scan_base, the routing matrix and expert counts into scan_omega and
+// scan_count (tile_scan.h), and zeros into those columns of scan_zero.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout ly, const int32_t* __restrict__ omega,
+                                                            const uint64_t* __restrict__ scan_mask,
+                                                            int32_t* __restrict__ scan_base,
+                                                            int32_t* __restrict__ scan_omega,
+                                                            int32_t* __restrict__ scan_count,
+                                                            int32_t* __restrict__ scan_zero, moe_plan_out out,
+                                                            Workspace ws) {
+  if (blockIdx.x > 0) {
+    const int blk = blockIdx.x - 1;
+    tile_scan_block<kPlanThreads>(d, scan_mask, scan_base, scan_omega, scan_count, blk, plan_lds);
+    if (scan_zero) {
+      for (int q = threadIdx.x; q < d.R * kScanEB; q += kPlanThreads) {
+        const int s = q / kScanEB, e = blk * kScanEB + (q - s * kScanEB);
+        if (e < d.E) scan_zero[(int64_t)s * d.E + e] = 0;
+      }
+    }
+    return;
+  }
   int32_t* lds = plan_lds;
   int32_t* L = lds + ly.L;
   int32_t* nrep = lds + ly.nrep;
@@ -530,28 +551,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
   };
 
   // ---- domain demand D[m][e] (Eq. 4), expert loads, main placement (C5) ----
-  if (omega_acc) {
-    for (int idx = tid; idx < M * E; idx += kPlanThreads) {
-      const int m = idx / E, e = idx - m * E;
-      const int64_t o = (int64_t)m * G * E + e;
-      int sum = 0;
-      for (int g = 0; g < G; ++g) {
-        const int v = omega_acc[o + (int64_t)g * E];
-        omega[o + (int64_t)g * E] = v;
-        omega_acc[o + (int64_t)g * E] = 0;
-        sum += v;
-      }
-      D[idx] = sum;
-    }
-  } else {
-    for (int idx = tid; idx < M * E; idx += kPlanThreads) {
-      const int m = idx / E, e = idx - m * E;
-      const int32_t* o = omega + (int64_t)m * G * E + e;
-      int sum = 0;
+  for (int idx = tid; idx < M * E; idx += kPlanThreads) {
+    const int m = idx / E, e = idx - m * E;
+    const int32_t* o = omega + (int64_t)m * G * E + e;
+    int sum = 0;
 #pragma unroll 8
-      for (int g = 0; g < G; ++g) sum += o[(int64_t)g * E];
-      D[idx] = sum;
-    }
+    for (int g = 0; g < G; ++g) sum += o[(int64_t)g * E];
+    D[idx] = sum;
   }
   for (int q = tid; q < E * RW; q += kPlanThreads) {
     const int e = q / RW, w = q - e * RW;
@@ -565,7 +571,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
     int cnt = 0;
     for (int m = 0; m < M; ++m) cnt += D[m * E + e];
     Umain[e] = cnt;  // every assignment on the main instance until replicas exist
-    if (count_out) count_out[e] = cnt;
   }
 
   // ---- stage 1: inter-node placement (Eq. 9), one wave per domain ----------
@@ -1020,17 +1025,20 @@ PlanLayout plan_layout(const Dims& d) {
 
 size_t plan_lds_bytes(const Dims& d) { return sizeof(int32_t) * (size_t)plan_layout(d).total; }
 
-hipError_t launch_plan(const Dims& d, int32_t* omega, int32_t* omega_acc, int32_t* count_out, const moe_plan_out& out,
-                       const Workspace& ws,
-                       hipStream_t st) {
+hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan_mask, int32_t* scan_base,
+                       int32_t* scan_omega, int32_t* scan_count, int32_t* scan_zero, const moe_plan_out& out,
+                       const Workspace& ws, hipStream_t st) {
   const PlanLayout ly = plan_layout(d);
-  const size_t lds = sizeof(int32_t) * (size_t)ly.total;
+  size_t lds = sizeof(int32_t) * (size_t)ly.total;
+  const int n_scan = scan_mask ? (d.E + kScanEB - 1) / kScanEB : 0;
+  if (n_scan > 0) lds = std::max(lds, tile_scan_lds_bytes(d, kPlanThreads));
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, st, d, ly, omega, omega_acc, count_out, out, ws);
+  hipLaunchKernelGGL(plan_kernel, dim3(1 + n_scan), dim3(kPlanThreads), lds, st, d, ly, omega, scan_mask, scan_base,
+                     scan_omega, scan_count, scan_zero, out, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_transport = d.B < d.E ? d.B : d.E;  // each replicated expert owns at least one replica

@@ -18,6 +18,7 @@
 //   trans[a][b]      = sum over tiles of popcount(prev[x][a] & mask[x][b])
 // so the route step writes NT*E*8 bytes of masks instead of sorting slots.
 #include "internal.h"
+#include "tile_scan.h"
 
 namespace moe {
 namespace {
@@ -380,73 +381,13 @@ __global__ __launch_bounds__(256) void build_masks_kernel(Dims d, const int32_t*
   }
 }
 
-// omega, expert counts and the exclusive tile prefix.  One workgroup per 16
-// experts and all source ranks: thread (row, e) with 64 rows; when there are
-// fewer than 64 sources each source's tiles are split over several rows.
-// Prefixes: over the rows of a source (chunks of tiles), then over sources.
-constexpr int kScanEB = 16;
-constexpr int kScanRows = 1024 / kScanEB;
-
+// omega, expert counts and the exclusive tile prefix: one workgroup of 1024
+// threads per kScanEB experts (tile_scan.h).
 __global__ __launch_bounds__(1024) void scan_kernel(Dims d, const uint64_t* __restrict__ tile_mask,
                                                     int32_t* __restrict__ tile_base, int32_t* __restrict__ omega,
                                                     int32_t* __restrict__ count) {
   extern __shared__ int32_t smem_scan[];
-  const int el = threadIdx.x % kScanEB, row = threadIdx.x / kScanEB;
-  const int e = blockIdx.x * kScanEB + el;
-  const bool ok = e < d.E;
-  const int R = d.R, C = d.C;
-  const int rps = R < kScanRows ? kScanRows / R : 1;      // rows per source
-  const int cc = (C + rps - 1) / rps;                     // tiles per row
-  int32_t* part = smem_scan;                              // [R][rps][EB] chunk sums -> chunk prefixes
-  int32_t* tot = smem_scan + R * rps * kScanEB;           // [R][EB] source sums -> source prefixes
-  // rows handle (source, chunk) pairs r = row, row + 64, ... over R * rps pairs
-  for (int r = row; r < R * rps; r += kScanRows) {
-    const int src = r / rps, ch = r - src * rps;
-    const int c0 = ch * cc, c1 = min(C, c0 + cc);
-    int sum = 0;
-    if (ok) {
-      const uint64_t* m = tile_mask + ((int64_t)src * C) * d.E + e;
-#pragma unroll 4
-      for (int c2 = c0; c2 < c1; ++c2) sum += __popcll(m[(int64_t)c2 * d.E]);
-    }
-    part[r * kScanEB + el] = sum;
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < R * kScanEB; q += blockDim.x) {
-    const int src = q / kScanEB, l = q - src * kScanEB;
-    int run = 0;
-    for (int ch = 0; ch < rps; ++ch) {
-      const int v = part[(src * rps + ch) * kScanEB + l];
-      part[(src * rps + ch) * kScanEB + l] = run;
-      run += v;
-    }
-    tot[src * kScanEB + l] = run;
-    if (omega && blockIdx.x * kScanEB + l < d.E) omega[(int64_t)src * d.E + blockIdx.x * kScanEB + l] = run;
-  }
-  __syncthreads();
-  if (threadIdx.x < kScanEB) {
-    int run = 0;
-    for (int src = 0; src < R; ++src) {
-      const int v = tot[src * kScanEB + el];
-      tot[src * kScanEB + el] = run;
-      run += v;
-    }
-    if (ok && count) count[e] = run;
-  }
-  __syncthreads();
-  for (int r = row; r < R * rps; r += kScanRows) {
-    const int src = r / rps, ch = r - src * rps;
-    const int c0 = ch * cc, c1 = min(C, c0 + cc);
-    if (!ok) continue;
-    int run = tot[src * kScanEB + el] + part[r * kScanEB + el];
-    const int64_t base = ((int64_t)src * C) * d.E + e;
-#pragma unroll 4
-    for (int c2 = c0; c2 < c1; ++c2) {
-      const int64_t idx = base + (int64_t)c2 * d.E;
-      tile_base[idx] = run;
-      run += __popcll(tile_mask[idx]);
-    }
-  }
+  tile_scan_block<1024>(d, tile_mask, tile_base, omega, count, blockIdx.x, smem_scan);
 }
 
 // Pair counts as a binary product over tiles:
@@ -624,10 +565,7 @@ hipError_t launch_build_masks(const Dims& d, const int32_t* topk_idx, const int3
   return hipGetLastError();
 }
 
-size_t scan_lds_bytes(const Dims& d) {
-  const int rps = d.R < kScanRows ? kScanRows / d.R : 1;
-  return sizeof(int32_t) * ((size_t)d.R * rps * kScanEB + (size_t)d.R * kScanEB);
-}
+size_t scan_lds_bytes(const Dims& d) { return tile_scan_lds_bytes(d, 1024); }
 
 hipError_t launch_scan(const Dims& d, const uint64_t* tile_mask, int32_t* tile_base, int32_t* omega,
                        int32_t* count, hipStream_t st) {
