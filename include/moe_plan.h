@@ -31,8 +31,8 @@
  *     calls only enqueue work: they never allocate, never synchronise and
  *     never copy to the host.  One handle serves one stream at a time; calls
  *     on one stream run in order.  The handle owns one more stream of default
- *     priority: the pair counts (cooc, trans) are forked onto it after the
- *     top-k and joined back into `stream` within the same call, so every
+ *     priority: the calls that compute pair counts (cooc, trans) fork them
+ *     onto it and join them back into `stream` within the same call, so every
  *     output is complete in `stream` order when the call's work ends.
  *   - Argument and configuration errors return a negative code synchronously
  *     and enqueue nothing.  A data-dependent error (a NaN gate logit) sets a
@@ -263,10 +263,12 @@ int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const uint16_t* hi
 /*
  * One whole pass of the path in a single call: moe_plan_route, then
  * moe_plan_plan on its outputs, then moe_plan_dispatch -- the same outputs,
- * bit for bit, as the three calls in order.  Inside the call the pair counts
- * (route->cooc, route->trans) run on the handle's side stream, overlapping
- * the plan, and are joined back into `stream` before the call's work ends.
- * Sources: those of the three calls.
+ * bit for bit, as the three calls in order.  Inside the call the tile prefix
+ * and the routing-matrix output are computed by extra workgroups of the
+ * solver launch, on the CUs the single solver workgroup leaves idle, and the
+ * pair counts (route->cooc, route->trans) run on the handle's side stream,
+ * overlapping the slot assignment and the gather; they are joined back into
+ * `stream` within the call.  Sources: those of the three calls.
  */
 int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* prev_topk, const uint16_t* hidden,
                   const moe_route_out* route, const moe_plan_out* plan, const moe_dispatch_out* out,

@@ -148,8 +148,9 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   h->fork = h->join = nullptr;
   h->acc_parity = 0;
   if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
-      hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess) {
+      // both streams are on one device: a device-scope release is enough
+      hipEventCreateWithFlags(&h->fork, hipEventDisableTiming | hipEventReleaseToDevice) != hipSuccess ||
+      hipEventCreateWithFlags(&h->join, hipEventDisableTiming | hipEventReleaseToDevice) != hipSuccess) {
     if (h->join) (void)hipEventDestroy(h->join);
     if (h->fork) (void)hipEventDestroy(h->fork);
     if (h->side) (void)hipStreamDestroy(h->side);
@@ -273,8 +274,9 @@ extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* p
   // workgroups on the CUs it leaves idle write the tile prefix, the routing
   // matrix and counts outputs, and clear the other accumulator for the next
   // call) -> quotas -> slot instances -> gather.  The pair counts, needed by
-  // nothing later, go to the side stream once the plan is enqueued, so that
-  // the fork does not delay it, and overlap the rest.
+  // nothing later, go to the side stream once the plan is enqueued -- forking
+  // earlier would put the fork's wait in front of the plan -- and overlap the
+  // slot assignment and the gather.
   const int64_t re = (int64_t)d.R * d.E;
   int32_t* acc = h->ws.omega_acc + (h->acc_parity ? re : 0);
   int32_t* other = h->ws.omega_acc + (h->acc_parity ? 0 : re);

@@ -44,6 +44,19 @@ struct Workspace {
                         // alternate calls; the one not in use is zero
 };
 
+// Pair-count job: presence masks in, co-selection / transition blocks out
+// (pair_count.h).  nz slices starting at zbase: 0 co-selection, 1 transitions.
+struct PairArgs {
+  const uint64_t* cur;   // this layer's masks
+  const uint64_t* prev;  // the previous layer's masks (transitions)
+  int32_t* cooc;
+  int32_t* trans;
+  int32_t* part;         // split partials (workspace)
+  int splits, nz, zbase;
+};
+PairArgs pair_args(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc, int32_t* trans,
+                   int32_t* part, int nthr);
+
 // Launchers (all asynchronous on `st`).
 // omega_acc (nullable): also add each tile's per-expert counts to this [R][E]
 // accumulator (which must be zero on entry).

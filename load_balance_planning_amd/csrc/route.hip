@@ -18,6 +18,7 @@
 //   trans[a][b]      = sum over tiles of popcount(prev[x][a] & mask[x][b])
 // so the route step writes NT*E*8 bytes of masks instead of sorting slots.
 #include "internal.h"
+#include "pair_count.h"
 #include "tile_scan.h"
 
 namespace moe {
@@ -390,115 +391,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(Dims d, const uint64_t* __re
   tile_scan_block<1024>(d, tile_mask, tile_base, omega, count, blockIdx.x, smem_scan);
 }
 
-// Pair counts as a binary product over tiles:
-//   out[a][b] = sum_x popcount(A[x][a] & B[x][b]).
-// Output blocks of 64 a x kPairB b.  Lane l of a wave holds A[x][a0 + l]; the
-// kPairB masks B[x][b0 ..] are wave-uniform and arrive through scalar loads,
-// so one b costs two AND and two popcount-accumulate VALU operations for 64
-// experts a and 64 tokens.  The tiles are split over `splits` workgroups per
-// block (and over the 4 waves of each) so that the launch fills the chip; the
-// waves meet in LDS and each workgroup stores its partial block, which
-// pair_reduce_kernel adds up in split order (with one split the block is
-// written directly).  The co-selection matrix is symmetric: blocks strictly
-// below the diagonal are skipped and each off-diagonal count is written to
-// (a, b) and (b, a).  Slice z (blockIdx.z + zbase): 0 co-selection (A = B =
-// this layer, zero diagonal), 1 transitions (A = previous layer, B = this layer).
-constexpr int kPairB = 16;
+// Pair counts on their own: partial blocks, then their sums (pair_count.h).
 constexpr int kPairThreads = 256;
-constexpr int kPairBlock = 64 * kPairB;
 
-// Write one finished 64 x kPairB block (co-selection: upper part mirrored).
-__device__ __forceinline__ void pair_store(const Dims& d, int32_t* __restrict__ out, bool is_trans, int a0, int b0,
-                                           int q, int v) {
-  const int al = q / kPairB, bl = q - al * kPairB;
-  const int aa = a0 + al, bb = b0 + bl;
-  if (aa >= d.E || bb >= d.E) return;
-  if (is_trans) {
-    out[(int64_t)aa * d.E + bb] = v;
-  } else if (aa == bb) {
-    out[(int64_t)aa * d.E + bb] = 0;
-  } else if (aa < bb) {
-    out[(int64_t)aa * d.E + bb] = v;
-    out[(int64_t)bb * d.E + aa] = v;
-  }
-}
-
-__global__ __launch_bounds__(kPairThreads) void pair_kernel(Dims d, const uint64_t* __restrict__ cur,
-                                                            const uint64_t* __restrict__ prev,
-                                                            int32_t* __restrict__ cooc, int32_t* __restrict__ trans,
-                                                            int32_t* __restrict__ part, int splits, int zbase) {
+__global__ __launch_bounds__(kPairThreads) void pair_kernel(Dims d, PairArgs pa) {
   __shared__ int32_t acc_s[kPairBlock];
-  const int z = (int)blockIdx.z + zbase;
-  const bool is_trans = z == 1;
-  const uint64_t* A = is_trans ? prev : cur;
-  const int nb = (d.E + kPairB - 1) / kPairB;
-  const int blk = blockIdx.x;  // a-block * nb + b-block
-  const int a0 = (blk / nb) * 64, b0 = (blk % nb) * kPairB;
-  if (!is_trans && b0 + kPairB - 1 < a0) return;  // strictly below the diagonal: written as mirrors
-  const int split = blockIdx.y;
-  const int x0 = (int)((int64_t)d.NT * split / splits), x1 = (int)((int64_t)d.NT * (split + 1) / splits);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  for (int q = threadIdx.x; q < kPairBlock; q += kPairThreads) acc_s[q] = 0;
-  __syncthreads();
-  const int a = a0 + lane;
-  const bool a_ok = a < d.E;
-  uint32_t acc[kPairB];
-#pragma unroll
-  for (int bb = 0; bb < kPairB; ++bb) acc[bb] = 0;
-  constexpr int kBatch = 2;
-  constexpr int kWaves = kPairThreads / 64;
-  for (int xb = x0 + wave * kBatch; xb < x1; xb += kWaves * kBatch) {
-    uint64_t am[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const bool in = xb + u < x1;
-      const int x = in ? xb + u : xb;
-      am[u] = A[(int64_t)x * d.E + (a_ok ? a : 0)];
-      am[u] = (a_ok && in) ? am[u] : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int x = xb + u < x1 ? xb + u : xb;
-      const uint64_t* brow = cur + (int64_t)x * d.E;
-      const uint32_t alo = (uint32_t)am[u], ahi = (uint32_t)(am[u] >> 32);
-#pragma unroll
-      for (int bb = 0; bb < kPairB; ++bb) {
-        const uint64_t bv = brow[b0 + bb < d.E ? b0 + bb : 0];
-        acc[bb] += __popc(alo & (uint32_t)bv) + __popc(ahi & (uint32_t)(bv >> 32));
-      }
-    }
-  }
-#pragma unroll
-  for (int bb = 0; bb < kPairB; ++bb)
-    if (acc[bb] != 0) atomicAdd(&acc_s[lane * kPairB + bb], (int)acc[bb]);
-  __syncthreads();
-  if (splits > 1) {
-    int32_t* mine = part + ((int64_t)(z * gridDim.x + blk) * splits + split) * kPairBlock;
-    for (int q = threadIdx.x; q < kPairBlock; q += kPairThreads) mine[q] = acc_s[q];
-    return;
-  }
-  int32_t* out = is_trans ? trans : cooc;
-  for (int q = threadIdx.x; q < kPairBlock; q += kPairThreads) pair_store(d, out, is_trans, a0, b0, q, acc_s[q]);
+  pair_partial_block<kPairThreads>(d, pa, (int)blockIdx.z + pa.zbase, blockIdx.x, blockIdx.y, acc_s);
 }
 
-// Sum of the split partials of each block, in split order.
-__global__ __launch_bounds__(kPairThreads) void pair_reduce_kernel(Dims d, const int32_t* __restrict__ part,
-                                                                   int32_t* __restrict__ cooc,
-                                                                   int32_t* __restrict__ trans, int splits,
-                                                                   int zbase) {
-  const int z = (int)blockIdx.z + zbase;
-  const bool is_trans = z == 1;
-  const int nb = (d.E + kPairB - 1) / kPairB;
-  const int blk = blockIdx.x;
-  const int a0 = (blk / nb) * 64, b0 = (blk % nb) * kPairB;
-  if (!is_trans && b0 + kPairB - 1 < a0) return;
-  const int q = blockIdx.y * kPairThreads + threadIdx.x;
-  if (q >= kPairBlock) return;
-  const int32_t* all = part + (int64_t)(z * gridDim.x + blk) * splits * kPairBlock + q;
-  int sum = 0;
-  for (int sp = 0; sp < splits; ++sp) sum += all[(int64_t)sp * kPairBlock];
-  pair_store(d, is_trans ? trans : cooc, is_trans, a0, b0, q, sum);
+__global__ __launch_bounds__(kPairThreads) void pair_reduce_kernel(Dims d, PairArgs pa) {
+  pair_reduce_one(d, pa, (int)blockIdx.z + pa.zbase, blockIdx.x, blockIdx.y * kPairThreads + threadIdx.x);
 }
 
 template <int P, int VPL>
@@ -580,35 +482,35 @@ hipError_t launch_scan(const Dims& d, const uint64_t* tile_mask, int32_t* tile_b
   return hipGetLastError();
 }
 
-// Tile splits of the pair kernel: enough workgroups to fill the chip (about
-// 1024), at least 8 tiles per workgroup.
-static int pair_splits(const Dims& d) {
-  const int na = (d.E + 63) / 64, nb = (d.E + kPairB - 1) / kPairB;
-  int s = 1024 / (na * nb);
-  if (s > d.NT / 8) s = d.NT / 8;
-  return s < 1 ? 1 : s;
+size_t pair_part_words(const Dims& d) {
+  const int sp = pair_splits(d, kPairThreads);  // the larger of the two split counts used
+  return sp > 1 ? (size_t)2 * pair_blocks(d) * sp * kPairBlock : 0;
 }
 
-size_t pair_part_words(const Dims& d) {
-  const int na = (d.E + 63) / 64, nb = (d.E + kPairB - 1) / kPairB;
-  const int sp = pair_splits(d);
-  return sp > 1 ? (size_t)2 * na * nb * sp * 64 * kPairB : 0;
+PairArgs pair_args(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc, int32_t* trans,
+                   int32_t* part, int nthr) {
+  PairArgs pa;
+  pa.cur = tile_mask;
+  pa.prev = prev_mask;
+  pa.cooc = cooc;
+  pa.trans = trans;
+  pa.part = part;
+  pa.splits = pair_splits(d, nthr);
+  pa.nz = (cooc ? 1 : 0) + (trans ? 1 : 0);
+  pa.zbase = cooc ? 0 : 1;
+  return pa;
 }
 
 hipError_t launch_pairs(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc,
                         int32_t* trans, int32_t* part, hipStream_t st) {
   if (!cooc && !trans) return hipSuccess;
   // slice 0 co-selection, slice 1 transitions; one launch covers the requested ones.
-  const int nz = (cooc ? 1 : 0) + (trans ? 1 : 0);
-  const int zbase = cooc ? 0 : 1;
-  const int na = (d.E + 63) / 64, nb = (d.E + kPairB - 1) / kPairB;
-  const int sp = pair_splits(d);
-  hipLaunchKernelGGL(pair_kernel, dim3(na * nb, sp, nz), dim3(kPairThreads), 0, st, d, tile_mask, prev_mask, cooc,
-                     trans, part, sp, zbase);
+  const PairArgs pa = pair_args(d, tile_mask, prev_mask, cooc, trans, part, kPairThreads);
+  hipLaunchKernelGGL(pair_kernel, dim3(pair_blocks(d), pa.splits, pa.nz), dim3(kPairThreads), 0, st, d, pa);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || sp == 1) return e;
-  hipLaunchKernelGGL(pair_reduce_kernel, dim3(na * nb, kPairBlock / kPairThreads, nz), dim3(kPairThreads), 0, st, d,
-                     part, cooc, trans, sp, zbase);
+  if (e != hipSuccess || pa.splits == 1) return e;
+  hipLaunchKernelGGL(pair_reduce_kernel, dim3(pair_blocks(d), kPairBlock / kPairThreads, pa.nz), dim3(kPairThreads), 0,
+                     st, d, pa);
   return hipGetLastError();
 }
 
