@@ -49,7 +49,9 @@ def _setup(l):
     l.oracle_route.argtypes = [vp] * 9
     l.oracle_plan.argtypes = [vp] * 12 + [ctypes.c_int32, vp]
     l.oracle_dispatch.argtypes = [vp, ctypes.c_int32] + [vp] * 9
-    for f in (l.oracle_params, l.oracle_domain_budget, l.oracle_route, l.oracle_plan, l.oracle_dispatch):
+    l.oracle_combine.argtypes = [vp] * 5
+    for f in (l.oracle_params, l.oracle_domain_budget, l.oracle_route, l.oracle_plan, l.oracle_dispatch,
+              l.oracle_combine):
         f.restype = ctypes.c_int
     return l
 
@@ -135,6 +137,20 @@ def dispatch(cfg: OracleCfg, n_inst: int, inst_rank: np.ndarray, slot_inst: np.n
     if rc != 0:
         raise ValueError("oracle_dispatch failed (%d)" % rc)
     out["dispatch"] = disp
+    return out
+
+
+def combine(cfg: OracleCfg, topk_val: np.ndarray, slot_pos: np.ndarray, expert_out: np.ndarray, l=None) -> np.ndarray:
+    """Gate-weighted combine in float64 (see oracle_combine); expert_out holds bf16 bit patterns."""
+    l = l or lib()
+    T, k, H = cfg.T, cfg.k, cfg.H
+    v = np.ascontiguousarray(topk_val, np.float32).reshape(T, k)
+    sp = np.ascontiguousarray(slot_pos, np.int32).reshape(T * k)
+    x = np.ascontiguousarray(expert_out).view(np.uint16).reshape(T * k, H)
+    out = np.zeros((T, H), np.float64)
+    rc = l.oracle_combine(ctypes.byref(cfg), _p(v), _p(sp), _p(x), _p(out))
+    if rc != 0:
+        raise ValueError("oracle_combine failed (%d)" % rc)
     return out
 
 

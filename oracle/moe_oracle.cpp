@@ -413,3 +413,45 @@ extern "C" int oracle_dispatch(const oracle_cfg* c, int32_t n_inst, const int32_
       std::memcpy(dispatch + pos * H, hidden + (int64_t)(perm[pos] / k) * H, (size_t)H * sizeof(uint16_t));
   return 0;
 }
+
+// Gate-weighted combine -- the return path of the dispatch ([TopoEP] section
+// 2.1, Fig. 1: each token's expert outputs come back and are summed).  The
+// pages do not define the weights; the reading taken is the softmax of the k
+// selected logits, subtracting their maximum before exp.  In double:
+//   w[t][j]   = exp(v[t][j] - max_j v[t][j]) / sum_j' exp(v[t][j'] - max)
+//   out[t][h] = sum over j = 0..k-1 of w[t][j] * expert_out[slot_pos[t*k+j]][h]
+// A non-finite selected logit is a precondition violation (-4).
+extern "C" int oracle_combine(const oracle_cfg* c, const float* topk_val, const int32_t* slot_pos,
+                              const uint16_t* expert_out, double* out) {
+  if (!valid(c)) return -1;
+  const int64_t T = c->T, k = c->k, H = c->H, N = T * k;
+  if (T > 0 && (!topk_val || !slot_pos || !expert_out || !out)) return -1;
+  for (int64_t q = 0; q < N; ++q)
+    if (slot_pos[q] < 0 || slot_pos[q] >= N) return -1;
+  std::vector<double> w(k);
+  for (int64_t t = 0; t < T; ++t) {
+    double m = -INFINITY;
+    for (int64_t j = 0; j < k; ++j) {
+      const double v = topk_val[t * k + j];
+      if (!std::isfinite(v)) return -4;
+      m = std::max(m, v);
+    }
+    double s = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      w[j] = std::exp((double)topk_val[t * k + j] - m);
+      s += w[j];
+    }
+    for (int64_t j = 0; j < k; ++j) w[j] /= s;
+    for (int64_t h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < k; ++j) {
+        const uint32_t bits = (uint32_t)expert_out[(int64_t)slot_pos[t * k + j] * H + h] << 16;
+        float x;
+        std::memcpy(&x, &bits, sizeof(x));
+        acc += w[j] * (double)x;
+      }
+      out[t * H + h] = acc;
+    }
+  }
+  return 0;
+}

@@ -13,6 +13,8 @@
  *             Eqs. 9 and 10, Fig. 9).
  *   [Coupling] "Expert Coupling in MoE Pretraining" -- within-layer expert
  *             co-selection counts and layer-to-layer routing counts.
+ *   Combine: [TopoEP] section 2.1, Fig. 1 (the return path of the dispatch);
+ *             the gate weights are a reading (softmax of the selected logits).
  *
  * Every function returns 0 on success or a negative status:
  *   -1 invalid argument / configuration, -4 a NaN gate logit,
@@ -66,6 +68,12 @@ int oracle_dispatch(const oracle_cfg* c, int32_t n_inst, const int32_t* inst_ran
                     const int32_t* slot_inst, const uint16_t* hidden,
                     int32_t* perm, int32_t* slot_pos, int32_t* inst_offset, int32_t* rank_offset,
                     int32_t* slot_rank, uint16_t* dispatch);
+
+/* Gate-weighted combine, in double: out[t][h] = sum_j w[t][j] *
+ * expert_out[slot_pos[t*k+j]][h] with w the softmax of the k selected logits
+ * topk_val[t][*].  expert_out: bf16 rows [T*k][H] in dispatch order. */
+int oracle_combine(const oracle_cfg* c, const float* topk_val, const int32_t* slot_pos,
+                   const uint16_t* expert_out, double* out);
 
 #ifdef __cplusplus
 }

@@ -56,6 +56,12 @@ MUTANTS = [
      "d.n_slot = c->n_slot > 0 ? c->n_slot : per_dom / c->G;"),
     ("expert bytes halved", "d.W = c->W >= 0 ? c->W : 9LL * c->H * c->H / 4;", "d.W = c->W >= 0 ? c->W : 9LL * c->H * c->H / 8;"),
     ("token bytes one byte per element", "d.S = c->S > 0 ? c->S : 2LL * c->H;", "d.S = c->S > 0 ? c->S : 1LL * c->H;"),
+    ("combine weights reversed", "acc += w[j] * (double)x;", "acc += w[k - 1 - j] * (double)x;"),
+    ("combine without the maximum", "w[j] = std::exp((double)topk_val[t * k + j] - m);",
+     "w[j] = std::exp((double)topk_val[t * k + j]);"),
+    ("combine not normalised", "for (int64_t j = 0; j < k; ++j) w[j] /= s;", ""),
+    ("combine ignores the dispatch positions", "expert_out[(int64_t)slot_pos[t * k + j] * H + h]",
+     "expert_out[(t * k + j) * H + h]"),
 ]
 
 
@@ -69,6 +75,7 @@ def test_pins_reject_mutant(tmp_path, name, old, new):
     lib = obuild.build(out=str(tmp_path / "libmutant.so"), src=str(src))
     env = dict(os.environ, MOE_ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_combine.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "the pins accept the mutant '%s'" % name
