@@ -11,6 +11,8 @@ the inputs resident in HBM.  Prints ONE JSON line:
               runs on, in a second pass of the same steps as three calls)
               against the 8 TB/s HBM peak
   chain       the same for the whole step (algorithmic bytes of every call)
+  combine     the return path (moe_plan_combine) on the same layer, timed
+              separately with the dispatch buffer as the expert outputs
   cpu_baseline  the CPU oracle on one core over a bounded sample
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -56,7 +58,10 @@ def algorithmic_bytes(w) -> dict:
     dispatch = (T * H * 2              # hidden rows read once
                 + T * k * H * 2        # dispatch rows written
                 + T * k * 4 * 4)       # slot instance/rank read, slot position and permutation written
-    return dict(route=route, plan=plan, dispatch=dispatch, total=(route + plan + dispatch) * w.L)
+    combine = (T * k * H * 2             # expert output rows read
+               + T * H * 2             # combined rows written
+               + T * k * 4 * 2)        # selected logits and slot positions read
+    return dict(route=route, plan=plan, dispatch=dispatch, combine=combine, total=(route + plan + dispatch) * w.L)
 
 
 def source_hash(path: str) -> str:
@@ -165,10 +170,24 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
             per["route"].append(e[0].elapsed_time(e[1]))
             per["plan"].append(e[1].elapsed_time(e[2]))
             per["dispatch"].append(e[2].elapsed_time(e[3]))
+    # Combine (the return path): the dispatch buffer stands in for the expert outputs.
+    comb_out = [torch.empty((w.T, w.H), dtype=torch.int16, device=dev) for _ in layers]
+    for l, layer in enumerate(layers):
+        layer.combine(layer.dispatch_out.dispatch, out=comb_out[l])
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps * w.L)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        for l, layer in enumerate(layers):
+            e = cev[s * w.L + l]
+            e[0].record(stream)
+            layer.combine(layer.dispatch_out.dispatch, out=comb_out[l])
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    comb_ms = [e[0].elapsed_time(e[1]) for e in cev]
     status = [layer.status() for layer in layers]
     for layer in layers:
         layer.close()
-    return dict(ms_total=ms_total, per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
+    return dict(ms_total=ms_total, combine_ms=float(np.mean(comb_ms)), per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
                 per_call_ms_min={k: float(np.min(v)) for k, v in per.items()}, status=status,
                 device=torch.cuda.get_device_name(dev))
 
@@ -237,6 +256,10 @@ def main():
                      "launch_ms": disp_ms},
         "chain": {"algorithmic_bytes_per_step": ab["total"], "achieved": chain_gbs, "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": chain_gbs / HBM_PEAK_GBS},
+        "combine": {"kernel": "combine (moe_plan_combine)", "us": g["combine_ms"] * 1e3,
+                    "algorithmic_bytes_per_launch": ab["combine"],
+                    "achieved": ab["combine"] / (g["combine_ms"] / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": ab["combine"] / (g["combine_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS},
         "per_call_us": {k: v * 1e3 for k, v in g["per_call_ms"].items()},
         "per_call_us_min": {k: v * 1e3 for k, v in g["per_call_ms_min"].items()},
         "cpu_baseline": cpu,

@@ -275,6 +275,25 @@ int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* prev_topk, c
                   void* stream);
 
 /*
+ * Gate-weighted combine, the return path of the dispatch [TopoEP section 2.1,
+ * Fig. 1]: for every token t,
+ *   out[t][:] = bf16( sum over j = 0..k-1 of w[t][j] * expert_out[slot_pos[t*k+j]][:] )
+ * with w[t][*] the softmax of the k selected logits topk_val[t][*] (their
+ * maximum subtracted before exp), accumulated in fp32 in slot order and
+ * rounded once to bf16, nearest even.  The weights are a reading: the pages
+ * do not define them.
+ *   topk_val    float [T][k] (device): moe_plan_route's topk_val.
+ *   slot_pos    int32 [T*k] (device): moe_plan_dispatch's slot_pos.
+ *   expert_out  uint16 [T*k][H] bf16 rows in dispatch order (device).
+ *   out         uint16 [T][H] bf16 (device), fully overwritten.
+ * A non-finite selected logit sets MOE_STATUS_NAN_LOGIT (that token's output
+ * is then unspecified); a position outside [0, T*k) sets
+ * MOE_STATUS_PLAN_CHECK and the slot is skipped.
+ */
+int moe_plan_combine(moe_plan_t h, const float* topk_val, const int32_t* slot_pos, const uint16_t* expert_out,
+                     uint16_t* out, void* stream);
+
+/*
  * Synchronise the handle's last stream, copy the device status word to
  * *host_flags (MOE_STATUS_* bits, 0 when clean) and clear it.
  */

@@ -70,7 +70,7 @@ class moe_dispatch_out(ctypes.Structure):
 
 
 EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
-           "moe_plan_dispatch", "moe_plan_step", "moe_plan_status", "moe_plan_destroy")
+           "moe_plan_dispatch", "moe_plan_step", "moe_plan_combine", "moe_plan_status", "moe_plan_destroy")
 
 _LIB = None
 
@@ -94,6 +94,7 @@ def lib():
         l.moe_plan_plan.argtypes = [vp, vp, vp, vp]
         l.moe_plan_dispatch.argtypes = [vp, vp, vp, vp, vp]
         l.moe_plan_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        l.moe_plan_combine.argtypes = [vp, vp, vp, vp, vp, vp]
         l.moe_plan_status.argtypes = [vp, vp]
         l.moe_plan_destroy.argtypes = [vp]
         l.moe_plan_destroy.restype = None
@@ -142,6 +143,10 @@ def moe_plan_step(h, logits: int, prev_topk, hidden: int, route: moe_route_out, 
                   out: moe_dispatch_out, stream: int):
     _check("moe_plan_step", lib().moe_plan_step(h, logits, prev_topk, hidden, ctypes.byref(route), ctypes.byref(plan),
                                                 ctypes.byref(out), stream))
+
+
+def moe_plan_combine(h, topk_val: int, slot_pos: int, expert_out: int, out: int, stream: int):
+    _check("moe_plan_combine", lib().moe_plan_combine(h, topk_val, slot_pos, expert_out, out, stream))
 
 
 def moe_plan_status(h) -> int:
@@ -282,6 +287,22 @@ class Layer:
         moe_plan_step(self.handle, _ptr(logits), _ptr(prev_topk), _ptr(hidden), self._route_s, self._plan_s,
                       self._disp_s, self._stream(stream))
         return self.route_out, self.plan_out, self.dispatch_out
+
+    def combine(self, expert_out, out=None, stream=None):
+        """Gate-weighted combine of expert outputs in dispatch order back to token order
+        (moe_plan_combine), using this layer's topk_val and slot_pos."""
+        T, k, H = self.cfg.T, self.cfg.k, self.cfg.H
+        self._check_tensor(expert_out, (T * k, H), None)
+        if expert_out.element_size() != 2:
+            raise TypeError("expert_out must be a 16-bit (bf16) tensor")
+        if self.route_out.topk_val is None:
+            raise ValueError("combine needs the layer's topk_val buffer (create the Layer with topk_val=True)")
+        if out is None:
+            out = self.torch.empty((T, H), dtype=expert_out.dtype, device=self.device)
+        self._check_tensor(out, (T, H), None)
+        moe_plan_combine(self.handle, _ptr(self.route_out.topk_val), _ptr(self.dispatch_out.slot_pos),
+                         _ptr(expert_out), _ptr(out), self._stream(stream))
+        return out
 
     def status(self) -> int:
         return moe_plan_status(self.handle)

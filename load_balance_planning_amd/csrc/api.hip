@@ -295,6 +295,16 @@ extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* p
   return hip_rc(e);
 }
 
+extern "C" int moe_plan_combine(moe_plan_t h, const float* topk_val, const int32_t* slot_pos,
+                                const uint16_t* expert_out, uint16_t* out, void* stream) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  const moe::Dims& d = h->d;
+  if (d.T > 0 && (!topk_val || !slot_pos || !expert_out || !out)) return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_rc(moe::launch_combine(d, topk_val, slot_pos, expert_out, out, h->ws.status, st));
+}
+
 extern "C" int moe_plan_status(moe_plan_t h, int32_t* host_flags) {
   if (!h || !host_flags) return MOE_ERR_INVALID_ARG;
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;

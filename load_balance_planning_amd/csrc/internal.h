@@ -84,6 +84,9 @@ hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t*
                          const int32_t* inst_offset, const uint16_t* hidden, int32_t* perm, int32_t* slot_pos,
                          uint16_t* dispatch, int32_t* status, hipStream_t st);
 
+hipError_t launch_combine(const Dims& d, const float* topk_val, const int32_t* slot_pos, const uint16_t* expert_out,
+                          uint16_t* out, int32_t* status, hipStream_t st);
+
 // LDS bytes the plan and scan kernels need for these dimensions.
 size_t plan_lds_bytes(const Dims& d);
 size_t scan_lds_bytes(const Dims& d);
