@@ -254,7 +254,7 @@ extern "C" int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const u
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm,
-                                          out->slot_pos, out->dispatch, h->ws.status, st);
+                                          out->slot_pos, out->dispatch, h->ws, st);
   return hip_rc(e);
 }
 
@@ -287,10 +287,18 @@ extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* p
                          h->ws, st);
   if (e == hipSuccess) h->acc_parity ^= 1;
   if (e == hipSuccess) e = fork_pairs(h, route, prev, st);
-  if (e == hipSuccess) e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *plan, h->ws, st);
-  if (e == hipSuccess)
-    e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm, out->slot_pos,
-                           out->dispatch, h->ws.status, st);
+  if (moe::gather_can_assign(d, hidden, out->dispatch)) {
+    // the gather assigns its token's slots itself, overlapping the row load
+    if (e == hipSuccess)
+      e = moe::launch_assign_gather(d, route->topk_idx, route->tile_mask, route->tile_base, *plan, hidden, out->perm,
+                                    out->slot_pos, out->dispatch, h->ws, st);
+  } else {
+    if (e == hipSuccess)
+      e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *plan, h->ws, st);
+    if (e == hipSuccess)
+      e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm,
+                             out->slot_pos, out->dispatch, h->ws, st);
+  }
   if (e == hipSuccess) e = join_pairs(h, route, prev, st);
   return hip_rc(e);
 }

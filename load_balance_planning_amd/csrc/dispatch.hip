@@ -13,31 +13,66 @@
 // k times (and measured slower on MI355X).  Plain stores: on MI355X they beat
 // non-temporal ones for this write pattern.
 #include "internal.h"
+#include "slot_assign.h"
 
 namespace moe {
 namespace {
 
-// One workgroup per token: threads j < k place slot t*k+j, then the whole
-// workgroup streams the row into its k destinations (16-byte vectors).
-template <int VPT>
+// Inputs of the slot assignment when the gather does it (single-call step).
+struct AssignIn {
+  const int32_t* topk;
+  const uint64_t* tile_mask;
+  const int32_t* tile_base;
+  const int32_t* quota;
+  int32_t* slot_inst;  // written
+  int32_t* slot_rank;  // written
+};
+
+// One workgroup per token.  Threads j < k place slot t*k+j -- reading its
+// instance and rank, or with ASSIGN computing them from the plan
+// (slot_assign.h) and writing them; the workgroup loads its hidden row (the
+// first 256*VPT vectors) and writes it to its k destinations (16-byte
+// vectors, plain stores).
+template <int VPT, bool ASSIGN>
 __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* __restrict__ slot_inst,
                                                          const int32_t* __restrict__ slot_rank,
                                                          const int32_t* __restrict__ inst_offset,
                                                          const uint4* __restrict__ hidden, int32_t* __restrict__ perm,
                                                          int32_t* __restrict__ slot_pos, uint4* __restrict__ dispatch,
-                                                         int32_t* __restrict__ status) {
+                                                         AssignIn as, Workspace ws) {
   __shared__ int32_t pos_s[kMaxK];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t N = (int64_t)d.T * d.k;
   const int vpr = d.H / 8;
+  const uint4* src = hidden + t * vpr;
+  // Measured on MI355X: with the long chain of the assignment, issuing the
+  // row loads first and overlapping them pays; with the two loads of a plain
+  // placement, loading after the positions is faster.
+  constexpr bool kLoadFirst = ASSIGN;
+  uint4 v[VPT];
+  if (kLoadFirst) {
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int c = tid + u * 256;
+      if (c < vpr) v[u] = src[c];
+    }
+  }
   if (tid < d.k) {
     const int64_t sigma = t * d.k + tid;
-    const int i = slot_inst[sigma];
+    int i, r;
+    if (ASSIGN) {
+      assign_slot(d, sigma, as.topk, as.tile_mask, as.tile_base, as.quota, ws, i, r);
+      as.slot_inst[sigma] = i;
+      as.slot_rank[sigma] = r;
+    } else {
+      i = slot_inst[sigma];
+      r = slot_rank[sigma];
+    }
     int64_t p = -1;
-    if ((unsigned)i < (unsigned)d.cap) p = (int64_t)inst_offset[i] + slot_rank[sigma];
+    if ((unsigned)i < (unsigned)d.cap) p = (int64_t)inst_offset[i] + r;
     if (p < 0 || p >= N) {
-      atomicOr(status, MOE_STATUS_PLAN_CHECK);
+      atomicOr(ws.status, MOE_STATUS_PLAN_CHECK);
       p = -1;
     } else {
       perm[p] = (int32_t)sigma;
@@ -45,14 +80,21 @@ __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* 
     slot_pos[sigma] = (int32_t)p;
     pos_s[tid] = (int32_t)p;
   }
-  __syncthreads();
-  const uint4* src = hidden + t * vpr;
-  for (int base = 0; base < vpr; base += 256 * VPT) {
-    uint4 v[VPT];
+  if (!kLoadFirst) {
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int c = base + tid + u * 256;
+      const int c = tid + u * 256;
       if (c < vpr) v[u] = src[c];
+    }
+  }
+  __syncthreads();
+  for (int base = 0; base < vpr; base += 256 * VPT) {
+    if (base > 0) {
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int c = base + tid + u * 256;
+        if (c < vpr) v[u] = src[c];
+      }
     }
     for (int j = 0; j < d.k; ++j) {
       const int p = pos_s[j];
@@ -107,17 +149,33 @@ __global__ __launch_bounds__(256) void gather_u16_kernel(Dims d, const int32_t* 
 
 hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t* slot_rank,
                          const int32_t* inst_offset, const uint16_t* hidden, int32_t* perm, int32_t* slot_pos,
-                         uint16_t* dispatch, int32_t* status, hipStream_t st) {
+                         uint16_t* dispatch, const Workspace& ws, hipStream_t st) {
   if (d.T == 0) return hipSuccess;
   const bool vec = (d.H % 8) == 0 && ((uintptr_t)hidden % 16) == 0 && ((uintptr_t)dispatch % 16) == 0;
   if (vec) {
-    hipLaunchKernelGGL((gather_vec_kernel<4>), dim3(d.T), dim3(256), 0, st, d, slot_inst, slot_rank, inst_offset,
-                       reinterpret_cast<const uint4*>(hidden), perm, slot_pos, reinterpret_cast<uint4*>(dispatch),
-                       status);
+    hipLaunchKernelGGL((gather_vec_kernel<4, false>), dim3(d.T), dim3(256), 0, st, d, slot_inst, slot_rank,
+                       inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                       reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws);
   } else {
     hipLaunchKernelGGL(gather_u16_kernel, dim3(d.T), dim3(256), 0, st, d, slot_inst, slot_rank, inst_offset, hidden,
-                       perm, slot_pos, dispatch, status);
+                       perm, slot_pos, dispatch, ws.status);
   }
+  return hipGetLastError();
+}
+
+bool gather_can_assign(const Dims& d, const uint16_t* hidden, const uint16_t* dispatch) {
+  return (d.H % 8) == 0 && ((uintptr_t)hidden % 16) == 0 && ((uintptr_t)dispatch % 16) == 0;
+}
+
+hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
+                                const int32_t* tile_base, const moe_plan_out& plan, const uint16_t* hidden,
+                                int32_t* perm, int32_t* slot_pos, uint16_t* dispatch, const Workspace& ws,
+                                hipStream_t st) {
+  if (d.T == 0) return hipSuccess;
+  const AssignIn as{topk_idx, tile_mask, tile_base, plan.quota, plan.slot_inst, plan.slot_rank};
+  hipLaunchKernelGGL((gather_vec_kernel<4, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr,
+                     plan.inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                     reinterpret_cast<uint4*>(dispatch), as, ws);
   return hipGetLastError();
 }
 

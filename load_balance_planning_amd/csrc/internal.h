@@ -82,7 +82,14 @@ hipError_t launch_assign(const Dims& d, const int32_t* topk_idx, const uint64_t*
                          const int32_t* tile_base, const moe_plan_out& out, const Workspace& ws, hipStream_t st);
 hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t* slot_rank,
                          const int32_t* inst_offset, const uint16_t* hidden, int32_t* perm, int32_t* slot_pos,
-                         uint16_t* dispatch, int32_t* status, hipStream_t st);
+                         uint16_t* dispatch, const Workspace& ws, hipStream_t st);
+// The gather that also assigns the slots (writes plan.slot_inst / slot_rank);
+// only for 16-byte-aligned rows with H a multiple of 8 (gather_can_assign).
+bool gather_can_assign(const Dims& d, const uint16_t* hidden, const uint16_t* dispatch);
+hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
+                                const int32_t* tile_base, const moe_plan_out& plan, const uint16_t* hidden,
+                                int32_t* perm, int32_t* slot_pos, uint16_t* dispatch, const Workspace& ws,
+                                hipStream_t st);
 
 hipError_t launch_combine(const Dims& d, const float* topk_val, const int32_t* slot_pos, const uint16_t* expert_out,
                           uint16_t* out, int32_t* status, hipStream_t st);

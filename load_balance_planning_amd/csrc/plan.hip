@@ -19,6 +19,7 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "slot_assign.h"
 #include "tile_scan.h"
 
 namespace moe {
@@ -956,39 +957,8 @@ __global__ __launch_bounds__(256) void assign_kernel(Dims d, const int32_t* __re
   const int64_t sigma = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t N = (int64_t)d.T * d.k;
   if (sigma >= N) return;
-  const int64_t t = sigma / d.k;
-  const int s = (int)(t / d.Tr);
-  const int tl = (int)(t - (int64_t)s * d.Tr);
-  const int x = s * d.C + (tl >> 6);
-  const int bit = tl & 63;
-  const int e = topk[sigma];
-  int inst = -1, rank = -1;
-  if ((unsigned)e < (unsigned)d.E) {
-    const uint64_t m = tile_mask[(int64_t)x * d.E + e];
-    const int low = __popcll(m & ((1ull << bit) - 1ull));
-    const int base = tile_base[(int64_t)x * d.E + e];
-    const int o0 = ws.einst_off[e], o1 = ws.einst_off[e + 1];
-    if (o1 - o0 == 1) {
-      // One instance: its segment holds the expert's slots of all sources in token order.
-      inst = ws.einst_list[o0];
-      rank = base + low;
-    } else {
-      const int p = base - tile_base[(int64_t)s * d.C * d.E + e] + low;
-      int cum = 0;
-      for (int a = o0; a < o1; ++a) {
-        const int i = ws.einst_list[a];
-        if ((unsigned)i >= (unsigned)d.cap) break;
-        const int qv = quota[(int64_t)s * d.cap + i];
-        if (p < cum + qv) {
-          inst = i;
-          rank = ws.colpre[(int64_t)i * d.R + s] + (p - cum);
-          break;
-        }
-        cum += qv;
-      }
-    }
-  }
-  if (inst < 0) atomicOr(ws.status, MOE_STATUS_PLAN_CHECK);
+  int inst, rank;
+  assign_slot(d, sigma, topk, tile_mask, tile_base, quota, ws, inst, rank);
   slot_inst[sigma] = inst;
   slot_rank[sigma] = rank;
 }
