@@ -50,8 +50,11 @@ def _setup(l):
     l.oracle_plan.argtypes = [vp] * 12 + [ctypes.c_int32, vp]
     l.oracle_dispatch.argtypes = [vp, ctypes.c_int32] + [vp] * 9
     l.oracle_combine.argtypes = [vp] * 5
+    l.oracle_place.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp]
+    l.oracle_dedup.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp, vp]
+    l.oracle_dedup_dispatch.argtypes = [vp, vp, vp, ctypes.c_int32] + [vp] * 7
     for f in (l.oracle_params, l.oracle_domain_budget, l.oracle_route, l.oracle_plan, l.oracle_dispatch,
-              l.oracle_combine):
+              l.oracle_combine, l.oracle_place, l.oracle_dedup, l.oracle_dedup_dispatch):
         f.restype = ctypes.c_int
     return l
 
@@ -151,6 +154,66 @@ def combine(cfg: OracleCfg, topk_val: np.ndarray, slot_pos: np.ndarray, expert_o
     rc = l.oracle_combine(ctypes.byref(cfg), _p(v), _p(sp), _p(x), _p(out))
     if rc != 0:
         raise ValueError("oracle_combine failed (%d)" % rc)
+    return out
+
+
+def place(cfg: OracleCfg, cooc: np.ndarray, max_swaps: int = -1, l=None) -> dict:
+    """Correlated expert placement (see oracle_place)."""
+    l = l or lib()
+    E, R = cfg.E, cfg.R
+    C = np.ascontiguousarray(cooc, np.int32).reshape(E, E)
+    out = dict(expert_rank=np.zeros(E, np.int32), rank_experts=np.zeros((R, E // R), np.int32))
+    intra = np.zeros(1, np.int64)
+    ns = np.zeros(1, np.int32)
+    rc = l.oracle_place(ctypes.byref(cfg), _p(C), int(max_swaps), _p(out["expert_rank"]), _p(out["rank_experts"]),
+                        _p(intra), _p(ns))
+    if rc != 0:
+        raise ValueError("oracle_place failed (%d)" % rc)
+    out["intra"] = int(intra[0])
+    out["n_swaps"] = int(ns[0])
+    return out
+
+
+def _keys(cfg, slot_key, key_rank):
+    sk = np.ascontiguousarray(slot_key, np.int32).reshape(cfg.T * cfg.k)
+    kr = None if key_rank is None else np.ascontiguousarray(key_rank, np.int32).reshape(-1)
+    return sk, kr, (0 if kr is None else int(kr.size))
+
+
+def dedup(cfg: OracleCfg, slot_key: np.ndarray, key_rank: np.ndarray | None = None, l=None) -> dict:
+    """Deduplicated row counts (see oracle_dedup)."""
+    l = l or lib()
+    T, R = cfg.T, cfg.R
+    sk, kr, nk = _keys(cfg, slot_key, key_rank)
+    out = dict(tok_ranks=np.zeros(T, np.int32), rank_rows=np.zeros((R, R), np.int32),
+               rank_slots=np.zeros((R, R), np.int32))
+    rc = l.oracle_dedup(ctypes.byref(cfg), _p(sk), _p(kr), nk, _p(out["tok_ranks"]), _p(out["rank_rows"]),
+                        _p(out["rank_slots"]))
+    if rc != 0:
+        raise ValueError("oracle_dedup failed (%d)" % rc)
+    return out
+
+
+def dedup_dispatch(cfg: OracleCfg, slot_key: np.ndarray, key_rank: np.ndarray | None = None,
+                   hidden: np.ndarray | None = None, l=None) -> dict:
+    """Deduplicated dispatch layout and row copy (see oracle_dedup_dispatch)."""
+    l = l or lib()
+    T, k, R, H = cfg.T, cfg.k, cfg.R, cfg.H
+    N = T * k
+    sk, kr, nk = _keys(cfg, slot_key, key_rank)
+    out = dict(n_rows=np.zeros(1, np.int32), row_token=np.zeros(N, np.int32), row_slots=np.zeros(N, np.int32),
+               rank_row_offset=np.zeros(R + 1, np.int32), slot_row=np.zeros(N, np.int32))
+    disp = None
+    if hidden is not None:
+        hidden = np.ascontiguousarray(hidden, np.uint16).reshape(T, H)
+        disp = np.zeros((N, H), np.uint16)
+    rc = l.oracle_dedup_dispatch(ctypes.byref(cfg), _p(sk), _p(kr), nk, _p(hidden), _p(out["n_rows"]),
+                                 _p(out["row_token"]), _p(out["row_slots"]), _p(out["rank_row_offset"]),
+                                 _p(out["slot_row"]), _p(disp))
+    if rc != 0:
+        raise ValueError("oracle_dedup_dispatch failed (%d)" % rc)
+    out["n_rows"] = int(out["n_rows"][0])
+    out["ddispatch"] = None if disp is None else disp[:out["n_rows"]]
     return out
 
 

@@ -455,3 +455,213 @@ extern "C" int oracle_combine(const oracle_cfg* c, const float* topk_val, const 
   }
   return 0;
 }
+
+// ---------------------------------------------------------------------------
+// Correlated expert placement ([Coupling] "Moving Correlated Experts
+// Together"): experts are the nodes of a graph whose edge weights are the
+// co-selection counts C[a][b]; the graph is partitioned over the R ranks with
+// exactly E/R experts on every rank, keeping heavily co-selected experts on one
+// rank.  The page names the goal and the constraint but no algorithm; the
+// reading taken here is the objective "co-selection weight inside the ranks"
+//   intra = sum over pairs a < b on the same rank of C[a][b]
+// (for top-2 routing this is exactly the number of rows a deduplicating
+// dispatcher saves), maximised by greedy graph growth followed by pair-swap
+// local search:
+//   growth: ranks are filled in order 0..R-1.  The first expert of a rank is
+//     the unplaced expert with the largest total co-selection deg(e) =
+//     sum_x C[e][x]; each further one is the unplaced expert with the largest
+//     co-selection with the experts already on the rank.  Ties: lower e.
+//   refinement: repeatedly swap the two experts a < b on different ranks whose
+//     exchange raises intra the most (ties: lower a, then lower b), while the
+//     gain is positive, at most max_swaps times (max_swaps < 0: 4096).
+// The gain of exchanging a (rank ra) and b (rank rb), with
+// aff[r][x] = sum over y on rank r of C[x][y], is
+//   aff[rb][a] - aff[ra][a] + aff[ra][b] - aff[rb][b] - 2 C[a][b].
+// cooc must be symmetric with a zero diagonal, entries >= 0, every row sum
+// below 2^31 (what oracle_route writes); otherwise -1.
+// ---------------------------------------------------------------------------
+namespace {
+
+bool cooc_valid(int64_t E, const int32_t* C) {
+  for (int64_t a = 0; a < E; ++a) {
+    int64_t sum = 0;
+    if (C[a * E + a] != 0) return false;
+    for (int64_t b = 0; b < E; ++b) {
+      if (C[a * E + b] < 0 || C[a * E + b] != C[b * E + a]) return false;
+      sum += C[a * E + b];
+    }
+    if (sum > INT32_MAX) return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" int oracle_place(const oracle_cfg* c, const int32_t* cooc, int32_t max_swaps, int32_t* expert_rank,
+                            int32_t* rank_experts, int64_t* intra, int32_t* n_swaps) {
+  if (!valid(c) || !cooc || !expert_rank || !rank_experts || !intra || !n_swaps) return -1;
+  const int64_t E = c->E, R = c->R, Er = E / R;
+  if (!cooc_valid(E, cooc)) return -1;
+  const int64_t cap = max_swaps < 0 ? 4096 : max_swaps;
+  auto C = [&](int64_t a, int64_t b) { return (int64_t)cooc[a * E + b]; };
+
+  std::vector<int64_t> rank(E, -1), deg(E, 0), aff(R * E, 0);
+  for (int64_t e = 0; e < E; ++e)
+    for (int64_t x = 0; x < E; ++x) deg[e] += C(e, x);
+
+  // Greedy growth, one rank after the other.
+  for (int64_t r = 0; r < R; ++r) {
+    for (int64_t m = 0; m < Er; ++m) {
+      int64_t pick = -1, best = -1;
+      for (int64_t e = 0; e < E; ++e) {
+        if (rank[e] >= 0) continue;
+        const int64_t score = m == 0 ? deg[e] : aff[r * E + e];
+        if (score > best) { best = score; pick = e; }
+      }
+      rank[pick] = r;
+      for (int64_t x = 0; x < E; ++x) aff[r * E + x] += C(x, pick);
+    }
+  }
+
+  // Pair-swap refinement.
+  int64_t swaps = 0;
+  while (swaps < cap) {
+    int64_t ba = -1, bb = -1, bg = 0;
+    for (int64_t a = 0; a < E; ++a)
+      for (int64_t b = a + 1; b < E; ++b) {
+        const int64_t ra = rank[a], rb = rank[b];
+        if (ra == rb) continue;
+        const int64_t g = aff[rb * E + a] - aff[ra * E + a] + aff[ra * E + b] - aff[rb * E + b] - 2 * C(a, b);
+        if (g > bg) { bg = g; ba = a; bb = b; }
+      }
+    if (ba < 0) break;
+    const int64_t ra = rank[ba], rb = rank[bb];
+    for (int64_t x = 0; x < E; ++x) {
+      aff[ra * E + x] += C(x, bb) - C(x, ba);
+      aff[rb * E + x] += C(x, ba) - C(x, bb);
+    }
+    rank[ba] = rb;
+    rank[bb] = ra;
+    ++swaps;
+  }
+
+  int64_t w = 0;
+  for (int64_t a = 0; a < E; ++a)
+    for (int64_t b = a + 1; b < E; ++b)
+      if (rank[a] == rank[b]) w += C(a, b);
+  std::vector<int64_t> fill(R, 0);
+  for (int64_t e = 0; e < E; ++e) {
+    expert_rank[e] = (int32_t)rank[e];
+    rank_experts[rank[e] * Er + fill[rank[e]]++] = (int32_t)e;  // e ascending within each rank
+  }
+  *intra = w;
+  *n_swaps = (int32_t)swaps;
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Deduplicated dispatch ([Coupling] "Moving Correlated Experts Together",
+// Fig. 3): a token whose selected experts share a destination rank is sent
+// there once, with the list of its slots that rank serves.  The rank of slot
+// q = t*k+j is key_rank[slot_key[q]] -- slot_key holds top-k expert ids with
+// key_rank a placement (expert -> rank), or instance ids with the planner's
+// instance ranks; key_rank = NULL means the contiguous placement
+// slot_key[q] / (E/R).  Token t comes from source rank t / (T/R).
+//   tok_ranks[t]     distinct destination ranks of token t
+//   rank_rows[s][r]  rows sent from source s to rank r: tokens of s with at
+//                    least one slot on r (the deduplicated count)
+//   rank_slots[s][r] slots of source s on rank r (one row each without
+//                    deduplication); nullable
+// Keys outside [0, n_keys) (or [0, E) without a table) and table entries
+// outside [0, R) are -1.
+// ---------------------------------------------------------------------------
+namespace {
+
+int slot_ranks(const oracle_cfg* c, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
+               std::vector<int64_t>& rank) {
+  const int64_t N = (int64_t)c->T * c->k, Er = c->E / c->R;
+  rank.assign(N, 0);
+  for (int64_t q = 0; q < N; ++q) {
+    const int64_t key = slot_key[q];
+    if (key_rank) {
+      if (key < 0 || key >= n_keys) return -1;
+      rank[q] = key_rank[key];
+    } else {
+      if (key < 0 || key >= c->E) return -1;
+      rank[q] = key / Er;
+    }
+    if (rank[q] < 0 || rank[q] >= c->R) return -1;
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" int oracle_dedup(const oracle_cfg* c, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
+                            int32_t* tok_ranks, int32_t* rank_rows, int32_t* rank_slots) {
+  if (!valid(c) || !tok_ranks || !rank_rows) return -1;
+  const int64_t T = c->T, k = c->k, R = c->R, Tr = T / R;
+  if (T > 0 && !slot_key) return -1;
+  std::vector<int64_t> rank;
+  if (slot_ranks(c, slot_key, key_rank, n_keys, rank) != 0) return -1;
+  for (int64_t i = 0; i < R * R; ++i) {
+    rank_rows[i] = 0;
+    if (rank_slots) rank_slots[i] = 0;
+  }
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t s = t / Tr;
+    int64_t distinct = 0;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t r = rank[t * k + j];
+      if (rank_slots) rank_slots[s * R + r] += 1;
+      bool seen = false;
+      for (int64_t i = 0; i < j; ++i) seen = seen || rank[t * k + i] == r;
+      if (!seen) {
+        ++distinct;
+        rank_rows[s * R + r] += 1;
+      }
+    }
+    tok_ranks[t] = (int32_t)distinct;
+  }
+  return 0;
+}
+
+// The deduplicated dispatch layout and row copy: one row per (destination
+// rank, token) pair that has at least one slot, ordered by rank, then token.
+//   n_rows[0]          number of rows (the sum of tok_ranks)
+//   row_token[p]       token of row p
+//   row_slots[p]       bit j set when slot j of that token goes to that rank
+//   rank_row_offset[r] first row of rank r; entry R is n_rows
+//   slot_row[q]        row carrying slot q
+//   ddispatch[p][:]    = hidden[row_token[p]][:] (nullable)
+// Capacity T*k rows; entries from n_rows on are -1 (ddispatch rows untouched).
+extern "C" int oracle_dedup_dispatch(const oracle_cfg* c, const int32_t* slot_key, const int32_t* key_rank,
+                                     int32_t n_keys, const uint16_t* hidden, int32_t* n_rows, int32_t* row_token,
+                                     int32_t* row_slots, int32_t* rank_row_offset, int32_t* slot_row,
+                                     uint16_t* ddispatch) {
+  if (!valid(c) || !n_rows || !row_token || !row_slots || !rank_row_offset || !slot_row) return -1;
+  const int64_t T = c->T, k = c->k, R = c->R, H = c->H, N = T * k;
+  if (k > 32 || (T > 0 && !slot_key)) return -1;
+  std::vector<int64_t> rank;
+  if (slot_ranks(c, slot_key, key_rank, n_keys, rank) != 0) return -1;
+  int64_t p = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    rank_row_offset[r] = (int32_t)p;
+    for (int64_t t = 0; t < T; ++t) {
+      uint32_t mask = 0;
+      for (int64_t j = 0; j < k; ++j)
+        if (rank[t * k + j] == r) mask |= 1u << j;
+      if (mask == 0) continue;
+      row_token[p] = (int32_t)t;
+      row_slots[p] = (int32_t)mask;
+      for (int64_t j = 0; j < k; ++j)
+        if (mask >> j & 1u) slot_row[t * k + j] = (int32_t)p;
+      if (ddispatch && hidden) std::memcpy(ddispatch + p * H, hidden + t * H, (size_t)H * sizeof(uint16_t));
+      ++p;
+    }
+  }
+  rank_row_offset[R] = (int32_t)p;
+  *n_rows = (int32_t)p;
+  for (int64_t q = p; q < N; ++q) row_token[q] = row_slots[q] = -1;
+  return 0;
+}

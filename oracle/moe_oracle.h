@@ -15,6 +15,8 @@
  *             co-selection counts and layer-to-layer routing counts.
  *   Combine: [TopoEP] section 2.1, Fig. 1 (the return path of the dispatch);
  *             the gate weights are a reading (softmax of the selected logits).
+ *   Placement and deduplication: [Coupling] "Moving Correlated Experts
+ *             Together", Fig. 3 (the partition algorithm is a reading).
  *
  * Every function returns 0 on success or a negative status:
  *   -1 invalid argument / configuration, -4 a NaN gate logit,
@@ -74,6 +76,28 @@ int oracle_dispatch(const oracle_cfg* c, int32_t n_inst, const int32_t* inst_ran
  * topk_val[t][*].  expert_out: bf16 rows [T*k][H] in dispatch order. */
 int oracle_combine(const oracle_cfg* c, const float* topk_val, const int32_t* slot_pos,
                    const uint16_t* expert_out, double* out);
+
+/* Correlated expert placement: partition of the E experts over the R ranks,
+ * exactly E/R per rank, maximising the co-selection weight kept inside ranks
+ * (greedy growth, then pair-swap refinement, at most max_swaps swaps;
+ * max_swaps < 0 means 4096).  cooc: int32 [E][E] as oracle_route writes it.
+ * expert_rank [E]; rank_experts [R][E/R] (ascending within a rank);
+ * intra [1] the kept weight; n_swaps [1]. */
+int oracle_place(const oracle_cfg* c, const int32_t* cooc, int32_t max_swaps, int32_t* expert_rank,
+                 int32_t* rank_experts, int64_t* intra, int32_t* n_swaps);
+
+/* Deduplicated row counts.  Slot q goes to rank key_rank[slot_key[q]]
+ * (key_rank NULL: slot_key[q] / (E/R)).  tok_ranks [T]; rank_rows [R][R];
+ * rank_slots [R][R] nullable. */
+int oracle_dedup(const oracle_cfg* c, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
+                 int32_t* tok_ranks, int32_t* rank_rows, int32_t* rank_slots);
+
+/* Deduplicated dispatch layout (rows by rank, then token) and row copy.
+ * Capacity T*k rows; k <= 32.  ddispatch nullable. */
+int oracle_dedup_dispatch(const oracle_cfg* c, const int32_t* slot_key, const int32_t* key_rank,
+                          int32_t n_keys, const uint16_t* hidden, int32_t* n_rows, int32_t* row_token,
+                          int32_t* row_slots, int32_t* rank_row_offset, int32_t* slot_row,
+                          uint16_t* ddispatch);
 
 #ifdef __cplusplus
 }

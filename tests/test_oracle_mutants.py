@@ -62,6 +62,20 @@ MUTANTS = [
     ("combine not normalised", "for (int64_t j = 0; j < k; ++j) w[j] /= s;", ""),
     ("combine ignores the dispatch positions", "expert_out[(int64_t)slot_pos[t * k + j] * H + h]",
      "expert_out[(t * k + j) * H + h]"),
+    ("placement seeds by lowest index", "const int64_t score = m == 0 ? deg[e] : aff[r * E + e];",
+     "const int64_t score = m == 0 ? 0 : aff[r * E + e];"),
+    ("placement growth ties to higher index", "if (score > best) { best = score; pick = e; }",
+     "if (score >= best) { best = score; pick = e; }"),
+    ("swap gain without the pair term", "aff[ra * E + b] - aff[rb * E + b] - 2 * C(a, b);",
+     "aff[ra * E + b] - aff[rb * E + b];"),
+    ("swap update reversed", "aff[ra * E + x] += C(x, bb) - C(x, ba);", "aff[ra * E + x] += C(x, ba) - C(x, bb);"),
+    ("swaps of zero gain accepted", "int64_t ba = -1, bb = -1, bg = 0;", "int64_t ba = -1, bb = -1, bg = -1;"),
+    ("dedup counts every slot", "if (!seen) {", "if (true) {"),
+    ("dedup interleaved ranks", "rank[q] = key / Er;", "rank[q] = key % c->R;"),
+    ("dedup layout tokens descending", "    for (int64_t t = 0; t < T; ++t) {\n      uint32_t mask = 0;",
+     "    for (int64_t t = T - 1; t >= 0; --t) {\n      uint32_t mask = 0;"),
+    ("dedup slot row off by one", "if (mask >> j & 1u) slot_row[t * k + j] = (int32_t)p;",
+     "if (mask >> j & 1u) slot_row[t * k + j] = (int32_t)(p + 1 < N ? p + 1 : p);"),
 ]
 
 
@@ -76,6 +90,7 @@ def test_pins_reject_mutant(tmp_path, name, old, new):
     env = dict(os.environ, MOE_ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_combine.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_combine.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_placement.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "the pins accept the mutant '%s'" % name
