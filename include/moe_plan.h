@@ -8,6 +8,12 @@
  *   moe_plan_hist      the histograms alone, from a given top-k
  *   moe_plan_plan      hot-expert replication + token re-routing
  *   moe_plan_dispatch  dispatch layout + bf16 row gather
+ *   moe_plan_step      the four above in one call
+ *   moe_plan_combine   the return path: gate-weighted sum of expert outputs
+ *   moe_plan_place     correlated expert placement from the co-selection counts
+ *   moe_plan_dedup_count / moe_plan_dedup_dispatch
+ *                      rows of a deduplicating dispatcher: counts, and the
+ *                      layout with its bf16 row gather
  * EP ranks and NVLink domains ("nodes") are logical partitions on one GPU:
  *   source rank of token t   src(t)  = t / (T/R)     (contiguous token blocks)
  *   domain of rank r          dom(r)  = r / G         (contiguous rank blocks)
@@ -20,7 +26,9 @@
  *              (section 4.3, Eqs. 9 and 10, Fig. 9), device-resident plan that
  *              drives dispatch (sections 3.1 and 5).
  *   [Coupling] "Expert Coupling in MoE Pretraining": within-layer expert
- *              co-selection counts, layer-to-layer routing counts.
+ *              co-selection counts, layer-to-layer routing counts, correlated
+ *              expert placement and deduplicated dispatch ("Moving Correlated
+ *              Experts Together", Fig. 3).
  *
  * Conventions for every call
  *   - Pointers named in the structs are HIP device pointers unless stated.
@@ -63,6 +71,10 @@ enum {
 #define MOE_STATUS_NAN_LOGIT 1
 #define MOE_STATUS_PLAN_CHECK 2
 #define MOE_STATUS_BAD_TOPK 4   /* a top-k entry out of [0, E) or repeated within a token */
+#define MOE_STATUS_BAD_PAIRS 8  /* moe_plan_place: a co-selection count < 0, a non-zero diagonal
+                                   entry or a row sum >= 2^31 */
+#define MOE_STATUS_BAD_KEY 16   /* moe_plan_dedup_*: a slot key outside the table, or a table
+                                   entry outside [0, R) */
 
 typedef struct moe_plan* moe_plan_t;
 
@@ -189,6 +201,57 @@ typedef struct {
   uint16_t* dispatch;
 } moe_dispatch_out;
 
+/*
+ * Outputs of moe_plan_place.
+ *   expert_rank   int32 [E]: rank holding expert e.
+ *   rank_experts  int32 [R][E/R]: the experts of each rank, ascending.  Giving
+ *                 expert rank_experts[p] the new id p turns the placement into
+ *                 the contiguous one moe_plan_plan assumes (main(e) = e/(E/R)):
+ *                 permute the router's expert columns accordingly.
+ *   intra         int64 [1]: co-selection weight kept inside ranks, the sum
+ *                 over expert pairs a < b on one rank of cooc[a][b].
+ *   n_swaps       int32 [1]: refinement swaps applied.
+ */
+typedef struct {
+  int32_t* expert_rank;
+  int32_t* rank_experts;
+  int64_t* intra;
+  int32_t* n_swaps;
+} moe_place_out;
+
+/*
+ * Outputs of moe_plan_dedup_count / moe_plan_dedup_dispatch.  Slot q = t*k+j
+ * goes to destination rank key_rank[slot_key[q]]; token t comes from source
+ * rank t / (T/R).
+ *   tok_ranks        int32 [T]: distinct destination ranks of token t.
+ *                    (With T = 0 the per-token and per-row pointers may be NULL.)
+ *   rank_rows        int32 [R][R]: rows sent from source s to rank r with
+ *                    deduplication -- tokens of s with at least one slot on r.
+ *   rank_slots       int32 [R][R] (nullable): slots of source s on rank r (one
+ *                    row each without deduplication).
+ * moe_plan_dedup_dispatch only (ignored by moe_plan_dedup_count):
+ *   n_rows           int32 [1]: rows of the deduplicated dispatch (sum of tok_ranks).
+ *   row_token        int32 [T*k]: token of each row; rows are ordered by
+ *                    destination rank, then token.  Entries from n_rows on are -1.
+ *   row_slots        int32 [T*k]: bit j set when slot j of the row's token goes
+ *                    to the row's rank (the local experts it serves); -1 past n_rows.
+ *   rank_row_offset  int32 [R+1]: first row of each rank; entry R is n_rows.
+ *   slot_row         int32 [T*k]: row carrying slot q.
+ *   ddispatch        uint16 [T*k][H] bf16: row p = hidden[row_token[p]];
+ *                    rows from n_rows on are not written.
+ */
+typedef struct {
+  int32_t* tok_ranks;
+  int32_t* rank_rows;
+  int32_t* rank_slots;
+  int32_t* n_rows;
+  int32_t* row_token;
+  int32_t* row_slots;
+  int32_t* rank_row_offset;
+  int32_t* slot_row;
+  uint16_t* ddispatch;
+} moe_dedup_out;
+
 /* Buffer sizes for a configuration (host only, no GPU work).  Returns
  * MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED as moe_plan_create would. */
 int moe_plan_query(const moe_plan_config* cfg, moe_plan_sizes* sizes);
@@ -292,6 +355,53 @@ int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* prev_topk, c
  */
 int moe_plan_combine(moe_plan_t h, const float* topk_val, const int32_t* slot_pos, const uint16_t* expert_out,
                      uint16_t* out, void* stream);
+
+/*
+ * Correlated expert placement [Coupling, "Moving Correlated Experts
+ * Together"]: the experts are partitioned over the R ranks, exactly E/R per
+ * rank, so that frequently co-selected experts share a rank.  The page gives
+ * the goal and the fixed count per rank, not an algorithm; this one maximises
+ * intra (see moe_place_out) by greedy growth then pair-swap refinement:
+ *   growth      ranks 0..R-1 in order; the first expert of a rank is the
+ *               unplaced one with the largest sum_x cooc[e][x], each further
+ *               one the unplaced expert with the largest co-selection with the
+ *               rank's experts so far; ties to the lower expert id;
+ *   refinement  swap the experts a < b (on different ranks) whose exchange
+ *               raises intra the most (ties: lower a, then lower b) while the
+ *               gain is positive, at most max_swaps times (< 0: 4096).
+ * cooc: int32 [E][E] (device) as moe_plan_route writes it -- symmetric, zero
+ * diagonal, entries >= 0, row sums < 2^31.  A negative entry, a non-zero
+ * diagonal or a row sum >= 2^31 sets MOE_STATUS_BAD_PAIRS (the result is
+ * then a valid partition but otherwise unspecified); asymmetric input is not
+ * detected and gives an unspecified partition.  One workgroup; time grows
+ * with E (a sequential greedy step per expert).
+ */
+int moe_plan_place(moe_plan_t h, const int32_t* cooc, int32_t max_swaps, const moe_place_out* out,
+                   void* stream);
+
+/*
+ * Deduplicated row counts [Coupling, "Moving Correlated Experts Together",
+ * Fig. 3: a token sends one row to each destination rank, however many of its
+ * experts live there].  slot_key int32 [T*k] (device): top-k expert ids or
+ * instance ids.  key_rank int32 [n_keys] (device, nullable): rank of each key
+ * -- a placement's expert_rank, or moe_plan_plan's inst_rank (n_keys = E+B);
+ * NULL means the contiguous placement key / (E/R) with keys in [0, E).  A key
+ * outside the table, or a table entry outside [0, R), sets MOE_STATUS_BAD_KEY
+ * and that slot is left out.  Writes tok_ranks, rank_rows and, when non-null,
+ * rank_slots.
+ */
+int moe_plan_dedup_count(moe_plan_t h, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
+                         const moe_dedup_out* out, void* stream);
+
+/*
+ * Deduplicated dispatch: the counts of moe_plan_dedup_count, the row layout
+ * (rank-major, tokens ascending within a rank: row of (r, t) = rank_row_offset[r]
+ * + number of earlier tokens with a slot on r) and the bf16 row copy --
+ * each hidden row read once and written to its token's distinct ranks.
+ * hidden: uint16 [T][H] (device).  A left-out slot (bad key) has slot_row -1.
+ */
+int moe_plan_dedup_dispatch(moe_plan_t h, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
+                            const uint16_t* hidden, const moe_dedup_out* out, void* stream);
 
 /*
  * Synchronise the handle's last stream, copy the device status word to

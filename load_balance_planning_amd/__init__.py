@@ -28,6 +28,8 @@ MOE_ERR_INTERNAL = -5
 MOE_STATUS_NAN_LOGIT = 1
 MOE_STATUS_PLAN_CHECK = 2
 MOE_STATUS_BAD_TOPK = 4
+MOE_STATUS_BAD_PAIRS = 8
+MOE_STATUS_BAD_KEY = 16
 
 _ERRORS = {MOE_ERR_INVALID_ARG: "invalid argument", MOE_ERR_UNSUPPORTED: "unsupported configuration",
            MOE_ERR_HIP: "HIP runtime error", MOE_ERR_NONFINITE: "non-finite gate logit",
@@ -69,8 +71,19 @@ class moe_dispatch_out(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("perm", "slot_pos", "dispatch")]
 
 
+class moe_place_out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("expert_rank", "rank_experts", "intra", "n_swaps")]
+
+
+class moe_dedup_out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "tok_ranks", "rank_rows", "rank_slots", "n_rows", "row_token", "row_slots", "rank_row_offset", "slot_row",
+        "ddispatch")]
+
+
 EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
-           "moe_plan_dispatch", "moe_plan_step", "moe_plan_combine", "moe_plan_status", "moe_plan_destroy")
+           "moe_plan_dispatch", "moe_plan_step", "moe_plan_combine", "moe_plan_place", "moe_plan_dedup_count",
+           "moe_plan_dedup_dispatch", "moe_plan_status", "moe_plan_destroy")
 
 _LIB = None
 
@@ -95,6 +108,9 @@ def lib():
         l.moe_plan_dispatch.argtypes = [vp, vp, vp, vp, vp]
         l.moe_plan_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         l.moe_plan_combine.argtypes = [vp, vp, vp, vp, vp, vp]
+        l.moe_plan_place.argtypes = [vp, vp, ctypes.c_int32, vp, vp]
+        l.moe_plan_dedup_count.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp]
+        l.moe_plan_dedup_dispatch.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp, vp]
         l.moe_plan_status.argtypes = [vp, vp]
         l.moe_plan_destroy.argtypes = [vp]
         l.moe_plan_destroy.restype = None
@@ -147,6 +163,19 @@ def moe_plan_step(h, logits: int, prev_topk, hidden: int, route: moe_route_out, 
 
 def moe_plan_combine(h, topk_val: int, slot_pos: int, expert_out: int, out: int, stream: int):
     _check("moe_plan_combine", lib().moe_plan_combine(h, topk_val, slot_pos, expert_out, out, stream))
+
+
+def moe_plan_place(h, cooc: int, max_swaps: int, out: moe_place_out, stream: int):
+    _check("moe_plan_place", lib().moe_plan_place(h, cooc, max_swaps, ctypes.byref(out), stream))
+
+
+def moe_plan_dedup_count(h, slot_key: int, key_rank, n_keys: int, out: moe_dedup_out, stream: int):
+    _check("moe_plan_dedup_count", lib().moe_plan_dedup_count(h, slot_key, key_rank, n_keys, ctypes.byref(out), stream))
+
+
+def moe_plan_dedup_dispatch(h, slot_key: int, key_rank, n_keys: int, hidden: int, out: moe_dedup_out, stream: int):
+    _check("moe_plan_dedup_dispatch",
+           lib().moe_plan_dedup_dispatch(h, slot_key, key_rank, n_keys, hidden, ctypes.byref(out), stream))
 
 
 def moe_plan_status(h) -> int:
@@ -212,6 +241,33 @@ class DispatchBuffers:
         return moe_dispatch_out(*(_ptr(getattr(self, n)) for n, _ in moe_dispatch_out._fields_))
 
 
+@dataclass
+class PlaceBuffers:
+    expert_rank: object
+    rank_experts: object
+    intra: object
+    n_swaps: object
+
+    def struct(self) -> moe_place_out:
+        return moe_place_out(*(_ptr(getattr(self, n)) for n, _ in moe_place_out._fields_))
+
+
+@dataclass
+class DedupBuffers:
+    tok_ranks: object
+    rank_rows: object
+    rank_slots: object
+    n_rows: object = None
+    row_token: object = None
+    row_slots: object = None
+    rank_row_offset: object = None
+    slot_row: object = None
+    ddispatch: object = None
+
+    def struct(self) -> moe_dedup_out:
+        return moe_dedup_out(*(_ptr(getattr(self, n)) for n, _ in moe_dedup_out._fields_))
+
+
 class Layer:
     """One MoE layer's planner: a handle plus torch-allocated output buffers."""
 
@@ -243,6 +299,8 @@ class Layer:
         self._route_s = self.route_out.struct()
         self._plan_s = self.plan_out.struct()
         self._disp_s = self.dispatch_out.struct()
+        self.place_out = None
+        self.dedup_out = None
 
     def _stream(self, stream=None) -> int:
         s = self.torch.cuda.current_stream(self.device) if stream is None else stream
@@ -303,6 +361,68 @@ class Layer:
         moe_plan_combine(self.handle, _ptr(self.route_out.topk_val), _ptr(self.dispatch_out.slot_pos),
                          _ptr(expert_out), _ptr(out), self._stream(stream))
         return out
+
+    def place(self, cooc=None, max_swaps: int = -1, stream=None):
+        """Correlated expert placement from co-selection counts (moe_plan_place);
+        cooc defaults to this layer's route_out.cooc."""
+        torch, E, R = self.torch, self.cfg.E, self.cfg.R
+        cooc = self.route_out.cooc if cooc is None else cooc
+        if cooc is None:
+            raise ValueError("place needs co-selection counts (create the Layer with cooc=True or pass cooc)")
+        self._check_tensor(cooc, (E, E), torch.int32)
+        if self.place_out is None:
+            e = lambda n, dt=torch.int32: torch.empty(int(n), dtype=dt, device=self.device)
+            self.place_out = PlaceBuffers(expert_rank=e(E), rank_experts=e(E).view(R, E // R),
+                                          intra=e(1, torch.int64), n_swaps=e(1))
+            self._place_s = self.place_out.struct()
+        moe_plan_place(self.handle, _ptr(cooc), int(max_swaps), self._place_s, self._stream(stream))
+        return self.place_out
+
+    def _dedup_buffers(self, layout: bool):
+        torch, T, k, R, H = self.torch, self.cfg.T, self.cfg.k, self.cfg.R, self.cfg.H
+        e = lambda n, dt=torch.int32: torch.empty(int(n), dtype=dt, device=self.device)
+        if self.dedup_out is None:
+            self.dedup_out = DedupBuffers(tok_ranks=e(T), rank_rows=e(R * R).view(R, R), rank_slots=e(R * R).view(R, R))
+        d = self.dedup_out
+        if layout and d.ddispatch is None:
+            d.n_rows, d.row_token, d.row_slots = e(1), e(T * k), e(T * k)
+            d.rank_row_offset, d.slot_row = e(R + 1), e(T * k)
+            d.ddispatch = e(T * k * H, torch.int16).view(T * k, H)
+        self._dedup_s = d.struct()
+        return d
+
+    def _keys(self, slot_key, key_rank):
+        T, k = self.cfg.T, self.cfg.k
+        slot_key = self.route_out.topk_idx if slot_key is None else slot_key
+        if tuple(slot_key.shape) not in ((T, k), (T * k,)) or not slot_key.is_contiguous() or \
+                slot_key.dtype != self.torch.int32 or slot_key.device != self.device:
+            raise ValueError("slot_key must be a contiguous int32 tensor of T*k keys on %s" % self.device)
+        n = 0
+        if key_rank is not None:
+            if key_rank.dim() != 1 or not key_rank.is_contiguous() or key_rank.dtype != self.torch.int32 or \
+                    key_rank.device != self.device:
+                raise ValueError("key_rank must be a contiguous 1-d int32 tensor on %s" % self.device)
+            n = key_rank.numel()
+        return slot_key, key_rank, n
+
+    def dedup_count(self, slot_key=None, key_rank=None, stream=None):
+        """Deduplicated row counts (moe_plan_dedup_count).  slot_key defaults to
+        this layer's top-k; key_rank None means the contiguous placement."""
+        slot_key, key_rank, n = self._keys(slot_key, key_rank)
+        self._dedup_buffers(False)
+        moe_plan_dedup_count(self.handle, _ptr(slot_key), _ptr(key_rank), n, self._dedup_s, self._stream(stream))
+        return self.dedup_out
+
+    def dedup_dispatch(self, hidden, slot_key=None, key_rank=None, stream=None):
+        """Deduplicated dispatch layout and row copy (moe_plan_dedup_dispatch)."""
+        self._check_tensor(hidden, (self.cfg.T, self.cfg.H), None)
+        if hidden.element_size() != 2:
+            raise TypeError("hidden must be a 16-bit (bf16) tensor")
+        slot_key, key_rank, n = self._keys(slot_key, key_rank)
+        self._dedup_buffers(True)
+        moe_plan_dedup_dispatch(self.handle, _ptr(slot_key), _ptr(key_rank), n, _ptr(hidden), self._dedup_s,
+                                self._stream(stream))
+        return self.dedup_out
 
     def status(self) -> int:
         return moe_plan_status(self.handle)

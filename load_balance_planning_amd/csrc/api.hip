@@ -28,7 +28,8 @@ constexpr size_t kMaxLds = 160 * 1024;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t status, prev_mask, demand, einst_off, einst_list, rlist, colpre, pair_part, omega_acc, total;
+  size_t status, prev_mask, demand, einst_off, einst_list, rlist, colpre, pair_part, omega_acc;
+  size_t place_aff, place_key, dd_mask, dd_cnt, dd_base, dd_count, total;
 };
 
 WsLayout ws_layout(const moe::Dims& d) {
@@ -44,6 +45,12 @@ WsLayout ws_layout(const moe::Dims& d) {
   l.colpre = take(sizeof(int32_t) * (size_t)d.cap * d.R);
   l.pair_part = take(sizeof(int32_t) * moe::pair_part_words(d));
   l.omega_acc = take(sizeof(int32_t) * 2 * (size_t)d.R * d.E);
+  l.place_aff = take(sizeof(int32_t) * (size_t)d.R * d.E);
+  l.place_key = take(sizeof(uint64_t) * (size_t)d.R * d.R);
+  l.dd_mask = take(sizeof(uint64_t) * (size_t)d.NT * d.R);
+  l.dd_cnt = take(sizeof(int32_t) * (size_t)d.NT * d.R);
+  l.dd_base = take(sizeof(int32_t) * (size_t)d.NT * d.R);
+  l.dd_count = take(sizeof(int32_t) * (size_t)d.R);
   l.total = o;
   return l;
 }
@@ -75,7 +82,9 @@ int derive(const moe_plan_config* c, moe::Dims* d) {
   x.S = c->token_bytes > 0 ? c->token_bytes : 2LL * c->H;
   x.W = c->expert_bytes >= 0 ? c->expert_bytes : 9LL * c->H * c->H / 4;
   if (x.Er + x.n_slot > 1024) return MOE_ERR_UNSUPPORTED;
-  if (moe::plan_lds_bytes(x) > kMaxLds || moe::scan_lds_bytes(x) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+  if (moe::plan_lds_bytes(x) > kMaxLds || moe::scan_lds_bytes(x) > kMaxLds || moe::place_lds_bytes(x) > kMaxLds ||
+      moe::dedup_scan_lds_bytes(x) > kMaxLds)
+    return MOE_ERR_UNSUPPORTED;
   *d = x;
   return MOE_OK;
 }
@@ -139,6 +148,12 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   h->ws.colpre = reinterpret_cast<int32_t*>(b + l.colpre);
   h->ws.pair_part = reinterpret_cast<int32_t*>(b + l.pair_part);
   h->ws.omega_acc = reinterpret_cast<int32_t*>(b + l.omega_acc);
+  h->ws.place_aff = reinterpret_cast<int32_t*>(b + l.place_aff);
+  h->ws.place_key = reinterpret_cast<uint64_t*>(b + l.place_key);
+  h->ws.dd_mask = reinterpret_cast<uint64_t*>(b + l.dd_mask);
+  h->ws.dd_cnt = reinterpret_cast<int32_t*>(b + l.dd_cnt);
+  h->ws.dd_base = reinterpret_cast<int32_t*>(b + l.dd_base);
+  h->ws.dd_count = reinterpret_cast<int32_t*>(b + l.dd_count);
   if (hipMemset(h->ws_base, 0, l.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->ws_base);
     delete h;
@@ -311,6 +326,49 @@ extern "C" int moe_plan_combine(moe_plan_t h, const float* topk_val, const int32
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_rc(moe::launch_combine(d, topk_val, slot_pos, expert_out, out, h->ws.status, st));
+}
+
+extern "C" int moe_plan_place(moe_plan_t h, const int32_t* cooc, int32_t max_swaps, const moe_place_out* out,
+                              void* stream) {
+  if (!h || !cooc || !out || !out->expert_rank || !out->rank_experts || !out->intra || !out->n_swaps)
+    return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  return hip_rc(moe::launch_place(h->d, cooc, max_swaps, *out, h->ws, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+int check_dedup(const moe::Dims& d, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
+                const moe_dedup_out* out) {
+  if (!out || !out->rank_rows) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!slot_key || !out->tok_ranks)) return MOE_ERR_INVALID_ARG;
+  if (key_rank && n_keys < 1) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_plan_dedup_count(moe_plan_t h, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
+                                    const moe_dedup_out* out, void* stream) {
+  if (!h || check_dedup(h->d, slot_key, key_rank, n_keys, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  return hip_rc(
+      moe::launch_dedup(h->d, slot_key, key_rank, n_keys, nullptr, *out, h->ws, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int moe_plan_dedup_dispatch(moe_plan_t h, const int32_t* slot_key, const int32_t* key_rank,
+                                       int32_t n_keys, const uint16_t* hidden, const moe_dedup_out* out,
+                                       void* stream) {
+  if (!h || check_dedup(h->d, slot_key, key_rank, n_keys, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
+  if (!out->n_rows || !out->rank_row_offset) return MOE_ERR_INVALID_ARG;
+  if (h->d.T > 0 && (!hidden || !out->row_token || !out->row_slots || !out->slot_row || !out->ddispatch))
+    return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  // a non-null row source selects the layout and copy; T = 0 still writes the offsets
+  static const uint16_t kNoRows = 0;
+  const uint16_t* src = hidden ? hidden : &kNoRows;
+  return hip_rc(
+      moe::launch_dedup(h->d, slot_key, key_rank, n_keys, src, *out, h->ws, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int moe_plan_status(moe_plan_t h, int32_t* host_flags) {

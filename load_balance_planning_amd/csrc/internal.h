@@ -42,6 +42,12 @@ struct Workspace {
   int32_t* pair_part;   // partial pair-count blocks of the tile splits (pair_part_words)
   int32_t* omega_acc;   // [2][R][E] routing matrices accumulated by the top-k kernel in
                         // alternate calls; the one not in use is zero
+  int32_t* place_aff;   // [R][E] placement affinities when they do not fit in LDS
+  uint64_t* place_key;  // [R][R] best swap key per rank pair when it does not fit in LDS
+  uint64_t* dd_mask;    // [NT][R] deduplication: tokens of each tile with a slot on each rank
+  int32_t* dd_cnt;      // [NT][R] slots of each tile on each rank
+  int32_t* dd_base;     // [NT][R] rows of each rank before each tile
+  int32_t* dd_count;    // [R] rows of each rank
 };
 
 // Pair-count job: presence masks in, co-selection / transition blocks out
@@ -94,9 +100,18 @@ hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const ui
 hipError_t launch_combine(const Dims& d, const float* topk_val, const int32_t* slot_pos, const uint16_t* expert_out,
                           uint16_t* out, int32_t* status, hipStream_t st);
 
+// Correlated placement (one workgroup) from co-selection counts.
+hipError_t launch_place(const Dims& d, const int32_t* cooc, int32_t max_swaps, const moe_place_out& out,
+                        const Workspace& ws, hipStream_t st);
+// Deduplicated counts; with hidden non-null also the layout and row copy.
+hipError_t launch_dedup(const Dims& d, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
+                        const uint16_t* hidden, const moe_dedup_out& out, const Workspace& ws, hipStream_t st);
+
 // LDS bytes the plan and scan kernels need for these dimensions.
 size_t plan_lds_bytes(const Dims& d);
 size_t scan_lds_bytes(const Dims& d);
+size_t place_lds_bytes(const Dims& d);
+size_t dedup_scan_lds_bytes(const Dims& d);
 // Workspace words of the pair kernel.
 size_t pair_part_words(const Dims& d);
 

@@ -1,0 +1,192 @@
+"""GPU parity of correlated placement (moe_plan_place) and the deduplicated
+dispatch (moe_plan_dedup_count / moe_plan_dedup_dispatch) against the CPU
+oracle.  Integer results: every output byte-equal; the dispatched rows are
+bit copies.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+from tests import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mp():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import load_balance_planning_amd as m
+    m.lib()
+    return m
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def sym(a):
+    u = np.triu(a, 1)
+    return (u + u.T).astype(np.int32)
+
+
+def gpu_place(mp, E, R, C, max_swaps=-1):
+    layer = mp.Layer(mp.make_config(R, E, 1, R, 1, 8, 0), cooc=False)
+    out = layer.place(dev(C), max_swaps)
+    torch.cuda.synchronize()
+    st = layer.status()
+    res = dict(expert_rank=out.expert_rank.cpu().numpy(), rank_experts=out.rank_experts.cpu().numpy(),
+               intra=int(out.intra.item()), n_swaps=int(out.n_swaps.item()), status=st)
+    layer.close()
+    return res
+
+
+def check_place(got, want, what):
+    assert got["status"] == 0, what
+    np.testing.assert_array_equal(got["expert_rank"], want["expert_rank"], err_msg=what)
+    np.testing.assert_array_equal(got["rank_experts"], want["rank_experts"], err_msg=what)
+    assert got["intra"] == want["intra"], what
+    assert got["n_swaps"] == want["n_swaps"], what
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_place_on_each_workload(mp, name):
+    w = synth.WORKLOADS[name]
+    print("place %s E=%d R=%d" % (name, w.E, w.R), flush=True)
+    c = oracle.make_cfg(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
+    C = oracle.route(c, synth.logits(w))["cooc"]
+    want = oracle.place(c, C)
+    check_place(gpu_place(mp, w.E, w.R, C), want, name)
+
+
+@pytest.mark.parametrize("E,R,hi", [(8, 4, 3), (12, 3, 2), (64, 8, 5), (96, 32, 4), (130, 10, 50), (256, 64, 9),
+                                    (512, 16, 3), (1024, 128, 6), (2048, 256, 4), (2048, 8, 1000), (40, 40, 9),
+                                    (40, 1, 9)])
+def test_place_random_coselection_with_ties(mp, E, R, hi):
+    """Small integer weights: many equal gains and scores, so the tie rules decide."""
+    print("place random E=%d R=%d" % (E, R), flush=True)
+    C = sym(inputs.rng(E * 7 + R).integers(0, hi, (E, E)))
+    c = oracle.make_cfg(R, E, 1, R, 1, 8, 0)
+    for cap in (-1, 0, 1, 3):
+        check_place(gpu_place(mp, E, R, C, cap), oracle.place(c, C, cap), "E=%d R=%d cap=%d" % (E, R, cap))
+
+
+def test_place_flags_invalid_counts(mp):
+    E, R = 32, 4
+    C = sym(inputs.rng(3).integers(0, 9, (E, E)))
+    C[5, 5] = 2
+    got = gpu_place(mp, E, R, C)
+    assert got["status"] & mp.MOE_STATUS_BAD_PAIRS
+    assert sorted(np.bincount(got["expert_rank"], minlength=R).tolist()) == [E // R] * R
+
+
+def dedup_case(mp, T, E, k, R, G, H, B, logits, hidden, table_kind):
+    c = oracle.make_cfg(T, E, k, R, G, H, B)
+    o = oracle.run_all(c, logits, hidden, want_cooc=table_kind == "placed")
+    if table_kind == "contiguous":
+        keys, table = o["topk_idx"], None
+    elif table_kind == "placed":
+        keys, table = o["topk_idx"], oracle.place(c, o["cooc"])["expert_rank"]
+    elif table_kind == "instances":
+        keys, table = o["slot_inst"], o["inst_rank"]
+    else:
+        keys, table = o["topk_idx"], inputs.rng(T + E).integers(0, R, E).astype(np.int32)
+    return c, keys, table
+
+
+def run_dedup(mp, layer, keys, table, hidden):
+    kt = dev(keys.reshape(-1).astype(np.int32))
+    tt = None if table is None else dev(table.astype(np.int32))
+    if hidden is None:
+        return layer.dedup_count(kt, tt)
+    return layer.dedup_dispatch(dev(hidden, torch.int16), kt, tt)
+
+
+@pytest.mark.parametrize("shape", [(256, 16, 3, 4, 2, 8, 2), (640, 24, 4, 8, 4, 13, 4), (4096, 64, 8, 8, 4, 64, 8),
+                                   (1152, 96, 16, 32, 8, 24, 16), (192, 8, 8, 4, 2, 16, 0), (0, 8, 2, 4, 2, 8, 1),
+                                   (130, 10, 3, 1, 1, 8, 0), (300, 10, 2, 10, 5, 8, 3)])
+@pytest.mark.parametrize("kind", ["contiguous", "placed", "instances", "random"])
+def test_dedup_against_the_oracle(mp, shape, kind):
+    T, E, k, R, G, H, B = shape
+    print("dedup %s T=%d E=%d k=%d R=%d H=%d" % (kind, T, E, k, R, H), flush=True)
+    lg = inputs.random_logits(T + E + k, T, E)
+    hid = inputs.random_hidden(T + 1, T, H)
+    c, keys, table = dedup_case(mp, T, E, k, R, G, H, B, lg, hid, kind)
+    want = oracle.dedup(c, keys, table)
+    lay = oracle.dedup_dispatch(c, keys, table, hid)
+    layer = mp.Layer(mp.make_config(T, E, k, R, G, H, B), cooc=False)
+    got = run_dedup(mp, layer, keys, table, None)
+    torch.cuda.synchronize()
+    assert layer.status() == 0
+    np.testing.assert_array_equal(got.tok_ranks.cpu().numpy(), want["tok_ranks"])
+    np.testing.assert_array_equal(got.rank_rows.cpu().numpy(), want["rank_rows"])
+    np.testing.assert_array_equal(got.rank_slots.cpu().numpy(), want["rank_slots"])
+    got = run_dedup(mp, layer, keys, table, hid)
+    torch.cuda.synchronize()
+    assert layer.status() == 0
+    n = lay["n_rows"]
+    assert int(got.n_rows.item()) == n
+    for f in ("row_token", "row_slots", "rank_row_offset", "slot_row"):
+        np.testing.assert_array_equal(getattr(got, f).cpu().numpy(), lay[f], err_msg=f)
+    np.testing.assert_array_equal(got.ddispatch[:n].cpu().numpy().view(np.uint16), lay["ddispatch"])
+    np.testing.assert_array_equal(got.tok_ranks.cpu().numpy(), want["tok_ranks"])
+    layer.close()
+
+
+@pytest.mark.parametrize("name", ["qwen3_layer", "deepseek_v3_layer", "kimi_layer"])
+def test_dedup_full_size_with_the_placement(mp, name):
+    """Full-size layer: GPU route -> GPU place -> GPU dedup dispatch; the
+    layout in full and 256 sampled rows against the oracle."""
+    w = synth.WORKLOADS[name]
+    print("dedup full size %s" % name, flush=True)
+    c = oracle.make_cfg(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
+    lg = synth.logits(w)
+    o = oracle.route(c, lg)
+    pl = oracle.place(c, o["cooc"])
+    layer = mp.Layer(mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B), cooc=True)
+    hid = synth.hidden(w)
+    hid_t = dev(hid, torch.int16)
+    layer.route(dev(lg))
+    p = layer.place()
+    out = layer.dedup_dispatch(hid_t, key_rank=p.expert_rank)
+    torch.cuda.synchronize()
+    assert layer.status() == 0
+    np.testing.assert_array_equal(p.expert_rank.cpu().numpy(), pl["expert_rank"])
+    assert int(p.intra.item()) == pl["intra"]
+    want = oracle.dedup(c, o["topk_idx"], pl["expert_rank"])
+    lay = oracle.dedup_dispatch(c, o["topk_idx"], pl["expert_rank"], None)
+    np.testing.assert_array_equal(out.rank_rows.cpu().numpy(), want["rank_rows"])
+    np.testing.assert_array_equal(out.tok_ranks.cpu().numpy(), want["tok_ranks"])
+    n = lay["n_rows"]
+    assert int(out.n_rows.item()) == n
+    for f in ("row_token", "row_slots", "rank_row_offset", "slot_row"):
+        np.testing.assert_array_equal(getattr(out, f).cpu().numpy(), lay[f], err_msg=f)
+    rows = np.random.default_rng(1).choice(n, 256, replace=False)
+    got = out.ddispatch[torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, hid[lay["row_token"][rows]])
+    layer.close()
+
+
+def test_dedup_flags_bad_keys(mp):
+    T, E, k, R = 128, 16, 2, 4
+    layer = mp.Layer(mp.make_config(T, E, k, R, 2, 8, 0), cooc=False)
+    keys = inputs.random_topk(1, T, E, k)
+    keys[3, 1] = E + 5
+    got = layer.dedup_dispatch(dev(inputs.random_hidden(2, T, 8), torch.int16), dev(keys))
+    torch.cuda.synchronize()
+    assert layer.status() & mp.MOE_STATUS_BAD_KEY
+    assert int(got.slot_row[3 * k + 1].item()) == -1
+    table = np.zeros(E, np.int32)
+    table[4] = R
+    layer.dedup_count(dev(inputs.random_topk(2, T, E, k)), dev(table))
+    torch.cuda.synchronize()
+    assert layer.status() & mp.MOE_STATUS_BAD_KEY
+    layer.close()
