@@ -13,6 +13,13 @@ the inputs resident in HBM.  Prints ONE JSON line:
   chain       the same for the whole step (algorithmic bytes of every call)
   combine     the return path (moe_plan_combine) on the same layer, timed
               separately with the dispatch buffer as the expert outputs
+  placement   correlated expert placement (moe_plan_place) from the first
+              layer's co-selection counts, the oracle's time on the same
+              counts beside it, and the share of rows a deduplicating
+              dispatcher saves with the contiguous placement, with the
+              correlated one, and with the planner's instances
+  dedup_dispatch  the deduplicated dispatch (moe_plan_dedup_dispatch) with the
+              correlated placement: its rows and HBM rate
   cpu_baseline  the CPU oracle on one core over a bounded sample
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -62,6 +69,20 @@ def algorithmic_bytes(w) -> dict:
                + T * H * 2             # combined rows written
                + T * k * 4 * 2)        # selected logits and slot positions read
     return dict(route=route, plan=plan, dispatch=dispatch, combine=combine, total=(route + plan + dispatch) * w.L)
+
+
+def dedup_bytes(w, n_rows: int) -> int:
+    """Bytes moe_plan_dedup_dispatch must move for a layer with n_rows deduplicated rows."""
+    T, k, R, H = w.T, w.k, w.R, w.H
+    tiles = R * ((T // R + 63) // 64)
+    return (T * k * 4 * 2              # slot keys read by the mask and gather kernels
+            + T * 4                    # distinct-rank counts written
+            + tiles * R * (8 + 4) * 2  # per-tile rank masks and slot counts, written then read
+            + tiles * R * 4 * 2        # per-tile row prefix written, read by the gather
+            + T * H * 2                # hidden rows read once
+            + n_rows * H * 2           # deduplicated rows written
+            + n_rows * 4 * 2           # row token and slot mask
+            + T * k * 4)               # row of each slot
 
 
 def source_hash(path: str) -> str:
@@ -184,12 +205,67 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
             e[1].record(stream)
     torch.cuda.synchronize()
     comb_ms = [e[0].elapsed_time(e[1]) for e in cev]
+    # Correlated placement from the first layer's co-selection counts, and the
+    # deduplicated dispatch with it.
+    lay0 = layers[0]
+    lay0.place()
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    torch.cuda.synchronize()
+    for e in pev:
+        e[0].record(stream)
+        pl = lay0.place()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    place_ms = [e[0].elapsed_time(e[1]) for e in pev]
+    expert_rank = pl.expert_rank.clone()
+    place = dict(us=float(np.mean(place_ms)) * 1e3, swaps=int(pl.n_swaps.item()), intra=int(pl.intra.item()),
+                 cooc=lay0.route_out.cooc.cpu().numpy())
+    slots = w.T * w.k
+    saved = {}
+    for name, keys, table in (("contiguous", None, None), ("placed", None, expert_rank),
+                              ("plan_instances", lay0.plan_out.slot_inst, lay0.plan_out.inst_rank)):
+        d = lay0.dedup_count(keys, table)
+        saved[name] = 1.0 - int(d.tok_ranks.sum().item()) / slots
+    lay0.dedup_dispatch(hidden, key_rank=expert_rank)
+    dev_ = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in dev_:
+        e[0].record(stream)
+        dd = lay0.dedup_dispatch(hidden, key_rank=expert_rank)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    place["rows_saved_frac"] = saved
+    dedup = dict(us=float(np.mean([e[0].elapsed_time(e[1]) for e in dev_])) * 1e3, n_rows=int(dd.n_rows.item()))
     status = [layer.status() for layer in layers]
     for layer in layers:
         layer.close()
-    return dict(ms_total=ms_total, combine_ms=float(np.mean(comb_ms)), per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
+    return dict(ms_total=ms_total, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup, per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
                 per_call_ms_min={k: float(np.min(v)) for k, v in per.items()}, status=status,
                 device=torch.cuda.get_device_name(dev))
+
+
+def placement_report(w, p: dict, with_oracle: bool) -> dict:
+    """The GPU placement's figures, with the oracle timed on the same counts (one core)."""
+    out = {"kernel": "moe_plan_place", "us": p["us"], "swaps": p["swaps"], "intra": p["intra"],
+           "rows_saved_frac": p["rows_saved_frac"]}
+    if with_oracle:
+        import oracle
+        cfg = oracle.make_cfg(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
+        orig = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(orig)})
+        try:
+            t0 = time.perf_counter()
+            n = 0
+            while n < 3 or time.perf_counter() - t0 < 1.0:
+                ref = oracle.place(cfg, p["cooc"])
+                n += 1
+            ms = (time.perf_counter() - t0) / n * 1e3
+        finally:
+            os.sched_setaffinity(0, orig)
+        out["oracle_ms"] = ms
+        out["oracle_cores"] = 1
+        out["matches_oracle"] = ref["intra"] == p["intra"] and ref["n_swaps"] == p["swaps"]
+    return out
 
 
 def copy_reference(nbytes: int, steps: int) -> dict:
@@ -260,6 +336,14 @@ def main():
                     "algorithmic_bytes_per_launch": ab["combine"],
                     "achieved": ab["combine"] / (g["combine_ms"] / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": ab["combine"] / (g["combine_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "placement": placement_report(w, g["place"], cpu is not None),
+        "dedup_dispatch": {"kernel": "deduplicated dispatch (moe_plan_dedup_dispatch, correlated placement)",
+                           "us": g["dedup"]["us"], "rows": g["dedup"]["n_rows"], "slot_rows": w.T * w.k,
+                           "algorithmic_bytes_per_launch": dedup_bytes(w, g["dedup"]["n_rows"]),
+                           "achieved": dedup_bytes(w, g["dedup"]["n_rows"]) / (g["dedup"]["us"] / 1e6) / 1e9,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": dedup_bytes(w, g["dedup"]["n_rows"]) / (g["dedup"]["us"] / 1e6) / 1e9 / HBM_PEAK_GBS,
+                           "vs_dispatch_us": disp_ms * 1e3},
         "per_call_us": {k: v * 1e3 for k, v in g["per_call_ms"].items()},
         "per_call_us_min": {k: v * 1e3 for k, v in g["per_call_ms_min"].items()},
         "cpu_baseline": cpu,

@@ -16,14 +16,16 @@
 //               (aff[r][x] = sum over y on rank r of C[x][y]; ties to the lower
 //               a, then b) while the gain is positive, at most max_swaps times.
 //
-// One workgroup of 1024 threads; the problem is tiny and sequential.  The
-// growth runs in wave 0 alone (E sequential argmax steps, no barriers: each
-// lane holds E/64 affinities in registers).  Refinement keeps, for every rank
-// pair (r1 < r2), the best swap key of the pairs between them; a swap between
-// ra and rb changes only the gains of pairs with an expert on ra or rb, so an
-// iteration re-evaluates 2R-3 rank pairs (about 2*E*E/R expert pairs) instead
-// of all E*E/2.  aff and the rank-pair keys live in LDS when they fit, else in
-// the handle's workspace.
+// One workgroup of 1024 threads; the problem is tiny and sequential.  Growth
+// takes E steps of one argmax each: every thread holds the affinities of its
+// E/1024 experts in registers, a wave's maximum comes from a DPP butterfly
+// inside each 16-lane row and four lane reads, and the workgroup's from an LDS
+// atomic max into one of three rotating slots -- one barrier per step.
+// Refinement keeps, for every rank pair (r1 < r2), the best swap key of the
+// pairs between them; a swap between ra and rb changes only the gains of pairs
+// with an expert on ra or rb, so an iteration re-evaluates 2R-3 rank pairs
+// (about 2*E*E/R expert pairs) instead of all E*E/2.  aff and the rank-pair
+// keys live in LDS when they fit, else in the handle's workspace.
 #include "internal.h"
 
 namespace moe {
@@ -48,7 +50,7 @@ struct PlaceArgs {
 };
 
 struct PlaceLds {
-  size_t rank_of, mem, pos, deg, red, aff, key, total;
+  size_t rank_of, mem, pos, deg, own, col, red, aff, key, total;
   bool aff_in_lds, key_in_lds;
 };
 
@@ -63,7 +65,9 @@ PlaceLds place_lds(const Dims& d) {
   l.mem = take(sizeof(int32_t) * d.E);
   l.pos = take(sizeof(int32_t) * d.E);
   l.deg = take(sizeof(int32_t) * d.E);
-  l.red = take(sizeof(uint64_t) * (kPlaceWaves + 1));
+  l.own = take(sizeof(int32_t) * d.E);
+  l.col = take(sizeof(int32_t) * kPlaceWaves * (size_t)d.R);
+  l.red = take(sizeof(uint64_t) * (kPlaceWaves + 1));  // also the growth's three argmax slots
   const size_t aff_b = sizeof(int32_t) * (size_t)d.R * d.E;
   const size_t key_b = sizeof(uint64_t) * (size_t)d.R * d.R;
   l.aff_in_lds = aff_b <= kPlaceAffLds;
@@ -74,13 +78,44 @@ PlaceLds place_lds(const Dims& d) {
   return l;
 }
 
-__device__ __forceinline__ uint64_t wave_max(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
+// DPP moves inside a 16-lane row (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror): after the four steps every lane holds its
+// row's maximum.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ uint32_t row_max(uint32_t v) {
+  v = max(v, dpp32<0xB1>(v));
+  v = max(v, dpp32<0x4E>(v));
+  v = max(v, dpp32<0x141>(v));
+  return max(v, dpp32<0x140>(v));
+}
+
+__device__ __forceinline__ uint64_t row_max(uint64_t v) {
+  auto step = [](uint64_t x, uint32_t lo, uint32_t hi) {
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > x ? o : x;
+  };
+  v = step(v, dpp32<0xB1>((uint32_t)v), dpp32<0xB1>((uint32_t)(v >> 32)));
+  v = step(v, dpp32<0x4E>((uint32_t)v), dpp32<0x4E>((uint32_t)(v >> 32)));
+  v = step(v, dpp32<0x141>((uint32_t)v), dpp32<0x141>((uint32_t)(v >> 32)));
+  return step(v, dpp32<0x140>((uint32_t)v), dpp32<0x140>((uint32_t)(v >> 32)));
+}
+
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
+__device__ __forceinline__ uint64_t lane_read(uint64_t v, int l) {
+  return ((uint64_t)lane_read((uint32_t)(v >> 32), l) << 32) | lane_read((uint32_t)v, l);
+}
+
+// Maximum over the wave, wave-uniform.
+template <class K>
+__device__ __forceinline__ K wave_max(K v) {
+  v = row_max(v);
+  const K a = lane_read(v, 0), b = lane_read(v, 16), c = lane_read(v, 32), e = lane_read(v, 48);
+  const K x = a > b ? a : b, y = c > e ? c : e;
+  return x > y ? x : y;
 }
 
 __device__ __forceinline__ int64_t wave_sum(int64_t v) {
@@ -104,168 +139,202 @@ __device__ __forceinline__ uint64_t block_max(uint64_t v, uint64_t* red) {
   return red[kPlaceWaves];
 }
 
-// Swap key of experts x (rank r1) and y (rank r2): the gain, then the pair
-// (lower id first) preferring lower ids.
-__device__ __forceinline__ uint64_t swap_key(const Dims& d, const int32_t* __restrict__ C, const int32_t* aff,
-                                             int x, int y, int r1, int r2) {
-  const int64_t g = (int64_t)aff[(int64_t)r2 * d.E + x] - aff[(int64_t)r1 * d.E + x] + aff[(int64_t)r1 * d.E + y] -
-                    aff[(int64_t)r2 * d.E + y] - 2 * (int64_t)C[(int64_t)x * d.E + y];
-  const int a = min(x, y), b = max(x, y);
-  const uint64_t pair = (uint64_t)a * d.E + b;
-  return ((uint64_t)(g + (int64_t)kGainBias) << kPairBits) | (kPairMask - pair);
+// Rank-pair swap keys live in LDS (ds atomics) or in global memory (device
+// atomics at L2; reads bypass the L1).
+template <bool LDS>
+__device__ __forceinline__ uint64_t key_load(const uint64_t* p) {
+  if constexpr (LDS) return *p;
+  else return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Best swap key of every rank pair in a set of nb candidate pairs: pair_of(b)
-// returns the ranks (r1 < r2) of candidate b, or r1 < 0 to skip it.  A group
-// of tpb lanes (a power of two within one wave) evaluates one rank pair.
-template <class PairOf>
-__device__ __forceinline__ void eval_blocks(const Dims& d, const int32_t* __restrict__ C, const int32_t* aff,
-                                            const int32_t* mem, uint64_t* key, int nb, PairOf pair_of) {
-  int tpb = kPlaceThreads / max(nb, 1);
-  tpb = tpb >= 64 ? 64 : tpb >= 32 ? 32 : tpb >= 16 ? 16 : tpb >= 8 ? 8 : tpb >= 4 ? 4 : tpb >= 2 ? 2 : 1;
-  const int groups = kPlaceThreads / tpb;
-  const int sub = threadIdx.x % tpb;
-  const int Er = d.Er, items = Er * Er;
-  for (int b = threadIdx.x / tpb; b < nb; b += groups) {
-    int r1, r2;
-    pair_of(b, r1, r2);
-    if (r1 < 0) continue;  // uniform within the group
-    uint64_t best = 0;
-    for (int it = sub; it < items; it += tpb) {
-      const int ix = it / Er, iy = it - ix * Er;
-      const int x = mem[r1 * Er + ix], y = mem[r2 * Er + iy];
-      const uint64_t kk = swap_key(d, C, aff, x, y, r1, r2);
-      best = kk > best ? kk : best;
+// Swap keys of the pairs (x, y), y on another rank than x, folded into
+// key[min(rx, ry)][max(rx, ry)] by atomic max.  A key is the gain, then the
+// pair (lower id first) preferring lower ids:
+//   gain = aff[ry][x] - own[x] + aff[rx][y] - own[y] - 2 C[x][y],
+// own[e] = aff[rank(e)][e].  ALL: every x, with y > x.  Otherwise x runs over
+// the experts of ranks ra and rb and y over all experts.  One wave per x:
+// the C row and the aff[rx] row are read along y (coalesced); the column
+// aff[*][x] goes to the wave's LDS buffer col.
+template <bool ALL, bool KEY_LDS>
+__device__ __forceinline__ void eval_rows(const Dims& d, const int32_t* __restrict__ C, const int32_t* aff,
+                                          const int32_t* own, const int32_t* rank_of, const int32_t* mem,
+                                          uint64_t* key, int32_t* col, int ra, int rb) {
+  const int E = d.E, R = d.R, Er = d.Er;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nx = ALL ? E : 2 * Er;
+  for (int i = wave; i < nx; i += kPlaceWaves) {
+    const int x = ALL ? i : (i < Er ? mem[ra * Er + i] : mem[rb * Er + i - Er]);
+    const int rx = rank_of[x];
+    const int64_t ox = own[x];
+    for (int r = lane; r < R; r += 64) col[r] = aff[(int64_t)r * E + x];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const int32_t* crow = C + (int64_t)x * E;
+    const int32_t* arow = aff + (int64_t)rx * E;
+#pragma unroll 2
+    for (int y = (ALL ? x + 1 : 0) + lane; y < E; y += 64) {
+      const int ry = rank_of[y];
+      if (ry == rx) continue;
+      const int64_t g = (int64_t)col[ry] - ox + arow[y] - own[y] - 2 * (int64_t)crow[y];
+      const uint64_t pair = (uint64_t)min(x, y) * E + max(x, y);
+      const uint64_t kk = ((uint64_t)(g + (int64_t)kGainBias) << kPairBits) | (kPairMask - pair);
+      atomicMax(&key[min(rx, ry) * R + max(rx, ry)], kk);
     }
-    for (int off = tpb >> 1; off >= 1; off >>= 1) {
-      const uint64_t o = __shfl_xor(best, off, tpb);
-      best = o > best ? o : best;
-    }
-    if (sub == 0) key[(int64_t)r1 * d.R + r2] = best;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // col is rewritten for the next x
   }
 }
 
-template <int NPL>
+// Greedy growth, one expert per step for E steps; thread t holds the
+// affinities to the rank being filled of experts t, t + 1024, ... (NPL of
+// them).  The step's argmax goes through slot[g % 3]: step g clears the slot
+// of step g + 1, whose last readers (step g - 2) all passed barrier g - 1.
+template <class K, int NPL>
+__device__ __forceinline__ void grow(const Dims& d, const int32_t* __restrict__ C, const int32_t* deg, int32_t* rank_of,
+                                     int32_t* mem, int32_t* pos, int32_t* aff, uint64_t* red) {
+  const int E = d.E, R = d.R, Er = d.Er;
+  const int tid = threadIdx.x, lane = tid & 63;
+  constexpr int kShift = 12;  // kIdx - e >= 2048: a candidate's key is never 0
+  constexpr K kIdx = ((K)1 << kShift) - 1;
+  K* slot = reinterpret_cast<K*>(red);  // three slots
+  if (tid < 3) slot[tid] = 0;
+  __syncthreads();
+  bool placed[NPL];
+  int32_t a[NPL];
+#pragma unroll
+  for (int u = 0; u < NPL; ++u) placed[u] = false;
+  int g = 0;
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int u = 0; u < NPL; ++u) a[u] = 0;
+    for (int m = 0; m < Er; ++m, ++g) {
+      K best = 0;
+#pragma unroll
+      for (int u = 0; u < NPL; ++u) {
+        const int e = tid + kPlaceThreads * u;
+        if (e < E && !placed[u]) {
+          const int32_t sc = m == 0 ? deg[e] : max(a[u], 0);
+          const K kk = ((K)sc << kShift) | (K)(kIdx - e);
+          best = kk > best ? kk : best;
+        }
+      }
+      best = wave_max(best);
+      if (lane == 0 && best != 0) atomicMax(&slot[g % 3], best);
+      if (tid == 0) slot[(g + 1) % 3] = 0;
+      __syncthreads();
+      const int pick = (int)(kIdx - (slot[g % 3] & kIdx));
+#pragma unroll
+      for (int u = 0; u < NPL; ++u)
+        if (tid + kPlaceThreads * u == pick) placed[u] = true;
+      if (tid == 0) {
+        rank_of[pick] = r;
+        mem[r * Er + m] = pick;
+        pos[pick] = r * Er + m;
+      }
+      const int32_t* row = C + (int64_t)pick * E;  // C[pick][e] = C[e][pick]
+#pragma unroll
+      for (int u = 0; u < NPL; ++u) {
+        const int e = tid + kPlaceThreads * u;
+        if (e < E) a[u] += row[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NPL; ++u) {
+      const int e = tid + kPlaceThreads * u;
+      if (e < E) aff[(int64_t)r * E + e] = a[u];
+    }
+  }
+}
+
+template <int NPL, bool AFF_LDS, bool KEY_LDS>
 __global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds ly, PlaceArgs pa) {
   extern __shared__ __align__(16) char smem_place[];
   int32_t* rank_of = reinterpret_cast<int32_t*>(smem_place + ly.rank_of);
   int32_t* mem = reinterpret_cast<int32_t*>(smem_place + ly.mem);  // [R][Er] experts of each rank
   int32_t* pos = reinterpret_cast<int32_t*>(smem_place + ly.pos);  // slot of each expert in mem
   int32_t* deg = reinterpret_cast<int32_t*>(smem_place + ly.deg);
+  int32_t* own = reinterpret_cast<int32_t*>(smem_place + ly.own);
+  int32_t* col = reinterpret_cast<int32_t*>(smem_place + ly.col) + (threadIdx.x >> 6) * d.R;
   uint64_t* red = reinterpret_cast<uint64_t*>(smem_place + ly.red);
-  int32_t* aff = ly.aff_in_lds ? reinterpret_cast<int32_t*>(smem_place + ly.aff) : pa.aff_ws;
-  uint64_t* key = ly.key_in_lds ? reinterpret_cast<uint64_t*>(smem_place + ly.key) : pa.key_ws;
+  int32_t* aff;
+  uint64_t* key;
+  if constexpr (AFF_LDS) aff = reinterpret_cast<int32_t*>(smem_place + ly.aff);
+  else aff = pa.aff_ws;
+  if constexpr (KEY_LDS) key = reinterpret_cast<uint64_t*>(smem_place + ly.key);
+  else key = pa.key_ws;
   const int E = d.E, R = d.R, Er = d.Er;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t* __restrict__ C = pa.C;
 
-  // Degrees and input checks: zero diagonal, no negative count, row sums
-  // below 2^31 (symmetry is the caller's contract).
-  for (int e = wave; e < E; e += kPlaceWaves) {
+  // Degrees (column sums, equal to the row sums of a symmetric matrix) and
+  // input checks: zero diagonal, no negative count, sums below 2^31
+  // (symmetry itself is the caller's contract).
+  int64_t my_max_deg = 0;
+  for (int e = tid; e < E; e += kPlaceThreads) {
     int64_t s = 0;
     bool bad = false;
-    for (int x = lane; x < E; x += 64) {
-      const int32_t v = C[(int64_t)e * E + x];
+#pragma unroll 8
+    for (int x = 0; x < E; ++x) {
+      const int32_t v = C[(int64_t)x * E + e];
       bad |= v < 0 || (x == e && v != 0);
       s += v;
     }
-    s = wave_sum(s);
-    bad = __any(bad);
-    if (lane == 0) {
-      if (bad || s > INT32_MAX) atomicOr(pa.status, MOE_STATUS_BAD_PAIRS);
-      deg[e] = (int32_t)(s < 0 ? 0 : s > INT32_MAX ? INT32_MAX : s);
-    }
+    if (bad || s > INT32_MAX) atomicOr(pa.status, MOE_STATUS_BAD_PAIRS);
+    const int32_t dg = (int32_t)(s < 0 ? 0 : s > INT32_MAX ? INT32_MAX : s);
+    deg[e] = dg;
+    my_max_deg = max(my_max_deg, (int64_t)dg);
   }
   for (int64_t q = tid; q < (int64_t)R * R; q += kPlaceThreads) key[q] = 0;
-  __syncthreads();
+  const uint64_t max_deg = block_max((uint64_t)my_max_deg, red);  // also publishes deg[]
 
-  // Greedy growth in wave 0: lane l holds experts l, l+64, ...
-  if (wave == 0) {
-    uint32_t placed = 0;
-    int32_t a[NPL];
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int u = 0; u < NPL; ++u) a[u] = 0;
-      for (int m = 0; m < Er; ++m) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int u = 0; u < NPL; ++u) {
-          const int e = lane + 64 * u;
-          if (e < E && !(placed >> u & 1u)) {
-            const int32_t sc = m == 0 ? deg[e] : max(a[u], 0);
-            const uint64_t kk = ((uint64_t)sc << 12) | (uint64_t)(4095 - e);
-            best = kk > best ? kk : best;
-          }
-        }
-        best = wave_max(best);
-        const int pick = 4095 - (int)(best & 4095);
-        if ((pick & 63) == lane) placed |= 1u << (pick >> 6);
-        if (lane == 0) {
-          rank_of[pick] = r;
-          mem[r * Er + m] = pick;
-          pos[pick] = r * Er + m;
-        }
-        const int32_t* row = C + (int64_t)pick * E;  // C[pick][e] = C[e][pick]
-#pragma unroll
-        for (int u = 0; u < NPL; ++u) {
-          const int e = lane + 64 * u;
-          if (e < E) a[u] += row[e];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NPL; ++u) {
-        const int e = lane + 64 * u;
-        if (e < E) aff[(int64_t)r * E + e] = a[u];
-      }
-    }
-  }
+  // Greedy growth.  Scores are sums of counts, so never above the largest
+  // degree: when that is below 2^20 a 32-bit key (score, then 4095 - e) suffices.
+  if (max_deg < (1u << 20)) grow<uint32_t, NPL>(d, C, deg, rank_of, mem, pos, aff, red);
+  else grow<uint64_t, NPL>(d, C, deg, rank_of, mem, pos, aff, red);
+  __syncthreads();
+  for (int e = tid; e < E; e += kPlaceThreads) own[e] = aff[(int64_t)rank_of[e] * E + e];
   __syncthreads();
 
   // Best swap of every rank pair.
-  eval_blocks(d, C, aff, mem, key, R * R, [&](int b, int& r1, int& r2) {
-    r1 = b / R;
-    r2 = b - r1 * R;
-    if (r1 >= r2) r1 = -1;
-  });
+  eval_rows<true, KEY_LDS>(d, C, aff, own, rank_of, mem, key, col, 0, 0);
   __syncthreads();
 
   const int cap = pa.max_swaps < 0 ? 4096 : pa.max_swaps;
   int swaps = 0;
   for (;;) {
     uint64_t best = 0;
-    for (int64_t q = tid; q < (int64_t)R * R; q += kPlaceThreads) best = key[q] > best ? key[q] : best;
+    for (int q = tid; q < R * R; q += kPlaceThreads) {
+      const uint64_t v = key_load<KEY_LDS>(&key[q]);
+      best = v > best ? v : best;
+    }
     best = block_max(best, red);
     const int64_t gain = (int64_t)(best >> kPairBits) - (int64_t)kGainBias;
     if (best == 0 || gain <= 0 || swaps >= cap) break;
     const int64_t pair = (int64_t)(kPairMask - (best & kPairMask));
     const int xa = (int)(pair / E), xb = (int)(pair - (int64_t)xa * E);
     const int ra = rank_of[xa], rb = rank_of[xb];
+    // aff of ranks ra and rb; clear the keys of every rank pair with ra or rb.
     for (int x = tid; x < E; x += kPlaceThreads) {
       const int32_t ca = C[(int64_t)xa * E + x], cb = C[(int64_t)xb * E + x];
       aff[(int64_t)ra * E + x] += cb - ca;
       aff[(int64_t)rb * E + x] += ca - cb;
     }
+    for (int q = tid; q < 2 * R; q += kPlaceThreads) {
+      const int c = q < R ? ra : rb, o = q < R ? q : q - R;
+      if (o != c) key[min(c, o) * R + max(c, o)] = 0;
+    }
     __syncthreads();  // every thread has read rank_of[xa], rank_of[xb]
-    if (tid == 0) {
-      const int pa_ = pos[xa], pb_ = pos[xb];
-      rank_of[xa] = rb;
-      rank_of[xb] = ra;
-      mem[pa_] = xb;
-      mem[pb_] = xa;
-      pos[xa] = pb_;
-      pos[xb] = pa_;
+    // The swap: each of the 2*Er slots of ranks ra and rb is rewritten by one
+    // thread (xa and xb trade places), with its expert's rank, slot and own.
+    for (int q = tid; q < 2 * Er; q += kPlaceThreads) {
+      const int r = q < Er ? ra : rb, slot = r * Er + (q < Er ? q : q - Er);
+      int e = mem[slot];
+      e = e == xa ? xb : e == xb ? xa : e;
+      mem[slot] = e;
+      rank_of[e] = r;
+      pos[e] = slot;
+      own[e] = aff[(int64_t)r * E + e];
     }
     __syncthreads();
-    // The rank pairs with ra or rb on one side; (ra, rb) once.
-    eval_blocks(d, C, aff, mem, key, 2 * R, [&](int b, int& r1, int& r2) {
-      const int c = b < R ? ra : rb, o = b < R ? b : b - R;
-      if (o == c || (b >= R && o == ra)) {
-        r1 = -1;
-        return;
-      }
-      r1 = min(c, o);
-      r2 = max(c, o);
-    });
+    eval_rows<false, KEY_LDS>(d, C, aff, own, rank_of, mem, key, col, ra, rb);
     __syncthreads();
     ++swaps;
   }
@@ -278,7 +347,7 @@ __global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds l
     for (int i = 0; i < Er; ++i) before += mem[r * Er + i] < e;
     pa.expert_rank[e] = r;
     pa.rank_experts[r * Er + before] = e;
-    w += aff[(int64_t)r * E + e];
+    w += own[e];
   }
   w = wave_sum(w);
   __syncthreads();
@@ -292,15 +361,24 @@ __global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds l
   }
 }
 
-template <int NPL>
+template <int NPL, bool AFF_LDS, bool KEY_LDS>
 hipError_t launch_place_n(const Dims& d, const PlaceLds& ly, const PlaceArgs& pa, hipStream_t st) {
+  auto kern = place_kernel<NPL, AFF_LDS, KEY_LDS>;
   if (ly.total > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(place_kernel<NPL>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ly.total);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(place_kernel<NPL>, dim3(1), dim3(kPlaceThreads), ly.total, st, d, ly, pa);
+  hipLaunchKernelGGL(kern, dim3(1), dim3(kPlaceThreads), ly.total, st, d, ly, pa);
   return hipGetLastError();
+}
+
+template <int NPL>
+hipError_t launch_place_lds(const Dims& d, const PlaceLds& ly, const PlaceArgs& pa, hipStream_t st) {
+  if (ly.aff_in_lds && ly.key_in_lds) return launch_place_n<NPL, true, true>(d, ly, pa, st);
+  if (ly.aff_in_lds) return launch_place_n<NPL, true, false>(d, ly, pa, st);
+  if (ly.key_in_lds) return launch_place_n<NPL, false, true>(d, ly, pa, st);
+  return launch_place_n<NPL, false, false>(d, ly, pa, st);
 }
 
 }  // namespace
@@ -312,13 +390,8 @@ hipError_t launch_place(const Dims& d, const int32_t* cooc, int32_t max_swaps, c
   const PlaceLds ly = place_lds(d);
   const PlaceArgs pa{cooc, max_swaps, out.expert_rank, out.rank_experts, out.intra, out.n_swaps,
                      ws.place_aff, ws.place_key, ws.status};
-  const int npl = (d.E + 63) / 64;
-  if (npl <= 1) return launch_place_n<1>(d, ly, pa, st);
-  if (npl <= 2) return launch_place_n<2>(d, ly, pa, st);
-  if (npl <= 4) return launch_place_n<4>(d, ly, pa, st);
-  if (npl <= 8) return launch_place_n<8>(d, ly, pa, st);
-  if (npl <= 16) return launch_place_n<16>(d, ly, pa, st);
-  return launch_place_n<32>(d, ly, pa, st);
+  if (d.E <= kPlaceThreads) return launch_place_lds<1>(d, ly, pa, st);
+  return launch_place_lds<2>(d, ly, pa, st);
 }
 
 }  // namespace moe
