@@ -53,8 +53,9 @@ def _setup(l):
     l.oracle_place.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp]
     l.oracle_dedup.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp, vp]
     l.oracle_dedup_dispatch.argtypes = [vp, vp, vp, ctypes.c_int32] + [vp] * 7
+    l.oracle_quality.argtypes = [vp, ctypes.c_int32] + [vp] * 5
     for f in (l.oracle_params, l.oracle_domain_budget, l.oracle_route, l.oracle_plan, l.oracle_dispatch,
-              l.oracle_combine, l.oracle_place, l.oracle_dedup, l.oracle_dedup_dispatch):
+              l.oracle_combine, l.oracle_place, l.oracle_dedup, l.oracle_dedup_dispatch, l.oracle_quality):
         f.restype = ctypes.c_int
     return l
 
@@ -215,6 +216,26 @@ def dedup_dispatch(cfg: OracleCfg, slot_key: np.ndarray, key_rank: np.ndarray | 
     out["n_rows"] = int(out["n_rows"][0])
     out["ddispatch"] = None if disp is None else disp[:out["n_rows"]]
     return out
+
+
+QUALITY_FIELDS = ("assignments", "same_rank", "same_node", "other_node", "replica_served", "max_rank_load",
+                  "min_rank_load", "replicas")
+
+
+def quality(cfg: OracleCfg, plan_out: dict, l=None) -> dict:
+    """Plan-quality counters of a plan (see oracle_quality), plus the imbalance max / mean."""
+    l = l or lib()
+    cap = cfg.E + cfg.B
+    out = np.zeros(8, np.int64)
+    args = [np.ascontiguousarray(plan_out[k], np.int32) for k in ("inst_expert", "inst_rank", "rank_load")]
+    quota = np.ascontiguousarray(plan_out["quota"], np.int32).reshape(cfg.R, cap)
+    rc = l.oracle_quality(ctypes.byref(cfg), int(np.asarray(plan_out["n_inst"]).reshape(-1)[0]), _p(args[0]),
+                          _p(args[1]), _p(args[2]), _p(quota), _p(out))
+    if rc != 0:
+        raise ValueError("oracle_quality failed (%d)" % rc)
+    res = {k: int(v) for k, v in zip(QUALITY_FIELDS, out)}
+    res["imbalance"] = res["max_rank_load"] * cfg.R / res["assignments"] if res["assignments"] else 1.0
+    return res
 
 
 def run_all(cfg: OracleCfg, logits: np.ndarray, hidden: np.ndarray | None,

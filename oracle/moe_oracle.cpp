@@ -665,3 +665,46 @@ extern "C" int oracle_dedup_dispatch(const oracle_cfg* c, const int32_t* slot_ke
   for (int64_t q = p; q < N; ++q) row_token[q] = row_slots[q] = -1;
   return 0;
 }
+
+// ---------------------------------------------------------------------------
+// Plan quality ([TopoEP] section 6.2 Fig. 10 and section 6.4 Fig. 13(b): the
+// rank-load imbalance, the largest per-rank token-expert load over the mean;
+// section 6.6 Fig. 16: the share of assignments executed on another node than
+// their source, and the share executed by replicas).  From a plan:
+//   out[0] assignments             sum of q[s][i]
+//   out[1] same rank               sum of q[s][i] with rank(i) = s
+//   out[2] same node               sum of q[s][i] with dom(rank(i)) = dom(s)
+//   out[3] other node              out[0] - out[2]
+//   out[4] served by replicas      sum of q[s][i] with rank(i) != main(expert(i))
+//   out[5] largest rank load       max_r rank_load[r]
+//   out[6] smallest rank load      min_r rank_load[r]
+//   out[7] replicas                n_inst - E
+// The imbalance of Fig. 10 is out[5] * R / out[0].
+// ---------------------------------------------------------------------------
+extern "C" int oracle_quality(const oracle_cfg* c, int32_t n_inst, const int32_t* inst_expert,
+                              const int32_t* inst_rank, const int32_t* rank_load, const int32_t* quota,
+                              int64_t* out) {
+  if (!valid(c) || !inst_expert || !inst_rank || !rank_load || !quota || !out) return -1;
+  const Derived d = derive(c);
+  const int64_t R = c->R, cap = (int64_t)c->E + c->B;
+  if (n_inst < c->E || n_inst > cap) return -1;
+  for (int k = 0; k < 8; ++k) out[k] = 0;
+  for (int64_t s = 0; s < R; ++s)
+    for (int64_t i = 0; i < n_inst; ++i) {
+      const int64_t q = quota[s * cap + i], r = inst_rank[i], e = inst_expert[i];
+      if (r < 0 || r >= R || e < 0 || e >= c->E) return -1;
+      out[0] += q;
+      if (r == s) out[1] += q;
+      if (dom_of(c, r) == dom_of(c, s)) out[2] += q;
+      if (r != main_of(d, e)) out[4] += q;
+    }
+  out[3] = out[0] - out[2];
+  out[5] = rank_load[0];
+  out[6] = rank_load[0];
+  for (int64_t r = 1; r < R; ++r) {
+    out[5] = std::max<int64_t>(out[5], rank_load[r]);
+    out[6] = std::min<int64_t>(out[6], rank_load[r]);
+  }
+  out[7] = n_inst - c->E;
+  return 0;
+}

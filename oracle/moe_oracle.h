@@ -17,6 +17,7 @@
  *             the gate weights are a reading (softmax of the selected logits).
  *   Placement and deduplication: [Coupling] "Moving Correlated Experts
  *             Together", Fig. 3 (the partition algorithm is a reading).
+ *   Plan quality: [TopoEP] sections 6.2, 6.4, 6.6 (Figs. 10, 13(b), 16).
  *
  * Every function returns 0 on success or a negative status:
  *   -1 invalid argument / configuration, -4 a NaN gate logit,
@@ -98,6 +99,12 @@ int oracle_dedup_dispatch(const oracle_cfg* c, const int32_t* slot_key, const in
                           int32_t n_keys, const uint16_t* hidden, int32_t* n_rows, int32_t* row_token,
                           int32_t* row_slots, int32_t* rank_row_offset, int32_t* slot_row,
                           uint16_t* ddispatch);
+
+/* Plan quality [TopoEP Figs. 10, 13(b), 16]: out[8] = assignments, same rank,
+ * same node, other node, served by replicas, largest and smallest rank
+ * load, replicas. */
+int oracle_quality(const oracle_cfg* c, int32_t n_inst, const int32_t* inst_expert, const int32_t* inst_rank,
+                   const int32_t* rank_load, const int32_t* quota, int64_t* out);
 
 #ifdef __cplusplus
 }

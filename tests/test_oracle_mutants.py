@@ -76,6 +76,12 @@ MUTANTS = [
      "    for (int64_t t = T - 1; t >= 0; --t) {\n      uint32_t mask = 0;"),
     ("dedup slot row off by one", "if (mask >> j & 1u) slot_row[t * k + j] = (int32_t)p;",
      "if (mask >> j & 1u) slot_row[t * k + j] = (int32_t)(p + 1 < N ? p + 1 : p);"),
+    ("quality counts main instances as replicas", "if (r != main_of(d, e)) out[4] += q;",
+     "if (r == main_of(d, e)) out[4] += q;"),
+    ("quality same node excludes the source rank", "if (dom_of(c, r) == dom_of(c, s)) out[2] += q;",
+     "if (dom_of(c, r) == dom_of(c, s) && r != s) out[2] += q;"),
+    ("quality smallest load is a maximum", "out[6] = std::min<int64_t>(out[6], rank_load[r]);",
+     "out[6] = std::max<int64_t>(out[6], rank_load[r]);"),
 ]
 
 
@@ -91,6 +97,7 @@ def test_pins_reject_mutant(tmp_path, name, old, new):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_combine.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_placement.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_placement.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_quality.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "the pins accept the mutant '%s'" % name
