@@ -20,6 +20,12 @@ the inputs resident in HBM.  Prints ONE JSON line:
               correlated one, and with the planner's instances
   dedup_dispatch  the deduplicated dispatch (moe_plan_dedup_dispatch) with the
               correlated placement: its rows and HBM rate
+  plan_quality  the plan's rank-load imbalance (max / mean) and its shares of
+              assignments on the source's rank, on another node and on replicas
+              (moe_plan_quality), beside the static placement's
+With --sweep quality / --sweep solver it instead prints one JSON line per point
+of TopoEP's plan-quality study (router_skew 0..-4 x replica slots per rank
+0..4 on the Fig. 10 shape) or solver-scaling study (Fig. 11 shapes).
   cpu_baseline  the CPU oracle on one core over a bounded sample
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -235,13 +241,69 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
         e[1].record(stream)
     torch.cuda.synchronize()
     place["rows_saved_frac"] = saved
+    quality = {"plan": quality_dict(lay0.quality(), w.R)}
     dedup = dict(us=float(np.mean([e[0].elapsed_time(e[1]) for e in dev_])) * 1e3, n_rows=int(dd.n_rows.item()))
     status = [layer.status() for layer in layers]
     for layer in layers:
         layer.close()
-    return dict(ms_total=ms_total, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup, per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
+    static = mp.Layer(mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, 0), device=dev, cooc=False)
+    static.route(logits[0])
+    static.plan()
+    quality["static_placement"] = quality_dict(static.quality(), w.R)
+    static.close()
+    return dict(ms_total=ms_total, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup, quality=quality,
+                per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
                 per_call_ms_min={k: float(np.min(v)) for k, v in per.items()}, status=status,
                 device=torch.cuda.get_device_name(dev))
+
+
+def quality_dict(q, R: int) -> dict:
+    """moe_plan_quality's counters as the shares the pages report."""
+    import load_balance_planning_amd as mp
+    v = dict(zip(mp.QUALITY_FIELDS, (int(x) for x in q.cpu().numpy())))
+    n = max(v["assignments"], 1)
+    return {"imbalance": v["max_rank_load"] * R / n, "same_rank_frac": v["same_rank"] / n,
+            "other_node_frac": v["other_node"] / n, "replica_served_frac": v["replica_served"] / n,
+            "replicas": v["replicas"]}
+
+
+def sweep(kind: str, warmup: int, reps: int):
+    """One JSON line per point: TopoEP's plan-quality study (section 6.2 Fig. 10,
+    section 6.6 Fig. 16) over its section 6.4 router_skew range, or its solver-scaling
+    study (section 6.3 Fig. 11), with moe_plan_plan event-timed (warm-up, then reps)."""
+    import torch
+    import load_balance_planning_amd as mp
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if kind == "quality":
+        points = [synth.skew_layer(sk, n) for sk in (0, -1, -2, -3, -4) for n in (0, 1, 2, 3, 4)]
+    else:
+        points = ([synth.skew_layer(-4, 2, E=640, R=r) for r in (8, 16, 32, 64, 128)] +
+                  [synth.skew_layer(-4, 2, E=e, R=32) for e in (128, 256, 512, 1024, 2048)])
+    stream = torch.cuda.current_stream(dev)
+    for w in points:
+        layer = mp.Layer(mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B), device=dev, cooc=False)
+        layer.route(torch.from_numpy(synth.logits(w)).to(dev))
+        for _ in range(warmup):
+            layer.plan()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record(stream)
+            layer.plan()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = [e[0].elapsed_time(e[1]) for e in ev]
+        q = quality_dict(layer.quality(), w.R)
+        st = layer.status()
+        layer.close()
+        line = {"sweep": kind, "workload": w.name, "router_skew": -w.zipf_s, "slots_per_rank": w.B // w.R,
+                "T": w.T, "E": w.E, "k": w.k, "R": w.R, "G": w.G, "plan_us_mean": float(np.mean(ms)) * 1e3,
+                "plan_us_min": float(np.min(ms)) * 1e3, "reps": reps}
+        line.update(q)
+        if st:
+            line["status_flags"] = st
+        print(json.dumps(line), flush=True)
 
 
 def placement_report(w, p: dict, with_oracle: bool) -> dict:
@@ -297,6 +359,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=synth.WORKLOAD_ORDER)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", choices=("quality", "solver"), default=None,
+                    help="print TopoEP's plan-quality or solver-scaling study instead of the path benchmark")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the path, time a plain copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -304,6 +368,9 @@ def main():
         print("bench.py measures one GPU: the planning path runs its logical EP ranks on a single device. "
               "Run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(args.sweep, 20, 200)
+        return
     if args.copy_bytes > 0:
         print(json.dumps(copy_reference(args.copy_bytes, args.steps)), flush=True)
         return
@@ -344,6 +411,7 @@ def main():
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": dedup_bytes(w, g["dedup"]["n_rows"]) / (g["dedup"]["us"] / 1e6) / 1e9 / HBM_PEAK_GBS,
                            "vs_dispatch_us": disp_ms * 1e3},
+        "plan_quality": g["quality"],
         "per_call_us": {k: v * 1e3 for k, v in g["per_call_ms"].items()},
         "per_call_us_min": {k: v * 1e3 for k, v in g["per_call_ms_min"].items()},
         "cpu_baseline": cpu,

@@ -14,6 +14,8 @@
  *   moe_plan_dedup_count / moe_plan_dedup_dispatch
  *                      rows of a deduplicating dispatcher: counts, and the
  *                      layout with its bf16 row gather
+ *   moe_plan_quality   plan-quality counters: rank-load imbalance, assignments
+ *                      crossing nodes, assignments served by replicas
  * EP ranks and NVLink domains ("nodes") are logical partitions on one GPU:
  *   source rank of token t   src(t)  = t / (T/R)     (contiguous token blocks)
  *   domain of rank r          dom(r)  = r / G         (contiguous rank blocks)
@@ -402,6 +404,21 @@ int moe_plan_dedup_count(moe_plan_t h, const int32_t* slot_key, const int32_t* k
  */
 int moe_plan_dedup_dispatch(moe_plan_t h, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
                             const uint16_t* hidden, const moe_dedup_out* out, void* stream);
+
+/*
+ * Plan-quality counters [TopoEP section 6.2 Fig. 10 and section 6.4 Fig. 13(b):
+ * rank-load imbalance = largest rank load / mean; section 6.6 Fig. 16: the
+ * shares of assignments executed on another node than their source and
+ * executed by replicas].  From moe_plan_plan's n_inst, inst_expert,
+ * inst_rank, rank_load and quota (device), writes int64 out[8] (device):
+ *   out[0] assignments (sum of the quotas)     out[1] on the source's own rank
+ *   out[2] on the source's node                out[3] on another node
+ *   out[4] on a replica (rank != e / (E/R))     out[5] largest rank load
+ *   out[6] smallest rank load                  out[7] replicas (n_inst - E)
+ * The imbalance is out[5] * R / out[0].  An n_inst outside [E, E+B] or an
+ * instance with a rank or expert out of range sets MOE_STATUS_PLAN_CHECK.
+ */
+int moe_plan_quality(moe_plan_t h, const moe_plan_out* plan, int64_t* out, void* stream);
 
 /*
  * Synchronise the handle's last stream, copy the device status word to

@@ -83,7 +83,7 @@ class moe_dedup_out(ctypes.Structure):
 
 EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
            "moe_plan_dispatch", "moe_plan_step", "moe_plan_combine", "moe_plan_place", "moe_plan_dedup_count",
-           "moe_plan_dedup_dispatch", "moe_plan_status", "moe_plan_destroy")
+           "moe_plan_dedup_dispatch", "moe_plan_quality", "moe_plan_status", "moe_plan_destroy")
 
 _LIB = None
 
@@ -111,6 +111,7 @@ def lib():
         l.moe_plan_place.argtypes = [vp, vp, ctypes.c_int32, vp, vp]
         l.moe_plan_dedup_count.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp]
         l.moe_plan_dedup_dispatch.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp, vp]
+        l.moe_plan_quality.argtypes = [vp, vp, vp, vp]
         l.moe_plan_status.argtypes = [vp, vp]
         l.moe_plan_destroy.argtypes = [vp]
         l.moe_plan_destroy.restype = None
@@ -176,6 +177,14 @@ def moe_plan_dedup_count(h, slot_key: int, key_rank, n_keys: int, out: moe_dedup
 def moe_plan_dedup_dispatch(h, slot_key: int, key_rank, n_keys: int, hidden: int, out: moe_dedup_out, stream: int):
     _check("moe_plan_dedup_dispatch",
            lib().moe_plan_dedup_dispatch(h, slot_key, key_rank, n_keys, hidden, ctypes.byref(out), stream))
+
+
+def moe_plan_quality(h, plan: moe_plan_out, out: int, stream: int):
+    _check("moe_plan_quality", lib().moe_plan_quality(h, ctypes.byref(plan), out, stream))
+
+
+QUALITY_FIELDS = ("assignments", "same_rank", "same_node", "other_node", "replica_served", "max_rank_load",
+                  "min_rank_load", "replicas")
 
 
 def moe_plan_status(h) -> int:
@@ -423,6 +432,14 @@ class Layer:
         moe_plan_dedup_dispatch(self.handle, _ptr(slot_key), _ptr(key_rank), n, _ptr(hidden), self._dedup_s,
                                 self._stream(stream))
         return self.dedup_out
+
+    def quality(self, stream=None):
+        """Plan-quality counters of this layer's plan (moe_plan_quality): an int64 tensor of 8
+        on the device, in QUALITY_FIELDS order."""
+        if getattr(self, "_quality", None) is None:
+            self._quality = self.torch.empty(8, dtype=self.torch.int64, device=self.device)
+        moe_plan_quality(self.handle, self._plan_s, _ptr(self._quality), self._stream(stream))
+        return self._quality
 
     def status(self) -> int:
         return moe_plan_status(self.handle)

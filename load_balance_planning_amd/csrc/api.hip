@@ -371,6 +371,14 @@ extern "C" int moe_plan_dedup_dispatch(moe_plan_t h, const int32_t* slot_key, co
       moe::launch_dedup(h->d, slot_key, key_rank, n_keys, src, *out, h->ws, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int moe_plan_quality(moe_plan_t h, const moe_plan_out* plan, int64_t* out, void* stream) {
+  if (!h || !plan || !out || !plan->n_inst || !plan->inst_expert || !plan->inst_rank || !plan->rank_load ||
+      !plan->quota)
+    return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  return hip_rc(moe::launch_quality(h->d, *plan, out, h->ws.status, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int moe_plan_status(moe_plan_t h, int32_t* host_flags) {
   if (!h || !host_flags) return MOE_ERR_INVALID_ARG;
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;

@@ -107,6 +107,9 @@ hipError_t launch_place(const Dims& d, const int32_t* cooc, int32_t max_swaps, c
 hipError_t launch_dedup(const Dims& d, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
                         const uint16_t* hidden, const moe_dedup_out& out, const Workspace& ws, hipStream_t st);
 
+// Plan-quality counters (int64 [8]) from a plan's quotas, instances and loads.
+hipError_t launch_quality(const Dims& d, const moe_plan_out& plan, int64_t* out, int32_t* status, hipStream_t st);
+
 // LDS bytes the plan and scan kernels need for these dimensions.
 size_t plan_lds_bytes(const Dims& d);
 size_t scan_lds_bytes(const Dims& d);

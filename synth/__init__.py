@@ -92,6 +92,18 @@ WORKLOADS = {
 WORKLOAD_ORDER = ["mixtral_tiny", "qwen3_layer", "deepseek_v3_layer", "kimi_layer", "coupled_4layer"]
 
 
+def skew_layer(router_skew: float, n_slot: int, E: int = 640, R: int = 32, T: int = 32768, k: int = 8, G: int = 8,
+               H: int = 2048) -> Workload:
+    """A layer of TopoEP section 6.4's synthetic routing: random logits plus a fixed
+    expert-specific bias, router_skew 0 uniform in expectation and more negative
+    values concentrating the load.  The bias is router_skew * ln(1 + rank(e)) over a
+    seeded expert permutation (a Zipf law with exponent -router_skew).  Replica
+    budget n_slot per rank.  Default shape: the Fig. 10 workload (32 ranks in
+    nodes of 8, 640 experts, top-8)."""
+    return Workload("skew%g_slots%d_E%d_R%d" % (router_skew, n_slot, E, R), T=T, E=E, k=k, R=R, G=G, H=H,
+                    B=n_slot * R, zipf_s=-float(router_skew))
+
+
 def permutation(seed: int, layer: int, kind: int, n: int) -> np.ndarray:
     out = np.empty(n, dtype=np.int32)
     _lib().synth_permutation(seed, layer, kind, n, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
