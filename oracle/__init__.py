@@ -54,8 +54,10 @@ def _setup(l):
     l.oracle_dedup.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp, vp]
     l.oracle_dedup_dispatch.argtypes = [vp, vp, vp, ctypes.c_int32] + [vp] * 7
     l.oracle_quality.argtypes = [vp, ctypes.c_int32] + [vp] * 5
+    l.oracle_predict.argtypes = [vp] * 9
     for f in (l.oracle_params, l.oracle_domain_budget, l.oracle_route, l.oracle_plan, l.oracle_dispatch,
-              l.oracle_combine, l.oracle_place, l.oracle_dedup, l.oracle_dedup_dispatch, l.oracle_quality):
+              l.oracle_combine, l.oracle_place, l.oracle_dedup, l.oracle_dedup_dispatch, l.oracle_quality,
+              l.oracle_predict):
         f.restype = ctypes.c_int
     return l
 
@@ -236,6 +238,26 @@ def quality(cfg: OracleCfg, plan_out: dict, l=None) -> dict:
     res = {k: int(v) for k, v in zip(QUALITY_FIELDS, out)}
     res["imbalance"] = res["max_rank_load"] * cfg.R / res["assignments"] if res["assignments"] else 1.0
     return res
+
+
+def predict(cfg: OracleCfg, topk_cur: np.ndarray, trans: np.ndarray, count_cur: np.ndarray,
+            key_rank: np.ndarray | None = None, topk_next: np.ndarray | None = None, l=None) -> dict:
+    """Token-shuffle prediction (see oracle_predict)."""
+    l = l or lib()
+    T, E, k, R = cfg.T, cfg.E, cfg.k, cfg.R
+    cur = np.ascontiguousarray(topk_cur, np.int32).reshape(T, k)
+    X = np.ascontiguousarray(trans, np.int32).reshape(E, E)
+    cnt = np.ascontiguousarray(count_cur, np.int32).reshape(E)
+    kr = None if key_rank is None else np.ascontiguousarray(key_rank, np.int32).reshape(E)
+    nxt = None if topk_next is None else np.ascontiguousarray(topk_next, np.int32).reshape(T, k)
+    out = dict(pred=np.zeros(T, np.int32), rank_tokens=np.zeros(R, np.int32))
+    local = np.zeros(2, np.int64)
+    rc = l.oracle_predict(ctypes.byref(cfg), _p(cur), _p(X), _p(cnt), _p(kr), _p(nxt), _p(out["pred"]),
+                          _p(out["rank_tokens"]), _p(local))
+    if rc != 0:
+        raise ValueError("oracle_predict failed (%d)" % rc)
+    out["local_predicted"], out["local_source"] = int(local[0]), int(local[1])
+    return out
 
 
 def run_all(cfg: OracleCfg, logits: np.ndarray, hidden: np.ndarray | None,

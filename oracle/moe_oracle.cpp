@@ -708,3 +708,65 @@ extern "C" int oracle_quality(const oracle_cfg* c, int32_t n_inst, const int32_t
   out[7] = n_inst - c->E;
   return 0;
 }
+
+// ---------------------------------------------------------------------------
+// Token-shuffle prediction ([Coupling] "Moving Tokens Toward Their Next
+// Experts": a token's experts at this layer predict which GPU holds most of
+// its next-layer experts; the token is moved there before the next router).
+// The page gives no formula; the reading taken is that each of the token's
+// experts a votes with its empirical next-layer distribution:
+//   P[a][r]   = (sum over experts b on rank r of X[a][b]) / count[a]
+//               (X: this layer -> next layer transition counts, count[a]:
+//               this layer's assignments of a; 0 when count[a] = 0)
+//   score[r]  = P[a_0][r] + P[a_1][r] + ... + P[a_{k-1}][r]   (slot order)
+//   pred[t]   = argmax_r score[r], ties to the lower rank
+// score[r] / k is the expected share of the token's next-layer experts on r.
+// All of it in IEEE double, in this order.  The rank of b is key_rank[b]
+// (NULL: contiguous b / (E/R)).  With topk_next given, local[0] counts the
+// next layer's slots on the predicted rank and local[1] those on the token's
+// own source rank t / (T/R) (no shuffling).  rank_tokens[r]: tokens predicted
+// for rank r.
+// ---------------------------------------------------------------------------
+extern "C" int oracle_predict(const oracle_cfg* c, const int32_t* topk_cur, const int32_t* trans,
+                              const int32_t* count_cur, const int32_t* key_rank, const int32_t* topk_next,
+                              int32_t* pred, int32_t* rank_tokens, int64_t* local) {
+  if (!valid(c) || !trans || !count_cur || !pred || !rank_tokens) return -1;
+  const int64_t T = c->T, E = c->E, k = c->k, R = c->R, Tr = T / R, Er = E / R;
+  if (T > 0 && !topk_cur) return -1;
+  std::vector<int64_t> rank_of(E);
+  for (int64_t b = 0; b < E; ++b) {
+    rank_of[b] = key_rank ? key_rank[b] : b / Er;
+    if (rank_of[b] < 0 || rank_of[b] >= R) return -1;
+  }
+  std::vector<double> P(E * R, 0.0);
+  for (int64_t a = 0; a < E; ++a) {
+    if (count_cur[a] < 0) return -1;
+    std::vector<int64_t> n(R, 0);
+    for (int64_t b = 0; b < E; ++b) n[rank_of[b]] += trans[a * E + b];
+    for (int64_t r = 0; r < R; ++r) P[a * R + r] = count_cur[a] > 0 ? (double)n[r] / (double)count_cur[a] : 0.0;
+  }
+  for (int64_t r = 0; r < R; ++r) rank_tokens[r] = 0;
+  if (local) local[0] = local[1] = 0;
+  std::vector<double> score(R);
+  for (int64_t t = 0; t < T; ++t) {
+    std::fill(score.begin(), score.end(), 0.0);
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t a = topk_cur[t * k + j];
+      if (a < 0 || a >= E) return -1;
+      for (int64_t r = 0; r < R; ++r) score[r] += P[a * R + r];
+    }
+    int64_t best = 0;
+    for (int64_t r = 1; r < R; ++r)
+      if (score[r] > score[best]) best = r;
+    pred[t] = (int32_t)best;
+    rank_tokens[best] += 1;
+    if (local && topk_next)
+      for (int64_t j = 0; j < k; ++j) {
+        const int64_t b = topk_next[t * k + j];
+        if (b < 0 || b >= E) return -1;
+        if (rank_of[b] == best) local[0] += 1;
+        if (rank_of[b] == t / Tr) local[1] += 1;
+      }
+  }
+  return 0;
+}

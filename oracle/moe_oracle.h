@@ -18,6 +18,8 @@
  *   Placement and deduplication: [Coupling] "Moving Correlated Experts
  *             Together", Fig. 3 (the partition algorithm is a reading).
  *   Plan quality: [TopoEP] sections 6.2, 6.4, 6.6 (Figs. 10, 13(b), 16).
+ *   Token-shuffle prediction: [Coupling] "Moving Tokens Toward Their Next
+ *             Experts" (the scoring rule is a reading).
  *
  * Every function returns 0 on success or a negative status:
  *   -1 invalid argument / configuration, -4 a NaN gate logit,
@@ -105,6 +107,15 @@ int oracle_dedup_dispatch(const oracle_cfg* c, const int32_t* slot_key, const in
  * load, replicas. */
 int oracle_quality(const oracle_cfg* c, int32_t n_inst, const int32_t* inst_expert, const int32_t* inst_rank,
                    const int32_t* rank_load, const int32_t* quota, int64_t* out);
+
+/* Token-shuffle prediction [Coupling]: pred [T] = the rank with the largest
+ * sum over the token's experts a of (transitions from a to that rank's
+ * experts) / count_cur[a], in double, ties to the lower rank; rank_tokens [R];
+ * with topk_next, local[2] = next-layer slots on the predicted rank / on the
+ * source rank.  key_rank [E] nullable (contiguous). */
+int oracle_predict(const oracle_cfg* c, const int32_t* topk_cur, const int32_t* trans, const int32_t* count_cur,
+                   const int32_t* key_rank, const int32_t* topk_next, int32_t* pred, int32_t* rank_tokens,
+                   int64_t* local);
 
 #ifdef __cplusplus
 }

@@ -82,6 +82,14 @@ MUTANTS = [
      "if (dom_of(c, r) == dom_of(c, s) && r != s) out[2] += q;"),
     ("quality smallest load is a maximum", "out[6] = std::min<int64_t>(out[6], rank_load[r]);",
      "out[6] = std::max<int64_t>(out[6], rank_load[r]);"),
+    ("prediction without the count normalisation",
+     "P[a * R + r] = count_cur[a] > 0 ? (double)n[r] / (double)count_cur[a] : 0.0;",
+     "P[a * R + r] = count_cur[a] > 0 ? (double)n[r] : 0.0;"),
+    ("prediction transposed transitions", "for (int64_t b = 0; b < E; ++b) n[rank_of[b]] += trans[a * E + b];",
+     "for (int64_t b = 0; b < E; ++b) n[rank_of[b]] += trans[b * E + a];"),
+    ("prediction ties to the higher rank", "if (score[r] > score[best]) best = r;", "if (score[r] >= score[best]) best = r;"),
+    ("locality counts the predicted rank of the wrong layer", "if (rank_of[b] == best) local[0] += 1;",
+     "if (rank_of[topk_cur[t * k + j]] == best) local[0] += 1;"),
 ]
 
 
@@ -98,6 +106,7 @@ def test_pins_reject_mutant(tmp_path, name, old, new):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_combine.py"),
                         os.path.join(ROOT, "tests", "test_oracle_placement.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_quality.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_quality.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_predict.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "the pins accept the mutant '%s'" % name
