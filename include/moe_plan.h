@@ -16,6 +16,8 @@
  *                      layout with its bf16 row gather
  *   moe_plan_quality   plan-quality counters: rank-load imbalance, assignments
  *                      crossing nodes, assignments served by replicas
+ *   moe_plan_predict   token-shuffle prediction: the rank expected to hold most
+ *                      of each token's next-layer experts
  * EP ranks and NVLink domains ("nodes") are logical partitions on one GPU:
  *   source rank of token t   src(t)  = t / (T/R)     (contiguous token blocks)
  *   domain of rank r          dom(r)  = r / G         (contiguous rank blocks)
@@ -254,6 +256,20 @@ typedef struct {
   uint16_t* ddispatch;
 } moe_dedup_out;
 
+/*
+ * Outputs of moe_plan_predict.
+ *   pred         int32 [T]: predicted rank of each token (NULL allowed when T = 0).
+ *   rank_tokens  int32 [R]: tokens predicted for each rank.
+ *   local        int64 [2] (nullable): with the next layer's top-k, its slots
+ *                on the predicted rank (local[0]) and on the token's own
+ *                source rank t / (T/R) (local[1], no shuffling).
+ */
+typedef struct {
+  int32_t* pred;
+  int32_t* rank_tokens;
+  int64_t* local;
+} moe_predict_out;
+
 /* Buffer sizes for a configuration (host only, no GPU work).  Returns
  * MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED as moe_plan_create would. */
 int moe_plan_query(const moe_plan_config* cfg, moe_plan_sizes* sizes);
@@ -419,6 +435,32 @@ int moe_plan_dedup_dispatch(moe_plan_t h, const int32_t* slot_key, const int32_t
  * instance with a rank or expert out of range sets MOE_STATUS_PLAN_CHECK.
  */
 int moe_plan_quality(moe_plan_t h, const moe_plan_out* plan, int64_t* out, void* stream);
+
+/*
+ * Token-shuffle prediction [Coupling, "Moving Tokens Toward Their Next
+ * Experts": a token's experts at this layer predict the GPU holding most of its
+ * next-layer experts, and the token moves there before the next router].  The
+ * page gives no formula; each of the token's experts a votes with its
+ * empirical next-layer distribution over ranks:
+ *   P[a][r]  = (sum over experts b on rank r of trans[a][b]) / count_cur[a]
+ *              (0 when count_cur[a] = 0)
+ *   score[r] = P[a_0][r] + ... + P[a_{k-1}][r]   (IEEE double, slot order)
+ *   pred[t]  = argmax_r score[r], ties to the lower rank.
+ * topk_cur   int32 [T][k] this layer's top-k (device).
+ * trans      int32 [E][E] transitions from this layer to the next (device):
+ *            moe_plan_route's trans of the next layer (its prev_topk = topk_cur),
+ *            or counts gathered earlier.
+ * count_cur  int32 [E] this layer's expert counts (device).
+ * key_rank   int32 [E] (device, nullable): rank of each next-layer expert;
+ *            NULL means the contiguous placement b / (E/R).
+ * topk_next  int32 [T][k] (device, nullable): the next layer's top-k, for
+ *            out->local.
+ * An expert id out of range sets MOE_STATUS_BAD_TOPK (that slot is left out),
+ * a rank out of range MOE_STATUS_BAD_KEY, a negative count
+ * MOE_STATUS_BAD_PAIRS.
+ */
+int moe_plan_predict(moe_plan_t h, const int32_t* topk_cur, const int32_t* trans, const int32_t* count_cur,
+                     const int32_t* key_rank, const int32_t* topk_next, const moe_predict_out* out, void* stream);
 
 /*
  * Synchronise the handle's last stream, copy the device status word to

@@ -75,6 +75,10 @@ class moe_place_out(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("expert_rank", "rank_experts", "intra", "n_swaps")]
 
 
+class moe_predict_out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("pred", "rank_tokens", "local")]
+
+
 class moe_dedup_out(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "tok_ranks", "rank_rows", "rank_slots", "n_rows", "row_token", "row_slots", "rank_row_offset", "slot_row",
@@ -83,7 +87,7 @@ class moe_dedup_out(ctypes.Structure):
 
 EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
            "moe_plan_dispatch", "moe_plan_step", "moe_plan_combine", "moe_plan_place", "moe_plan_dedup_count",
-           "moe_plan_dedup_dispatch", "moe_plan_quality", "moe_plan_status", "moe_plan_destroy")
+           "moe_plan_dedup_dispatch", "moe_plan_quality", "moe_plan_predict", "moe_plan_status", "moe_plan_destroy")
 
 _LIB = None
 
@@ -112,6 +116,7 @@ def lib():
         l.moe_plan_dedup_count.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp]
         l.moe_plan_dedup_dispatch.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp, vp]
         l.moe_plan_quality.argtypes = [vp, vp, vp, vp]
+        l.moe_plan_predict.argtypes = [vp] * 8
         l.moe_plan_status.argtypes = [vp, vp]
         l.moe_plan_destroy.argtypes = [vp]
         l.moe_plan_destroy.restype = None
@@ -181,6 +186,12 @@ def moe_plan_dedup_dispatch(h, slot_key: int, key_rank, n_keys: int, hidden: int
 
 def moe_plan_quality(h, plan: moe_plan_out, out: int, stream: int):
     _check("moe_plan_quality", lib().moe_plan_quality(h, ctypes.byref(plan), out, stream))
+
+
+def moe_plan_predict(h, topk_cur: int, trans: int, count_cur: int, key_rank, topk_next, out: moe_predict_out,
+                     stream: int):
+    _check("moe_plan_predict", lib().moe_plan_predict(h, topk_cur, trans, count_cur, key_rank, topk_next,
+                                                      ctypes.byref(out), stream))
 
 
 QUALITY_FIELDS = ("assignments", "same_rank", "same_node", "other_node", "replica_served", "max_rank_load",
@@ -440,6 +451,27 @@ class Layer:
             self._quality = self.torch.empty(8, dtype=self.torch.int64, device=self.device)
         moe_plan_quality(self.handle, self._plan_s, _ptr(self._quality), self._stream(stream))
         return self._quality
+
+    def predict(self, topk_cur, trans, count_cur, key_rank=None, topk_next=None, stream=None):
+        """Token-shuffle prediction (moe_plan_predict): returns (pred [T], rank_tokens [R], local [2])
+        device tensors; local counts next-layer slots on the predicted / source rank when
+        topk_next is given."""
+        torch, T, E, k, R = self.torch, self.cfg.T, self.cfg.E, self.cfg.k, self.cfg.R
+        self._check_tensor(topk_cur, (T, k), torch.int32)
+        self._check_tensor(trans, (E, E), torch.int32)
+        self._check_tensor(count_cur, (E,), torch.int32)
+        if key_rank is not None:
+            self._check_tensor(key_rank, (E,), torch.int32)
+        if topk_next is not None:
+            self._check_tensor(topk_next, (T, k), torch.int32)
+        if getattr(self, "_pred", None) is None:
+            self._pred = (torch.empty(T, dtype=torch.int32, device=self.device),
+                          torch.empty(R, dtype=torch.int32, device=self.device),
+                          torch.empty(2, dtype=torch.int64, device=self.device))
+        out = moe_predict_out(*(_ptr(x) for x in self._pred))
+        moe_plan_predict(self.handle, _ptr(topk_cur), _ptr(trans), _ptr(count_cur), _ptr(key_rank), _ptr(topk_next),
+                         out, self._stream(stream))
+        return self._pred
 
     def status(self) -> int:
         return moe_plan_status(self.handle)

@@ -29,7 +29,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
   size_t status, prev_mask, demand, einst_off, einst_list, rlist, colpre, pair_part, omega_acc;
-  size_t place_aff, place_key, dd_mask, dd_cnt, dd_base, dd_count, total;
+  size_t place_aff, place_key, dd_mask, dd_cnt, dd_base, dd_count, pred_vote, total;
 };
 
 WsLayout ws_layout(const moe::Dims& d) {
@@ -51,6 +51,7 @@ WsLayout ws_layout(const moe::Dims& d) {
   l.dd_cnt = take(sizeof(int32_t) * (size_t)d.NT * d.R);
   l.dd_base = take(sizeof(int32_t) * (size_t)d.NT * d.R);
   l.dd_count = take(sizeof(int32_t) * (size_t)d.R);
+  l.pred_vote = take(sizeof(double) * (size_t)d.E * d.R);
   l.total = o;
   return l;
 }
@@ -154,6 +155,7 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   h->ws.dd_cnt = reinterpret_cast<int32_t*>(b + l.dd_cnt);
   h->ws.dd_base = reinterpret_cast<int32_t*>(b + l.dd_base);
   h->ws.dd_count = reinterpret_cast<int32_t*>(b + l.dd_count);
+  h->ws.pred_vote = reinterpret_cast<double*>(b + l.pred_vote);
   if (hipMemset(h->ws_base, 0, l.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->ws_base);
     delete h;
@@ -377,6 +379,16 @@ extern "C" int moe_plan_quality(moe_plan_t h, const moe_plan_out* plan, int64_t*
     return MOE_ERR_INVALID_ARG;
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;
   return hip_rc(moe::launch_quality(h->d, *plan, out, h->ws.status, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int moe_plan_predict(moe_plan_t h, const int32_t* topk_cur, const int32_t* trans, const int32_t* count_cur,
+                                const int32_t* key_rank, const int32_t* topk_next, const moe_predict_out* out,
+                                void* stream) {
+  if (!h || !trans || !count_cur || !out || !out->rank_tokens) return MOE_ERR_INVALID_ARG;
+  if (h->d.T > 0 && (!topk_cur || !out->pred)) return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  return hip_rc(moe::launch_predict(h->d, topk_cur, trans, count_cur, key_rank, topk_next, *out, h->ws,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int moe_plan_status(moe_plan_t h, int32_t* host_flags) {

@@ -48,6 +48,7 @@ struct Workspace {
   int32_t* dd_cnt;      // [NT][R] slots of each tile on each rank
   int32_t* dd_base;     // [NT][R] rows of each rank before each tile
   int32_t* dd_count;    // [R] rows of each rank
+  double* pred_vote;    // [E][R] token-shuffle votes: each expert's next-layer share per rank
 };
 
 // Pair-count job: presence masks in, co-selection / transition blocks out
@@ -109,6 +110,11 @@ hipError_t launch_dedup(const Dims& d, const int32_t* slot_key, const int32_t* k
 
 // Plan-quality counters (int64 [8]) from a plan's quotas, instances and loads.
 hipError_t launch_quality(const Dims& d, const moe_plan_out& plan, int64_t* out, int32_t* status, hipStream_t st);
+
+// Token-shuffle prediction from the layer-to-layer transition counts.
+hipError_t launch_predict(const Dims& d, const int32_t* topk_cur, const int32_t* trans, const int32_t* count_cur,
+                          const int32_t* key_rank, const int32_t* topk_next, const moe_predict_out& out,
+                          const Workspace& ws, hipStream_t st);
 
 // LDS bytes the plan and scan kernels need for these dimensions.
 size_t plan_lds_bytes(const Dims& d);
