@@ -20,6 +20,10 @@ the inputs resident in HBM.  Prints ONE JSON line:
               correlated one, and with the planner's instances
   dedup_dispatch  the deduplicated dispatch (moe_plan_dedup_dispatch) with the
               correlated placement: its rows and HBM rate
+  token_shuffle (workloads of several layers) moe_plan_predict from each layer
+              to the next: its time and the share of the next layer's slots on
+              the predicted rank, against staying on the source rank, with the
+              contiguous and with the correlated placement of the next layer
   plan_quality  the plan's rank-load imbalance (max / mean) and its shares of
               assignments on the source's rank, on another node and on replicas
               (moe_plan_quality), beside the static placement's
@@ -243,6 +247,31 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     place["rows_saved_frac"] = saved
     quality = {"plan": quality_dict(lay0.quality(), w.R)}
     dedup = dict(us=float(np.mean([e[0].elapsed_time(e[1]) for e in dev_])) * 1e3, n_rows=int(dd.n_rows.item()))
+    shuffle = None
+    if w.L > 1:
+        shuffle = []
+        slots = w.T * w.k
+        for l in range(1, w.L):
+            a, b = layers[l - 1], layers[l]
+            args = (a.route_out.topk_idx, b.route_out.trans, a.route_out.expert_count)
+            b.predict(*args, topk_next=b.route_out.topk_idx)
+            sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+            torch.cuda.synchronize()
+            for e in sev:
+                e[0].record(stream)
+                _, _, loc = b.predict(*args, topk_next=b.route_out.topk_idx)
+                e[1].record(stream)
+            torch.cuda.synchronize()
+            contiguous = loc.cpu().numpy().copy()
+            placed_rank = b.place().expert_rank.clone()
+            _, _, loc = b.predict(*args, key_rank=placed_rank, topk_next=b.route_out.topk_idx)
+            placed = loc.cpu().numpy()
+            shuffle.append({"from_layer": l - 1, "to_layer": l,
+                            "us": float(np.mean([e[0].elapsed_time(e[1]) for e in sev])) * 1e3,
+                            "local_frac_contiguous": {"shuffled": int(contiguous[0]) / slots,
+                                                      "unshuffled": int(contiguous[1]) / slots},
+                            "local_frac_correlated_placement": {"shuffled": int(placed[0]) / slots,
+                                                                "unshuffled": int(placed[1]) / slots}})
     status = [layer.status() for layer in layers]
     for layer in layers:
         layer.close()
@@ -252,6 +281,7 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     quality["static_placement"] = quality_dict(static.quality(), w.R)
     static.close()
     return dict(ms_total=ms_total, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup, quality=quality,
+                shuffle=shuffle,
                 per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
                 per_call_ms_min={k: float(np.min(v)) for k, v in per.items()}, status=status,
                 device=torch.cuda.get_device_name(dev))
@@ -412,6 +442,7 @@ def main():
                            "frac": dedup_bytes(w, g["dedup"]["n_rows"]) / (g["dedup"]["us"] / 1e6) / 1e9 / HBM_PEAK_GBS,
                            "vs_dispatch_us": disp_ms * 1e3},
         "plan_quality": g["quality"],
+        "token_shuffle": g["shuffle"],
         "per_call_us": {k: v * 1e3 for k, v in g["per_call_ms"].items()},
         "per_call_us_min": {k: v * 1e3 for k, v in g["per_call_ms_min"].items()},
         "cpu_baseline": cpu,

@@ -12,10 +12,11 @@
 //
 // Two launches: one workgroup per expert a sums its transition row by
 // destination rank in LDS (64-bit) and writes P[a][*] (E x R doubles, the
-// handle's workspace); then one wave per token, lane r holding ranks r, r+64,
-// ..., adds its experts' rows in slot order and takes the argmax (largest
-// score, then lowest rank, by two wave reductions).  With the next layer's
-// top-k the same wave counts its slots on the predicted rank and on its own
+// handle's workspace); then a group of P lanes per token (P the power of two
+// covering R, at most 64), lane r of the group holding ranks r, r+P, ...,
+// adds its experts' rows in slot order and takes the argmax (largest score,
+// then lowest rank, by two reductions over the group).  With the next layer's
+// top-k the same group counts its slots on the predicted rank and on its own
 // source rank (the locality with and without the shuffle).
 #include "internal.h"
 
@@ -23,9 +24,8 @@ namespace moe {
 namespace {
 
 constexpr int kVoteThreads = 256;
-constexpr int kPredThreads = 256;
-constexpr int kPredTokens = 64;  // tokens per workgroup (16 per wave)
-constexpr int kPredRpl = kMaxR / 64;
+constexpr int kPredThreads = 1024;
+constexpr int kPredTokens = 64;  // tokens per workgroup
 
 struct PredictArgs {
   const int32_t* cur;      // [T][k] this layer's top-k
@@ -76,43 +76,50 @@ __global__ __launch_bounds__(kVoteThreads) void vote_kernel(Dims d, PredictArgs 
 // Order-preserving bits of a non-negative double (sums of votes are >= +0).
 __device__ __forceinline__ uint64_t dbits(double x) { return (uint64_t)__double_as_longlong(x); }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+template <int P>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off);
+  for (int off = P / 2; off >= 1; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off, P);
     v = o > v ? o : v;
   }
   return v;
 }
 
-__device__ __forceinline__ int wave_min_i32(int v) {
+template <int P>
+__device__ __forceinline__ int group_min(int v) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  for (int off = P / 2; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, P));
   return v;
 }
 
-__device__ __forceinline__ int wave_sum_i32(int v) {
+template <int P>
+__device__ __forceinline__ int group_sum(int v) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  for (int off = P / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, P);
   return v;
 }
 
+// A group of P lanes (a power of two, P >= min(R, 64)) per token; lane l of
+// the group holds ranks l, l + P, ... (RPL of them).  A workgroup of 1024
+// threads takes kPredTokens consecutive tokens.
+template <int P, int RPL>
 __global__ __launch_bounds__(kPredThreads) void predict_kernel(Dims d, PredictArgs pa) {
   __shared__ int32_t hist[kMaxR];
   __shared__ int32_t loc[2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kGroups = kPredThreads / P;
+  const int tid = threadIdx.x, sub = tid % P, grp = tid / P;
   for (int r = tid; r < d.R; r += kPredThreads) hist[r] = 0;
   if (tid < 2) loc[tid] = 0;
   __syncthreads();
-  int my_pred_hits = 0, my_src_hits = 0;
-  const int64_t t0 = (int64_t)blockIdx.x * kPredTokens;
   bool bad = false;
-  for (int i = wave; i < kPredTokens; i += kPredThreads / 64) {
-    const int64_t t = t0 + i;
-    if (t >= d.T) break;  // uniform across the wave
-    double score[kPredRpl];
+  int hp = 0, hs = 0;
+  for (int i = grp; i < kPredTokens; i += kGroups) {
+    const int64_t t = (int64_t)blockIdx.x * kPredTokens + i;
+    if (t >= d.T) break;  // uniform across the group
+    double score[RPL];
 #pragma unroll
-    for (int u = 0; u < kPredRpl; ++u) score[u] = 0.0;
+    for (int u = 0; u < RPL; ++u) score[u] = 0.0;
     for (int j = 0; j < d.k; ++j) {
       const int a = pa.cur[t * d.k + j];
       if ((unsigned)a >= (unsigned)d.E) {
@@ -121,59 +128,62 @@ __global__ __launch_bounds__(kPredThreads) void predict_kernel(Dims d, PredictAr
       }
       const double* row = pa.vote + (int64_t)a * d.R;
 #pragma unroll
-      for (int u = 0; u < kPredRpl; ++u) {
-        const int r = lane + 64 * u;
+      for (int u = 0; u < RPL; ++u) {
+        const int r = sub + P * u;
         if (r < d.R) score[u] += row[r];
       }
     }
     uint64_t best = 0;
 #pragma unroll
-    for (int u = 0; u < kPredRpl; ++u) {
-      const int r = lane + 64 * u;
+    for (int u = 0; u < RPL; ++u) {
+      const int r = sub + P * u;
       if (r < d.R) best = dbits(score[u]) > best ? dbits(score[u]) : best;
     }
-    best = wave_max_u64(best);
+    best = group_max_u64<P>(best);
     int br = INT32_MAX;
 #pragma unroll
-    for (int u = 0; u < kPredRpl; ++u) {
-      const int r = lane + 64 * u;
+    for (int u = 0; u < RPL; ++u) {
+      const int r = sub + P * u;
       if (r < d.R && dbits(score[u]) == best) br = min(br, r);
     }
-    br = wave_min_i32(br);
-    if (lane == 0) {
+    br = group_min<P>(br);
+    if (sub == 0) {
       pa.pred[t] = br;
       atomicAdd(&hist[br], 1);
     }
     if (pa.next && pa.local) {
-      int hp = 0, hs = 0;
-      if (lane < d.k) {
-        const int b = pa.next[t * d.k + lane];
+      for (int j = sub; j < d.k; j += P) {
+        const int b = pa.next[t * d.k + j];
         if ((unsigned)b < (unsigned)d.E) {
           const int rb = dest_rank(d, pa.rank_of, b);
-          hp = rb == br;
-          hs = rb == (int)(t / d.Tr);
+          hp += rb == br;
+          hs += rb == (int)(t / d.Tr);
         } else {
           bad = true;
         }
       }
-      hp = wave_sum_i32(hp);
-      hs = wave_sum_i32(hs);
-      if (lane == 0) {
-        my_pred_hits += hp;
-        my_src_hits += hs;
-      }
     }
   }
   if (bad) atomicOr(pa.status, MOE_STATUS_BAD_TOPK);
-  if (lane == 0 && (my_pred_hits | my_src_hits)) {
-    atomicAdd(&loc[0], my_pred_hits);
-    atomicAdd(&loc[1], my_src_hits);
+  if (pa.next && pa.local) {
+    hp = group_sum<64>(hp);
+    hs = group_sum<64>(hs);
+    if ((tid & 63) == 0 && (hp | hs)) {
+      atomicAdd(&loc[0], hp);
+      atomicAdd(&loc[1], hs);
+    }
   }
   __syncthreads();
   for (int r = tid; r < d.R; r += kPredThreads)
     if (hist[r]) atomicAdd(&pa.rank_tokens[r], hist[r]);
   if (pa.local && tid < 2 && loc[tid]) atomicAdd(reinterpret_cast<unsigned long long*>(&pa.local[tid]),
                                                  (unsigned long long)loc[tid]);
+}
+
+template <int P, int RPL>
+void launch_pred(const Dims& d, const PredictArgs& pa, hipStream_t st) {
+  hipLaunchKernelGGL((predict_kernel<P, RPL>), dim3((d.T + kPredTokens - 1) / kPredTokens), dim3(kPredThreads), 0,
+                     st, d, pa);
 }
 
 }  // namespace
@@ -184,8 +194,17 @@ hipError_t launch_predict(const Dims& d, const int32_t* topk_cur, const int32_t*
   const PredictArgs pa{topk_cur, trans, count_cur, key_rank, topk_next, ws.pred_vote,
                        out.pred, out.rank_tokens, out.local, ws.status};
   hipLaunchKernelGGL(vote_kernel, dim3(d.E), dim3(kVoteThreads), 0, st, d, pa);
-  if (d.T > 0)
-    hipLaunchKernelGGL(predict_kernel, dim3((d.T + kPredTokens - 1) / kPredTokens), dim3(kPredThreads), 0, st, d, pa);
+  if (d.T > 0) {
+    if (d.R <= 1) launch_pred<1, 1>(d, pa, st);
+    else if (d.R <= 2) launch_pred<2, 1>(d, pa, st);
+    else if (d.R <= 4) launch_pred<4, 1>(d, pa, st);
+    else if (d.R <= 8) launch_pred<8, 1>(d, pa, st);
+    else if (d.R <= 16) launch_pred<16, 1>(d, pa, st);
+    else if (d.R <= 32) launch_pred<32, 1>(d, pa, st);
+    else if (d.R <= 64) launch_pred<64, 1>(d, pa, st);
+    else if (d.R <= 128) launch_pred<64, 2>(d, pa, st);
+    else launch_pred<64, kMaxR / 64>(d, pa, st);
+  }
   return hipGetLastError();
 }
 
