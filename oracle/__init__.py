@@ -55,9 +55,12 @@ def _setup(l):
     l.oracle_dedup_dispatch.argtypes = [vp, vp, vp, ctypes.c_int32] + [vp] * 7
     l.oracle_quality.argtypes = [vp, ctypes.c_int32] + [vp] * 5
     l.oracle_predict.argtypes = [vp] * 9
+    l.oracle_slot_map.argtypes = [vp, ctypes.c_int32] + [vp] * 5
+    l.oracle_replica_pull.argtypes = [vp, vp, vp, ctypes.c_int64, vp]
+    l.oracle_replica_push.argtypes = [vp, vp, vp, ctypes.c_int64, vp]
     for f in (l.oracle_params, l.oracle_domain_budget, l.oracle_route, l.oracle_plan, l.oracle_dispatch,
               l.oracle_combine, l.oracle_place, l.oracle_dedup, l.oracle_dedup_dispatch, l.oracle_quality,
-              l.oracle_predict):
+              l.oracle_predict, l.oracle_slot_map, l.oracle_replica_pull, l.oracle_replica_push):
         f.restype = ctypes.c_int
     return l
 
@@ -258,6 +261,50 @@ def predict(cfg: OracleCfg, topk_cur: np.ndarray, trans: np.ndarray, count_cur: 
         raise ValueError("oracle_predict failed (%d)" % rc)
     out["local_predicted"], out["local_source"] = int(local[0]), int(local[1])
     return out
+
+
+def slot_map(cfg: OracleCfg, plan_out: dict, l=None) -> dict:
+    """Replica slot map of a plan (see oracle_slot_map)."""
+    l = l or lib()
+    ns = params(cfg, l)["n_slot"]
+    R, cap = cfg.R, cfg.E + cfg.B
+    out = dict(slot_expert=np.zeros((R, ns), np.int32), slot_main=np.zeros((R, ns), np.int32),
+               inst_slot=np.zeros(cap, np.int32))
+    ie = np.ascontiguousarray(plan_out["inst_expert"], np.int32)
+    ir = np.ascontiguousarray(plan_out["inst_rank"], np.int32)
+    rc = l.oracle_slot_map(ctypes.byref(cfg), int(np.asarray(plan_out["n_inst"]).reshape(-1)[0]), _p(ie), _p(ir),
+                           _p(out["slot_expert"]), _p(out["slot_main"]), _p(out["inst_slot"]))
+    if rc != 0:
+        raise ValueError("oracle_slot_map failed (%d)" % rc)
+    return out
+
+
+def replica_pull(cfg: OracleCfg, slot_expert: np.ndarray, main_params: np.ndarray, replica_params: np.ndarray,
+                 l=None) -> np.ndarray:
+    """replica_params [R][N_slot][P] (modified in place and returned) from main_params [E][P]."""
+    l = l or lib()
+    P = main_params.shape[-1]
+    se = np.ascontiguousarray(slot_expert, np.int32)
+    mp_ = np.ascontiguousarray(main_params, np.uint16)
+    assert replica_params.flags.c_contiguous and replica_params.dtype == np.uint16
+    rc = l.oracle_replica_pull(ctypes.byref(cfg), _p(se), _p(mp_), int(P), _p(replica_params))
+    if rc != 0:
+        raise ValueError("oracle_replica_pull failed (%d)" % rc)
+    return replica_params
+
+
+def replica_push(cfg: OracleCfg, slot_expert: np.ndarray, replica_grads: np.ndarray, grad_accum: np.ndarray,
+                 l=None) -> np.ndarray:
+    """grad_accum [R][R][E/R][P] (modified in place and returned) from replica_grads [R][N_slot][P]."""
+    l = l or lib()
+    P = replica_grads.shape[-1]
+    se = np.ascontiguousarray(slot_expert, np.int32)
+    rg = np.ascontiguousarray(replica_grads, np.uint16)
+    assert grad_accum.flags.c_contiguous and grad_accum.dtype == np.uint16
+    rc = l.oracle_replica_push(ctypes.byref(cfg), _p(se), _p(rg), int(P), _p(grad_accum))
+    if rc != 0:
+        raise ValueError("oracle_replica_push failed (%d)" % rc)
+    return grad_accum
 
 
 def run_all(cfg: OracleCfg, logits: np.ndarray, hidden: np.ndarray | None,

@@ -770,3 +770,71 @@ extern "C" int oracle_predict(const oracle_cfg* c, const int32_t* topk_cur, cons
   }
   return 0;
 }
+
+// ---------------------------------------------------------------------------
+// Replica slots ([TopoEP] section 3.2, Replica Buffer Management, and Fig. 6:
+// every rank keeps N_slot replica slots; the plan maps each occupied slot to
+// an expert and so to its main rank, the source of the BF16 parameters pulled
+// in the forward pass and the destination of the gradients returned in the
+// backward pass; the main instance keeps the optimizer state).  Reading: the
+// replicas of rank r, in instance order (ascending expert), fill its slots
+// 0, 1, ...; the remaining slots are empty (-1).
+//   slot_expert [R][N_slot], slot_main [R][N_slot] = main(expert), inst_slot [E+B]
+//   (the slot of each replica instance; -1 for main and unused instances).
+// Parameter pull: replica_params[r][j][:] = main_params[slot_expert[r][j]][:]
+// (main_params [E][P]: rank m owns rows m*E/R ... (m+1)*E/R - 1).
+// Gradient return: grad_accum[m][r][e - m*E/R][:] = replica_grads[r][j][:]
+// for the expert e in slot j of rank r and m = main(e) -- the main rank's
+// buffer split by source rank.  Empty slots move nothing.
+// ---------------------------------------------------------------------------
+extern "C" int oracle_slot_map(const oracle_cfg* c, int32_t n_inst, const int32_t* inst_expert,
+                               const int32_t* inst_rank, int32_t* slot_expert, int32_t* slot_main, int32_t* inst_slot) {
+  if (!valid(c) || !inst_expert || !inst_rank || !slot_expert || !slot_main || !inst_slot) return -1;
+  const Derived d = derive(c);
+  const int64_t R = c->R, cap = (int64_t)c->E + c->B, ns = d.n_slot;
+  if (n_inst < c->E || n_inst > cap) return -1;
+  for (int64_t q = 0; q < R * ns; ++q) slot_expert[q] = slot_main[q] = -1;
+  for (int64_t i = 0; i < cap; ++i) inst_slot[i] = -1;
+  std::vector<int64_t> used(R, 0);
+  for (int64_t i = 0; i < n_inst; ++i) {  // instances are rank-major
+    const int64_t r = inst_rank[i], e = inst_expert[i];
+    if (r < 0 || r >= R || e < 0 || e >= c->E) return -1;
+    if (main_of(d, e) == r) continue;
+    if (used[r] >= ns) return -5;
+    slot_expert[r * ns + used[r]] = (int32_t)e;
+    slot_main[r * ns + used[r]] = (int32_t)main_of(d, e);
+    inst_slot[i] = (int32_t)used[r];
+    ++used[r];
+  }
+  return 0;
+}
+
+extern "C" int oracle_replica_pull(const oracle_cfg* c, const int32_t* slot_expert, const uint16_t* main_params,
+                                   int64_t P, uint16_t* replica_params) {
+  if (!valid(c) || !slot_expert || !main_params || !replica_params || P < 0) return -1;
+  const Derived d = derive(c);
+  for (int64_t q = 0; q < (int64_t)c->R * d.n_slot; ++q) {
+    const int64_t e = slot_expert[q];
+    if (e < 0) continue;
+    if (e >= c->E) return -1;
+    std::memcpy(replica_params + q * P, main_params + e * P, (size_t)P * sizeof(uint16_t));
+  }
+  return 0;
+}
+
+extern "C" int oracle_replica_push(const oracle_cfg* c, const int32_t* slot_expert, const uint16_t* replica_grads,
+                                   int64_t P, uint16_t* grad_accum) {
+  if (!valid(c) || !slot_expert || !replica_grads || !grad_accum || P < 0) return -1;
+  const Derived d = derive(c);
+  const int64_t R = c->R, ns = d.n_slot, Er = d.Er;
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t j = 0; j < ns; ++j) {
+      const int64_t e = slot_expert[r * ns + j];
+      if (e < 0) continue;
+      if (e >= c->E) return -1;
+      const int64_t m = main_of(d, e);
+      std::memcpy(grad_accum + ((m * R + r) * Er + (e - m * Er)) * P, replica_grads + (r * ns + j) * P,
+                  (size_t)P * sizeof(uint16_t));
+    }
+  return 0;
+}

@@ -20,6 +20,7 @@
  *   Plan quality: [TopoEP] sections 6.2, 6.4, 6.6 (Figs. 10, 13(b), 16).
  *   Token-shuffle prediction: [Coupling] "Moving Tokens Toward Their Next
  *             Experts" (the scoring rule is a reading).
+ *   Replica slots and transfers: [TopoEP] section 3.2, Fig. 6.
  *
  * Every function returns 0 on success or a negative status:
  *   -1 invalid argument / configuration, -4 a NaN gate logit,
@@ -116,6 +117,17 @@ int oracle_quality(const oracle_cfg* c, int32_t n_inst, const int32_t* inst_expe
 int oracle_predict(const oracle_cfg* c, const int32_t* topk_cur, const int32_t* trans, const int32_t* count_cur,
                    const int32_t* key_rank, const int32_t* topk_next, int32_t* pred, int32_t* rank_tokens,
                    int64_t* local);
+
+/* Replica slots [TopoEP 3.2]: slot_expert / slot_main [R][N_slot] (-1 empty),
+ * inst_slot [E+B]; the parameter pull replica_params[r][j] = main_params[e]
+ * ([R][N_slot][P] from [E][P]) and the gradient return
+ * grad_accum[main(e)][r][e - main(e)*E/R] = replica_grads[r][j] ([R][R][E/R][P]). */
+int oracle_slot_map(const oracle_cfg* c, int32_t n_inst, const int32_t* inst_expert, const int32_t* inst_rank,
+                    int32_t* slot_expert, int32_t* slot_main, int32_t* inst_slot);
+int oracle_replica_pull(const oracle_cfg* c, const int32_t* slot_expert, const uint16_t* main_params, int64_t P,
+                        uint16_t* replica_params);
+int oracle_replica_push(const oracle_cfg* c, const int32_t* slot_expert, const uint16_t* replica_grads, int64_t P,
+                        uint16_t* grad_accum);
 
 #ifdef __cplusplus
 }

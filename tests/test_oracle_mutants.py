@@ -90,6 +90,13 @@ MUTANTS = [
     ("prediction ties to the higher rank", "if (score[r] > score[best]) best = r;", "if (score[r] >= score[best]) best = r;"),
     ("locality counts the predicted rank of the wrong layer", "if (rank_of[b] == best) local[0] += 1;",
      "if (rank_of[topk_cur[t * k + j]] == best) local[0] += 1;"),
+    ("slot map counts main instances", "    if (main_of(d, e) == r) continue;\n    if (used[r] >= ns) return -5;",
+     "    if (used[r] >= ns) return -5;"),
+    ("slot map records the replica's own rank as the source",
+     "slot_main[r * ns + used[r]] = (int32_t)main_of(d, e);", "slot_main[r * ns + used[r]] = (int32_t)r;"),
+    ("gradient return ignores the source rank",
+     "std::memcpy(grad_accum + ((m * R + r) * Er + (e - m * Er)) * P, replica_grads + (r * ns + j) * P,",
+     "std::memcpy(grad_accum + ((m * R + 0) * Er + (e - m * Er)) * P, replica_grads + (r * ns + j) * P,"),
 ]
 
 
@@ -107,6 +114,7 @@ def test_pins_reject_mutant(tmp_path, name, old, new):
                         os.path.join(ROOT, "tests", "test_oracle_combine.py"),
                         os.path.join(ROOT, "tests", "test_oracle_placement.py"),
                         os.path.join(ROOT, "tests", "test_oracle_quality.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_predict.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_predict.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_slots.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "the pins accept the mutant '%s'" % name
