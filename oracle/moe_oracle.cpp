@@ -45,6 +45,8 @@ Derived derive(const oracle_cfg* c) {
   // largest per-domain share of the budget spread over the domain's ranks.
   int64_t per_dom = (c->B + d.M - 1) / d.M;
   d.n_slot = c->n_slot > 0 ? c->n_slot : (per_dom + c->G - 1) / c->G;
+  // More slots than the whole budget can never be filled.
+  if (d.n_slot > c->B) d.n_slot = c->B;
   // S_tok: one bf16 activation row.  ||W_e||: three H x I bf16 matrices with
   // I = 3H/8, i.e. 9H^2/4 bytes (9 MiB at H = 2048, the TopoEP Fig. 3 example).
   d.S = c->S > 0 ? c->S : 2LL * c->H;

@@ -97,3 +97,11 @@ def test_bad_instance_is_rejected():
     p["inst_rank"][3] = 9
     with pytest.raises(ValueError):
         oracle.slot_map(cfg, p)
+
+
+def test_slots_per_rank_never_exceed_the_budget():
+    """A rank can hold at most B replicas (the whole layer's budget), so a configured
+    slot count above B is clamped to B; with B = 0 there are no slots at all."""
+    assert oracle.params(oracle.make_cfg(8, 4, 2, 2, 1, 8, 0, 2))["n_slot"] == 0
+    assert oracle.params(oracle.make_cfg(8, 4, 2, 2, 1, 8, 3, 5))["n_slot"] == 3
+    assert oracle.params(oracle.make_cfg(8, 4, 2, 2, 1, 8, 3, 2))["n_slot"] == 2
