@@ -18,6 +18,9 @@
  *                      crossing nodes, assignments served by replicas
  *   moe_plan_predict   token-shuffle prediction: the rank expected to hold most
  *                      of each token's next-layer experts
+ *   moe_plan_slot_map / moe_plan_replica_pull / moe_plan_replica_push
+ *                      replica slots of a plan; expert parameters into the
+ *                      slots, replica gradients back to the main ranks
  * EP ranks and NVLink domains ("nodes") are logical partitions on one GPU:
  *   source rank of token t   src(t)  = t / (T/R)     (contiguous token blocks)
  *   domain of rank r          dom(r)  = r / G         (contiguous rank blocks)
@@ -270,6 +273,20 @@ typedef struct {
   int64_t* local;
 } moe_predict_out;
 
+/*
+ * Outputs of moe_plan_slot_map (N_slot = moe_plan_sizes.n_slot).
+ *   slot_expert  int32 [R][N_slot]: expert held by slot j of rank r, -1 empty.
+ *   slot_main    int32 [R][N_slot]: its main rank e / (E/R), -1 empty -- the
+ *                source of the parameters and destination of the gradients.
+ *   inst_slot    int32 [E+B]: slot of each replica instance on its rank; -1
+ *                for main instances and unused entries.
+ */
+typedef struct {
+  int32_t* slot_expert;
+  int32_t* slot_main;
+  int32_t* inst_slot;
+} moe_slot_out;
+
 /* Buffer sizes for a configuration (host only, no GPU work).  Returns
  * MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED as moe_plan_create would. */
 int moe_plan_query(const moe_plan_config* cfg, moe_plan_sizes* sizes);
@@ -461,6 +478,39 @@ int moe_plan_quality(moe_plan_t h, const moe_plan_out* plan, int64_t* out, void*
  */
 int moe_plan_predict(moe_plan_t h, const int32_t* topk_cur, const int32_t* trans, const int32_t* count_cur,
                      const int32_t* key_rank, const int32_t* topk_next, const moe_predict_out* out, void* stream);
+
+/*
+ * Replica slots [TopoEP section 3.2, Replica Buffer Management, and Fig. 6:
+ * every rank keeps N_slot preallocated replica slots; the plan's mapping from
+ * occupied slots to experts names the main rank that supplies a replica's
+ * BF16 parameters in the forward pass and receives its gradients in the
+ * backward pass].  The replicas of rank r fill its slots in instance order
+ * (ascending expert); the rest are empty.  Reads plan->n_inst, inst_expert,
+ * inst_rank (device).  A plan whose instances are not rank-major with main
+ * experts first, or with more replicas on a rank than N_slot, sets
+ * MOE_STATUS_PLAN_CHECK.
+ */
+int moe_plan_slot_map(moe_plan_t h, const moe_plan_out* plan, const moe_slot_out* out, void* stream);
+
+/*
+ * Parameter pull into the replica slots: replica_params[r][j][:] =
+ * main_params[slot_expert[r][j]][:] for every occupied slot, param_elems bf16
+ * elements per expert.  main_params: uint16 [E][param_elems] (rank m owns rows
+ * m*E/R ... (m+1)*E/R-1); replica_params: uint16 [R][N_slot][param_elems]
+ * (device); empty slots are not written.
+ */
+int moe_plan_replica_pull(moe_plan_t h, const int32_t* slot_expert, const uint16_t* main_params,
+                          int64_t param_elems, uint16_t* replica_params, void* stream);
+
+/*
+ * Gradient return from the replica slots: for the expert e in slot j of rank
+ * r and m = e / (E/R), grad_accum[m][r][e - m*E/R][:] = replica_grads[r][j][:]
+ * -- main rank m's gradient buffer, split by source rank.  replica_grads:
+ * uint16 [R][N_slot][param_elems]; grad_accum: uint16 [R][R][E/R][param_elems]
+ * (device); regions of no slot are not written.
+ */
+int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, const uint16_t* replica_grads,
+                          int64_t param_elems, uint16_t* grad_accum, void* stream);
 
 /*
  * Synchronise the handle's last stream, copy the device status word to

@@ -79,6 +79,10 @@ class moe_predict_out(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("pred", "rank_tokens", "local")]
 
 
+class moe_slot_out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("slot_expert", "slot_main", "inst_slot")]
+
+
 class moe_dedup_out(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "tok_ranks", "rank_rows", "rank_slots", "n_rows", "row_token", "row_slots", "rank_row_offset", "slot_row",
@@ -87,7 +91,8 @@ class moe_dedup_out(ctypes.Structure):
 
 EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
            "moe_plan_dispatch", "moe_plan_step", "moe_plan_combine", "moe_plan_place", "moe_plan_dedup_count",
-           "moe_plan_dedup_dispatch", "moe_plan_quality", "moe_plan_predict", "moe_plan_status", "moe_plan_destroy")
+           "moe_plan_dedup_dispatch", "moe_plan_quality", "moe_plan_predict", "moe_plan_slot_map",
+           "moe_plan_replica_pull", "moe_plan_replica_push", "moe_plan_status", "moe_plan_destroy")
 
 _LIB = None
 
@@ -117,6 +122,9 @@ def lib():
         l.moe_plan_dedup_dispatch.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp, vp]
         l.moe_plan_quality.argtypes = [vp, vp, vp, vp]
         l.moe_plan_predict.argtypes = [vp] * 8
+        l.moe_plan_slot_map.argtypes = [vp, vp, vp, vp]
+        l.moe_plan_replica_pull.argtypes = [vp, vp, vp, ctypes.c_int64, vp, vp]
+        l.moe_plan_replica_push.argtypes = [vp, vp, vp, ctypes.c_int64, vp, vp]
         l.moe_plan_status.argtypes = [vp, vp]
         l.moe_plan_destroy.argtypes = [vp]
         l.moe_plan_destroy.restype = None
@@ -192,6 +200,20 @@ def moe_plan_predict(h, topk_cur: int, trans: int, count_cur: int, key_rank, top
                      stream: int):
     _check("moe_plan_predict", lib().moe_plan_predict(h, topk_cur, trans, count_cur, key_rank, topk_next,
                                                       ctypes.byref(out), stream))
+
+
+def moe_plan_slot_map(h, plan: moe_plan_out, out: moe_slot_out, stream: int):
+    _check("moe_plan_slot_map", lib().moe_plan_slot_map(h, ctypes.byref(plan), ctypes.byref(out), stream))
+
+
+def moe_plan_replica_pull(h, slot_expert: int, main_params: int, param_elems: int, replica_params: int, stream: int):
+    _check("moe_plan_replica_pull",
+           lib().moe_plan_replica_pull(h, slot_expert, main_params, param_elems, replica_params, stream))
+
+
+def moe_plan_replica_push(h, slot_expert: int, replica_grads: int, param_elems: int, grad_accum: int, stream: int):
+    _check("moe_plan_replica_push",
+           lib().moe_plan_replica_push(h, slot_expert, replica_grads, param_elems, grad_accum, stream))
 
 
 QUALITY_FIELDS = ("assignments", "same_rank", "same_node", "other_node", "replica_served", "max_rank_load",
@@ -472,6 +494,40 @@ class Layer:
         moe_plan_predict(self.handle, _ptr(topk_cur), _ptr(trans), _ptr(count_cur), _ptr(key_rank), _ptr(topk_next),
                          out, self._stream(stream))
         return self._pred
+
+    def slot_map(self, stream=None):
+        """Replica slot map of this layer's plan (moe_plan_slot_map): (slot_expert [R][N_slot],
+        slot_main [R][N_slot], inst_slot [E+B]) device tensors."""
+        torch, R = self.torch, self.cfg.R
+        ns, cap = int(self.sizes.n_slot), int(self.sizes.inst_cap)
+        if getattr(self, "_slots", None) is None:
+            e = lambda n: torch.empty(n, dtype=torch.int32, device=self.device)
+            self._slots = (e(R * ns).view(R, ns), e(R * ns).view(R, ns), e(cap))
+        moe_plan_slot_map(self.handle, self._plan_s, moe_slot_out(*(_ptr(x) for x in self._slots)),
+                          self._stream(stream))
+        return self._slots
+
+    def replica_pull(self, main_params, replica_params, stream=None):
+        """moe_plan_replica_pull with this layer's slot map: main_params [E][P] -> replica_params
+        [R][N_slot][P] (16-bit tensors)."""
+        E, R, ns = self.cfg.E, self.cfg.R, int(self.sizes.n_slot)
+        P = main_params.shape[-1]
+        self._check_tensor(main_params, (E, P), None)
+        self._check_tensor(replica_params, (R, ns, P), None)
+        moe_plan_replica_pull(self.handle, _ptr(self._slots[0]), _ptr(main_params), int(P), _ptr(replica_params),
+                              self._stream(stream))
+        return replica_params
+
+    def replica_push(self, replica_grads, grad_accum, stream=None):
+        """moe_plan_replica_push with this layer's slot map: replica_grads [R][N_slot][P] ->
+        grad_accum [R][R][E/R][P]."""
+        E, R, ns = self.cfg.E, self.cfg.R, int(self.sizes.n_slot)
+        P = replica_grads.shape[-1]
+        self._check_tensor(replica_grads, (R, ns, P), None)
+        self._check_tensor(grad_accum, (R, R, E // R, P), None)
+        moe_plan_replica_push(self.handle, _ptr(self._slots[0]), _ptr(replica_grads), int(P), _ptr(grad_accum),
+                              self._stream(stream))
+        return grad_accum
 
     def status(self) -> int:
         return moe_plan_status(self.handle)

@@ -391,6 +391,34 @@ extern "C" int moe_plan_predict(moe_plan_t h, const int32_t* topk_cur, const int
                                     static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int moe_plan_slot_map(moe_plan_t h, const moe_plan_out* plan, const moe_slot_out* out, void* stream) {
+  if (!h || !plan || !out || !plan->n_inst || !plan->inst_expert || !plan->inst_rank || !out->inst_slot)
+    return MOE_ERR_INVALID_ARG;
+  if (h->d.n_slot > 0 && (!out->slot_expert || !out->slot_main)) return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  return hip_rc(moe::launch_slot_map(h->d, *plan, *out, h->ws.status, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int moe_plan_replica_pull(moe_plan_t h, const int32_t* slot_expert, const uint16_t* main_params,
+                                     int64_t param_elems, uint16_t* replica_params, void* stream) {
+  if (!h || param_elems < 0) return MOE_ERR_INVALID_ARG;
+  if (h->d.n_slot > 0 && param_elems > 0 && (!slot_expert || !main_params || !replica_params))
+    return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  return hip_rc(moe::launch_replica_pull(h->d, slot_expert, main_params, param_elems, replica_params, h->ws.status,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, const uint16_t* replica_grads,
+                                     int64_t param_elems, uint16_t* grad_accum, void* stream) {
+  if (!h || param_elems < 0) return MOE_ERR_INVALID_ARG;
+  if (h->d.n_slot > 0 && param_elems > 0 && (!slot_expert || !replica_grads || !grad_accum))
+    return MOE_ERR_INVALID_ARG;
+  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  return hip_rc(moe::launch_replica_push(h->d, slot_expert, replica_grads, param_elems, grad_accum, h->ws.status,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int moe_plan_status(moe_plan_t h, int32_t* host_flags) {
   if (!h || !host_flags) return MOE_ERR_INVALID_ARG;
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;

@@ -116,6 +116,15 @@ hipError_t launch_predict(const Dims& d, const int32_t* topk_cur, const int32_t*
                           const int32_t* key_rank, const int32_t* topk_next, const moe_predict_out& out,
                           const Workspace& ws, hipStream_t st);
 
+// Replica slot map of a plan, and the row copies that move expert parameters
+// into the slots and gradients back to the main ranks.
+hipError_t launch_slot_map(const Dims& d, const moe_plan_out& plan, const moe_slot_out& out, int32_t* status,
+                           hipStream_t st);
+hipError_t launch_replica_pull(const Dims& d, const int32_t* slot_expert, const uint16_t* main_params, int64_t P,
+                               uint16_t* replica_params, int32_t* status, hipStream_t st);
+hipError_t launch_replica_push(const Dims& d, const int32_t* slot_expert, const uint16_t* replica_grads, int64_t P,
+                               uint16_t* grad_accum, int32_t* status, hipStream_t st);
+
 // LDS bytes the plan and scan kernels need for these dimensions.
 size_t plan_lds_bytes(const Dims& d);
 size_t scan_lds_bytes(const Dims& d);
