@@ -24,6 +24,11 @@ the inputs resident in HBM.  Prints ONE JSON line:
               to the next: its time and the share of the next layer's slots on
               the predicted rank, against staying on the source rank, with the
               contiguous and with the correlated placement of the next layer
+  replica_pull  the replica slot map of the first layer's plan and the bf16
+              parameter pull into the occupied slots (moe_plan_slot_map +
+              moe_plan_replica_pull) at the modelled expert size ||W||
+              (9H^2/4 bytes, capped so that all E main rows fit in 32 GB),
+              event-timed, against the HBM peak
   plan_quality  the plan's rank-load imbalance (max / mean) and its shares of
               assignments on the source's rank, on another node and on replicas
               (moe_plan_quality), beside the static placement's
@@ -247,6 +252,32 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     place["rows_saved_frac"] = saved
     quality = {"plan": quality_dict(lay0.quality(), w.R)}
     dedup = dict(us=float(np.mean([e[0].elapsed_time(e[1]) for e in dev_])) * 1e3, n_rows=int(dd.n_rows.item()))
+    # Replica slots of the first layer's plan and the parameter pull at the modelled expert size.
+    pull = None
+    lay0.slot_map()
+    occupied = int((lay0._slots[0] >= 0).sum().item())
+    P = (9 * w.H * w.H // 4) // 2  # bf16 elements of ||W||
+    P = min(P, (32 * 10**9 // (2 * w.E)) // 8 * 8)  # keep all E main rows within 32 GB
+    ns = int(lay0.sizes.n_slot)
+    if occupied > 0 and ns > 0:
+        main_params = torch.empty((w.E, P), dtype=torch.int16, device=dev)
+        main_params.random_(-32768, 32767)
+        replica = torch.empty((w.R, ns, P), dtype=torch.int16, device=dev)
+        lay0.replica_pull(main_params, replica)
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+        torch.cuda.synchronize()
+        for e in pev:
+            e[0].record(stream)
+            lay0.replica_pull(main_params, replica)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([e[0].elapsed_time(e[1]) for e in pev])) * 1e3
+        nbytes = 2 * occupied * P * 2
+        pull = {"kernel": "slot_copy_kernel (moe_plan_replica_pull)", "us": us, "occupied_slots": occupied,
+                "slots": w.R * ns, "bytes_per_expert": P * 2, "algorithmic_bytes_per_launch": nbytes,
+                "achieved": nbytes / (us / 1e6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS}
+        del main_params, replica
     shuffle = None
     if w.L > 1:
         shuffle = []
@@ -281,7 +312,7 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     quality["static_placement"] = quality_dict(static.quality(), w.R)
     static.close()
     return dict(ms_total=ms_total, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup, quality=quality,
-                shuffle=shuffle,
+                shuffle=shuffle, pull=pull,
                 per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
                 per_call_ms_min={k: float(np.min(v)) for k, v in per.items()}, status=status,
                 device=torch.cuda.get_device_name(dev))
@@ -441,6 +472,7 @@ def main():
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": dedup_bytes(w, g["dedup"]["n_rows"]) / (g["dedup"]["us"] / 1e6) / 1e9 / HBM_PEAK_GBS,
                            "vs_dispatch_us": disp_ms * 1e3},
+        "replica_pull": g["pull"],
         "plan_quality": g["quality"],
         "token_shuffle": g["shuffle"],
         "per_call_us": {k: v * 1e3 for k, v in g["per_call_ms"].items()},
