@@ -3,7 +3,10 @@
 
 A step is one pass of the whole path over every layer of the workload --
 moe_plan_step, i.e. route -> plan -> dispatch in one call per layer -- with
-the inputs resident in HBM.  Prints ONE JSON line:
+the inputs resident in HBM.  Consecutive steps (independent batches) alternate
+between two handles on two streams, so one batch's route + plan overlaps the
+previous batch's gather; latency_ms_per_step gives the same steps run one at
+a time on one stream.  Prints ONE JSON line:
   value       routed token-slots per second (T*k*L / step time)
   roofline    the dominant kernel (the bf16 gather, the one kernel of
               moe_plan_dispatch): algorithmic bytes per launch / its mean
@@ -156,14 +159,20 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     cfg = mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
     hidden = torch.from_numpy(synth.hidden(w).view(np.int16)).to(dev)
     logits = [torch.from_numpy(lg).to(dev) for lg in synth.all_logits(w)]
-    layers = [mp.Layer(cfg, device=dev, cooc=True, trans=(l > 0)) for l in range(w.L)]
+    # Two batches in flight: consecutive steps alternate between two handles (each
+    # with its own buffers) on two streams, so the latency-bound route + plan of
+    # one batch overlaps the HBM-bound gather of the other.
+    sets = [[mp.Layer(cfg, device=dev, cooc=True, trans=(l > 0)) for l in range(w.L)] for _ in range(2)]
+    layers = sets[0]
     stream = torch.cuda.current_stream(dev)
+    streams = [stream, torch.cuda.Stream(dev)]
 
-    def step():
+    def step(i=0):
         # one pass of the whole path per layer: moe_plan_step (route + plan + dispatch in one call)
-        for l, layer in enumerate(layers):
-            prev = layers[l - 1].route_out.topk_idx if l > 0 else None
-            layer.step(logits[l], hidden, prev)
+        with torch.cuda.stream(streams[i]):
+            for l, layer in enumerate(sets[i]):
+                prev = sets[i][l - 1].route_out.topk_idx if l > 0 else None
+                layer.step(logits[l], hidden, prev)
 
     def staged(ev):
         # the same pass as three calls, with events around each call
@@ -177,22 +186,38 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
             layer.dispatch(hidden)
             ev[l][3].record(stream)
 
-    for _ in range(warmup):
-        step()
+    for s_ in range(warmup):
+        step(s_ % 2)
     torch.cuda.synchronize()
-    for layer in layers:
+    for layer in sets[0] + sets[1]:
         if layer.status() != 0:
             raise RuntimeError("device status word set during warm-up")
-    # Timed region: exactly `steps` steps, synchronised on both sides.
+    # Timed region: exactly `steps` steps, synchronised on both sides; the end
+    # event waits for both streams.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    t_side = torch.cuda.Event()
     torch.cuda.synchronize()
     t_start.record(stream)
-    for _ in range(steps):
-        step()
+    streams[1].wait_event(t_start)
+    for s_ in range(steps):
+        step(s_ % 2)
+    t_side.record(streams[1])
+    stream.wait_event(t_side)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
+    # The same steps one at a time on one stream: the latency of a step.
+    t_start.record(stream)
+    for _ in range(steps):
+        step(0)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_serial = t_start.elapsed_time(t_end)
+    for layer in sets[1]:
+        if layer.status() != 0:
+            raise RuntimeError("device status word set on the second handle")
+        layer.close()
     # Per-call durations from events around each call, in a second timed pass of the same steps.
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(w.L)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -311,7 +336,8 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     static.plan()
     quality["static_placement"] = quality_dict(static.quality(), w.R)
     static.close()
-    return dict(ms_total=ms_total, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup, quality=quality,
+    return dict(ms_total=ms_total, ms_serial=ms_serial, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup,
+                quality=quality,
                 shuffle=shuffle, pull=pull,
                 per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
                 per_call_ms_min={k: float(np.min(v)) for k, v in per.items()}, status=status,
@@ -450,6 +476,8 @@ def main():
         "metric": "routed token-slots/sec for route+plan+dispatch; gather HBM GB/s vs peak",
         "value": value, "unit": "token-slots/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "pipeline": "2 batches in flight (two handles on two streams; consecutive steps alternate)",
+        "latency_ms_per_step": g["ms_serial"] / args.steps,
         "dtype": "int32", "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "R": w.R, "G": w.G, "H": w.H,
                    "replica_budget": w.B, "layers": w.L, "zipf_s": w.zipf_s, "beta": w.beta,
