@@ -276,6 +276,17 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     place["rows_saved_frac"] = saved
     quality = {"plan": quality_dict(lay0.quality(), w.R)}
+    # The planner on the correlated placement: renumber the experts so that expert
+    # rank_experts[p] becomes p (the caller permutes its router columns once), then
+    # route, plan, and count what deduplication still saves over the plan's instances.
+    order = pl.rank_experts.reshape(-1).long()
+    relabel = mp.Layer(cfg, device=dev, cooc=False)
+    relabel.route(logits[0].index_select(1, order).contiguous())
+    relabel.plan()
+    quality["plan_on_correlated_placement"] = quality_dict(relabel.quality(), w.R)
+    d = relabel.dedup_count(relabel.plan_out.slot_inst, relabel.plan_out.inst_rank)
+    place["rows_saved_frac"]["plan_instances_on_correlated_placement"] = 1.0 - int(d.tok_ranks.sum().item()) / slots
+    relabel.close()
     dedup = dict(us=float(np.mean([e[0].elapsed_time(e[1]) for e in dev_])) * 1e3, n_rows=int(dd.n_rows.item()))
     # Replica slots of the first layer's plan and the parameter pull at the modelled expert size.
     pull = None
