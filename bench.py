@@ -89,6 +89,20 @@ def algorithmic_bytes(w) -> dict:
     return dict(route=route, plan=plan, dispatch=dispatch, combine=combine, total=(route + plan + dispatch) * w.L)
 
 
+def working_set(w) -> int:
+    """Bytes of logits, hidden rows and dispatch rows of one layer (below the 256 MB
+    Infinity Cache the path is cache-resident rather than HBM-bound)."""
+    return w.T * w.E * 4 + w.T * w.H * 2 + w.T * w.k * w.H * 2
+
+
+def inputs_sha(w) -> dict:
+    """SHA-256 (first 16 hex digits) of the generated input buffers."""
+    out = {"hidden": hashlib.sha256(synth.hidden(w).tobytes()).hexdigest()[:16]}
+    for l, lg in enumerate(synth.all_logits(w)):
+        out["logits_layer%d" % l] = hashlib.sha256(lg.tobytes()).hexdigest()[:16]
+    return out
+
+
 def dedup_bytes(w, n_rows: int) -> int:
     """Bytes moe_plan_dedup_dispatch must move for a layer with n_rows deduplicated rows."""
     T, k, R, H = w.T, w.k, w.R, w.H
@@ -123,11 +137,13 @@ def gather_traffic(w):
 
 def cpu_baseline(w, budget_s: float) -> dict:
     """The oracle, single-threaded on one core, on whole layers of the workload until the
-    time budget is spent (at least one layer)."""
+    time budget is spent (at least one layer); then each stage of the first layer three
+    times (medians)."""
     import oracle
     orig = os.sched_getaffinity(0)
     core = min(orig)
     os.sched_setaffinity(0, {core})
+    stages = {"route": [], "plan": [], "dispatch": []}
     try:
         cfg = oracle.make_cfg(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
         hidden = synth.hidden(w)
@@ -143,12 +159,32 @@ def cpu_baseline(w, budget_s: float) -> dict:
             done += 1
             if time.perf_counter() - t0 > budget_s:
                 break
+        for _ in range(3):
+            t1 = time.perf_counter()
+            r = oracle.route(cfg, layers[0], l=l)
+            t2 = time.perf_counter()
+            p = oracle.plan(cfg, r["omega"], r["topk_idx"], l=l)
+            t3 = time.perf_counter()
+            oracle.dispatch(cfg, int(p["n_inst"][0]), p["inst_rank"], p["slot_inst"], hidden, l=l)
+            t4 = time.perf_counter()
+            stages["route"].append(t2 - t1)
+            stages["plan"].append(t3 - t2)
+            stages["dispatch"].append(t4 - t3)
     finally:
         os.sched_setaffinity(0, orig)
     slots = w.T * w.k * done
+    model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": slots / elapsed, "unit": "token-slots/s", "cores": 1, "kind": "oracle",
-            "sample": "%d full layer(s) of %s (route+plan+dispatch incl. the bf16 row copy), %.1f s on core %d"
-                      % (done, w.name, elapsed, core)}
+            "sample": "%d full layer(s) of %s (route+plan+dispatch incl. the bf16 row copy), %.1f s on 1 core of a "
+                      "%d-core %s" % (done, w.name, elapsed, os.cpu_count() or 0, model),
+            "stage_ms_median_of_3": {k: float(np.median(v)) * 1e3 for k, v in stages.items()}}
 
 
 def run_gpu(w, steps: int, warmup: int) -> dict:
@@ -208,12 +244,14 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     # The same steps one at a time on one stream: the latency of a step.
-    t_start.record(stream)
-    for _ in range(steps):
+    lev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    lev[0].record(stream)
+    for s_ in range(steps):
         step(0)
-    t_end.record(stream)
+        lev[s_ + 1].record(stream)
     torch.cuda.synchronize()
-    ms_serial = t_start.elapsed_time(t_end)
+    step_ms = [lev[i].elapsed_time(lev[i + 1]) for i in range(steps)]
+    ms_serial = lev[0].elapsed_time(lev[steps])
     for layer in sets[1]:
         if layer.status() != 0:
             raise RuntimeError("device status word set on the second handle")
@@ -347,7 +385,10 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     static.plan()
     quality["static_placement"] = quality_dict(static.quality(), w.R)
     static.close()
-    return dict(ms_total=ms_total, ms_serial=ms_serial, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup,
+    dinfo = mp.moe_plan_device_info(0)
+    copy = copy_reference(1 << 30, 10)
+    return dict(ms_total=ms_total, ms_serial=ms_serial, step_ms=step_ms, dinfo=dinfo, copy=copy,
+                per_call_ms_median={k: float(np.median(v)) for k, v in per.items()}, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup,
                 quality=quality,
                 shuffle=shuffle, pull=pull,
                 per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
@@ -489,10 +530,13 @@ def main():
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "pipeline": "2 batches in flight (two handles on two streams; consecutive steps alternate)",
         "latency_ms_per_step": g["ms_serial"] / args.steps,
+        "latency_us": {"median": float(np.median(g["step_ms"])) * 1e3, "min": float(np.min(g["step_ms"])) * 1e3,
+                       "mean": float(np.mean(g["step_ms"])) * 1e3},
         "dtype": "int32", "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "R": w.R, "G": w.G, "H": w.H,
                    "replica_budget": w.B, "layers": w.L, "zipf_s": w.zipf_s, "beta": w.beta,
-                   "couple_p": w.couple_p, "seed": w.seed},
+                   "couple_p": w.couple_p, "seed": w.seed, "cache_resident": working_set(w) < 256 * 2**20,
+                   "inputs_sha256_16": inputs_sha(w)},
         "roofline": {"bound": "hbm", "kernel": "gather (moe_plan_dispatch)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": ab["dispatch"],
@@ -514,6 +558,13 @@ def main():
         "replica_pull": g["pull"],
         "plan_quality": g["quality"],
         "token_shuffle": g["shuffle"],
+        "stages": {name: {"us_mean": g["per_call_ms"][name] * 1e3, "us_median": g["per_call_ms_median"][name] * 1e3,
+                          "us_min": g["per_call_ms_min"][name] * 1e3, "algorithmic_bytes": ab[name],
+                          "achieved_GBps": ab[name] / (g["per_call_ms"][name] / 1e3) / 1e9,
+                          "frac": ab[name] / (g["per_call_ms"][name] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                          "bound": "hbm" if name == "dispatch" else "latency"}
+                   for name in ("route", "plan", "dispatch")},
+        "device_info": dict(g["dinfo"], hbm_peak_GBps=HBM_PEAK_GBS, measured_copy_GBps=g["copy"]["GBps"]),
         "per_call_us": {k: v * 1e3 for k, v in g["per_call_ms"].items()},
         "per_call_us_min": {k: v * 1e3 for k, v in g["per_call_ms_min"].items()},
         "cpu_baseline": cpu,

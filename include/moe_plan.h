@@ -513,6 +513,14 @@ int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, const uint16
                           int64_t param_elems, uint16_t* grad_accum, void* stream);
 
 /*
+ * Figures of a HIP device for roofline reports (host call, no handle):
+ * out[0] compute units, out[1] peak shader clock (kHz), out[2] peak memory
+ * clock (kHz), out[3] memory bus width (bits), out[4] L2 cache bytes,
+ * out[5] device memory bytes.
+ */
+int moe_plan_device_info(int device, int64_t* out);
+
+/*
  * Synchronise the handle's last stream, copy the device status word to
  * *host_flags (MOE_STATUS_* bits, 0 when clean) and clear it.
  */

@@ -92,7 +92,8 @@ class moe_dedup_out(ctypes.Structure):
 EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
            "moe_plan_dispatch", "moe_plan_step", "moe_plan_combine", "moe_plan_place", "moe_plan_dedup_count",
            "moe_plan_dedup_dispatch", "moe_plan_quality", "moe_plan_predict", "moe_plan_slot_map",
-           "moe_plan_replica_pull", "moe_plan_replica_push", "moe_plan_status", "moe_plan_destroy")
+           "moe_plan_replica_pull", "moe_plan_replica_push", "moe_plan_device_info", "moe_plan_status",
+           "moe_plan_destroy")
 
 _LIB = None
 
@@ -123,6 +124,7 @@ def lib():
         l.moe_plan_quality.argtypes = [vp, vp, vp, vp]
         l.moe_plan_predict.argtypes = [vp] * 8
         l.moe_plan_slot_map.argtypes = [vp, vp, vp, vp]
+        l.moe_plan_device_info.argtypes = [ctypes.c_int, vp]
         l.moe_plan_replica_pull.argtypes = [vp, vp, vp, ctypes.c_int64, vp, vp]
         l.moe_plan_replica_push.argtypes = [vp, vp, vp, ctypes.c_int64, vp, vp]
         l.moe_plan_status.argtypes = [vp, vp]
@@ -214,6 +216,13 @@ def moe_plan_replica_pull(h, slot_expert: int, main_params: int, param_elems: in
 def moe_plan_replica_push(h, slot_expert: int, replica_grads: int, param_elems: int, grad_accum: int, stream: int):
     _check("moe_plan_replica_push",
            lib().moe_plan_replica_push(h, slot_expert, replica_grads, param_elems, grad_accum, stream))
+
+
+def moe_plan_device_info(device: int = 0) -> dict:
+    out = (ctypes.c_int64 * 6)()
+    _check("moe_plan_device_info", lib().moe_plan_device_info(device, out))
+    return dict(compute_units=out[0], clock_khz=out[1], memory_clock_khz=out[2], memory_bus_bits=out[3],
+                l2_bytes=out[4], memory_bytes=out[5])
 
 
 QUALITY_FIELDS = ("assignments", "same_rank", "same_node", "other_node", "replica_served", "max_rank_load",

@@ -419,6 +419,27 @@ extern "C" int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, c
                                          static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int moe_plan_device_info(int device, int64_t* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  const hipDeviceAttribute_t attrs[5] = {hipDeviceAttributeMultiprocessorCount, hipDeviceAttributeClockRate,
+                                         hipDeviceAttributeMemoryClockRate, hipDeviceAttributeMemoryBusWidth,
+                                         hipDeviceAttributeL2CacheSize};
+  for (int i = 0; i < 5; ++i) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, attrs[i], device) != hipSuccess) return MOE_ERR_HIP;
+    out[i] = v;
+  }
+  size_t free_b = 0, total_b = 0;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+  if (cur != device && hipSetDevice(device) != hipSuccess) return MOE_ERR_HIP;
+  const hipError_t e = hipMemGetInfo(&free_b, &total_b);
+  if (cur != device) (void)hipSetDevice(cur);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  out[5] = (int64_t)total_b;
+  return MOE_OK;
+}
+
 extern "C" int moe_plan_status(moe_plan_t h, int32_t* host_flags) {
   if (!h || !host_flags) return MOE_ERR_INVALID_ARG;
   if (bind(h) != MOE_OK) return MOE_ERR_HIP;
