@@ -60,3 +60,33 @@ def test_query_sizes_and_validation():
         with pytest.raises(m.MoePlanError) as ei:
             m.moe_plan_query(c)
         assert ei.value.code == m.MOE_ERR_UNSUPPORTED
+
+
+def test_every_call_rejects_a_null_handle_synchronously():
+    """Argument errors return MOE_ERR_INVALID_ARG before any device work (so this runs without a GPU)."""
+    import load_balance_planning_amd as m
+    lib = m.lib()
+    calls = {
+        "moe_plan_route": (None, None, None, None, None),
+        "moe_plan_hist": (None, None, None, None, None),
+        "moe_plan_plan": (None, None, None, None),
+        "moe_plan_dispatch": (None, None, None, None, None),
+        "moe_plan_step": (None,) * 8,
+        "moe_plan_combine": (None,) * 6,
+        "moe_plan_place": (None, None, -1, None, None),
+        "moe_plan_dedup_count": (None, None, None, 0, None, None),
+        "moe_plan_dedup_dispatch": (None, None, None, 0, None, None, None),
+        "moe_plan_quality": (None, None, None, None),
+        "moe_plan_predict": (None,) * 8,
+        "moe_plan_slot_map": (None, None, None, None),
+        "moe_plan_replica_pull": (None, None, None, 0, None, None),
+        "moe_plan_replica_push": (None, None, None, 0, None, None),
+        "moe_plan_status": (None, None),
+        "moe_plan_create": (None, None),
+        "moe_plan_query": (None, None),
+        "moe_plan_device_info": (0, None),
+    }
+    assert set(calls) | {"moe_plan_destroy"} == set(declared_functions())
+    for name, args in calls.items():
+        assert getattr(lib, name)(*args) == m.MOE_ERR_INVALID_ARG, name
+    lib.moe_plan_destroy(None)  # a no-op
