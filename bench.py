@@ -469,6 +469,61 @@ def placement_report(w, p: dict, with_oracle: bool) -> dict:
     return out
 
 
+def _timeit(fn, min_runs: int = 3, budget_s: float = 1.0):
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_runs or time.perf_counter() - t0 < budget_s:
+        fn()
+        n += 1
+    return (time.perf_counter() - t0) / n
+
+
+def oracle_beside(w, P: int, with_shuffle: bool) -> dict:
+    """The oracle's time for each further call the bench measures, on one core, on the
+    same layer (or a stated sample of it), to print beside the GPU's."""
+    import oracle
+    orig = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(orig)})
+    out = {}
+    try:
+        cfg = oracle.make_cfg(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
+        layers = synth.all_logits(w)
+        hid = synth.hidden(w)
+        r = oracle.route(cfg, layers[0])
+        p = oracle.plan(cfg, r["omega"], r["topk_idx"])
+        out["plan_quality"] = {"oracle_ms": _timeit(lambda: oracle.quality(cfg, p)) * 1e3}
+        pl = oracle.place(cfg, r["cooc"])
+        out["dedup_dispatch"] = {"oracle_ms": _timeit(lambda: oracle.dedup_dispatch(cfg, r["topk_idx"],
+                                                                                    pl["expert_rank"], hid),
+                                                      min_runs=1, budget_s=0.0) * 1e3}
+        n = min(512, w.T)
+        sub = oracle.make_cfg(n, w.E, w.k, 1, 1, w.H, 0)
+        rows = hid[np.repeat(np.arange(n), w.k)]
+        t = _timeit(lambda: oracle.combine(sub, r["topk_val"][:n], np.arange(n * w.k, dtype=np.int32), rows))
+        out["combine"] = {"oracle_ms": t * w.T / n * 1e3,
+                          "oracle_sample": "the first %d tokens, scaled to the layer's %d" % (n, w.T)}
+        m = oracle.slot_map(cfg, p)
+        ps = min(P, 1 << 20)
+        main = np.zeros((w.E, ps), np.uint16)
+        repl = np.zeros((w.R, m["slot_expert"].shape[1], ps), np.uint16)
+        t = _timeit(lambda: oracle.replica_pull(cfg, m["slot_expert"], main, repl))
+        out["replica_pull"] = {"oracle_ms": t * P / ps * 1e3,
+                               "oracle_sample": "rows of %d of the %d bf16 elements, scaled" % (ps, P)}
+        if with_shuffle:
+            prev = r["topk_idx"]
+            pred = []
+            for l in range(1, w.L):
+                nxt = oracle.route(cfg, layers[l], prev_topk=prev, want_cooc=False)
+                cur_count = np.bincount(prev.reshape(-1), minlength=w.E).astype(np.int32)
+                pred.append(_timeit(lambda: oracle.predict(cfg, prev, nxt["trans"], cur_count, None,
+                                                           nxt["topk_idx"]), min_runs=1) * 1e3)
+                prev = nxt["topk_idx"]
+            out["token_shuffle"] = {"oracle_ms": pred}
+    finally:
+        os.sched_setaffinity(0, orig)
+    return out
+
+
 def copy_reference(nbytes: int, steps: int) -> dict:
     """A plain device-to-device copy of nbytes (torch's copy kernel), the known-size reference
     against which the HBM byte counters of the profiler are scaled."""
@@ -570,6 +625,17 @@ def main():
         "cpu_baseline": cpu,
         "device": g["device"],
     }
+    if cpu is not None:
+        P = g["pull"]["bytes_per_expert"] // 2 if g["pull"] else (9 * w.H * w.H // 4) // 2
+        beside = oracle_beside(w, P, w.L > 1)
+        for key, val in beside.items():
+            if key == "token_shuffle" and out["token_shuffle"]:
+                for entry, ms in zip(out["token_shuffle"], val["oracle_ms"]):
+                    entry["oracle_ms"] = ms
+            elif isinstance(out.get(key), dict):
+                out[key].update(val)
+            elif out.get(key) is None and key != "token_shuffle":
+                out[key] = val
     if any(g["status"]):
         out["status_flags"] = g["status"]
     print(json.dumps(out), flush=True)
