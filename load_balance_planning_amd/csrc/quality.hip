@@ -9,7 +9,7 @@
 // another node, on a replica (an instance not on its expert's main rank
 // e / (E/R)); and takes the largest and smallest rank load and the replica
 // count.  The quota matrix is R x (E+B) int32 -- tens of KiB -- read once,
-// coalesced along instances.
+// coalesced along instances, one source row per wave at a time.
 #include "internal.h"
 
 namespace moe {
@@ -32,6 +32,7 @@ __global__ __launch_bounds__(kQualThreads) void quality_kernel(Dims d, const int
   extern __shared__ int32_t smem_q[];
   int32_t* rank_s = smem_q;              // [cap] rank of each instance
   int32_t* repl_s = smem_q + d.cap;      // [cap] 1 when the instance is a replica
+  int32_t* node_s = smem_q + 2 * d.cap;  // [cap] node of each instance's rank
   __shared__ int64_t part[4][kQualThreads / 64];
   __shared__ int32_t lo_s[kQualThreads / 64], hi_s[kQualThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -47,18 +48,22 @@ __global__ __launch_bounds__(kQualThreads) void quality_kernel(Dims d, const int
     bad |= !ok;
     rank_s[i] = ok ? r : -1;
     repl_s[i] = ok && r != e / d.Er;
+    node_s[i] = ok ? r / d.G : -1;
   }
   if (bad) atomicOr(status, MOE_STATUS_PLAN_CHECK);
   __syncthreads();
   int64_t tot = 0, same_rank = 0, same_node = 0, repl = 0;
-  for (int s = 0; s < d.R; ++s) {
+  // one source row per wave at a time, lanes along the instances
+  for (int s = wave; s < d.R; s += kQualThreads / 64) {
     const int32_t* row = quota + (int64_t)s * d.cap;
-    for (int i = tid; i < n; i += kQualThreads) {
+    const int sn = s / d.G;
+#pragma unroll 4
+    for (int i = lane; i < n; i += 64) {
       const int64_t q = row[i];
       const int r = rank_s[i];
       tot += q;
       same_rank += r == s ? q : 0;
-      same_node += (r >= 0 && r / d.G == s / d.G) ? q : 0;
+      same_node += node_s[i] == sn ? q : 0;
       repl += repl_s[i] ? q : 0;
     }
   }
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(kQualThreads) void quality_kernel(Dims d, const int
 }  // namespace
 
 hipError_t launch_quality(const Dims& d, const moe_plan_out& plan, int64_t* out, int32_t* status, hipStream_t st) {
-  const size_t lds = sizeof(int32_t) * 2 * (size_t)d.cap;
+  const size_t lds = sizeof(int32_t) * 3 * (size_t)d.cap;
   hipLaunchKernelGGL(quality_kernel, dim3(1), dim3(kQualThreads), lds, st, d, plan.n_inst, plan.inst_expert,
                      plan.inst_rank, plan.rank_load, plan.quota, out, status);
   return hipGetLastError();
