@@ -20,7 +20,10 @@
 // takes E steps of one argmax each: every thread holds the affinities of its
 // E/1024 experts in registers, a wave's maximum comes from a DPP butterfly
 // inside each 16-lane row and four lane reads, and the workgroup's from an LDS
-// atomic max into one of three rotating slots -- one barrier per step.
+// atomic max into one of three rotating slots -- one barrier per step.  When
+// the counts fit 16 bits and E*E*2 bytes fit in LDS (E up to ~270), C is
+// copied to LDS during the degree pass and one wave runs the whole growth
+// (wave-uniform argmax, no atomic, no barrier per step).
 // Refinement keeps, for every rank pair (r1 < r2), the best swap key of the
 // pairs between them; a swap between ra and rb changes only the gains of pairs
 // with an expert on ra or rb, so an iteration re-evaluates 2R-3 rank pairs
@@ -50,13 +53,24 @@ struct PlaceArgs {
 };
 
 struct PlaceLds {
-  size_t rank_of, mem, pos, deg, own, col, red, aff, key, total;
-  bool aff_in_lds, key_in_lds;
+  size_t rank_of, mem, pos, deg, own, col, red, aff, key, c16, total;
+  bool aff_in_lds, key_in_lds, c_in_lds;
 };
 
 constexpr size_t kPlaceAffLds = 64 * 1024;
 constexpr size_t kPlaceKeyLds = 32 * 1024;
 
+constexpr size_t kPlaceLdsBudget = 160 * 1024;
+constexpr int kWaveGrowMaxE = 384;  // the one-wave growth holds up to 6 experts per lane
+
+// Row stride (16-bit elements) of the LDS copy of C: even, so that a lane's
+// two experts 2l, 2l + 1 are one aligned 32-bit word.  A tail pad of 128
+// elements covers the last row's reads past E.
+__host__ __device__ inline int c16_stride(int E) { return E + (E & 1); }
+
+// LDS: the arrays of the whole kernel first; then a region that the growth
+// uses for a 16-bit copy of the co-selection counts (when it fits) and the
+// refinement for own, the per-wave columns, aff and the rank-pair keys.
 PlaceLds place_lds(const Dims& d) {
   PlaceLds l;
   size_t o = 0;
@@ -65,16 +79,20 @@ PlaceLds place_lds(const Dims& d) {
   l.mem = take(sizeof(int32_t) * d.E);
   l.pos = take(sizeof(int32_t) * d.E);
   l.deg = take(sizeof(int32_t) * d.E);
+  l.red = take(sizeof(uint64_t) * (kPlaceWaves + 1));  // also the growth's three argmax slots
+  const size_t shared_at = o;
   l.own = take(sizeof(int32_t) * d.E);
   l.col = take(sizeof(int32_t) * kPlaceWaves * (size_t)d.R);
-  l.red = take(sizeof(uint64_t) * (kPlaceWaves + 1));  // also the growth's three argmax slots
   const size_t aff_b = sizeof(int32_t) * (size_t)d.R * d.E;
   const size_t key_b = sizeof(uint64_t) * (size_t)d.R * d.R;
   l.aff_in_lds = aff_b <= kPlaceAffLds;
   l.key_in_lds = key_b <= kPlaceKeyLds;
   l.aff = l.aff_in_lds ? take(aff_b) : 0;
   l.key = l.key_in_lds ? take(key_b) : 0;
-  l.total = o;
+  const size_t c16_b = sizeof(uint16_t) * ((size_t)d.E * c16_stride(d.E) + 128);
+  l.c16 = shared_at;
+  l.c_in_lds = shared_at + c16_b <= kPlaceLdsBudget && d.E <= kWaveGrowMaxE;
+  l.total = l.c_in_lds && shared_at + c16_b > o ? shared_at + c16_b : o;
   return l;
 }
 
@@ -183,6 +201,82 @@ __device__ __forceinline__ void eval_rows(const Dims& d, const int32_t* __restri
   }
 }
 
+// Greedy growth in one wave, with C's rows in LDS (16-bit, row stride
+// c16_stride(E), even): lane l holds the affinities of experts 2l + 128u and
+// 2l + 128u + 1 (u < U), read as one 32-bit word per u and step with no
+// bounds branch -- lanes past E read the next row (or the tail pad) into
+// experts that are never alive.  The argmax is wave-uniform (DPP and lane
+// reads), so a step needs no atomic and no barrier; the picks are kept one
+// per lane and written out every 64 steps and at the end of each rank.
+template <class K, int U>
+__device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, const int32_t* deg, int32_t* rank_of,
+                                          int32_t* mem, int32_t* pos, int32_t* aff) {
+  const int E = d.E, R = d.R, Er = d.Er, Es = c16_stride(E);
+  const int lane = threadIdx.x & 63;
+  constexpr int J = 2 * U;
+  constexpr int kShift = 12;
+  constexpr K kIdx = ((K)1 << kShift) - 1;
+  int32_t dg[J], a[J];
+  uint32_t alive = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = 2 * lane + 128 * (j >> 1) + (j & 1);
+    dg[j] = e < E ? deg[e] : 0;
+    if (e < E) alive |= 1u << j;
+  }
+  int32_t pk = 0;  // lane i: the pick of step (m - m % 64 + i) of the current rank
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) a[j] = 0;
+    for (int m = 0; m < Er; ++m) {
+      K best = 0;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int e = 2 * lane + 128 * (j >> 1) + (j & 1);
+        const K kk = ((K)(m == 0 ? dg[j] : a[j]) << kShift) | (K)(kIdx - e);
+        best = ((alive >> j) & 1u) && kk > best ? kk : best;
+      }
+      best = wave_max(best);
+      const int pick = (int)(kIdx - (best & kIdx));
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(c16 + pick * Es) + lane;
+      uint32_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = row[64 * u];
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (2 * lane + 128 * (j >> 1) + (j & 1) == pick) alive &= ~(1u << j);
+      const int q = m & 63;
+      if (lane == q) pk = pick;
+      if (q == 63 || m == Er - 1) {
+        const int base = r * Er + m - q;
+        if (lane <= q) {
+          mem[base + lane] = pk;
+          rank_of[pk] = r;
+          pos[pk] = base + lane;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a[2 * u] += (int32_t)(v[u] & 0xffffu);
+        a[2 * u + 1] += (int32_t)(v[u] >> 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = 2 * lane + 128 * (j >> 1) + (j & 1);
+      if (e < E) aff[(int64_t)r * E + e] = a[j];
+    }
+  }
+}
+
+template <class K>
+__device__ __forceinline__ void grow_wave_any(const Dims& d, const uint16_t* c16, const int32_t* deg, int32_t* rank_of,
+                                              int32_t* mem, int32_t* pos, int32_t* aff) {
+  if (d.E <= 128) grow_wave<K, 1>(d, c16, deg, rank_of, mem, pos, aff);
+  else if (d.E <= 256) grow_wave<K, 2>(d, c16, deg, rank_of, mem, pos, aff);
+  else grow_wave<K, 3>(d, c16, deg, rank_of, mem, pos, aff);
+}
+
 // Greedy growth, one expert per step for E steps; thread t holds the
 // affinities to the rank being filled of experts t, t + 1024, ... (NPL of
 // them).  The step's argmax goes through slot[g % 3]: step g clears the slot
@@ -244,7 +338,7 @@ __device__ __forceinline__ void grow(const Dims& d, const int32_t* __restrict__ 
   }
 }
 
-template <int NPL, bool AFF_LDS, bool KEY_LDS>
+template <int NPL, bool AFF_LDS, bool KEY_LDS, bool C_LDS>
 __global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds ly, PlaceArgs pa) {
   extern __shared__ __align__(16) char smem_place[];
   int32_t* rank_of = reinterpret_cast<int32_t*>(smem_place + ly.rank_of);
@@ -268,6 +362,8 @@ __global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds l
   // input checks: zero diagonal, no negative count, sums below 2^31
   // (symmetry itself is the caller's contract).
   int64_t my_max_deg = 0;
+  uint32_t my_max_entry = 0;  // a negative count reads as a large one here
+  uint16_t* c16 = reinterpret_cast<uint16_t*>(smem_place + ly.c16);
   for (int e = tid; e < E; e += kPlaceThreads) {
     int64_t s = 0;
     bool bad = false;
@@ -276,19 +372,38 @@ __global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds l
       const int32_t v = C[(int64_t)x * E + e];
       bad |= v < 0 || (x == e && v != 0);
       s += v;
+      if constexpr (C_LDS) {
+        my_max_entry = max(my_max_entry, (uint32_t)v);
+        c16[x * c16_stride(E) + e] = (uint16_t)v;  // used only when every entry fits
+      }
     }
     if (bad || s > INT32_MAX) atomicOr(pa.status, MOE_STATUS_BAD_PAIRS);
     const int32_t dg = (int32_t)(s < 0 ? 0 : s > INT32_MAX ? INT32_MAX : s);
     deg[e] = dg;
     my_max_deg = max(my_max_deg, (int64_t)dg);
   }
-  for (int64_t q = tid; q < (int64_t)R * R; q += kPlaceThreads) key[q] = 0;
-  const uint64_t max_deg = block_max((uint64_t)my_max_deg, red);  // also publishes deg[]
+  const uint64_t max_deg = block_max((uint64_t)my_max_deg, red);  // also publishes deg[] and c16
+  bool use_c16 = false;
+  if constexpr (C_LDS) use_c16 = block_max((uint64_t)my_max_entry, red) <= 0xffffu;
 
   // Greedy growth.  Scores are sums of counts, so never above the largest
   // degree: when that is below 2^20 a 32-bit key (score, then 4095 - e) suffices.
-  if (max_deg < (1u << 20)) grow<uint32_t, NPL>(d, C, deg, rank_of, mem, pos, aff, red);
-  else grow<uint64_t, NPL>(d, C, deg, rank_of, mem, pos, aff, red);
+  // With the LDS copy of C the first wave grows alone; as the refinement
+  // reuses that LDS space, aff goes to the workspace first and into LDS after.
+  if (use_c16) {
+    if (wave == 0) {
+      if (max_deg < (1u << 20)) grow_wave_any<uint32_t>(d, c16, deg, rank_of, mem, pos, pa.aff_ws);
+      else grow_wave_any<uint64_t>(d, c16, deg, rank_of, mem, pos, pa.aff_ws);
+    }
+    __syncthreads();
+    if constexpr (AFF_LDS)
+      for (int q = tid; q < R * E; q += kPlaceThreads) aff[q] = pa.aff_ws[q];
+  } else if (max_deg < (1u << 20)) {
+    grow<uint32_t, NPL>(d, C, deg, rank_of, mem, pos, aff, red);
+  } else {
+    grow<uint64_t, NPL>(d, C, deg, rank_of, mem, pos, aff, red);
+  }
+  for (int64_t q = tid; q < (int64_t)R * R; q += kPlaceThreads) key[q] = 0;
   __syncthreads();
   for (int e = tid; e < E; e += kPlaceThreads) own[e] = aff[(int64_t)rank_of[e] * E + e];
   __syncthreads();
@@ -361,9 +476,9 @@ __global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds l
   }
 }
 
-template <int NPL, bool AFF_LDS, bool KEY_LDS>
+template <int NPL, bool AFF_LDS, bool KEY_LDS, bool C_LDS>
 hipError_t launch_place_n(const Dims& d, const PlaceLds& ly, const PlaceArgs& pa, hipStream_t st) {
-  auto kern = place_kernel<NPL, AFF_LDS, KEY_LDS>;
+  auto kern = place_kernel<NPL, AFF_LDS, KEY_LDS, C_LDS>;
   if (ly.total > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ly.total);
@@ -373,12 +488,12 @@ hipError_t launch_place_n(const Dims& d, const PlaceLds& ly, const PlaceArgs& pa
   return hipGetLastError();
 }
 
-template <int NPL>
+template <int NPL, bool C_LDS>
 hipError_t launch_place_lds(const Dims& d, const PlaceLds& ly, const PlaceArgs& pa, hipStream_t st) {
-  if (ly.aff_in_lds && ly.key_in_lds) return launch_place_n<NPL, true, true>(d, ly, pa, st);
-  if (ly.aff_in_lds) return launch_place_n<NPL, true, false>(d, ly, pa, st);
-  if (ly.key_in_lds) return launch_place_n<NPL, false, true>(d, ly, pa, st);
-  return launch_place_n<NPL, false, false>(d, ly, pa, st);
+  if (ly.aff_in_lds && ly.key_in_lds) return launch_place_n<NPL, true, true, C_LDS>(d, ly, pa, st);
+  if (ly.aff_in_lds) return launch_place_n<NPL, true, false, C_LDS>(d, ly, pa, st);
+  if (ly.key_in_lds) return launch_place_n<NPL, false, true, C_LDS>(d, ly, pa, st);
+  return launch_place_n<NPL, false, false, C_LDS>(d, ly, pa, st);
 }
 
 }  // namespace
@@ -390,8 +505,9 @@ hipError_t launch_place(const Dims& d, const int32_t* cooc, int32_t max_swaps, c
   const PlaceLds ly = place_lds(d);
   const PlaceArgs pa{cooc, max_swaps, out.expert_rank, out.rank_experts, out.intra, out.n_swaps,
                      ws.place_aff, ws.place_key, ws.status};
-  if (d.E <= kPlaceThreads) return launch_place_lds<1>(d, ly, pa, st);
-  return launch_place_lds<2>(d, ly, pa, st);
+  if (ly.c_in_lds) return launch_place_lds<1, true>(d, ly, pa, st);  // E <= 384 here
+  if (d.E <= kPlaceThreads) return launch_place_lds<1, false>(d, ly, pa, st);
+  return launch_place_lds<2, false>(d, ly, pa, st);
 }
 
 }  // namespace moe

@@ -69,7 +69,8 @@ def test_place_on_each_workload(mp, name):
 
 @pytest.mark.parametrize("E,R,hi", [(8, 4, 3), (12, 3, 2), (64, 8, 5), (96, 32, 4), (130, 10, 50), (256, 64, 9),
                                     (512, 16, 3), (1024, 128, 6), (2048, 256, 4), (2048, 8, 1000), (40, 40, 9),
-                                    (40, 1, 9)])
+                                    (40, 1, 9), (99, 9, 7), (255, 5, 4), (270, 10, 6), (200, 2, 5), (128, 1, 3),
+                                    (384, 12, 5)])
 def test_place_random_coselection_with_ties(mp, E, R, hi):
     """Small integer weights: many equal gains and scores, so the tie rules decide."""
     print("place random E=%d R=%d" % (E, R), flush=True)
@@ -77,6 +78,16 @@ def test_place_random_coselection_with_ties(mp, E, R, hi):
     c = oracle.make_cfg(R, E, 1, R, 1, 8, 0)
     for cap in (-1, 0, 1, 3):
         check_place(gpu_place(mp, E, R, C, cap), oracle.place(c, C, cap), "E=%d R=%d cap=%d" % (E, R, cap))
+
+
+@pytest.mark.parametrize("lo,hi", [(10000, 30000), (60000, 70000), (0, 1 << 20)])
+def test_place_large_counts(mp, lo, hi):
+    """Counts near and past 16 bits, degrees past 2^20 (the 64-bit growth keys)."""
+    for E, R in [(64, 8), (130, 13)]:
+        print("place large E=%d R=%d lo=%d hi=%d" % (E, R, lo, hi), flush=True)
+        C = sym(inputs.rng(E + lo).integers(lo, hi, (E, E)))
+        c = oracle.make_cfg(R, E, 1, R, 1, 8, 0)
+        check_place(gpu_place(mp, E, R, C), oracle.place(c, C), "E=%d R=%d lo=%d" % (E, R, lo))
 
 
 def test_place_flags_invalid_counts(mp):
