@@ -15,16 +15,26 @@
 //   grad_accum[main(e)][r][e - main(e)*E/R] = replica_grads[r][j]   ([R][R][E/R][P])
 // One workgroup column per slot (grid.x), chunks of 8192 elements along the
 // row (grid.y, strided), 16-byte vectors when the rows allow; HBM traffic is
-// one read and one write of every occupied slot's row.
+// one read and one write of every occupied slot's row.  The vector stores
+// carry the nontemporal hint (nothing here reads the copied rows back): on
+// MI355X that lifts the copy from 4.7 to 5.3 TB/s, with 512 threads of two
+// vectors each (256 x 4 reaches 5.2).
 #include "internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kMapThreads = 1024;
-constexpr int kCopyThreads = 256;
-constexpr int kCopyVpt = 4;                                  // 16-byte vectors per thread
+constexpr int kCopyThreads = 512;
+constexpr int kCopyVpt = 2;                                  // 16-byte vectors per thread
 constexpr int64_t kChunk = (int64_t)kCopyThreads * kCopyVpt * 8;  // bf16 elements per chunk
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_stream(uint4* p, const uint4& v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
 
 __global__ __launch_bounds__(kMapThreads) void slot_map_kernel(Dims d, const int32_t* __restrict__ n_inst_p,
                                                                const int32_t* __restrict__ inst_expert,
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(kCopyThreads) void slot_copy_kernel(Dims d, const i
 #pragma unroll
       for (int u = 0; u < kCopyVpt; ++u) {
         const int64_t i = threadIdx.x + (int64_t)u * kCopyThreads;
-        if (i < nv) tv[i] = v[u];
+        if (i < nv) store_stream(tv + i, v[u]);
       }
     } else {
       const int64_t n = min(kChunk, P - c0);
