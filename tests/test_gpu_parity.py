@@ -270,6 +270,23 @@ def test_degenerate_layers(mp):
         compare(gpu_layer(mp, cfg, logits=lg, hidden=hid), oracle_layer(cfg, logits=lg, hidden=hid), str(c))
 
 
+@pytest.mark.parametrize("shape", [(2048, 2048, 32, 256, 8, 1024, -1, False), (2048, 2048, 32, 256, 64, 1024, 0, True),
+                                   (1024, 256, 8, 256, 1, 1024, 0, False), (4096, 2048, 32, 256, 64, 512, 0, True)])
+def test_maximum_supported_sizes(mp, shape):
+    """The library's limits: E = 2048, k = 32, R = 256, G up to 64, B = 1024 (expert_bytes 0 makes
+    stage 1 spend the whole budget); with the layer-to-layer transition counts."""
+    T, E, k, R, G, B, W, fused = shape
+    H = 8
+    cfg = mp.make_config(T, E, k, R, G, H, B, expert_bytes=W)
+    print("max sizes T=%d E=%d k=%d R=%d G=%d B=%d W=%d fused=%s" % shape, flush=True)
+    lg = inputs.random_logits(E + R, T, E)
+    hid = inputs.random_hidden(T, T, H)
+    prev = inputs.random_topk(G, T, E, k)
+    got = gpu_layer(mp, cfg, logits=lg, hidden=hid, prev_topk=prev, trans=True, fused=fused)
+    want = oracle_layer(cfg, logits=lg, hidden=hid, prev_topk=prev)
+    compare(got, want, "max sizes %s" % (shape,))
+
+
 def test_gpu_runs_are_bitwise_identical(mp):
     w = synth.WORKLOADS["qwen3_layer"]
     cfg = mp.make_config(w.T, w.E, w.k, w.R, w.G, 64, w.B, expert_bytes=0)
