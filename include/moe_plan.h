@@ -49,6 +49,9 @@
  *     priority: the calls that compute pair counts (cooc, trans) fork them
  *     onto it and join them back into `stream` within the same call, so every
  *     output is complete in `stream` order when the call's work ends.
+ *   - A handle belongs to the HIP device that was current at moe_plan_create;
+ *     each call runs on that device and gives the caller's current device
+ *     back before it returns.  `stream` must belong to the handle's device.
  *   - Argument and configuration errors return a negative code synchronously
  *     and enqueue nothing.  A data-dependent error (a NaN gate logit) sets a
  *     device status word that moe_plan_status reads.

@@ -90,12 +90,28 @@ int derive(const moe_plan_config* c, moe::Dims* d) {
   return MOE_OK;
 }
 
-int bind(moe_plan_t h) {
-  int cur = -1;
-  if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
-  if (cur != h->device && hipSetDevice(h->device) != hipSuccess) return MOE_ERR_HIP;
-  return MOE_OK;
-}
+// Makes `device` current for the duration of a call and gives the caller's
+// current device back when the call returns.
+class DeviceScope {
+ public:
+  explicit DeviceScope(int device) {
+    if (hipGetDevice(&prev_) != hipSuccess) return;
+    if (prev_ != device && hipSetDevice(device) != hipSuccess) return;
+    switched_ = prev_ != device;
+    ok_ = true;
+  }
+  ~DeviceScope() {
+    if (switched_) (void)hipSetDevice(prev_);
+  }
+  DeviceScope(const DeviceScope&) = delete;
+  DeviceScope& operator=(const DeviceScope&) = delete;
+  bool ok() const { return ok_; }
+
+ private:
+  int prev_ = -1;
+  bool switched_ = false;
+  bool ok_ = false;
+};
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -226,7 +242,8 @@ extern "C" int moe_plan_route(moe_plan_t h, const float* logits, const int32_t* 
   if (!h || check_route_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
   if (d.T > 0 && !logits) return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* prev = (prev_topk && out->trans) ? prev_topk : nullptr;
   hipError_t e = moe::launch_route_topk(d, logits, prev, out->topk_idx, out->topk_val, out->tile_mask,
@@ -242,7 +259,8 @@ extern "C" int moe_plan_hist(moe_plan_t h, const int32_t* topk_idx, const int32_
   if (!h || check_route_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
   if (d.T > 0 && !topk_idx) return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* prev = (prev_topk && out->trans) ? prev_topk : nullptr;
   hipError_t e = moe::launch_build_masks(d, topk_idx, prev, out->tile_mask, h->ws.prev_mask, h->ws.status, st);
@@ -256,7 +274,8 @@ extern "C" int moe_plan_plan(moe_plan_t h, const moe_route_out* route, const moe
   if (!h || !route || !route->omega || check_plan_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
   if (d.T > 0 && (!route->topk_idx || !route->tile_mask || !route->tile_base)) return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = moe::launch_plan(d, route->omega, nullptr, nullptr, nullptr, nullptr, nullptr, *out, h->ws, st);
   if (e == hipSuccess) e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *out, h->ws, st);
@@ -268,7 +287,8 @@ extern "C" int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const u
   if (!h || !plan || check_dispatch_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
   if (d.T > 0 && (!plan->slot_inst || !plan->slot_rank || !plan->inst_offset || !hidden)) return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm,
                                           out->slot_pos, out->dispatch, h->ws, st);
@@ -283,7 +303,8 @@ extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* p
     return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
   if (d.T > 0 && (!logits || !hidden)) return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* prev = (prev_topk && route->trans) ? prev_topk : nullptr;
   // On `st`: top-k (which also accumulates the routing matrix into one of the
@@ -325,7 +346,8 @@ extern "C" int moe_plan_combine(moe_plan_t h, const float* topk_val, const int32
   if (!h) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
   if (d.T > 0 && (!topk_val || !slot_pos || !expert_out || !out)) return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_rc(moe::launch_combine(d, topk_val, slot_pos, expert_out, out, h->ws.status, st));
 }
@@ -334,7 +356,8 @@ extern "C" int moe_plan_place(moe_plan_t h, const int32_t* cooc, int32_t max_swa
                               void* stream) {
   if (!h || !cooc || !out || !out->expert_rank || !out->rank_experts || !out->intra || !out->n_swaps)
     return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(moe::launch_place(h->d, cooc, max_swaps, *out, h->ws, static_cast<hipStream_t>(stream)));
 }
 
@@ -353,7 +376,8 @@ int check_dedup(const moe::Dims& d, const int32_t* slot_key, const int32_t* key_
 extern "C" int moe_plan_dedup_count(moe_plan_t h, const int32_t* slot_key, const int32_t* key_rank, int32_t n_keys,
                                     const moe_dedup_out* out, void* stream) {
   if (!h || check_dedup(h->d, slot_key, key_rank, n_keys, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(
       moe::launch_dedup(h->d, slot_key, key_rank, n_keys, nullptr, *out, h->ws, static_cast<hipStream_t>(stream)));
 }
@@ -365,7 +389,8 @@ extern "C" int moe_plan_dedup_dispatch(moe_plan_t h, const int32_t* slot_key, co
   if (!out->n_rows || !out->rank_row_offset) return MOE_ERR_INVALID_ARG;
   if (h->d.T > 0 && (!hidden || !out->row_token || !out->row_slots || !out->slot_row || !out->ddispatch))
     return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   // a non-null row source selects the layout and copy; T = 0 still writes the offsets
   static const uint16_t kNoRows = 0;
   const uint16_t* src = hidden ? hidden : &kNoRows;
@@ -377,7 +402,8 @@ extern "C" int moe_plan_quality(moe_plan_t h, const moe_plan_out* plan, int64_t*
   if (!h || !plan || !out || !plan->n_inst || !plan->inst_expert || !plan->inst_rank || !plan->rank_load ||
       !plan->quota)
     return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(moe::launch_quality(h->d, *plan, out, h->ws.status, static_cast<hipStream_t>(stream)));
 }
 
@@ -386,7 +412,8 @@ extern "C" int moe_plan_predict(moe_plan_t h, const int32_t* topk_cur, const int
                                 void* stream) {
   if (!h || !trans || !count_cur || !out || !out->rank_tokens) return MOE_ERR_INVALID_ARG;
   if (h->d.T > 0 && (!topk_cur || !out->pred)) return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(moe::launch_predict(h->d, topk_cur, trans, count_cur, key_rank, topk_next, *out, h->ws,
                                     static_cast<hipStream_t>(stream)));
 }
@@ -395,7 +422,8 @@ extern "C" int moe_plan_slot_map(moe_plan_t h, const moe_plan_out* plan, const m
   if (!h || !plan || !out || !plan->n_inst || !plan->inst_expert || !plan->inst_rank || !out->inst_slot)
     return MOE_ERR_INVALID_ARG;
   if (h->d.n_slot > 0 && (!out->slot_expert || !out->slot_main)) return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(moe::launch_slot_map(h->d, *plan, *out, h->ws.status, static_cast<hipStream_t>(stream)));
 }
 
@@ -404,7 +432,8 @@ extern "C" int moe_plan_replica_pull(moe_plan_t h, const int32_t* slot_expert, c
   if (!h || param_elems < 0) return MOE_ERR_INVALID_ARG;
   if (h->d.n_slot > 0 && param_elems > 0 && (!slot_expert || !main_params || !replica_params))
     return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(moe::launch_replica_pull(h->d, slot_expert, main_params, param_elems, replica_params, h->ws.status,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -414,7 +443,8 @@ extern "C" int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, c
   if (!h || param_elems < 0) return MOE_ERR_INVALID_ARG;
   if (h->d.n_slot > 0 && param_elems > 0 && (!slot_expert || !replica_grads || !grad_accum))
     return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(moe::launch_replica_push(h->d, slot_expert, replica_grads, param_elems, grad_accum, h->ws.status,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -430,19 +460,16 @@ extern "C" int moe_plan_device_info(int device, int64_t* out) {
     out[i] = v;
   }
   size_t free_b = 0, total_b = 0;
-  int cur = -1;
-  if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
-  if (cur != device && hipSetDevice(device) != hipSuccess) return MOE_ERR_HIP;
-  const hipError_t e = hipMemGetInfo(&free_b, &total_b);
-  if (cur != device) (void)hipSetDevice(cur);
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  const DeviceScope on_device(device);
+  if (!on_device.ok() || hipMemGetInfo(&free_b, &total_b) != hipSuccess) return MOE_ERR_HIP;
   out[5] = (int64_t)total_b;
   return MOE_OK;
 }
 
 extern "C" int moe_plan_status(moe_plan_t h, int32_t* host_flags) {
   if (!h || !host_flags) return MOE_ERR_INVALID_ARG;
-  if (bind(h) != MOE_OK) return MOE_ERR_HIP;
+  const DeviceScope on_device(h->device);
+  if (!on_device.ok()) return MOE_ERR_HIP;
   if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
   int32_t v = 0;
   if (hipMemcpy(&v, h->ws.status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
@@ -454,7 +481,8 @@ extern "C" int moe_plan_status(moe_plan_t h, int32_t* host_flags) {
 
 extern "C" void moe_plan_destroy(moe_plan_t h) {
   if (!h) return;
-  if (bind(h) == MOE_OK) {
+  const DeviceScope on_device(h->device);
+  if (on_device.ok()) {
     (void)hipDeviceSynchronize();
     (void)hipEventDestroy(h->join);
     (void)hipEventDestroy(h->fork);
