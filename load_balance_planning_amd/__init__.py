@@ -8,8 +8,9 @@ allocates the caller-owned buffers as torch tensors on the current HIP device
 and runs the calls on torch's current stream -- PyTorch is used for device
 memory and streams only.
 
-There is no CPU fallback: importing this package without the built library
-raises.
+There is no CPU fallback: the first call loads the HIP library (building it
+in-tree with hipcc when none is there yet), and when it can be neither loaded
+nor built that call raises.
 """
 from __future__ import annotations
 
