@@ -369,7 +369,11 @@ int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const uint16_t* hi
  * solver launch, on the CUs the single solver workgroup leaves idle, and the
  * pair counts (route->cooc, route->trans) run on the handle's side stream,
  * overlapping the slot assignment and the gather; they are joined back into
- * `stream` within the call.  Sources: those of the three calls.
+ * `stream` within the call.  The call keeps no state in the handle from one
+ * call to the next (its routing-matrix accumulator is zero again when the
+ * call's work ends), so it can be captured into a HIP graph and the graph
+ * replayed, with the same pointers, in place of the call.  Sources: those of
+ * the three calls.
  */
 int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* prev_topk, const uint16_t* hidden,
                   const moe_route_out* route, const moe_plan_out* plan, const moe_dispatch_out* out,

@@ -17,7 +17,6 @@ struct moe_plan {
   // caller's stream at the end of the call.
   hipStream_t side;
   hipEvent_t fork, join;
-  int acc_parity;  // which of the two routing-matrix accumulators the next moe_plan_step fills
 };
 
 namespace {
@@ -44,7 +43,7 @@ WsLayout ws_layout(const moe::Dims& d) {
   l.rlist = take(sizeof(int32_t) * (size_t)(d.E + 1));
   l.colpre = take(sizeof(int32_t) * (size_t)d.cap * d.R);
   l.pair_part = take(sizeof(int32_t) * moe::pair_part_words(d));
-  l.omega_acc = take(sizeof(int32_t) * 2 * (size_t)d.R * d.E);
+  l.omega_acc = take(sizeof(int32_t) * (size_t)d.R * d.E);
   l.place_aff = take(sizeof(int32_t) * (size_t)d.R * d.E);
   l.place_key = take(sizeof(uint64_t) * (size_t)d.R * d.R);
   l.dd_mask = take(sizeof(uint64_t) * (size_t)d.NT * d.R);
@@ -179,7 +178,6 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   }
   h->side = nullptr;
   h->fork = h->join = nullptr;
-  h->acc_parity = 0;
   if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
       // both streams are on one device: a device-scope release is enough
       hipEventCreateWithFlags(&h->fork, hipEventDisableTiming | hipEventReleaseToDevice) != hipSuccess ||
@@ -277,8 +275,9 @@ extern "C" int moe_plan_plan(moe_plan_t h, const moe_route_out* route, const moe
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = moe::launch_plan(d, route->omega, nullptr, nullptr, nullptr, nullptr, nullptr, *out, h->ws, st);
-  if (e == hipSuccess) e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *out, h->ws, st);
+  hipError_t e = moe::launch_plan(d, route->omega, nullptr, nullptr, nullptr, nullptr, *out, h->ws, st);
+  if (e == hipSuccess)
+    e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *out, h->ws, nullptr, 0, st);
   return hip_rc(e);
 }
 
@@ -307,32 +306,32 @@ extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* p
   if (!on_device.ok()) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* prev = (prev_topk && route->trans) ? prev_topk : nullptr;
-  // On `st`: top-k (which also accumulates the routing matrix into one of the
-  // two workspace accumulators) -> plan (the solver reads that accumulator;
-  // workgroups on the CUs it leaves idle write the tile prefix, the routing
-  // matrix and counts outputs, and clear the other accumulator for the next
-  // call) -> quotas -> slot instances -> gather.  The pair counts, needed by
-  // nothing later, go to the side stream once the plan is enqueued -- forking
-  // earlier would put the fork's wait in front of the plan -- and overlap the
-  // slot assignment and the gather.
+  // On `st`: top-k (which also accumulates the routing matrix into the
+  // workspace accumulator, zero on entry) -> plan (the solver reads the
+  // accumulator; workgroups on the CUs it leaves idle write the tile prefix,
+  // the routing matrix and counts outputs) -> quotas (read the accumulator
+  // too) -> slot instances + gather, which zero the accumulator again: the
+  // handle carries no state from one call to the next, so the call can be
+  // captured in a HIP graph and replayed.  The pair counts, needed by nothing
+  // later, go to the side stream once the plan is enqueued -- forking earlier
+  // would put the fork's wait in front of the plan -- and overlap the slot
+  // assignment and the gather.
   const int64_t re = (int64_t)d.R * d.E;
-  int32_t* acc = h->ws.omega_acc + (h->acc_parity ? re : 0);
-  int32_t* other = h->ws.omega_acc + (h->acc_parity ? 0 : re);
+  int32_t* acc = h->ws.omega_acc;
   hipError_t e = moe::launch_route_topk(d, logits, prev, route->topk_idx, route->topk_val, route->tile_mask,
                                         h->ws.prev_mask, acc, h->ws.status, st);
   if (e == hipSuccess)
-    e = moe::launch_plan(d, acc, route->tile_mask, route->tile_base, route->omega, route->expert_count, other, *plan,
-                         h->ws, st);
-  if (e == hipSuccess) h->acc_parity ^= 1;
+    e = moe::launch_plan(d, acc, route->tile_mask, route->tile_base, route->omega, route->expert_count, *plan, h->ws,
+                         st);
   if (e == hipSuccess) e = fork_pairs(h, route, prev, st);
   if (moe::gather_can_assign(d, hidden, out->dispatch)) {
     // the gather assigns its token's slots itself, overlapping the row load
     if (e == hipSuccess)
       e = moe::launch_assign_gather(d, route->topk_idx, route->tile_mask, route->tile_base, *plan, hidden, out->perm,
-                                    out->slot_pos, out->dispatch, h->ws, st);
+                                    out->slot_pos, out->dispatch, h->ws, acc, re, st);
   } else {
     if (e == hipSuccess)
-      e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *plan, h->ws, st);
+      e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *plan, h->ws, acc, re, st);
     if (e == hipSuccess)
       e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm,
                              out->slot_pos, out->dispatch, h->ws, st);

@@ -26,6 +26,8 @@ struct AssignIn {
   const int32_t* quota;
   int32_t* slot_inst;  // written
   int32_t* slot_rank;  // written
+  int32_t* clear;      // zeroed, [0, clear_n) (nullable): a buffer no earlier kernel still reads
+  int64_t clear_n;
 };
 
 // One workgroup per token.  Threads j < k place slot t*k+j -- reading its
@@ -58,6 +60,8 @@ __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* 
       if (c < vpr) v[u] = src[c];
     }
   }
+  if (ASSIGN)
+    for (int64_t q = t * 256 + tid; q < as.clear_n; q += (int64_t)gridDim.x * 256) as.clear[q] = 0;
   if (tid < d.k) {
     const int64_t sigma = t * d.k + tid;
     int i, r;
@@ -170,9 +174,10 @@ bool gather_can_assign(const Dims& d, const uint16_t* hidden, const uint16_t* di
 hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
                                 const int32_t* tile_base, const moe_plan_out& plan, const uint16_t* hidden,
                                 int32_t* perm, int32_t* slot_pos, uint16_t* dispatch, const Workspace& ws,
-                                hipStream_t st) {
+                                int32_t* clear, int64_t clear_n, hipStream_t st) {
   if (d.T == 0) return hipSuccess;
-  const AssignIn as{topk_idx, tile_mask, tile_base, plan.quota, plan.slot_inst, plan.slot_rank};
+  const AssignIn as{topk_idx, tile_mask, tile_base, plan.quota, plan.slot_inst, plan.slot_rank, clear,
+                    clear ? clear_n : 0};
   hipLaunchKernelGGL((gather_vec_kernel<4, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr,
                      plan.inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
                      reinterpret_cast<uint4*>(dispatch), as, ws);

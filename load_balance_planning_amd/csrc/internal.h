@@ -40,8 +40,8 @@ struct Workspace {
   int32_t* rlist;       // [E+1] experts with more than one instance; entry E is their count
   int32_t* colpre;      // [cap][R] exclusive prefix of each instance's quotas over sources
   int32_t* pair_part;   // partial pair-count blocks of the tile splits (pair_part_words)
-  int32_t* omega_acc;   // [2][R][E] routing matrices accumulated by the top-k kernel in
-                        // alternate calls; the one not in use is zero
+  int32_t* omega_acc;   // [R][E] routing matrix accumulated by the top-k kernel of
+                        // moe_plan_step; zero between calls (the slot assignment clears it)
   int32_t* place_aff;   // [R][E] placement affinities when they do not fit in LDS
   uint64_t* place_key;  // [R][R] best swap key per rank pair when it does not fit in LDS
   uint64_t* dd_mask;    // [NT][R] deduplication: tokens of each tile with a slot on each rank
@@ -80,13 +80,15 @@ hipError_t launch_pairs(const Dims& d, const uint64_t* tile_mask, const uint64_t
 // Solver, quotas and dispatch offsets from the routing matrix omega.  When
 // scan_mask is given, extra workgroups of the solver launch also write the
 // tile prefix of those masks to scan_base, the routing matrix and expert
-// counts recomputed from the masks to scan_omega / scan_count, and zeros to
-// scan_zero (each nullable).
+// counts recomputed from the masks to scan_omega / scan_count (each nullable).
 hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan_mask, int32_t* scan_base,
-                       int32_t* scan_omega, int32_t* scan_count, int32_t* scan_zero, const moe_plan_out& out,
-                       const Workspace& ws, hipStream_t st);
+                       int32_t* scan_omega, int32_t* scan_count, const moe_plan_out& out, const Workspace& ws,
+                       hipStream_t st);
+// The slot assignment; it also zeroes clear[0, clear_n) (nullable), which no
+// kernel before it on the stream still reads.
 hipError_t launch_assign(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
-                         const int32_t* tile_base, const moe_plan_out& out, const Workspace& ws, hipStream_t st);
+                         const int32_t* tile_base, const moe_plan_out& out, const Workspace& ws,
+                         int32_t* clear, int64_t clear_n, hipStream_t st);
 hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t* slot_rank,
                          const int32_t* inst_offset, const uint16_t* hidden, int32_t* perm, int32_t* slot_pos,
                          uint16_t* dispatch, const Workspace& ws, hipStream_t st);
@@ -96,7 +98,7 @@ bool gather_can_assign(const Dims& d, const uint16_t* hidden, const uint16_t* di
 hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
                                 const int32_t* tile_base, const moe_plan_out& plan, const uint16_t* hidden,
                                 int32_t* perm, int32_t* slot_pos, uint16_t* dispatch, const Workspace& ws,
-                                hipStream_t st);
+                                int32_t* clear, int64_t clear_n, hipStream_t st);
 
 hipError_t launch_combine(const Dims& d, const float* topk_val, const int32_t* slot_pos, const uint16_t* expert_out,
                           uint16_t* out, int32_t* status, hipStream_t st);

@@ -502,23 +502,16 @@ __device__ void stage2_domain(const Dims& d, const PlanLayout& ly, int m) {
 // Workgroups 1.. (when scan_mask is given) run on the CUs the solver leaves
 // idle: for kScanEB experts each, the tile prefix of the presence masks into
 // scan_base, the routing matrix and expert counts into scan_omega and
-// scan_count (tile_scan.h), and zeros into those columns of scan_zero.
+// scan_count (tile_scan.h).
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout ly, const int32_t* __restrict__ omega,
                                                             const uint64_t* __restrict__ scan_mask,
                                                             int32_t* __restrict__ scan_base,
                                                             int32_t* __restrict__ scan_omega,
-                                                            int32_t* __restrict__ scan_count,
-                                                            int32_t* __restrict__ scan_zero, moe_plan_out out,
+                                                            int32_t* __restrict__ scan_count, moe_plan_out out,
                                                             Workspace ws) {
   if (blockIdx.x > 0) {
     const int blk = blockIdx.x - 1;
     tile_scan_block<kPlanThreads>(d, scan_mask, scan_base, scan_omega, scan_count, blk, plan_lds);
-    if (scan_zero) {
-      for (int q = threadIdx.x; q < d.R * kScanEB; q += kPlanThreads) {
-        const int s = q / kScanEB, e = blk * kScanEB + (q - s * kScanEB);
-        if (e < d.E) scan_zero[(int64_t)s * d.E + e] = 0;
-      }
-    }
     return;
   }
   int32_t* lds = plan_lds;
@@ -953,9 +946,11 @@ __global__ __launch_bounds__(256) void assign_kernel(Dims d, const int32_t* __re
                                                      const uint64_t* __restrict__ tile_mask,
                                                      const int32_t* __restrict__ tile_base,
                                                      const int32_t* __restrict__ quota, Workspace ws,
-                                                     int32_t* __restrict__ slot_inst, int32_t* __restrict__ slot_rank) {
+                                                     int32_t* __restrict__ slot_inst, int32_t* __restrict__ slot_rank,
+                                                     int32_t* __restrict__ clear, int64_t clear_n) {
   const int64_t sigma = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t N = (int64_t)d.T * d.k;
+  for (int64_t i = sigma; i < clear_n; i += (int64_t)gridDim.x * blockDim.x) clear[i] = 0;
   if (sigma >= N) return;
   int inst, rank;
   assign_slot(d, sigma, topk, tile_mask, tile_base, quota, ws, inst, rank);
@@ -996,8 +991,8 @@ PlanLayout plan_layout(const Dims& d) {
 size_t plan_lds_bytes(const Dims& d) { return sizeof(int32_t) * (size_t)plan_layout(d).total; }
 
 hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan_mask, int32_t* scan_base,
-                       int32_t* scan_omega, int32_t* scan_count, int32_t* scan_zero, const moe_plan_out& out,
-                       const Workspace& ws, hipStream_t st) {
+                       int32_t* scan_omega, int32_t* scan_count, const moe_plan_out& out, const Workspace& ws,
+                       hipStream_t st) {
   const PlanLayout ly = plan_layout(d);
   size_t lds = sizeof(int32_t) * (size_t)ly.total;
   const int n_scan = scan_mask ? (d.E + kScanEB - 1) / kScanEB : 0;
@@ -1008,7 +1003,7 @@ hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(plan_kernel, dim3(1 + n_scan), dim3(kPlanThreads), lds, st, d, ly, omega, scan_mask, scan_base,
-                     scan_omega, scan_count, scan_zero, out, ws);
+                     scan_omega, scan_count, out, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_transport = d.B < d.E ? d.B : d.E;  // each replicated expert owns at least one replica
@@ -1019,12 +1014,13 @@ hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan
 }
 
 hipError_t launch_assign(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
-                         const int32_t* tile_base, const moe_plan_out& out, const Workspace& ws, hipStream_t st) {
+                         const int32_t* tile_base, const moe_plan_out& out, const Workspace& ws, int32_t* clear,
+                         int64_t clear_n, hipStream_t st) {
   const int64_t N = (int64_t)d.T * d.k;
   if (N == 0) return hipSuccess;
   const int64_t blocks = (N + 255) / 256;
   hipLaunchKernelGGL(assign_kernel, dim3((unsigned)blocks), dim3(256), 0, st, d, topk_idx, tile_mask, tile_base,
-                     out.quota, ws, out.slot_inst, out.slot_rank);
+                     out.quota, ws, out.slot_inst, out.slot_rank, clear, clear ? clear_n : 0);
   return hipGetLastError();
 }
 
