@@ -1,0 +1,92 @@
+"""Parity in the launch configuration bench.py times: two handles on two
+streams, consecutive steps alternating between them with no synchronisation
+in between, at the full DeepSeek-V3-shaped size.
+
+The two handles plan two different batches (the workload's logits and those
+of the same recipe with another seed), so a handle that read the other's
+buffers would show.  After every step its outputs are copied aside on its own
+stream (the integers whole, 4096 sampled rows of the dispatch buffer), and
+afterwards every copy is checked against the oracle: the integers byte for
+byte, each sampled row against its definition, hidden[perm[p] / k].
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+INT_OUTPUTS = ("topk_idx", "expert_count", "omega", "cooc", "n_inst", "inst_expert", "inst_rank", "inst_load",
+               "rank_load", "quota", "slot_inst", "slot_rank", "inst_offset", "rank_offset", "perm", "slot_pos")
+
+
+@pytest.fixture(scope="module")
+def mp():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    import load_balance_planning_amd as m
+    m.lib()
+    return m
+
+
+def small_outputs(layer):
+    r, p, d = layer.route_out, layer.plan_out, layer.dispatch_out
+    return dict(topk_idx=r.topk_idx, expert_count=r.expert_count, omega=r.omega, cooc=r.cooc, n_inst=p.n_inst,
+                inst_expert=p.inst_expert, inst_rank=p.inst_rank, inst_load=p.inst_load, rank_load=p.rank_load,
+                quota=p.quota, slot_inst=p.slot_inst, slot_rank=p.slot_rank, inst_offset=p.inst_offset,
+                rank_offset=p.rank_offset, perm=d.perm, slot_pos=d.slot_pos)
+
+
+def test_two_stream_pipeline_full_size(mp):
+    w = synth.WORKLOADS["deepseek_v3_layer"]
+    batches = [w, dataclasses.replace(w, seed=1)]
+    cfg = mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
+    ocfg = oracle.make_cfg(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
+    logits = [synth.logits(b) for b in batches]
+    hidden = synth.hidden(w)
+    want = []
+    for i, lg in enumerate(logits):
+        print("pipeline: oracle for batch %d" % i, flush=True)
+        want.append(oracle.run_all(ocfg, lg, None, want_cooc=True))
+    assert not np.array_equal(want[0]["slot_pos"], want[1]["slot_pos"])
+
+    dev = torch.device("cuda", torch.cuda.current_device())
+    hid = torch.from_numpy(hidden.view(np.int16)).to(dev)
+    lgs = [torch.from_numpy(lg).to(dev) for lg in logits]
+    layers = [mp.Layer(cfg, device=dev, cooc=True) for _ in range(2)]
+    streams = [torch.cuda.current_stream(dev), torch.cuda.Stream(dev)]
+    rng = np.random.default_rng(11)
+    rows = torch.from_numpy(rng.choice(w.T * w.k, 4096, replace=False).astype(np.int64)).to(dev)
+    torch.cuda.synchronize()
+    copies = []
+    n_steps = 6
+    print("pipeline: %d alternating steps on two streams" % n_steps, flush=True)
+    for s in range(n_steps):
+        i = s % 2
+        with torch.cuda.stream(streams[i]):
+            layers[i].step(lgs[i], hid)
+            snap = {k: v.clone() for k, v in small_outputs(layers[i]).items()}
+            snap["rows"] = layers[i].dispatch_out.dispatch.index_select(0, rows)
+            copies.append((i, snap))
+    torch.cuda.synchronize()
+    for layer in layers:
+        assert layer.status() == 0
+    rows_np = rows.cpu().numpy()
+    for s, (i, snap) in enumerate(copies):
+        o = want[i]
+        for k in INT_OUTPUTS:
+            ok = "count" if k == "expert_count" else k
+            np.testing.assert_array_equal(snap[k].cpu().numpy().reshape(-1), np.asarray(o[ok]).reshape(-1),
+                                          err_msg="step %d (handle %d): %s" % (s, i, k))
+        expect = hidden[o["perm"][rows_np] // w.k]
+        np.testing.assert_array_equal(snap["rows"].cpu().numpy().view(np.uint16), expect,
+                                      err_msg="step %d (handle %d): dispatch rows" % (s, i))
+    for layer in layers:
+        layer.close()
