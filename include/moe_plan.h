@@ -8,7 +8,7 @@
  *   moe_plan_hist      the histograms alone, from a given top-k
  *   moe_plan_plan      hot-expert replication + token re-routing
  *   moe_plan_dispatch  dispatch layout + bf16 row gather
- *   moe_plan_step      the four above in one call
+ *   moe_plan_step      route, plan and dispatch in one call
  *   moe_plan_combine   the return path: gate-weighted sum of expert outputs
  *   moe_plan_place     correlated expert placement from the co-selection counts
  *   moe_plan_dedup_count / moe_plan_dedup_dispatch
