@@ -44,6 +44,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -101,6 +102,11 @@ def inputs_sha(w) -> dict:
     for l, lg in enumerate(synth.all_logits(w)):
         out["logits_layer%d" % l] = hashlib.sha256(lg.tobytes()).hexdigest()[:16]
     return out
+
+
+def second_batch(w):
+    """The batch of the second handle: the workload's recipe with the next seed."""
+    return dataclasses.replace(w, seed=w.seed + 1)
 
 
 def dedup_bytes(w, n_rows: int) -> int:
@@ -195,9 +201,14 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     cfg = mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
     hidden = torch.from_numpy(synth.hidden(w).view(np.int16)).to(dev)
     logits = [torch.from_numpy(lg).to(dev) for lg in synth.all_logits(w)]
+    # The second handle's batch: the same recipe with the next seed, so that no
+    # step re-reads the inputs the step before it read.
+    w2 = second_batch(w)
+    batches = [(logits, hidden), ([torch.from_numpy(lg).to(dev) for lg in synth.all_logits(w2)],
+                                  torch.from_numpy(synth.hidden(w2).view(np.int16)).to(dev))]
     # Two batches in flight: consecutive steps alternate between two handles (each
-    # with its own buffers) on two streams, so the latency-bound route + plan of
-    # one batch overlaps the HBM-bound gather of the other.
+    # with its own buffers and batch) on two streams, so the latency-bound route +
+    # plan of one batch overlaps the HBM-bound gather of the other.
     sets = [[mp.Layer(cfg, device=dev, cooc=True, trans=(l > 0)) for l in range(w.L)] for _ in range(2)]
     layers = sets[0]
     stream = torch.cuda.current_stream(dev)
@@ -205,10 +216,11 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
 
     def step(i=0):
         # one pass of the whole path per layer: moe_plan_step (route + plan + dispatch in one call)
+        lgs, hid = batches[i]
         with torch.cuda.stream(streams[i]):
             for l, layer in enumerate(sets[i]):
                 prev = sets[i][l - 1].route_out.topk_idx if l > 0 else None
-                layer.step(logits[l], hidden, prev)
+                layer.step(lgs[l], hid, prev)
 
     def staged(ev):
         # the same pass as three calls, with events around each call
@@ -583,7 +595,7 @@ def main():
         "metric": "routed token-slots/sec for route+plan+dispatch; gather HBM GB/s vs peak",
         "value": value, "unit": "token-slots/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "pipeline": "2 batches in flight (two handles on two streams; consecutive steps alternate)",
+        "pipeline": "2 batches in flight (two handles on two streams, each with its own input batch; consecutive steps alternate)",
         "latency_ms_per_step": g["ms_serial"] / args.steps,
         "latency_us": {"median": float(np.median(g["step_ms"])) * 1e3, "min": float(np.min(g["step_ms"])) * 1e3,
                        "mean": float(np.mean(g["step_ms"])) * 1e3},
@@ -591,7 +603,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "R": w.R, "G": w.G, "H": w.H,
                    "replica_budget": w.B, "layers": w.L, "zipf_s": w.zipf_s, "beta": w.beta,
                    "couple_p": w.couple_p, "seed": w.seed, "cache_resident": working_set(w) < 256 * 2**20,
-                   "inputs_sha256_16": inputs_sha(w)},
+                   "inputs_sha256_16": inputs_sha(w), "second_batch_seed": second_batch(w).seed,
+                   "second_batch_sha256_16": inputs_sha(second_batch(w))},
         "roofline": {"bound": "hbm", "kernel": "gather (moe_plan_dispatch)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": ab["dispatch"],
