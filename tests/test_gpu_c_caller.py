@@ -27,7 +27,9 @@ OUTPUTS = {"topk_idx": np.int32, "topk_val": np.float32, "count": np.int32, "ome
 @pytest.mark.parametrize("shape", [(4096, 64, 4, 8, 4, 64, 8), (1600, 256, 8, 16, 8, 24, 16)])
 def test_c_caller_matches_the_oracle(tmp_path, shape):
     if not os.path.exists(EXE):  # built by __graft_entry__.build(); built here only when missing
+        import load_balance_planning_amd as m
         from tests import c_caller_build
+        m.lib()  # the library it links against
         c_caller_build.build()
     T, E, k, R, G, H, B = shape
     print("C caller T=%d E=%d k=%d R=%d G=%d H=%d B=%d" % shape, flush=True)
