@@ -46,9 +46,9 @@
  *     calls only enqueue work: they never allocate, never synchronise and
  *     never copy to the host.  One handle serves one stream at a time; calls
  *     on one stream run in order.  The handle owns one more stream of default
- *     priority: the calls that compute pair counts (cooc, trans) fork them
- *     onto it and join them back into `stream` within the same call, so every
- *     output is complete in `stream` order when the call's work ends.
+ *     priority: moe_plan_step forks its pair counts (cooc, trans) onto it and
+ *     joins them back into `stream` within the same call, so every output is
+ *     complete in `stream` order when the call's work ends.
  *   - A handle belongs to the HIP device that was current at moe_plan_create;
  *     each call runs on that device and gives the caller's current device
  *     back before it returns.  `stream` must belong to the handle's device.

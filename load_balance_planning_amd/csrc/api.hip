@@ -246,9 +246,10 @@ extern "C" int moe_plan_route(moe_plan_t h, const float* logits, const int32_t* 
   const int32_t* prev = (prev_topk && out->trans) ? prev_topk : nullptr;
   hipError_t e = moe::launch_route_topk(d, logits, prev, out->topk_idx, out->topk_val, out->tile_mask,
                                         h->ws.prev_mask, nullptr, h->ws.status, st);
-  if (e == hipSuccess) e = fork_pairs(h, out, prev, st);
-  if (e == hipSuccess) e = moe::launch_scan(d, out->tile_mask, out->tile_base, out->omega, out->expert_count, st);
-  if (e == hipSuccess) e = join_pairs(h, out, prev, st);
+  // scan and pair counts side by side in one launch: nothing else of the call would overlap them
+  if (e == hipSuccess)
+    e = moe::launch_scan_pairs(d, out->tile_mask, out->tile_base, out->omega, out->expert_count, h->ws.prev_mask,
+                               out->cooc, prev ? out->trans : nullptr, h->ws.pair_part, st);
   return hip_rc(e);
 }
 
@@ -262,9 +263,9 @@ extern "C" int moe_plan_hist(moe_plan_t h, const int32_t* topk_idx, const int32_
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* prev = (prev_topk && out->trans) ? prev_topk : nullptr;
   hipError_t e = moe::launch_build_masks(d, topk_idx, prev, out->tile_mask, h->ws.prev_mask, h->ws.status, st);
-  if (e == hipSuccess) e = fork_pairs(h, out, prev, st);
-  if (e == hipSuccess) e = moe::launch_scan(d, out->tile_mask, out->tile_base, out->omega, out->expert_count, st);
-  if (e == hipSuccess) e = join_pairs(h, out, prev, st);
+  if (e == hipSuccess)
+    e = moe::launch_scan_pairs(d, out->tile_mask, out->tile_base, out->omega, out->expert_count, h->ws.prev_mask,
+                               out->cooc, prev ? out->trans : nullptr, h->ws.pair_part, st);
   return hip_rc(e);
 }
 

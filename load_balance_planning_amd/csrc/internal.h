@@ -63,6 +63,11 @@ struct PairArgs {
 };
 PairArgs pair_args(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc, int32_t* trans,
                    int32_t* part, int nthr);
+// The scan of launch_scan and the pair counts of launch_pairs (nullable
+// outputs) in one launch plus the pairs' reduction, all on `st`.
+hipError_t launch_scan_pairs(const Dims& d, const uint64_t* tile_mask, int32_t* tile_base, int32_t* omega,
+                             int32_t* count, const uint64_t* prev_mask, int32_t* cooc, int32_t* trans, int32_t* part,
+                             hipStream_t st);
 
 // Launchers (all asynchronous on `st`).
 // omega_acc (nullable): also add each tile's per-expert counts to this [R][E]

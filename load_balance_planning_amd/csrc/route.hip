@@ -399,6 +399,21 @@ __global__ __launch_bounds__(kPairThreads) void pair_kernel(Dims d, PairArgs pa)
   pair_partial_block<kPairThreads>(d, pa, (int)blockIdx.z + pa.zbase, blockIdx.x, blockIdx.y, acc_s);
 }
 
+// The staged calls: the scan's workgroups first, then the pair-count
+// partials, in one launch of 1024-thread workgroups (no side stream).
+__global__ __launch_bounds__(1024) void scan_pair_kernel(Dims d, const uint64_t* __restrict__ tile_mask,
+                                                         int32_t* __restrict__ tile_base, int32_t* __restrict__ omega,
+                                                         int32_t* __restrict__ count, PairArgs pa, int n_scan) {
+  extern __shared__ int32_t smem_scan[];
+  if ((int)blockIdx.x < n_scan) {
+    tile_scan_block<1024>(d, tile_mask, tile_base, omega, count, blockIdx.x, smem_scan);
+    return;
+  }
+  const int q = (int)blockIdx.x - n_scan, nb = pair_blocks(d);
+  const int blk = q % nb, rest = q / nb;
+  pair_partial_block<1024>(d, pa, rest / pa.splits + pa.zbase, blk, rest % pa.splits, smem_scan);
+}
+
 __global__ __launch_bounds__(kPairThreads) void pair_reduce_kernel(Dims d, PairArgs pa) {
   pair_reduce_one(d, pa, (int)blockIdx.z + pa.zbase, blockIdx.x, blockIdx.y * kPairThreads + threadIdx.x);
 }
@@ -499,6 +514,29 @@ PairArgs pair_args(const Dims& d, const uint64_t* tile_mask, const uint64_t* pre
   pa.nz = (cooc ? 1 : 0) + (trans ? 1 : 0);
   pa.zbase = cooc ? 0 : 1;
   return pa;
+}
+
+hipError_t launch_scan_pairs(const Dims& d, const uint64_t* tile_mask, int32_t* tile_base, int32_t* omega,
+                             int32_t* count, const uint64_t* prev_mask, int32_t* cooc, int32_t* trans, int32_t* part,
+                             hipStream_t st) {
+  if (!cooc && !trans) return launch_scan(d, tile_mask, tile_base, omega, count, st);
+  const PairArgs pa = pair_args(d, tile_mask, prev_mask, cooc, trans, part, 1024);
+  const int n_scan = (d.E + kScanEB - 1) / kScanEB;
+  const int64_t n_pair = (int64_t)pair_blocks(d) * pa.splits * pa.nz;
+  size_t lds = scan_lds_bytes(d);
+  if (lds < sizeof(int32_t) * kPairBlock) lds = sizeof(int32_t) * kPairBlock;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_pair_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(scan_pair_kernel, dim3((unsigned)(n_scan + n_pair)), dim3(1024), lds, st, d, tile_mask, tile_base,
+                     omega, count, pa, n_scan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pa.splits == 1) return e;
+  hipLaunchKernelGGL(pair_reduce_kernel, dim3(pair_blocks(d), kPairBlock / kPairThreads, pa.nz), dim3(kPairThreads), 0,
+                     st, d, pa);
+  return hipGetLastError();
 }
 
 hipError_t launch_pairs(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc,
