@@ -45,10 +45,8 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  The compute
  *     calls only enqueue work: they never allocate, never synchronise and
  *     never copy to the host.  One handle serves one stream at a time; calls
- *     on one stream run in order.  The handle owns one more stream of default
- *     priority: moe_plan_step forks its pair counts (cooc, trans) onto it and
- *     joins them back into `stream` within the same call, so every output is
- *     complete in `stream` order when the call's work ends.
+ *     on one stream run in order; every output is complete in `stream` order
+ *     when the call's work ends.
  *   - A handle belongs to the HIP device that was current at moe_plan_create;
  *     each call runs on that device and gives the caller's current device
  *     back before it returns.  `stream` must belong to the handle's device.
@@ -364,12 +362,12 @@ int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const uint16_t* hi
 /*
  * One whole pass of the path in a single call: moe_plan_route, then
  * moe_plan_plan on its outputs, then moe_plan_dispatch -- the same outputs,
- * bit for bit, as the three calls in order.  Inside the call the tile prefix
- * and the routing-matrix output are computed by extra workgroups of the
- * solver launch, on the CUs the single solver workgroup leaves idle, and the
- * pair counts (route->cooc, route->trans) run on the handle's side stream,
- * overlapping the slot assignment and the gather; they are joined back into
- * `stream` within the call.  The call keeps no state in the handle from one
+ * bit for bit, as the three calls in order.  Inside the call the tile
+ * prefix, the routing-matrix output and the pair counts (route->cooc,
+ * route->trans) are computed by extra workgroups of the solver launch, on the
+ * CUs the single solver workgroup leaves idle (the pair counts' partial sums
+ * are added by extra workgroups of the quota launch), so every kernel of the
+ * call runs on `stream`.  The call keeps no state in the handle from one
  * call to the next (its routing-matrix accumulator is zero again when the
  * call's work ends), so it can be captured into a HIP graph and the graph
  * replayed, with the same pointers, in place of the call.  Sources: those of

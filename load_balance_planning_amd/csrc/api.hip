@@ -11,12 +11,6 @@ struct moe_plan {
   moe::Workspace ws;
   void* ws_base;
   size_t ws_bytes;
-  // The pair counts (co-selection, transitions) depend only on the presence
-  // masks and nothing later on the path reads them, so they run on a side
-  // stream of the handle, forked after the top-k and joined back into the
-  // caller's stream at the end of the call.
-  hipStream_t side;
-  hipEvent_t fork, join;
 };
 
 namespace {
@@ -176,42 +170,11 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
     delete h;
     return MOE_ERR_HIP;
   }
-  h->side = nullptr;
-  h->fork = h->join = nullptr;
-  if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
-      // both streams are on one device: a device-scope release is enough
-      hipEventCreateWithFlags(&h->fork, hipEventDisableTiming | hipEventReleaseToDevice) != hipSuccess ||
-      hipEventCreateWithFlags(&h->join, hipEventDisableTiming | hipEventReleaseToDevice) != hipSuccess) {
-    if (h->join) (void)hipEventDestroy(h->join);
-    if (h->fork) (void)hipEventDestroy(h->fork);
-    if (h->side) (void)hipStreamDestroy(h->side);
-    (void)hipFree(h->ws_base);
-    delete h;
-    return MOE_ERR_HIP;
-  }
   *out = h;
   return MOE_OK;
 }
 
 namespace {
-
-// Pair counts on the side stream: fork after the masks exist on `st`; the
-// caller joins (join_pairs) once everything else of the call is enqueued.
-hipError_t fork_pairs(moe_plan_t h, const moe_route_out* out, const int32_t* prev, hipStream_t st) {
-  if (!out->cooc && !(prev && out->trans)) return hipSuccess;
-  hipError_t e = hipEventRecord(h->fork, st);
-  if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
-  if (e == hipSuccess)
-    e = moe::launch_pairs(h->d, out->tile_mask, h->ws.prev_mask, out->cooc, prev ? out->trans : nullptr,
-                          h->ws.pair_part, h->side);
-  if (e == hipSuccess) e = hipEventRecord(h->join, h->side);
-  return e;
-}
-
-hipError_t join_pairs(moe_plan_t h, const moe_route_out* out, const int32_t* prev, hipStream_t st) {
-  if (!out->cooc && !(prev && out->trans)) return hipSuccess;
-  return hipStreamWaitEvent(st, h->join, 0);
-}
 
 int check_route_out(const moe::Dims& d, const moe_route_out* out) {
   if (!out || !out->expert_count || !out->omega) return MOE_ERR_INVALID_ARG;
@@ -276,7 +239,8 @@ extern "C" int moe_plan_plan(moe_plan_t h, const moe_route_out* route, const moe
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = moe::launch_plan(d, route->omega, nullptr, nullptr, nullptr, nullptr, *out, h->ws, st);
+  hipError_t e = moe::launch_plan(d, route->omega, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                  nullptr, *out, h->ws, st);
   if (e == hipSuccess)
     e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *out, h->ws, nullptr, 0, st);
   return hip_rc(e);
@@ -310,21 +274,18 @@ extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* p
   // On `st`: top-k (which also accumulates the routing matrix into the
   // workspace accumulator, zero on entry) -> plan (the solver reads the
   // accumulator; workgroups on the CUs it leaves idle write the tile prefix,
-  // the routing matrix and counts outputs) -> quotas (read the accumulator
-  // too) -> slot instances + gather, which zero the accumulator again: the
-  // handle carries no state from one call to the next, so the call can be
-  // captured in a HIP graph and replayed.  The pair counts, needed by nothing
-  // later, go to the side stream once the plan is enqueued -- forking earlier
-  // would put the fork's wait in front of the plan -- and overlap the slot
-  // assignment and the gather.
+  // the routing matrix and counts outputs and the pair-count partials) ->
+  // quotas (read the accumulator too; extra workgroups sum the pair-count
+  // partials) -> slot instances + gather, which zero the accumulator again:
+  // the handle carries no state from one call to the next, so the call can
+  // be captured in a HIP graph and replayed.
   const int64_t re = (int64_t)d.R * d.E;
   int32_t* acc = h->ws.omega_acc;
   hipError_t e = moe::launch_route_topk(d, logits, prev, route->topk_idx, route->topk_val, route->tile_mask,
                                         h->ws.prev_mask, acc, h->ws.status, st);
   if (e == hipSuccess)
-    e = moe::launch_plan(d, acc, route->tile_mask, route->tile_base, route->omega, route->expert_count, *plan, h->ws,
-                         st);
-  if (e == hipSuccess) e = fork_pairs(h, route, prev, st);
+    e = moe::launch_plan(d, acc, route->tile_mask, route->tile_base, route->omega, route->expert_count, h->ws.prev_mask,
+                         route->cooc, prev ? route->trans : nullptr, h->ws.pair_part, *plan, h->ws, st);
   if (moe::gather_can_assign(d, hidden, out->dispatch)) {
     // the gather assigns its token's slots itself, overlapping the row load
     if (e == hipSuccess)
@@ -337,7 +298,6 @@ extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* p
       e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm,
                              out->slot_pos, out->dispatch, h->ws, st);
   }
-  if (e == hipSuccess) e = join_pairs(h, route, prev, st);
   return hip_rc(e);
 }
 
@@ -484,9 +444,6 @@ extern "C" void moe_plan_destroy(moe_plan_t h) {
   const DeviceScope on_device(h->device);
   if (on_device.ok()) {
     (void)hipDeviceSynchronize();
-    (void)hipEventDestroy(h->join);
-    (void)hipEventDestroy(h->fork);
-    (void)hipStreamDestroy(h->side);
     (void)hipFree(h->ws_base);
   }
   delete h;

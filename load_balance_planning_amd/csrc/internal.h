@@ -63,8 +63,8 @@ struct PairArgs {
 };
 PairArgs pair_args(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc, int32_t* trans,
                    int32_t* part, int nthr);
-// The scan of launch_scan and the pair counts of launch_pairs (nullable
-// outputs) in one launch plus the pairs' reduction, all on `st`.
+// The scan of launch_scan and the pair counts of the masks (cooc, and trans
+// from prev_mask; nullable) in one launch plus the pairs' reduction, on `st`.
 hipError_t launch_scan_pairs(const Dims& d, const uint64_t* tile_mask, int32_t* tile_base, int32_t* omega,
                              int32_t* count, const uint64_t* prev_mask, int32_t* cooc, int32_t* trans, int32_t* part,
                              hipStream_t st);
@@ -80,15 +80,15 @@ hipError_t launch_build_masks(const Dims& d, const int32_t* topk_idx, const int3
 // omega / count nullable: then only the tile prefix is written.
 hipError_t launch_scan(const Dims& d, const uint64_t* tile_mask, int32_t* tile_base, int32_t* omega,
                        int32_t* count, hipStream_t st);
-hipError_t launch_pairs(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc,
-                        int32_t* trans, int32_t* part, hipStream_t st);
 // Solver, quotas and dispatch offsets from the routing matrix omega.  When
 // scan_mask is given, extra workgroups of the solver launch also write the
 // tile prefix of those masks to scan_base, the routing matrix and expert
-// counts recomputed from the masks to scan_omega / scan_count (each nullable).
+// counts recomputed from the masks to scan_omega / scan_count, and the pair
+// counts of those masks (and of prev_mask) to cooc / trans, reduced by extra
+// workgroups of the quota launch (each output nullable; part: workspace).
 hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan_mask, int32_t* scan_base,
-                       int32_t* scan_omega, int32_t* scan_count, const moe_plan_out& out, const Workspace& ws,
-                       hipStream_t st);
+                       int32_t* scan_omega, int32_t* scan_count, const uint64_t* prev_mask, int32_t* cooc,
+                       int32_t* trans, int32_t* part, const moe_plan_out& out, const Workspace& ws, hipStream_t st);
 // The slot assignment; it also zeroes clear[0, clear_n) (nullable), which no
 // kernel before it on the stream still reads.
 hipError_t launch_assign(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,

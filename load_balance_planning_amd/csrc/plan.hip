@@ -19,6 +19,7 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "pair_count.h"
 #include "slot_assign.h"
 #include "tile_scan.h"
 
@@ -508,10 +509,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
                                                             int32_t* __restrict__ scan_base,
                                                             int32_t* __restrict__ scan_omega,
                                                             int32_t* __restrict__ scan_count, moe_plan_out out,
-                                                            Workspace ws) {
+                                                            Workspace ws, PairArgs pa, int n_scan) {
   if (blockIdx.x > 0) {
     const int blk = blockIdx.x - 1;
-    tile_scan_block<kPlanThreads>(d, scan_mask, scan_base, scan_omega, scan_count, blk, plan_lds);
+    if (blk < n_scan) {
+      tile_scan_block<kPlanThreads>(d, scan_mask, scan_base, scan_omega, scan_count, blk, plan_lds);
+      return;
+    }
+    // pair-count partials (pair_count.h), summed by the quota launch
+    const int q = blk - n_scan, nb = pair_blocks(d);
+    pair_partial_block<kPlanThreads>(d, pa, (q / nb) / pa.splits + pa.zbase, q % nb, (q / nb) % pa.splits, plan_lds);
     return;
   }
   int32_t* lds = plan_lds;
@@ -832,9 +839,16 @@ __device__ void offsets_block(const Dims& d, const moe_plan_out& out, int32_t* s
 // computes the dispatch offsets.
 __global__ __launch_bounds__(kQuotaThreads) void quota_kernel(Dims d, const int32_t* __restrict__ omega,
                                                               moe_plan_out out, Workspace ws, int n_transport,
-                                                              int n_fill) {
+                                                              int n_fill, PairArgs pa) {
   const int E = d.E, R = d.R, G = d.G, cap = d.cap;
   const int tid = threadIdx.x;
+  if ((int)blockIdx.x > n_transport + n_fill) {  // the pair counts: sums of the solver launch's partials
+    constexpr int kChunks = kPairBlock / kQuotaThreads;
+    const int r = (int)blockIdx.x - (n_transport + n_fill + 1), nb = pair_blocks(d);
+    const int rest = r / nb;
+    pair_reduce_one(d, pa, rest / kChunks + pa.zbase, r % nb, (rest % kChunks) * kQuotaThreads + tid);
+    return;
+  }
   if ((int)blockIdx.x == n_transport + n_fill) {
     offsets_block(d, out, ws.status);
     return;
@@ -991,25 +1005,32 @@ PlanLayout plan_layout(const Dims& d) {
 size_t plan_lds_bytes(const Dims& d) { return sizeof(int32_t) * (size_t)plan_layout(d).total; }
 
 hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan_mask, int32_t* scan_base,
-                       int32_t* scan_omega, int32_t* scan_count, const moe_plan_out& out, const Workspace& ws,
-                       hipStream_t st) {
+                       int32_t* scan_omega, int32_t* scan_count, const uint64_t* prev_mask, int32_t* cooc,
+                       int32_t* trans, int32_t* part, const moe_plan_out& out, const Workspace& ws, hipStream_t st) {
   const PlanLayout ly = plan_layout(d);
   size_t lds = sizeof(int32_t) * (size_t)ly.total;
   const int n_scan = scan_mask ? (d.E + kScanEB - 1) / kScanEB : 0;
   if (n_scan > 0) lds = std::max(lds, tile_scan_lds_bytes(d, kPlanThreads));
+  // Pair counts from the masks: partials on the CUs the solver leaves idle,
+  // their sums in the quota launch (with one split the partials are final).
+  PairArgs pa = pair_args(d, scan_mask, prev_mask, cooc, trans, part, kPlanThreads);
+  if (!scan_mask) pa.nz = 0;
+  const int64_t n_pair = (int64_t)pair_blocks(d) * pa.splits * pa.nz;
+  const int64_t n_reduce = pa.splits > 1 ? (int64_t)pair_blocks(d) * (kPairBlock / kQuotaThreads) * pa.nz : 0;
+  if (n_pair > 0) lds = std::max(lds, sizeof(int32_t) * (size_t)kPairBlock);
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(plan_kernel, dim3(1 + n_scan), dim3(kPlanThreads), lds, st, d, ly, omega, scan_mask, scan_base,
-                     scan_omega, scan_count, out, ws);
+  hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(1 + n_scan + n_pair)), dim3(kPlanThreads), lds, st, d, ly, omega,
+                     scan_mask, scan_base, scan_omega, scan_count, out, ws, pa, n_scan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_transport = d.B < d.E ? d.B : d.E;  // each replicated expert owns at least one replica
   const int n_fill = (int)(((int64_t)d.R * d.cap + kFillCells - 1) / kFillCells);
-  hipLaunchKernelGGL(quota_kernel, dim3((unsigned)(n_transport + n_fill + 1)), dim3(kQuotaThreads), 0, st, d, omega,
-                     out, ws, n_transport, n_fill);
+  hipLaunchKernelGGL(quota_kernel, dim3((unsigned)(n_transport + n_fill + 1 + n_reduce)), dim3(kQuotaThreads), 0, st, d,
+                     omega, out, ws, n_transport, n_fill, pa);
   return hipGetLastError();
 }
 

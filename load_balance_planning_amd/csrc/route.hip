@@ -391,16 +391,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(Dims d, const uint64_t* __re
   tile_scan_block<1024>(d, tile_mask, tile_base, omega, count, blockIdx.x, smem_scan);
 }
 
-// Pair counts on their own: partial blocks, then their sums (pair_count.h).
+// Sums of the pair-count partials (pair_count.h), 256 threads per workgroup.
 constexpr int kPairThreads = 256;
 
-__global__ __launch_bounds__(kPairThreads) void pair_kernel(Dims d, PairArgs pa) {
-  __shared__ int32_t acc_s[kPairBlock];
-  pair_partial_block<kPairThreads>(d, pa, (int)blockIdx.z + pa.zbase, blockIdx.x, blockIdx.y, acc_s);
-}
-
 // The staged calls: the scan's workgroups first, then the pair-count
-// partials, in one launch of 1024-thread workgroups (no side stream).
+// partials, in one launch of 1024-thread workgroups.
 __global__ __launch_bounds__(1024) void scan_pair_kernel(Dims d, const uint64_t* __restrict__ tile_mask,
                                                          int32_t* __restrict__ tile_base, int32_t* __restrict__ omega,
                                                          int32_t* __restrict__ count, PairArgs pa, int n_scan) {
@@ -498,7 +493,7 @@ hipError_t launch_scan(const Dims& d, const uint64_t* tile_mask, int32_t* tile_b
 }
 
 size_t pair_part_words(const Dims& d) {
-  const int sp = pair_splits(d, kPairThreads);  // the larger of the two split counts used
+  const int sp = pair_splits(d, kPairThreads);  // bounds the split counts of 512- and 1024-thread workgroups
   return sp > 1 ? (size_t)2 * pair_blocks(d) * sp * kPairBlock : 0;
 }
 
@@ -532,19 +527,6 @@ hipError_t launch_scan_pairs(const Dims& d, const uint64_t* tile_mask, int32_t* 
   }
   hipLaunchKernelGGL(scan_pair_kernel, dim3((unsigned)(n_scan + n_pair)), dim3(1024), lds, st, d, tile_mask, tile_base,
                      omega, count, pa, n_scan);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pa.splits == 1) return e;
-  hipLaunchKernelGGL(pair_reduce_kernel, dim3(pair_blocks(d), kPairBlock / kPairThreads, pa.nz), dim3(kPairThreads), 0,
-                     st, d, pa);
-  return hipGetLastError();
-}
-
-hipError_t launch_pairs(const Dims& d, const uint64_t* tile_mask, const uint64_t* prev_mask, int32_t* cooc,
-                        int32_t* trans, int32_t* part, hipStream_t st) {
-  if (!cooc && !trans) return hipSuccess;
-  // slice 0 co-selection, slice 1 transitions; one launch covers the requested ones.
-  const PairArgs pa = pair_args(d, tile_mask, prev_mask, cooc, trans, part, kPairThreads);
-  hipLaunchKernelGGL(pair_kernel, dim3(pair_blocks(d), pa.splits, pa.nz), dim3(kPairThreads), 0, st, d, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pa.splits == 1) return e;
   hipLaunchKernelGGL(pair_reduce_kernel, dim3(pair_blocks(d), kPairBlock / kPairThreads, pa.nz), dim3(kPairThreads), 0,
