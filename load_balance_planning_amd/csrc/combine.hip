@@ -159,8 +159,13 @@ hipError_t launch_combine(const Dims& d, const float* topk_val, const int32_t* s
   if (d.T == 0) return hipSuccess;
   const bool vec = (d.H % 8) == 0 && ((uintptr_t)expert_out % 16) == 0 && ((uintptr_t)out % 16) == 0;
   if (vec) {
-    hipLaunchKernelGGL((combine_vec_kernel<4>), dim3(d.T), dim3(kCombThreads), 0, st, d, topk_val, slot_pos,
-                       reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(out), status);
+    // a row of at most kCombThreads vectors takes one round: no dead registers
+    if (d.H / 8 <= kCombThreads)
+      hipLaunchKernelGGL((combine_vec_kernel<1>), dim3(d.T), dim3(kCombThreads), 0, st, d, topk_val, slot_pos,
+                         reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(out), status);
+    else
+      hipLaunchKernelGGL((combine_vec_kernel<4>), dim3(d.T), dim3(kCombThreads), 0, st, d, topk_val, slot_pos,
+                         reinterpret_cast<const uint4*>(expert_out), reinterpret_cast<uint4*>(out), status);
   } else {
     hipLaunchKernelGGL(combine_u16_kernel, dim3(d.T), dim3(kCombThreads), 0, st, d, topk_val, slot_pos, expert_out,
                        out, status);

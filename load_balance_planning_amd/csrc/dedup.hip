@@ -120,7 +120,7 @@ struct GatherOut {
 
 // One workgroup per token (the grid has at least one workgroup, which also
 // writes the rank offsets when T = 0).
-template <bool VEC>
+template <bool VEC, int VPT>
 __global__ __launch_bounds__(256) void dedup_gather_kernel(Dims d, KeyMap km, const uint64_t* __restrict__ mask,
                                                            const int32_t* __restrict__ base,
                                                            const int32_t* __restrict__ rank_count,
@@ -134,7 +134,6 @@ __global__ __launch_bounds__(256) void dedup_gather_kernel(Dims d, KeyMap km, co
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool live = t < d.T;
   const int64_t N = (int64_t)d.T * d.k;
-  constexpr int VPT = 4;
   const int vpr = VEC ? d.H / 8 : d.H;
   uint4 v[VPT];
   if (VEC && live) {
@@ -263,11 +262,15 @@ hipError_t launch_dedup(const Dims& d, const int32_t* slot_key, const int32_t* k
   const GatherOut go{out.row_token, out.row_slots, out.slot_row, out.rank_row_offset, out.n_rows, ws.status};
   const bool vec = (d.H % 8) == 0 && ((uintptr_t)hidden % 16) == 0 && ((uintptr_t)out.ddispatch % 16) == 0;
   const dim3 grid(d.T > 0 ? d.T : 1);
-  if (vec)
-    hipLaunchKernelGGL(dedup_gather_kernel<true>, grid, dim3(256), 0, st, d, km, ws.dd_mask, ws.dd_base, ws.dd_count,
-                       hidden, out.ddispatch, go);
+  // a row of at most 256 vectors takes one store round: no dead registers
+  if (vec && d.H / 8 <= 256)
+    hipLaunchKernelGGL((dedup_gather_kernel<true, 1>), grid, dim3(256), 0, st, d, km, ws.dd_mask, ws.dd_base,
+                       ws.dd_count, hidden, out.ddispatch, go);
+  else if (vec)
+    hipLaunchKernelGGL((dedup_gather_kernel<true, 4>), grid, dim3(256), 0, st, d, km, ws.dd_mask, ws.dd_base,
+                       ws.dd_count, hidden, out.ddispatch, go);
   else
-    hipLaunchKernelGGL(dedup_gather_kernel<false>, grid, dim3(256), 0, st, d, km, ws.dd_mask, ws.dd_base,
+    hipLaunchKernelGGL((dedup_gather_kernel<false, 4>), grid, dim3(256), 0, st, d, km, ws.dd_mask, ws.dd_base,
                        ws.dd_count, hidden, out.ddispatch, go);
   return hipGetLastError();
 }

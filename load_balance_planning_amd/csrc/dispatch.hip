@@ -149,6 +149,11 @@ __global__ __launch_bounds__(256) void gather_u16_kernel(Dims d, const int32_t* 
   }
 }
 
+// A row of at most 256 vectors is one store round of the workgroup: the
+// VPT = 1 instantiation then carries no dead loads, stores or registers
+// (measured on MI355X: Qwen3-shaped step 160 -> 154 us, Mixtral-shaped 45 -> 32 us).
+bool one_round(const Dims& d) { return d.H / 8 <= 256; }
+
 }  // namespace
 
 hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t* slot_rank,
@@ -157,9 +162,14 @@ hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t*
   if (d.T == 0) return hipSuccess;
   const bool vec = (d.H % 8) == 0 && ((uintptr_t)hidden % 16) == 0 && ((uintptr_t)dispatch % 16) == 0;
   if (vec) {
-    hipLaunchKernelGGL((gather_vec_kernel<4, false>), dim3(d.T), dim3(256), 0, st, d, slot_inst, slot_rank,
-                       inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
-                       reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws);
+    if (one_round(d))
+      hipLaunchKernelGGL((gather_vec_kernel<1, false>), dim3(d.T), dim3(256), 0, st, d, slot_inst, slot_rank,
+                         inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                         reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws);
+    else
+      hipLaunchKernelGGL((gather_vec_kernel<4, false>), dim3(d.T), dim3(256), 0, st, d, slot_inst, slot_rank,
+                         inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                         reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws);
   } else {
     hipLaunchKernelGGL(gather_u16_kernel, dim3(d.T), dim3(256), 0, st, d, slot_inst, slot_rank, inst_offset, hidden,
                        perm, slot_pos, dispatch, ws.status);
@@ -178,9 +188,14 @@ hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const ui
   if (d.T == 0) return hipSuccess;
   const AssignIn as{topk_idx, tile_mask, tile_base, plan.quota, plan.slot_inst, plan.slot_rank, clear,
                     clear ? clear_n : 0};
-  hipLaunchKernelGGL((gather_vec_kernel<4, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr,
-                     plan.inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
-                     reinterpret_cast<uint4*>(dispatch), as, ws);
+  if (one_round(d))
+    hipLaunchKernelGGL((gather_vec_kernel<1, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr,
+                       plan.inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                       reinterpret_cast<uint4*>(dispatch), as, ws);
+  else
+    hipLaunchKernelGGL((gather_vec_kernel<4, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr,
+                       plan.inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                       reinterpret_cast<uint4*>(dispatch), as, ws);
   return hipGetLastError();
 }
 
