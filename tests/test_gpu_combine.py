@@ -84,7 +84,9 @@ def test_identity_experts_return_the_tokens_bit_exact(mp, name):
 
 
 @pytest.mark.parametrize("shape", [(4096, 64, 8, 8, 4, 512), (1536, 128, 6, 32, 8, 264), (640, 8, 2, 4, 2, 13),
-                                   (1152, 896, 16, 64, 8, 7168), (2048, 2048, 32, 256, 8, 24)])
+                                   (1152, 896, 16, 64, 8, 7168), (2048, 2048, 32, 256, 8, 24),
+                                   # rows of 256, 257 and 1025 vectors: the edges of the store rounds
+                                   (704, 64, 8, 8, 4, 2048), (704, 64, 8, 8, 4, 2056), (320, 64, 8, 8, 4, 8200)])
 def test_random_expert_outputs_against_the_oracle(mp, shape):
     T, E, k, R, G, H = shape
     cfg = mp.make_config(T, E, k, R, G, H, 2 * R)

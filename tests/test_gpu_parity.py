@@ -230,6 +230,22 @@ def test_ragged_tiles_and_odd_hidden(mp, shape):
         compare(got, want, "shape %s H=%d" % (shape, H))
 
 
+@pytest.mark.parametrize("H", [2048, 2056, 8200])
+@pytest.mark.parametrize("fused", [False, True])
+def test_row_rounds_of_the_gather(mp, H, fused):
+    """Rows at the edges of the gather's store rounds: 256 vectors (one round, the
+    one-vector-per-thread instantiation), 257 (the four-vector one with a ragged
+    second vector) and 1025 (two passes of four vectors, the second one vector
+    long), through the staged dispatch and the assigning gather of the step."""
+    T, E, k, R, G = 704, 64, 8, 8, 4
+    cfg = mp.make_config(T, E, k, R, G, H, 8)
+    lg = inputs.random_logits(H + fused, T, E)
+    hid = inputs.random_hidden(H, T, H)
+    print("row rounds H=%d fused=%s" % (H, fused), flush=True)
+    compare(gpu_layer(mp, cfg, logits=lg, hidden=hid, fused=fused), oracle_layer(cfg, logits=lg, hidden=hid),
+            "H=%d fused=%s" % (H, fused))
+
+
 def test_ties_signed_zero_and_infinities(mp):
     T, E, k, R, G = 256, 64, 8, 4, 2
     lg = inputs.random_logits(9, T, E, ties=True)

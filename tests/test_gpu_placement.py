@@ -123,7 +123,9 @@ def run_dedup(mp, layer, keys, table, hidden):
 
 @pytest.mark.parametrize("shape", [(256, 16, 3, 4, 2, 8, 2), (640, 24, 4, 8, 4, 13, 4), (4096, 64, 8, 8, 4, 64, 8),
                                    (1152, 96, 16, 32, 8, 24, 16), (192, 8, 8, 4, 2, 16, 0), (0, 8, 2, 4, 2, 8, 1),
-                                   (130, 10, 3, 1, 1, 8, 0), (300, 10, 2, 10, 5, 8, 3), (2048, 2048, 32, 256, 8, 8, 1024)])
+                                   (130, 10, 3, 1, 1, 8, 0), (300, 10, 2, 10, 5, 8, 3), (2048, 2048, 32, 256, 8, 8, 1024),
+                                   # rows of 256, 257 and 1025 vectors: the edges of the store rounds
+                                   (704, 64, 8, 8, 4, 2048, 8), (704, 64, 8, 8, 4, 2056, 8), (320, 64, 8, 8, 4, 8200, 8)])
 @pytest.mark.parametrize("kind", ["contiguous", "placed", "instances", "random"])
 def test_dedup_against_the_oracle(mp, shape, kind):
     T, E, k, R, G, H, B = shape
