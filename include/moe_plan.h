@@ -69,7 +69,7 @@ extern "C" {
 enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size or inconsistent configuration */
-  MOE_ERR_UNSUPPORTED = -2, /* valid but beyond this build's limits (see moe_plan_create) */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but beyond the library's limits (see moe_plan_create) */
   MOE_ERR_HIP = -3,         /* a HIP runtime call failed */
   MOE_ERR_NONFINITE = -4,   /* status flag: a gate logit was NaN */
   MOE_ERR_INTERNAL = -5     /* status flag: an internal consistency check failed on the device */
@@ -294,7 +294,7 @@ int moe_plan_query(const moe_plan_config* cfg, moe_plan_sizes* sizes);
 
 /*
  * Validate cfg, bind the current HIP device and allocate the handle's
- * workspace (it may synchronise).  Limits of this build: E <= 2048, k <= 32,
+ * workspace (it may synchronise).  Limits of the library: E <= 2048, k <= 32,
  * R <= 256, G <= 64, B <= 1024, E/R + N_slot <= 1024, T*k < 2^31, H >= 1.
  * On success *out is a new handle; on error *out is NULL.
  */

@@ -8,7 +8,7 @@
 
 namespace moe {
 
-// Limits of this build (checked by moe_plan_create).
+// Limits of the library (checked by moe_plan_create).
 constexpr int kMaxE = 2048;
 constexpr int kMaxK = 32;
 constexpr int kMaxR = 256;
