@@ -45,6 +45,13 @@ MUTANTS = [
      "if (is_new && !(rep_dom[m] < Bd)) continue;"),
     ("replicas listed before mains", "      if (main_of(d, e) == r) inst_of[e * R + r] = n++;\n    for (int64_t e = 0; e < E; ++e)\n      if (X(e, r) && main_of(d, e) != r) inst_of[e * R + r] = n++;",
      "      if (X(e, r) && main_of(d, e) != r) inst_of[e * R + r] = n++;\n    for (int64_t e = 0; e < E; ++e)\n      if (main_of(d, e) == r) inst_of[e * R + r] = n++;"),
+    ("stage 1 most occupied rank", "if (best < 0 || nrep[r] < nrep[best]) best = r;",
+     "if (best < 0 || nrep[r] > nrep[best]) best = r;"),
+    ("quota sources descending", "      for (int64_t s = 0; s < R; ++s)\n        for (size_t a = 0; a < insts.size(); ++a) {",
+     "      for (int64_t s = R - 1; s >= 0; --s)\n        for (size_t a = 0; a < insts.size(); ++a) {"),
+    ("quota instances in reverse rank order",
+     "      for (int64_t s = 0; s < R; ++s)\n        for (size_t a = 0; a < insts.size(); ++a) {",
+     "      for (int64_t s = 0; s < R; ++s)\n        for (size_t a = insts.size(); a-- > 0;) {"),
     ("quota without the same-rank pass", "bool ok = pass == 0 ? (r == s) :", "bool ok = pass == 0 ? (dom_of(c, r) == dom_of(c, s)) :"),
     ("quota without the same-domain pass", ": pass == 1 ? (dom_of(c, r) == dom_of(c, s)) : true;", ": pass == 1 ? true : true;"),
     ("slot walk off by one", "if (run > p) chosen = i;", "if (run >= p) chosen = i;"),

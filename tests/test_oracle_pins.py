@@ -191,6 +191,49 @@ def test_even_split_example():
     assert list(d["rank_offset"]) == ex["rank_offset"]
 
 
+def check_golden_plan(cfg, p, ex):
+    assert oracle.params(cfg)["n_slot"] == ex["n_slot"]
+    assert list(p["rank_load_stage1"]) == ex["rank_load_stage1"]
+    assert list(p["rank_load"]) == ex["rank_load"]
+    assert moves(p) == ex["refinement_moves"]
+    assert int(p["n_inst"][0]) == ex["n_inst"]
+    assert list(p["inst_expert"]) == ex["inst_expert"]
+    assert list(p["inst_rank"]) == ex["inst_rank"]
+    assert list(p["inst_load"]) == ex["inst_load"]
+    assert quota_nonzero(p) == ex["quota_nonzero"]
+
+
+def test_stage1_spread_example():
+    """TopoEP section 4.3: inter-node replicas go to the least occupied rank with a free slot.
+    With two slots per rank, three replicas of one domain spread over its two ranks (hand-derived)."""
+    g = json.load(open(os.path.join(GOLDEN, "stage1_spread_example.json")))
+    cfg, p = run_plan_from_omega(g["config"], g["omega"])
+    ex = g["expected"]
+    check_golden_plan(cfg, p, ex)
+    assert [list(x) for x in sorted(stage1_replicas(cfg, p))] == ex["stage1_replicas"]
+    for v in g["variants"]:
+        cfg2, p2 = run_plan_from_omega(g["config"], g["omega"], **v["override"])
+        assert [list(x) for x in sorted(stage1_replicas(cfg2, p2))] == v["stage1_replicas"], v["what"]
+        assert list(p2["rank_load_stage1"]) == v["rank_load_stage1"], v["what"]
+        assert list(p2["rank_load"]) == v["rank_load"], v["what"]
+        assert moves(p2) == v["refinement_moves"], v["what"]
+
+
+def test_quota_order_example():
+    """Quota transport (the reading of TopoEP section 4.3's routing): two sources of a domain
+    compete for residual capacity on two instances in the same-domain pass, and two sources of
+    another domain for two instances in the cross-domain pass (hand-derived)."""
+    g = json.load(open(os.path.join(GOLDEN, "quota_order_example.json")))
+    cfg, p = run_plan_from_omega(g["config"], g["omega"])
+    ex = g["expected"]
+    check_golden_plan(cfg, p, ex)
+    G = cfg.G
+    cross = sum(int(p["quota"][s, i]) for s in range(cfg.R) for i in range(int(p["n_inst"][0]))
+                if s // G != p["inst_rank"][i] // G)
+    assert cross == ex["cross_domain_assignments"]
+    check_quota_passes(cfg, {"omega": np.asarray(g["omega"], np.int32)}, p)
+
+
 def test_fig3_traffic_arithmetic_and_benefit_sign():
     """TopoEP section 2.3, Fig. 3: N = 4096 tokens of 2,048-wide bf16 activations, 9 MiB of
     parameters per expert; 64 MiB of token traffic versus 18 MiB + 9 MiB (about 2.4x).
@@ -315,6 +358,51 @@ def check_quota_locality(cfg, r, p):
         assert cross == want
 
 
+def comonotone_ok(F, dem, cap) -> bool:
+    """F is the north-west-corner (comonotone) coupling of dem and cap in the given orders: the flow
+    from the first a sources to the first b sinks is min(sum of their demands, sum of their capacities)."""
+    F = np.asarray(F, np.int64)
+    if F.size == 0:
+        return True
+    want = np.minimum.outer(np.cumsum(dem), np.cumsum(cap))
+    return bool((F >= 0).all() and np.array_equal(F.cumsum(0).cumsum(1), want))
+
+
+def check_quota_passes(cfg, r, p):
+    """The quota reading, pass by pass, from the final quota matrix alone.  Flows on the source's own
+    rank are pass A; other flows inside a domain pass B; flows across domains pass C (a pass cannot
+    add to a pair whose demand or capacity an earlier pass emptied).  Pass A takes min(demand,
+    load) on the source's own rank; passes B (per domain) and C (all) are the comonotone couplings
+    of the residual demands, sources ascending, with the residual loads, instances in rank order."""
+    G, R = cfg.G, cfg.R
+    M = R // G
+    n = int(p["n_inst"][0])
+    q = p["quota"].astype(np.int64)
+    omega = np.asarray(r["omega"]).astype(np.int64)
+    for e in range(cfg.E):
+        cols = [i for i in range(n) if p["inst_expert"][i] == e]
+        ranks = [int(p["inst_rank"][i]) for i in cols]
+        assert ranks == sorted(ranks)
+        dem = omega[:, e].copy()
+        cap = np.array([int(p["inst_load"][i]) for i in cols], np.int64)
+        for a, rr in enumerate(ranks):  # pass A
+            f = int(q[rr, cols[a]])
+            assert f == min(dem[rr], cap[a])
+            dem[rr] -= f
+            cap[a] -= f
+        for m in range(M):  # pass B, domain by domain
+            S = list(range(m * G, (m + 1) * G))
+            A = [a for a in range(len(cols)) if ranks[a] // G == m]
+            F = np.array([[0 if s == ranks[a] else int(q[s, cols[a]]) for a in A] for s in S], np.int64)
+            assert comonotone_ok(F, dem[S], cap[A]), (e, m)
+            dem[S] -= F.sum(1)
+            cap[A] -= F.sum(0)
+        F = np.array([[int(q[s, cols[a]]) if s // G != ranks[a] // G else 0 for a in range(len(cols))]
+                      for s in range(R)], np.int64)  # pass C
+        assert comonotone_ok(F, dem, cap), e
+        assert (dem - F.sum(1) == 0).all() and (cap - F.sum(0) == 0).all()
+
+
 def replay_refinement(cfg, r, p):
     """Undo the recorded refinement moves from the final state, then replay them forward and
     check each against a brute-force enumeration of the candidates of Eq. 10."""
@@ -395,6 +483,7 @@ def test_plan_properties_random(case):
     cfg, r, p = random_case(cfgd, case)
     check_plan_invariants(cfg, r, p)
     check_quota_locality(cfg, r, p)
+    check_quota_passes(cfg, r, p)
     replay_refinement(cfg, r, p)
 
 
@@ -404,17 +493,25 @@ def stage1_replicas(cfg, p):
     return {(e, rr) for (e, rr) in placement(cfg, p) if rr != e // prm["Er"]} - created
 
 
-@pytest.mark.parametrize("case", range(30))
+@pytest.mark.parametrize("case", range(40))
 def test_stage1_exhaustive(case):
     """Inter-node placement: positive-benefit remote experts only, budget and slots respected,
-    and the chosen set has the largest total benefit of any admissible set (enumerated)."""
+    and the chosen set has the largest total benefit of any admissible set (enumerated).  With
+    several ranks per domain and up to three slots per rank, "least occupied rank with a free
+    slot, ties to the lower rank" starting from empty ranks is a round robin: the j-th replica of
+    a domain (descending benefit, ties to the lower expert) lands on the domain's rank j mod G."""
     g = inputs.rng(500 + case)
-    G = int(g.choice([1, 2])); M = int(g.choice([2, 3])); R = G * M
+    G = int(g.choice([1, 2, 3, 4])); M = int(g.choice([2, 3])); R = G * M
     Er = int(g.choice([1, 2])); E = R * Er
-    k = int(g.integers(1, min(E, 3) + 1)); Tr = int(g.integers(4, 20)); T = Tr * R
-    B = int(g.integers(0, 2 * M + 1)); W = int(g.choice([0, 3, 9]))
-    cfg = oracle.make_cfg(T, E, k, R, G, 4, B, int(g.choice([0, 1])), W, 1, 0)
-    topk = inputs.random_topk(case, T, E, k, skew=2.0)
+    k = int(g.integers(1, min(E, 4) + 1)); Tr = int(g.integers(4, 20)); T = Tr * R
+    n_slot = int(g.choice([0, 1, 2, 3]))
+    B = int(g.integers(0, 3 * R + 1)); W = int(g.choice([0, 3, 9]))
+    stacked = case >= 30  # domains that must place more replicas than they have ranks
+    if stacked:
+        G, Er = max(G, 2), 2; R = G * M; E = R * Er; T = max(Tr, 10) * R; k = min(4, E)
+        n_slot, B, W = int(g.choice([2, 3])), 3 * R, 0
+    cfg = oracle.make_cfg(T, E, k, R, G, 4, B, n_slot, W, 1, 0)
+    topk = inputs.random_topk(case, T, E, k, skew=0.3 if stacked else 2.0)
     lg = np.zeros((T, E), np.float32)
     for j in range(k):
         lg[np.arange(T), topk[:, j]] = np.float32(k - j)
@@ -423,6 +520,7 @@ def test_stage1_exhaustive(case):
     prm = oracle.params(cfg)
     S1 = stage1_replicas(cfg, p)
     omega = r["omega"].astype(np.int64)
+    placed_beyond_ranks = False
     for m in range(M):
         Dm = omega[m * G:(m + 1) * G].sum(0)
         b = {e: 2 * int(Dm[e]) * prm["S"] - prm["W"] for e in range(E) if (e // Er) // G != m}
@@ -431,12 +529,22 @@ def test_stage1_exhaustive(case):
         chosen = [e for (e, rr) in S1 if rr // G == m]
         assert all(e in pos for e in chosen)
         assert len(chosen) == min(cap, len(pos))
-        best = max((sum(b[e] for e in sub) for size in range(0, cap + 1)
-                    for sub in itertools.combinations(pos, min(size, len(pos)))), default=0)
-        assert sum(b[e] for e in chosen) == best
-        # least-occupied ranks: the domain's stage-1 replicas are spread round-robin from its lowest rank
-        per_rank = [sum(1 for (_, rr) in S1 if rr == x) for x in range(m * G, (m + 1) * G)]
-        assert per_rank == sorted(per_rank, reverse=True) and max(per_rank, default=0) - min(per_rank, default=0) <= 1
+        # the largest total benefit over every admissible subset (greedy by benefit is optimal
+        # under a cardinality cap; the enumeration confirms it on these small domains)
+        top = sorted(pos, key=lambda e: -b[e])[:cap]
+        if len(pos) <= 14:
+            best = max((sum(b[e] for e in sub) for size in range(0, cap + 1)
+                        for sub in itertools.combinations(pos, min(size, len(pos)))), default=0)
+            assert best == sum(b[e] for e in top)
+        assert sum(b[e] for e in chosen) == sum(b[e] for e in top)
+        # where each replica went: round robin over the domain's ranks in placement order
+        order = sorted(chosen, key=lambda e: (-b[e], e))
+        where = {e: rr for (e, rr) in S1 if rr // G == m}
+        assert [where[e] for e in order] == [m * G + j % G for j in range(len(order))]
+        assert max([sum(1 for (_, rr) in S1 if rr == x) for x in range(m * G, (m + 1) * G)]) <= prm["n_slot"]
+        placed_beyond_ranks = placed_beyond_ranks or len(order) > G
+    if stacked:
+        assert placed_beyond_ranks  # a second slot of some rank was used
 
 
 def test_single_domain_has_no_inter_node_stage():
