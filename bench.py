@@ -8,12 +8,20 @@ between two handles on two streams, so one batch's route + plan overlaps the
 previous batch's gather; latency_ms_per_step gives the same steps run one at
 a time on one stream.  Prints ONE JSON line:
   value       routed token-slots per second (T*k*L / step time)
-  roofline    the dominant kernel (the bf16 gather, the one kernel of
-              moe_plan_dispatch): algorithmic bytes per launch / its mean
-              duration (HIP events around moe_plan_dispatch on the stream it
-              runs on, in a second pass of the same steps as three calls)
-              against the 8 TB/s HBM peak
-  chain       the same for the whole step (algorithmic bytes of every call)
+  roofline    the dominant kernel (the bf16 row copy of moe_plan_step, which
+              also assigns the slots): the row bytes per launch (hidden rows
+              read once, dispatch rows written) / its mean duration, from HIP
+              events the library records right around that kernel's launch
+              (moe_plan_set_events) in a one-stream pass of the same steps
+              of its own,
+              against the 8 TB/s HBM peak; `traffic` is the profiler's byte
+              count for the kernel, read from the committed counter summary
+              named in `traffic_source` while it describes the current source
+  chain       the same for the whole step (the method's bytes of every call:
+              logits, top-k, histograms, quotas, permutation, rows)
+  configs     the other four workloads: step time with two batches in flight
+              and one at a time, the chain's and the gather's share of the
+              HBM peak, and whether the layer fits the 256 MB Infinity Cache
   combine     the return path (moe_plan_combine) on the same layer, timed
               separately with the dispatch buffer as the expert outputs
   placement   correlated expert placement (moe_plan_place) from the first
@@ -66,28 +74,24 @@ GATHER_PMC = os.path.join(ROOT, "profiles", "gather_deepseek_v3_layer_pmc.txt")
 
 
 def algorithmic_bytes(w) -> dict:
-    """Bytes each call must move per layer (the dense alternatives it avoids are not counted)."""
-    T, E, k, R, H, B = w.T, w.E, w.k, w.R, w.H, w.B
-    cap = E + B
-    tiles = R * ((T // R + 63) // 64)
-    route = (T * E * 4                 # logits read
-             + T * k * 4 * 2           # top-k indices and values written
-             + tiles * E * 8 * 2       # presence masks written, re-read by the scan
-             + tiles * E * 4           # tile prefix written
-             + (R * E + E) * 4         # routing matrix and expert counts
-             + E * E * 4 * (2 if w.L > 1 else 1))  # co-selection (+ transitions)
-    plan = (R * E * 4                  # routing matrix read
-            + R * cap * 4              # quotas written
-            + T * k * 4                # top-k re-read
-            + tiles * E * 12           # masks and prefix re-read
-            + T * k * 4 * 2)           # slot instance and in-instance rank written
-    dispatch = (T * H * 2              # hidden rows read once
-                + T * k * H * 2        # dispatch rows written
-                + T * k * 4 * 4)       # slot instance/rank read, slot position and permutation written
+    """Bytes the method itself must move per step (every layer), call by call: logits read,
+    top-k written and re-read across the plan's grid-wide dependency, the routing matrix,
+    expert counts, co-selection (and transition) counts, the quotas, the permutation, the
+    hidden rows read once and the dispatch rows written.  Implementation traffic (the
+    presence masks, tile prefixes, per-slot instances) and the dense alternatives the path
+    avoids are not counted.  `gather` is the row copy alone: hidden rows read once plus the
+    dispatch rows written."""
+    T, E, k, R, H, B, L = w.T, w.E, w.k, w.R, w.H, w.B, w.L
+    route_layer = T * E * 4 + T * k * 4 + (R * E + E + E * E) * 4
+    route = route_layer * L + E * E * 4 * (L - 1)  # transition counts for every layer after the first
+    plan = (T * k * 4 + R * (E + B) * 4) * L
+    gather = T * H * 2 + T * k * H * 2
+    dispatch = (gather + T * k * 4) * L
     combine = (T * k * H * 2             # expert output rows read
                + T * H * 2             # combined rows written
                + T * k * 4 * 2)        # selected logits and slot positions read
-    return dict(route=route, plan=plan, dispatch=dispatch, combine=combine, total=(route + plan + dispatch) * w.L)
+    return dict(route=route, plan=plan, dispatch=dispatch, gather=gather, combine=combine,
+                total=route + plan + dispatch)
 
 
 def working_set(w) -> int:
@@ -128,17 +132,23 @@ def source_hash(path: str) -> str:
 
 
 def gather_traffic(w):
-    """HBM bytes per gather launch from the committed rocprofv3 counter runs, if they still
-    describe the current kernel source (else None)."""
+    """HBM bytes per gather launch as measured by the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, each in a run of its own, scaled by a plain copy), if they
+    still describe the current kernel source; else None.  Returns (bytes, source note)."""
     if w.name != DEFAULT_WORKLOAD or not os.path.exists(GATHER_PMC):
-        return None
+        return None, None
     text = open(GATHER_PMC).read()
     m = re.search(r"source_sha256_16:\s*(\w+)", text)
     src = os.path.join(ROOT, "load_balance_planning_amd", "csrc", "dispatch.hip")
+    rel = os.path.relpath(GATHER_PMC, ROOT)
     if not m or m.group(1) != source_hash(src):
-        return None
+        return None, "%s describes another dispatch.hip (source %s, now %s): not used" % (
+            rel, m.group(1) if m else "?", source_hash(src))
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    return float(t.group(1)) if t else None
+    if not t:
+        return None, None
+    return float(t.group(1)), "%s (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this bench; dispatch.hip " \
+                             "sha256 %s), not measured in this run" % (rel, m.group(1))
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -193,11 +203,15 @@ def cpu_baseline(w, budget_s: float) -> dict:
             "stage_ms_median_of_3": {k: float(np.median(v)) * 1e3 for k, v in stages.items()}}
 
 
-def run_gpu(w, steps: int, warmup: int) -> dict:
+def time_path(w, steps: int, warmup: int, dev, keep: bool = False) -> dict:
+    """The timed passes of one workload: `steps` steps with two batches in flight (the headline
+    configuration), the same steps one at a time on one stream with the gather kernel of every
+    moe_plan_step bracketed by HIP events (moe_plan_set_events), and the same steps as three
+    calls per layer with events around each call and around the gather kernel of
+    moe_plan_dispatch.  With keep, the first batch's layers and inputs stay open for further
+    measurements (else everything is freed)."""
     import torch
     import load_balance_planning_amd as mp
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
     cfg = mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
     hidden = torch.from_numpy(synth.hidden(w).view(np.int16)).to(dev)
     logits = [torch.from_numpy(lg).to(dev) for lg in synth.all_logits(w)]
@@ -222,18 +236,6 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
                 prev = sets[i][l - 1].route_out.topk_idx if l > 0 else None
                 layer.step(lgs[l], hid, prev)
 
-    def staged(ev):
-        # the same pass as three calls, with events around each call
-        for l, layer in enumerate(layers):
-            prev = layers[l - 1].route_out.topk_idx if l > 0 else None
-            ev[l][0].record(stream)
-            layer.route(logits[l], prev)
-            ev[l][1].record(stream)
-            layer.plan()
-            ev[l][2].record(stream)
-            layer.dispatch(hidden)
-            ev[l][3].record(stream)
-
     for s_ in range(warmup):
         step(s_ % 2)
     torch.cuda.synchronize()
@@ -255,32 +257,116 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
+
+    def event_pairs(n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:  # torch creates the HIP event on its first record
+            a.record(stream)
+            b.record(stream)
+        return ev
+
     # The same steps one at a time on one stream: the latency of a step.
-    lev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    lev[0].record(stream)
-    for s_ in range(steps):
-        step(0)
-        lev[s_ + 1].record(stream)
-    torch.cuda.synchronize()
+    def one_stream(gev=None):
+        lev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        lev[0].record(stream)
+        for s_ in range(steps):
+            for l, layer in enumerate(layers):
+                if gev is not None:
+                    layer.time_gather(*gev[s_ * w.L + l])
+                prev = layers[l - 1].route_out.topk_idx if l > 0 else None
+                layer.step(logits[l], hidden, prev)
+            lev[s_ + 1].record(stream)
+        torch.cuda.synchronize()
+        return lev
+
+    lev = one_stream()
     step_ms = [lev[i].elapsed_time(lev[i + 1]) for i in range(steps)]
     ms_serial = lev[0].elapsed_time(lev[steps])
+    # Again, with the gather kernel of every moe_plan_step (the assigning gather)
+    # bracketed by events the library records right around its launch.
+    gev = event_pairs(steps * w.L)
+    one_stream(gev)
+    for layer in layers:
+        layer.time_gather()
+    step_gather_ms = [a.elapsed_time(b) for a, b in gev]
     for layer in sets[1]:
         if layer.status() != 0:
             raise RuntimeError("device status word set on the second handle")
         layer.close()
-    # Per-call durations from events around each call, in a second timed pass of the same steps.
+    # Per-call durations from events around each call, in a third pass of the same
+    # steps as three calls, and the gather kernel of moe_plan_dispatch alone.
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(w.L)] for _ in range(steps)]
+    dev_ = event_pairs(steps * w.L)
     torch.cuda.synchronize()
-    for s in range(steps):
-        staged(evs[s])
+    for s_ in range(steps):
+        for l, layer in enumerate(layers):
+            e = evs[s_][l]
+            prev = layers[l - 1].route_out.topk_idx if l > 0 else None
+            e[0].record(stream)
+            layer.route(logits[l], prev)
+            e[1].record(stream)
+            layer.plan()
+            e[2].record(stream)
+            layer.time_gather(*dev_[s_ * w.L + l])
+            layer.dispatch(hidden)
+            e[3].record(stream)
     torch.cuda.synchronize()
+    for layer in layers:
+        layer.time_gather()
     per = {"route": [], "plan": [], "dispatch": []}
-    for s in range(steps):
+    for s_ in range(steps):
         for l in range(w.L):
-            e = evs[s][l]
+            e = evs[s_][l]
             per["route"].append(e[0].elapsed_time(e[1]))
             per["plan"].append(e[1].elapsed_time(e[2]))
             per["dispatch"].append(e[2].elapsed_time(e[3]))
+    out = dict(ms_total=ms_total, ms_serial=ms_serial, step_ms=step_ms,
+               step_gather_ms=float(np.mean(step_gather_ms)), dispatch_gather_ms=float(np.mean([a.elapsed_time(b) for a, b in dev_])),
+               per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
+               per_call_ms_median={k: float(np.median(v)) for k, v in per.items()},
+               per_call_ms_min={k: float(np.min(v)) for k, v in per.items()})
+    if keep:
+        out.update(layers=layers, logits=logits, hidden=hidden, cfg=cfg)
+    else:
+        status = [layer.status() for layer in layers]
+        for layer in layers:
+            layer.close()
+        if any(status):
+            out["status_flags"] = status
+        del batches, logits, hidden
+        torch.cuda.empty_cache()
+    return out
+
+
+def config_line(w, steps: int, warmup: int, dev) -> dict:
+    """The headline measurements of one more workload, for the line's `configs` object."""
+    t = time_path(w, steps, warmup, dev)
+    ab = algorithmic_bytes(w)
+    ms = t["ms_total"] / steps
+    lat = t["ms_serial"] / steps
+    out = {"T": w.T, "E": w.E, "k": w.k, "R": w.R, "G": w.G, "H": w.H, "replica_budget": w.B, "layers": w.L,
+           "value": w.T * w.k * w.L / (ms / 1e3), "unit": "token-slots/s", "ms_per_step": ms,
+           "latency_ms_per_step": lat, "latency_us_median": float(np.median(t["step_ms"])) * 1e3,
+           "chain_algorithmic_bytes": ab["total"],
+           "chain_frac": ab["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+           "chain_frac_one_stream": ab["total"] / (lat / 1e3) / 1e9 / HBM_PEAK_GBS,
+           "gather_us": t["step_gather_ms"] * 1e3, "gather_algorithmic_bytes": ab["gather"],
+           "gather_frac": ab["gather"] / (t["step_gather_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+           "cache_resident": working_set(w) < 256 * 2**20}
+    if "status_flags" in t:
+        out["status_flags"] = t["status_flags"]
+    return out
+
+
+def run_gpu(w, steps: int, warmup: int) -> dict:
+    import torch
+    import load_balance_planning_amd as mp
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t = time_path(w, steps, warmup, dev, keep=True)
+    layers, logits, hidden, cfg = t["layers"], t["logits"], t["hidden"], t["cfg"]
+    stream = torch.cuda.current_stream(dev)
     # Combine (the return path): the dispatch buffer stands in for the expert outputs.
     comb_out = [torch.empty((w.T, w.H), dtype=torch.int16, device=dev) for _ in layers]
     for l, layer in enumerate(layers):
@@ -399,13 +485,12 @@ def run_gpu(w, steps: int, warmup: int) -> dict:
     static.close()
     dinfo = mp.moe_plan_device_info(0)
     copy = copy_reference(1 << 30, 10)
-    return dict(ms_total=ms_total, ms_serial=ms_serial, step_ms=step_ms, dinfo=dinfo, copy=copy,
-                per_call_ms_median={k: float(np.median(v)) for k, v in per.items()}, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup,
-                quality=quality,
-                shuffle=shuffle, pull=pull,
-                per_call_ms={k: float(np.mean(v)) for k, v in per.items()},
-                per_call_ms_min={k: float(np.min(v)) for k, v in per.items()}, status=status,
-                device=torch.cuda.get_device_name(dev))
+    out = {k: v for k, v in t.items() if k not in ("layers", "logits", "hidden", "cfg")}
+    out.update(dinfo=dinfo, copy=copy, combine_ms=float(np.mean(comb_ms)), place=place, dedup=dedup,
+               quality=quality, shuffle=shuffle, pull=pull, status=status, device=torch.cuda.get_device_name(dev))
+    del layers, logits, hidden
+    torch.cuda.empty_cache()
+    return out
 
 
 def quality_dict(q, R: int) -> dict:
@@ -569,6 +654,10 @@ def main():
                     help="print TopoEP's plan-quality or solver-scaling study instead of the path benchmark")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the path, time a plain copy of this many bytes (counter calibration)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the step timings of the other four workloads (the line's `configs` object)")
+    ap.add_argument("--config-steps", type=int, default=20)
+    ap.add_argument("--config-warmup", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the planning path runs its logical EP ranks on a single device. "
@@ -587,10 +676,19 @@ def main():
     slots = w.T * w.k * w.L
     value = slots / (ms_per_step / 1e3)
     ab = algorithmic_bytes(w)
-    disp_ms = g["per_call_ms"]["dispatch"]
-    achieved = ab["dispatch"] / (disp_ms / 1e3) / 1e9
-    traffic = gather_traffic(w)
+    gather_ms = g["step_gather_ms"]
+    achieved = ab["gather"] / (gather_ms / 1e3) / 1e9
+    traffic, traffic_source = gather_traffic(w)
     chain_gbs = ab["total"] / (ms_per_step / 1e3) / 1e9
+    chain_one = ab["total"] / (g["ms_serial"] / args.steps / 1e3) / 1e9
+    configs = {}
+    if not args.no_configs:
+        import torch
+        dev = torch.device("cuda", 0)
+        for name in synth.WORKLOAD_ORDER:
+            if name != w.name:
+                configs[name] = config_line(synth.WORKLOADS[name], args.config_steps, args.config_warmup, dev)
+    disp_gather_ms = g["dispatch_gather_ms"]
     out = {
         "metric": "routed token-slots/sec for route+plan+dispatch; gather HBM GB/s vs peak",
         "value": value, "unit": "token-slots/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -599,18 +697,23 @@ def main():
         "latency_ms_per_step": g["ms_serial"] / args.steps,
         "latency_us": {"median": float(np.median(g["step_ms"])) * 1e3, "min": float(np.min(g["step_ms"])) * 1e3,
                        "mean": float(np.mean(g["step_ms"])) * 1e3},
-        "dtype": "int32", "data": "synthetic",
+        "dtype": "fp32 compare (top-k), int32 plan (int64 benefits), bf16 row copy", "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "R": w.R, "G": w.G, "H": w.H,
                    "replica_budget": w.B, "layers": w.L, "zipf_s": w.zipf_s, "beta": w.beta,
                    "couple_p": w.couple_p, "seed": w.seed, "cache_resident": working_set(w) < 256 * 2**20,
                    "inputs_sha256_16": inputs_sha(w), "second_batch_seed": second_batch(w).seed,
                    "second_batch_sha256_16": inputs_sha(second_batch(w))},
-        "roofline": {"bound": "hbm", "kernel": "gather (moe_plan_dispatch)", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": ab["dispatch"],
-                     "launch_ms": disp_ms},
+        "roofline": {"bound": "hbm",
+                     "kernel": "gather_vec_kernel<4, true> (the row copy of moe_plan_step, with the slot assignment)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "traffic_source": traffic_source,
+                     "algorithmic_bytes_per_launch": ab["gather"], "launch_ms": gather_ms,
+                     "timing": "HIP events the library records right before and after the kernel's launch "
+                               "(moe_plan_set_events), in a one-stream pass of the same steps, mean of %d launches"
+                               % (args.steps * w.L)},
         "chain": {"algorithmic_bytes_per_step": ab["total"], "achieved": chain_gbs, "peak": HBM_PEAK_GBS,
-                  "unit": "GB/s", "frac": chain_gbs / HBM_PEAK_GBS},
+                  "unit": "GB/s", "frac": chain_gbs / HBM_PEAK_GBS, "frac_one_stream": chain_one / HBM_PEAK_GBS},
+        "configs": configs,
         "combine": {"kernel": "combine (moe_plan_combine)", "us": g["combine_ms"] * 1e3,
                     "algorithmic_bytes_per_launch": ab["combine"],
                     "achieved": ab["combine"] / (g["combine_ms"] / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -622,16 +725,19 @@ def main():
                            "achieved": dedup_bytes(w, g["dedup"]["n_rows"]) / (g["dedup"]["us"] / 1e6) / 1e9,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": dedup_bytes(w, g["dedup"]["n_rows"]) / (g["dedup"]["us"] / 1e6) / 1e9 / HBM_PEAK_GBS,
-                           "vs_dispatch_us": disp_ms * 1e3},
+                           "vs_dispatch_us": g["per_call_ms"]["dispatch"] * 1e3},
         "replica_pull": g["pull"],
         "plan_quality": g["quality"],
         "token_shuffle": g["shuffle"],
         "stages": {name: {"us_mean": g["per_call_ms"][name] * 1e3, "us_median": g["per_call_ms_median"][name] * 1e3,
-                          "us_min": g["per_call_ms_min"][name] * 1e3, "algorithmic_bytes": ab[name],
-                          "achieved_GBps": ab[name] / (g["per_call_ms"][name] / 1e3) / 1e9,
-                          "frac": ab[name] / (g["per_call_ms"][name] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                          "us_min": g["per_call_ms_min"][name] * 1e3, "algorithmic_bytes": ab[name] / w.L,
+                          "achieved_GBps": ab[name] / w.L / (g["per_call_ms"][name] / 1e3) / 1e9,
+                          "frac": ab[name] / w.L / (g["per_call_ms"][name] / 1e3) / 1e9 / HBM_PEAK_GBS,
                           "bound": "hbm" if name == "dispatch" else "latency"}
                    for name in ("route", "plan", "dispatch")},
+        "dispatch_gather": {"kernel": "gather_vec_kernel<4, false> (the row copy of moe_plan_dispatch)",
+                            "us": disp_gather_ms * 1e3, "algorithmic_bytes_per_launch": ab["gather"],
+                            "frac": ab["gather"] / (disp_gather_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "device_info": dict(g["dinfo"], hbm_peak_GBps=HBM_PEAK_GBS, measured_copy_GBps=g["copy"]["GBps"]),
         "per_call_us": {k: v * 1e3 for k, v in g["per_call_ms"].items()},
         "per_call_us_min": {k: v * 1e3 for k, v in g["per_call_ms_min"].items()},

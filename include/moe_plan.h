@@ -83,6 +83,8 @@ enum {
                                    entry or a row sum >= 2^31 */
 #define MOE_STATUS_BAD_KEY 16   /* moe_plan_dedup_*: a slot key outside the table, or a table
                                    entry outside [0, R) */
+#define MOE_STATUS_BAD_OMEGA 32 /* moe_plan_plan: the routing matrix is not the one of the top-k
+                                   it was given with */
 
 typedef struct moe_plan* moe_plan_t;
 
@@ -117,8 +119,6 @@ typedef struct {
   int64_t omega;         /* R*E      omega */
   int64_t experts;       /* E        expert_count */
   int64_t pair;          /* E*E      cooc, trans */
-  int64_t tiles;         /* NT = R * ceil((T/R)/64) token tiles of up to 64 tokens of one source */
-  int64_t tile_words;    /* NT*E     tile_mask (uint64) and tile_base (int32) */
   int64_t inst_cap;      /* E+B      inst_expert, inst_rank, inst_load */
   int64_t quota;         /* R*(E+B)  quota */
   int64_t inst_offset;   /* E+B+1 */
@@ -144,13 +144,6 @@ typedef struct {
  *   trans      int32 [E][E] (nullable; written only when prev_topk is given):
  *              tokens selecting a in the previous layer and b in this one
  *              [Coupling, cross-layer routing].
- *   tile_mask  uint64 [NT][E]: bit j of tile_mask[x][e] is set when the j-th
- *              token of tile x selects e.  Tile x = s*C + c covers tokens
- *              s*T/R + 64c ... of source s (C = ceil((T/R)/64)).
- *   tile_base  int32 [NT][E]: assignments of e in all earlier tiles
- *              (exclusive prefix over tiles in token order).
- * tile_mask and tile_base carry the stable per-(source, expert) token order
- * from the histogram step to moe_plan_plan; treat them as opaque.
  */
 typedef struct {
   int32_t* topk_idx;
@@ -159,8 +152,6 @@ typedef struct {
   int32_t* omega;
   int32_t* cooc;
   int32_t* trans;
-  uint64_t* tile_mask;
-  int32_t* tile_base;
 } moe_route_out;
 
 /*
@@ -176,13 +167,9 @@ typedef struct {
  *   quota        int32 [R][E+B]: q[s][i], assignments of source s run on
  *                instance i (zero for i >= n_inst).
  *   slot_inst    int32 [T*k]: instance of slot t*k+j.
- *   slot_rank    int32 [T*k]: position of the slot inside its instance's
- *                segment of the dispatch buffer (stable: slot order).
- *   inst_offset  int32 [E+B+1]: first dispatch row of each instance (the
- *                exclusive prefix of inst_load); entry n_inst is T*k, later
- *                entries are -1.  These are the receive counts of the
- *                dispatch, derived on the device [TopoEP section 5].
- *   rank_offset  int32 [R+1]: first dispatch row of each rank; entry R is T*k.
+ *   slot_rank    int32 [T*k]: the slot's position among the slots of its
+ *                instance, in slot order (the stable rank the dispatch layout
+ *                adds to the instance's first row).
  */
 typedef struct {
   int32_t* n_inst;
@@ -193,19 +180,26 @@ typedef struct {
   int32_t* quota;
   int32_t* slot_inst;
   int32_t* slot_rank;
-  int32_t* inst_offset;
-  int32_t* rank_offset;
 } moe_plan_out;
 
 /*
  * Outputs of moe_plan_dispatch.
  *   perm         int32 [T*k]: slot id (t*k+j) at each dispatch row.
  *   slot_pos     int32 [T*k]: dispatch row of each slot (inverse of perm).
+ *   inst_offset  int32 [E+B+1]: first dispatch row of each instance (the
+ *                exclusive prefix of the instance loads); entry n_inst is
+ *                T*k, later entries are -1.  These are the receive counts of
+ *                the dispatch, derived on the device [TopoEP section 5].
+ *   rank_offset  int32 [R+1]: first dispatch row of each rank; entry R is T*k.
+ *                Rank r's rows [rank_offset[r], rank_offset[r+1]) are what an
+ *                all-to-all would send to rank r.
  *   dispatch     uint16 [T*k][H]: bf16 rows, dispatch[pos] = hidden[perm[pos]/k].
  */
 typedef struct {
   int32_t* perm;
   int32_t* slot_pos;
+  int32_t* inst_offset;
+  int32_t* rank_offset;
   uint16_t* dispatch;
 } moe_dispatch_out;
 
@@ -304,7 +298,9 @@ int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out);
  * Top-k gating and histograms of one layer.  logits: float [T][E] (device).
  * prev_topk: int32 [T][k] of the previous layer (nullable); out->trans is
  * written only when both prev_topk and out->trans are non-null.  Required
- * outputs: topk_idx, expert_count, omega, tile_mask, tile_base.
+ * outputs: topk_idx, expert_count, omega.  A NaN logit sets
+ * MOE_STATUS_NAN_LOGIT (that token's outputs are then unspecified); a bad
+ * prev_topk row (entry outside [0, E) or repeated) MOE_STATUS_BAD_TOPK.
  * Sources: [TopoEP] section 2.1 (top-k gating) and Eq. 3; [Coupling].
  */
 int moe_plan_route(moe_plan_t h, const float* logits, const int32_t* prev_topk,
@@ -312,17 +308,28 @@ int moe_plan_route(moe_plan_t h, const float* logits, const int32_t* prev_topk,
 
 /*
  * The histogram half of moe_plan_route from a given top-k: topk_idx int32
- * [T][k] (device, each row k distinct experts in [0, E)).  Writes
- * expert_count, omega, tile_mask, tile_base and the nullable cooc / trans of
- * out; out->topk_idx and out->topk_val are ignored.  moe_plan_plan reads the
- * top-k through its route argument, so hand it a moe_route_out whose
- * topk_idx points at this same top-k.
+ * [T][k] (device, each row k distinct experts in [0, E); otherwise
+ * MOE_STATUS_BAD_TOPK is set and the histograms are unspecified).  Writes
+ * expert_count, omega and the nullable cooc / trans of out; out->topk_idx
+ * and out->topk_val are ignored.
  */
 int moe_plan_hist(moe_plan_t h, const int32_t* topk_idx, const int32_t* prev_topk,
                   const moe_route_out* out, void* stream);
 
 /*
- * Replica placement and token re-routing [TopoEP section 4.3]:
+ * Replica placement and token re-routing [TopoEP section 4.3].  As in the
+ * page's design, the input is the routing matrix of all ranks plus the layer
+ * configuration [TopoEP abstract and section 3.1]; the top-k that the matrix
+ * counts is passed too, for the per-slot instances:
+ *   omega     int32 [R][E] (device): omega[s][e], assignments of source s to
+ *             expert e [TopoEP Eq. 3] -- e.g. moe_plan_route's omega, or the
+ *             matrix gathered from every rank;
+ *   topk_idx  int32 [T][k] (device): each row k distinct experts in [0, E);
+ *             token t belongs to source t / (T/R).  (NULL allowed when T = 0.)
+ * omega must be the routing matrix of topk_idx: a mismatch sets
+ * MOE_STATUS_BAD_OMEGA, a bad top-k row MOE_STATUS_BAD_TOPK, and the outputs
+ * are then unspecified (every index still stays inside its buffer).  The
+ * plan itself:
  *   D[d][e] = sum of omega over the sources of domain d (Eq. 4);
  *   stage 1 (inter-node placement): per domain, experts whose main instance is
  *     elsewhere with benefit b = 2*D*S_tok - ||W_e|| > 0 (Eq. 9), in
@@ -341,29 +348,30 @@ int moe_plan_hist(moe_plan_t h, const int32_t* topk_idx, const int32_t* prev_top
  *     in three passes -- the source's own rank, its domain, anywhere -- each
  *     pass sources ascending, instances in rank order;
  *   slot instances: the p-th slot (token order) of source s and expert e goes
- *     to the first instance whose running quota sum exceeds p;
- *   dispatch offsets: exclusive prefix sums of the instance loads and of the
- *     rank loads (instances are rank-major).
- * route: the outputs of moe_plan_route / moe_plan_hist for this layer
- * (topk_idx, omega, tile_mask, tile_base are read).
+ *     to the first instance whose running quota sum exceeds p; slot_rank is
+ *     its position among its instance's slots in slot order.
  */
-int moe_plan_plan(moe_plan_t h, const moe_route_out* route, const moe_plan_out* out, void* stream);
+int moe_plan_plan(moe_plan_t h, const int32_t* omega, const int32_t* topk_idx, const moe_plan_out* out,
+                  void* stream);
 
 /*
  * Dispatch layout and bf16 gather [TopoEP section 5: the plan stays on the
- * device and the receive counts are derived there].  The slots are laid out
- * as a stable counting sort by instance: slot_pos = inst_offset[slot_inst] +
- * slot_rank.  hidden: uint16 [T][H] bf16 rows (device).  Reads
- * plan->slot_inst, slot_rank and inst_offset.
+ * device and the receive counts are derived there].  The receive counts are
+ * the instance loads: inst_offset is their exclusive prefix (instances are
+ * rank-major, so rank_offset follows), and the slots are laid out as a stable
+ * counting sort by instance: slot_pos = inst_offset[slot_inst] + slot_rank.
+ * hidden: uint16 [T][H] bf16 rows (device).  Reads plan->n_inst, inst_rank,
+ * inst_load, slot_inst and slot_rank.  A plan whose positions fall outside
+ * [0, T*k) sets MOE_STATUS_PLAN_CHECK and those slots are not copied.
  */
 int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const uint16_t* hidden,
                       const moe_dispatch_out* out, void* stream);
 
 /*
  * One whole pass of the path in a single call: moe_plan_route, then
- * moe_plan_plan on its outputs, then moe_plan_dispatch -- the same outputs,
- * bit for bit, as the three calls in order.  Inside the call the tile
- * prefix, the routing-matrix output and the pair counts (route->cooc,
+ * moe_plan_plan on its omega and topk_idx, then moe_plan_dispatch -- the
+ * same outputs, bit for bit, as the three calls in order.  Inside the call
+ * the routing-matrix output and the pair counts (route->cooc,
  * route->trans) are computed by extra workgroups of the solver launch, on the
  * CUs the single solver workgroup leaves idle (the pair counts' partial sums
  * are added by extra workgroups of the quota launch), so every kernel of the
@@ -518,6 +526,18 @@ int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, const uint16
                           int64_t param_elems, uint16_t* grad_accum, void* stream);
 
 /*
+ * Kernel timing for roofline reports [the measurement the pages' own solver
+ * latencies come from: HIP events, TopoEP section 6.3].  gather_begin and
+ * gather_end are hipEvent_t handles (created by the caller, on the handle's
+ * device) or both NULL to stop.  While set, every moe_plan_dispatch and
+ * moe_plan_step of this handle records gather_begin on its stream right
+ * before the launch of its row copy (the gather kernel) and gather_end right
+ * after it, so that hipEventElapsedTime gives that one kernel's duration.
+ * Host call; enqueues nothing.
+ */
+int moe_plan_set_events(moe_plan_t h, void* gather_begin, void* gather_end);
+
+/*
  * Figures of a HIP device for roofline reports (host call, no handle):
  * out[0] compute units, out[1] peak shader clock (kHz), out[2] peak memory
  * clock (kHz), out[3] memory bus width (bits), out[4] L2 cache bytes,
@@ -526,8 +546,10 @@ int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, const uint16
 int moe_plan_device_info(int device, int64_t* out);
 
 /*
- * Synchronise the handle's last stream, copy the device status word to
- * *host_flags (MOE_STATUS_* bits, 0 when clean) and clear it.
+ * Wait for the work of the handle's last call (it synchronises that call's
+ * stream only, which must still exist), copy the device status word to
+ * *host_flags (MOE_STATUS_* bits, 0 when clean) and clear it.  Not for use
+ * while that stream is being captured into a graph.
  */
 int moe_plan_status(moe_plan_t h, int32_t* host_flags);
 

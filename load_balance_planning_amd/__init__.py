@@ -31,6 +31,7 @@ MOE_STATUS_PLAN_CHECK = 2
 MOE_STATUS_BAD_TOPK = 4
 MOE_STATUS_BAD_PAIRS = 8
 MOE_STATUS_BAD_KEY = 16
+MOE_STATUS_BAD_OMEGA = 32
 
 _ERRORS = {MOE_ERR_INVALID_ARG: "invalid argument", MOE_ERR_UNSUPPORTED: "unsupported configuration",
            MOE_ERR_HIP: "HIP runtime error", MOE_ERR_NONFINITE: "non-finite gate logit",
@@ -52,24 +53,23 @@ class moe_plan_config(ctypes.Structure):
 
 class moe_plan_sizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
-        "topk", "omega", "experts", "pair", "tiles", "tile_words", "inst_cap", "quota", "inst_offset",
+        "topk", "omega", "experts", "pair", "inst_cap", "quota", "inst_offset",
         "rank_offset", "dispatch_elems", "n_slot", "expert_bytes", "token_bytes", "max_refine_iters",
         "workspace_bytes")]
 
 
 class moe_route_out(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "topk_idx", "topk_val", "expert_count", "omega", "cooc", "trans", "tile_mask", "tile_base")]
+        "topk_idx", "topk_val", "expert_count", "omega", "cooc", "trans")]
 
 
 class moe_plan_out(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "n_inst", "inst_expert", "inst_rank", "inst_load", "rank_load", "quota", "slot_inst", "slot_rank",
-        "inst_offset", "rank_offset")]
+        "n_inst", "inst_expert", "inst_rank", "inst_load", "rank_load", "quota", "slot_inst", "slot_rank")]
 
 
 class moe_dispatch_out(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("perm", "slot_pos", "dispatch")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("perm", "slot_pos", "inst_offset", "rank_offset", "dispatch")]
 
 
 class moe_place_out(ctypes.Structure):
@@ -93,8 +93,8 @@ class moe_dedup_out(ctypes.Structure):
 EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
            "moe_plan_dispatch", "moe_plan_step", "moe_plan_combine", "moe_plan_place", "moe_plan_dedup_count",
            "moe_plan_dedup_dispatch", "moe_plan_quality", "moe_plan_predict", "moe_plan_slot_map",
-           "moe_plan_replica_pull", "moe_plan_replica_push", "moe_plan_device_info", "moe_plan_status",
-           "moe_plan_destroy")
+           "moe_plan_replica_pull", "moe_plan_replica_push", "moe_plan_set_events", "moe_plan_device_info",
+           "moe_plan_status", "moe_plan_destroy")
 
 _LIB = None
 
@@ -104,10 +104,11 @@ def lib_path() -> str:
 
 
 def lib():
-    """The loaded HIP library (built in-tree on first use if it is not there yet)."""
+    """The loaded HIP library, built in-tree first when it is missing or was built from other
+    sources than the ones in the tree (a hash of the sources is kept beside it)."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
+        if not _build.up_to_date():
             _build.build()
         l = ctypes.CDLL(_build.LIB)
         vp = ctypes.c_void_p
@@ -115,7 +116,7 @@ def lib():
         l.moe_plan_create.argtypes = [vp, vp]
         l.moe_plan_route.argtypes = [vp, vp, vp, vp, vp]
         l.moe_plan_hist.argtypes = [vp, vp, vp, vp, vp]
-        l.moe_plan_plan.argtypes = [vp, vp, vp, vp]
+        l.moe_plan_plan.argtypes = [vp, vp, vp, vp, vp]
         l.moe_plan_dispatch.argtypes = [vp, vp, vp, vp, vp]
         l.moe_plan_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         l.moe_plan_combine.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -126,6 +127,7 @@ def lib():
         l.moe_plan_predict.argtypes = [vp] * 8
         l.moe_plan_slot_map.argtypes = [vp, vp, vp, vp]
         l.moe_plan_device_info.argtypes = [ctypes.c_int, vp]
+        l.moe_plan_set_events.argtypes = [vp, vp, vp]
         l.moe_plan_replica_pull.argtypes = [vp, vp, vp, ctypes.c_int64, vp, vp]
         l.moe_plan_replica_push.argtypes = [vp, vp, vp, ctypes.c_int64, vp, vp]
         l.moe_plan_status.argtypes = [vp, vp]
@@ -164,8 +166,8 @@ def moe_plan_hist(h, topk_idx: int, prev_topk: int | None, out: moe_route_out, s
     _check("moe_plan_hist", lib().moe_plan_hist(h, topk_idx, prev_topk, ctypes.byref(out), stream))
 
 
-def moe_plan_plan(h, route: moe_route_out, out: moe_plan_out, stream: int):
-    _check("moe_plan_plan", lib().moe_plan_plan(h, ctypes.byref(route), ctypes.byref(out), stream))
+def moe_plan_plan(h, omega: int, topk_idx: int | None, out: moe_plan_out, stream: int):
+    _check("moe_plan_plan", lib().moe_plan_plan(h, omega, topk_idx, ctypes.byref(out), stream))
 
 
 def moe_plan_dispatch(h, plan: moe_plan_out, hidden: int, out: moe_dispatch_out, stream: int):
@@ -219,6 +221,10 @@ def moe_plan_replica_push(h, slot_expert: int, replica_grads: int, param_elems: 
            lib().moe_plan_replica_push(h, slot_expert, replica_grads, param_elems, grad_accum, stream))
 
 
+def moe_plan_set_events(h, gather_begin, gather_end):
+    _check("moe_plan_set_events", lib().moe_plan_set_events(h, gather_begin, gather_end))
+
+
 def moe_plan_device_info(device: int = 0) -> dict:
     out = (ctypes.c_int64 * 6)()
     _check("moe_plan_device_info", lib().moe_plan_device_info(device, out))
@@ -259,8 +265,6 @@ class RouteBuffers:
     omega: object
     cooc: object
     trans: object
-    tile_mask: object
-    tile_base: object
 
     def struct(self) -> moe_route_out:
         return moe_route_out(*(_ptr(getattr(self, n)) for n, _ in moe_route_out._fields_))
@@ -276,8 +280,6 @@ class PlanBuffers:
     quota: object
     slot_inst: object
     slot_rank: object
-    inst_offset: object
-    rank_offset: object
 
     def struct(self) -> moe_plan_out:
         return moe_plan_out(*(_ptr(getattr(self, n)) for n, _ in moe_plan_out._fields_))
@@ -287,6 +289,8 @@ class PlanBuffers:
 class DispatchBuffers:
     perm: object
     slot_pos: object
+    inst_offset: object
+    rank_offset: object
     dispatch: object
 
     def struct(self) -> moe_dispatch_out:
@@ -340,14 +344,13 @@ class Layer:
         self.route_out = RouteBuffers(
             topk_idx=e(sz.topk).view(T, k), topk_val=e(sz.topk, torch.float32).view(T, k) if topk_val else None,
             expert_count=e(E), omega=e(sz.omega).view(R, E),
-            cooc=e(sz.pair).view(E, E) if cooc else None, trans=e(sz.pair).view(E, E) if trans else None,
-            tile_mask=e(sz.tile_words, torch.int64), tile_base=e(sz.tile_words))
+            cooc=e(sz.pair).view(E, E) if cooc else None, trans=e(sz.pair).view(E, E) if trans else None)
         self.plan_out = PlanBuffers(
             n_inst=e(1), inst_expert=e(sz.inst_cap), inst_rank=e(sz.inst_cap), inst_load=e(sz.inst_cap),
-            rank_load=e(R), quota=e(sz.quota).view(R, sz.inst_cap), slot_inst=e(sz.topk), slot_rank=e(sz.topk),
-            inst_offset=e(sz.inst_offset), rank_offset=e(sz.rank_offset))
+            rank_load=e(R), quota=e(sz.quota).view(R, sz.inst_cap), slot_inst=e(sz.topk), slot_rank=e(sz.topk))
         self.dispatch_out = DispatchBuffers(
-            perm=e(sz.topk), slot_pos=e(sz.topk), dispatch=e(sz.dispatch_elems, torch.int16).view(T * k, H))
+            perm=e(sz.topk), slot_pos=e(sz.topk), inst_offset=e(sz.inst_offset), rank_offset=e(sz.rank_offset),
+            dispatch=e(sz.dispatch_elems, torch.int16).view(T * k, H))
         self._route_s = self.route_out.struct()
         self._plan_s = self.plan_out.struct()
         self._disp_s = self.dispatch_out.struct()
@@ -366,17 +369,21 @@ class Layer:
         return self.route_out
 
     def hist(self, topk_idx, prev_topk=None, stream=None):
+        """Histograms of a given top-k (moe_plan_hist); route_out.topk_idx is not touched."""
         self._check_tensor(topk_idx, (self.cfg.T, self.cfg.k), self.torch.int32)
         if prev_topk is not None:
             self._check_tensor(prev_topk, (self.cfg.T, self.cfg.k), self.torch.int32)
-        # moe_plan_plan reads the top-k through the route struct: keep it pointing at this top-k.
-        if topk_idx.data_ptr() != self.route_out.topk_idx.data_ptr():
-            self.route_out.topk_idx.copy_(topk_idx)
         moe_plan_hist(self.handle, _ptr(topk_idx), _ptr(prev_topk), self._route_s, self._stream(stream))
         return self.route_out
 
-    def plan(self, stream=None):
-        moe_plan_plan(self.handle, self._route_s, self._plan_s, self._stream(stream))
+    def plan(self, omega=None, topk_idx=None, stream=None):
+        """moe_plan_plan from a routing matrix [R][E] and the top-k [T][k] it counts; both default
+        to this layer's route outputs."""
+        omega = self.route_out.omega if omega is None else omega
+        topk_idx = self.route_out.topk_idx if topk_idx is None else topk_idx
+        self._check_tensor(omega, (self.cfg.R, self.cfg.E), self.torch.int32)
+        self._check_tensor(topk_idx, (self.cfg.T, self.cfg.k), self.torch.int32)
+        moe_plan_plan(self.handle, _ptr(omega), _ptr(topk_idx), self._plan_s, self._stream(stream))
         return self.plan_out
 
     def dispatch(self, hidden, stream=None):
@@ -538,6 +545,15 @@ class Layer:
         moe_plan_replica_push(self.handle, _ptr(self._slots[0]), _ptr(replica_grads), int(P), _ptr(grad_accum),
                               self._stream(stream))
         return grad_accum
+
+    def time_gather(self, begin=None, end=None):
+        """Record two torch.cuda.Events around the gather kernel of every later dispatch / step
+        call of this layer (moe_plan_set_events); with no events, stop.  The events must have
+        been recorded once already (torch creates the HIP event on its first record)."""
+        if begin is None:
+            moe_plan_set_events(self.handle, None, None)
+        else:
+            moe_plan_set_events(self.handle, ctypes.c_void_p(begin.cuda_event), ctypes.c_void_p(end.cuda_event))
 
     def status(self) -> int:
         return moe_plan_status(self.handle)

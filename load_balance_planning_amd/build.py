@@ -1,5 +1,6 @@
 """Compile the HIP kernels and the C ABI into load_balance_planning_amd/libmoe_plan.so (gfx950)."""
 import glob
+import hashlib
 import os
 import subprocess
 
@@ -9,8 +10,30 @@ LIB = os.path.join(HERE, "libmoe_plan.so")
 ARCH = os.environ.get("MOE_PLAN_ARCH", "gfx950")
 
 
+HASH = LIB + ".srchash"
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+
+
+def source_hash() -> str:
+    """SHA-256 of every source the library is built from (kernels, headers, the public header)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*"))) + [os.path.join(ROOT, "include", "moe_plan.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def up_to_date() -> bool:
+    """The built library exists and was built from the sources now in the tree."""
+    if not os.path.exists(LIB) or not os.path.exists(HASH):
+        return False
+    with open(HASH) as fh:
+        return fh.read().strip() == source_hash()
 
 
 def build(verbose: bool = False) -> str:
@@ -30,7 +53,11 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+    digest = source_hash()
     os.replace(tmp, LIB)
+    with open(HASH + ".tmp", "w") as fh:
+        fh.write(digest + "\n")
+    os.replace(HASH + ".tmp", HASH)
     return LIB
 
 

@@ -11,6 +11,9 @@ struct moe_plan {
   moe::Workspace ws;
   void* ws_base;
   size_t ws_bytes;
+  hipStream_t last_stream;  // stream of the last call that enqueued work (moe_plan_status waits for it)
+  moe::KernelEvents gather_ev;  // moe_plan_set_events: recorded around every gather launch
+  bool acc_dirty;           // a step failed after its top-k was queued: the accumulator may hold counts
 };
 
 namespace {
@@ -21,7 +24,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t status, prev_mask, demand, einst_off, einst_list, rlist, colpre, pair_part, omega_acc;
+  size_t status, tile_mask, tile_base, prev_mask, demand, einst_off, einst_list, rlist, colpre, pair_part, omega_acc;
   size_t place_aff, place_key, dd_mask, dd_cnt, dd_base, dd_count, pred_vote, total;
 };
 
@@ -30,6 +33,8 @@ WsLayout ws_layout(const moe::Dims& d) {
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes > 0 ? bytes : 1); return at; };
   l.status = take(sizeof(int32_t));
+  l.tile_mask = take(sizeof(uint64_t) * (size_t)d.NT * d.E);
+  l.tile_base = take(sizeof(int32_t) * (size_t)d.NT * d.E);
   l.prev_mask = take(sizeof(uint64_t) * (size_t)d.NT * d.E);
   l.demand = take(sizeof(int32_t) * (size_t)d.M * d.E);
   l.einst_off = take(sizeof(int32_t) * (size_t)(d.E + 1));
@@ -119,8 +124,6 @@ extern "C" int moe_plan_query(const moe_plan_config* cfg, moe_plan_sizes* sz) {
   sz->omega = (int64_t)d.R * d.E;
   sz->experts = d.E;
   sz->pair = (int64_t)d.E * d.E;
-  sz->tiles = d.NT;
-  sz->tile_words = (int64_t)d.NT * d.E;
   sz->inst_cap = d.cap;
   sz->quota = (int64_t)d.R * d.cap;
   sz->inst_offset = d.cap + 1;
@@ -144,12 +147,17 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   if (!h) return MOE_ERR_INTERNAL;
   h->d = d;
   h->cfg = *cfg;
+  h->last_stream = nullptr;
+  h->gather_ev = moe::KernelEvents{nullptr, nullptr};
+  h->acc_dirty = false;
   if (hipGetDevice(&h->device) != hipSuccess) { delete h; return MOE_ERR_HIP; }
   const WsLayout l = ws_layout(d);
   if (hipMalloc(&h->ws_base, l.total) != hipSuccess) { delete h; return MOE_ERR_HIP; }
   h->ws_bytes = l.total;
   char* b = static_cast<char*>(h->ws_base);
   h->ws.status = reinterpret_cast<int32_t*>(b + l.status);
+  h->ws.tile_mask = reinterpret_cast<uint64_t*>(b + l.tile_mask);
+  h->ws.tile_base = reinterpret_cast<int32_t*>(b + l.tile_base);
   h->ws.prev_mask = reinterpret_cast<uint64_t*>(b + l.prev_mask);
   h->ws.demand = reinterpret_cast<int32_t*>(b + l.demand);
   h->ws.einst_off = reinterpret_cast<int32_t*>(b + l.einst_off);
@@ -178,22 +186,31 @@ namespace {
 
 int check_route_out(const moe::Dims& d, const moe_route_out* out) {
   if (!out || !out->expert_count || !out->omega) return MOE_ERR_INVALID_ARG;
-  if (d.T > 0 && (!out->topk_idx || !out->tile_mask || !out->tile_base)) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && !out->topk_idx) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
 int check_plan_out(const moe::Dims& d, const moe_plan_out* out) {
   if (!out || !out->n_inst || !out->inst_expert || !out->inst_rank || !out->inst_load || !out->rank_load ||
-      !out->quota || !out->inst_offset || !out->rank_offset)
+      !out->quota)
     return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && (!out->slot_inst || !out->slot_rank)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
 int check_dispatch_out(const moe::Dims& d, const moe_dispatch_out* out) {
-  if (!out) return MOE_ERR_INVALID_ARG;
+  if (!out || !out->inst_offset || !out->rank_offset) return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && (!out->perm || !out->slot_pos || !out->dispatch)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
+}
+
+// Set-up shared by the calls that enqueue work: clears an error an earlier
+// HIP call of the caller left behind (so that a failure reported by this
+// call is its own) and remembers the stream for moe_plan_status.
+hipStream_t begin_call(moe_plan_t h, void* stream) {
+  (void)hipGetLastError();
+  h->last_stream = static_cast<hipStream_t>(stream);
+  return h->last_stream;
 }
 
 }  // namespace
@@ -205,58 +222,67 @@ extern "C" int moe_plan_route(moe_plan_t h, const float* logits, const int32_t* 
   if (d.T > 0 && !logits) return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStream_t st = begin_call(h, stream);
   const int32_t* prev = (prev_topk && out->trans) ? prev_topk : nullptr;
-  hipError_t e = moe::launch_route_topk(d, logits, prev, out->topk_idx, out->topk_val, out->tile_mask,
+  // The presence masks live in the workspace; the scan reads them for the
+  // routing matrix and counts (no tile prefix is needed here) and the pair
+  // counts run beside it in the same launch.
+  hipError_t e = moe::launch_route_topk(d, logits, prev, out->topk_idx, out->topk_val, h->ws.tile_mask,
                                         h->ws.prev_mask, nullptr, h->ws.status, st);
-  // scan and pair counts side by side in one launch: nothing else of the call would overlap them
   if (e == hipSuccess)
-    e = moe::launch_scan_pairs(d, out->tile_mask, out->tile_base, out->omega, out->expert_count, h->ws.prev_mask,
+    e = moe::launch_scan_pairs(d, h->ws.tile_mask, nullptr, out->omega, out->expert_count, h->ws.prev_mask,
                                out->cooc, prev ? out->trans : nullptr, h->ws.pair_part, st);
   return hip_rc(e);
 }
 
 extern "C" int moe_plan_hist(moe_plan_t h, const int32_t* topk_idx, const int32_t* prev_topk, const moe_route_out* out,
                              void* stream) {
-  if (!h || check_route_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
+  if (!h || !out || !out->expert_count || !out->omega) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
   if (d.T > 0 && !topk_idx) return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStream_t st = begin_call(h, stream);
   const int32_t* prev = (prev_topk && out->trans) ? prev_topk : nullptr;
-  hipError_t e = moe::launch_build_masks(d, topk_idx, prev, out->tile_mask, h->ws.prev_mask, h->ws.status, st);
+  hipError_t e = moe::launch_build_masks(d, topk_idx, prev, h->ws.tile_mask, h->ws.prev_mask, h->ws.status, st);
   if (e == hipSuccess)
-    e = moe::launch_scan_pairs(d, out->tile_mask, out->tile_base, out->omega, out->expert_count, h->ws.prev_mask,
+    e = moe::launch_scan_pairs(d, h->ws.tile_mask, nullptr, out->omega, out->expert_count, h->ws.prev_mask,
                                out->cooc, prev ? out->trans : nullptr, h->ws.pair_part, st);
   return hip_rc(e);
 }
 
-extern "C" int moe_plan_plan(moe_plan_t h, const moe_route_out* route, const moe_plan_out* out, void* stream) {
-  if (!h || !route || !route->omega || check_plan_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
+extern "C" int moe_plan_plan(moe_plan_t h, const int32_t* omega, const int32_t* topk_idx, const moe_plan_out* out,
+                             void* stream) {
+  if (!h || !omega || check_plan_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
-  if (d.T > 0 && (!route->topk_idx || !route->tile_mask || !route->tile_base)) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && !topk_idx) return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = moe::launch_plan(d, route->omega, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                  nullptr, *out, h->ws, st);
+  hipStream_t st = begin_call(h, stream);
+  // The presence masks of the given top-k (checking every row), then the
+  // solver on the given routing matrix while extra workgroups of its launch
+  // build the tile prefix and compare the matrix with the masks' own, then
+  // the quotas, then each slot's instance and rank.
+  hipError_t e = moe::launch_build_masks(d, topk_idx, nullptr, h->ws.tile_mask, nullptr, h->ws.status, st);
+  const moe::ScanJob scan{d.T > 0 ? h->ws.tile_mask : nullptr, h->ws.tile_base, nullptr, nullptr, omega};
   if (e == hipSuccess)
-    e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *out, h->ws, nullptr, 0, st);
+    e = moe::launch_plan(d, omega, scan, nullptr, nullptr, nullptr, nullptr, *out, nullptr, nullptr, h->ws, st);
+  if (e == hipSuccess)
+    e = moe::launch_assign(d, topk_idx, h->ws.tile_mask, h->ws.tile_base, *out, h->ws, nullptr, 0, st);
   return hip_rc(e);
 }
 
 extern "C" int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const uint16_t* hidden,
                                  const moe_dispatch_out* out, void* stream) {
   if (!h || !plan || check_dispatch_out(h->d, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
+  if (!plan->n_inst || !plan->inst_rank || !plan->inst_load) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
-  if (d.T > 0 && (!plan->slot_inst || !plan->slot_rank || !plan->inst_offset || !hidden)) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!plan->slot_inst || !plan->slot_rank || !hidden)) return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm,
-                                          out->slot_pos, out->dispatch, h->ws, st);
-  return hip_rc(e);
+  hipStream_t st = begin_call(h, stream);
+  return hip_rc(moe::launch_gather(d, *plan, hidden, out->perm, out->slot_pos, out->inst_offset, out->rank_offset,
+                                   out->dispatch, h->ws, h->gather_ev, st));
 }
 
 extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* prev_topk, const uint16_t* hidden,
@@ -269,35 +295,47 @@ extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* p
   if (d.T > 0 && (!logits || !hidden)) return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStream_t st = begin_call(h, stream);
   const int32_t* prev = (prev_topk && route->trans) ? prev_topk : nullptr;
   // On `st`: top-k (which also accumulates the routing matrix into the
   // workspace accumulator, zero on entry) -> plan (the solver reads the
   // accumulator; workgroups on the CUs it leaves idle write the tile prefix,
   // the routing matrix and counts outputs and the pair-count partials) ->
-  // quotas (read the accumulator too; extra workgroups sum the pair-count
-  // partials) -> slot instances + gather, which zero the accumulator again:
-  // the handle carries no state from one call to the next, so the call can
-  // be captured in a HIP graph and replayed.
+  // quotas and dispatch offsets (read the accumulator too; extra workgroups
+  // sum the pair-count partials) -> slot instances + gather, which zero the
+  // accumulator again: the handle carries no state from one call to the
+  // next, so the call can be captured in a HIP graph and replayed.  If a
+  // launch fails after the top-k was queued, the accumulator may keep counts;
+  // the next call then clears it first.
   const int64_t re = (int64_t)d.R * d.E;
   int32_t* acc = h->ws.omega_acc;
-  hipError_t e = moe::launch_route_topk(d, logits, prev, route->topk_idx, route->topk_val, route->tile_mask,
-                                        h->ws.prev_mask, acc, h->ws.status, st);
+  hipError_t e = hipSuccess;
+  if (h->acc_dirty) {
+    e = moe::launch_zero(acc, re, st);
+    if (e != hipSuccess) return hip_rc(e);
+    h->acc_dirty = false;
+  }
+  h->acc_dirty = true;  // until the launch that clears the accumulator is queued
+  e = moe::launch_route_topk(d, logits, prev, route->topk_idx, route->topk_val, h->ws.tile_mask, h->ws.prev_mask,
+                             acc, h->ws.status, st);
+  const moe::ScanJob scan{h->ws.tile_mask, h->ws.tile_base, route->omega, route->expert_count, nullptr};
   if (e == hipSuccess)
-    e = moe::launch_plan(d, acc, route->tile_mask, route->tile_base, route->omega, route->expert_count, h->ws.prev_mask,
-                         route->cooc, prev ? route->trans : nullptr, h->ws.pair_part, *plan, h->ws, st);
+    e = moe::launch_plan(d, acc, scan, h->ws.prev_mask, route->cooc, prev ? route->trans : nullptr, h->ws.pair_part,
+                         *plan, out->inst_offset, out->rank_offset, h->ws, st);
   if (moe::gather_can_assign(d, hidden, out->dispatch)) {
     // the gather assigns its token's slots itself, overlapping the row load
     if (e == hipSuccess)
-      e = moe::launch_assign_gather(d, route->topk_idx, route->tile_mask, route->tile_base, *plan, hidden, out->perm,
-                                    out->slot_pos, out->dispatch, h->ws, acc, re, st);
+      e = moe::launch_assign_gather(d, route->topk_idx, h->ws.tile_mask, h->ws.tile_base, *plan, out->inst_offset,
+                                    hidden, out->perm, out->slot_pos, out->dispatch, h->ws, acc, re, h->gather_ev,
+                                    st);
   } else {
     if (e == hipSuccess)
-      e = moe::launch_assign(d, route->topk_idx, route->tile_mask, route->tile_base, *plan, h->ws, acc, re, st);
+      e = moe::launch_assign(d, route->topk_idx, h->ws.tile_mask, h->ws.tile_base, *plan, h->ws, acc, re, st);
     if (e == hipSuccess)
-      e = moe::launch_gather(d, plan->slot_inst, plan->slot_rank, plan->inst_offset, hidden, out->perm,
-                             out->slot_pos, out->dispatch, h->ws, st);
+      e = moe::launch_gather(d, *plan, hidden, out->perm, out->slot_pos, out->inst_offset, out->rank_offset,
+                             out->dispatch, h->ws, h->gather_ev, st);
   }
+  if (e == hipSuccess) h->acc_dirty = false;
   return hip_rc(e);
 }
 
@@ -308,7 +346,7 @@ extern "C" int moe_plan_combine(moe_plan_t h, const float* topk_val, const int32
   if (d.T > 0 && (!topk_val || !slot_pos || !expert_out || !out)) return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStream_t st = begin_call(h, stream);
   return hip_rc(moe::launch_combine(d, topk_val, slot_pos, expert_out, out, h->ws.status, st));
 }
 
@@ -318,7 +356,7 @@ extern "C" int moe_plan_place(moe_plan_t h, const int32_t* cooc, int32_t max_swa
     return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
-  return hip_rc(moe::launch_place(h->d, cooc, max_swaps, *out, h->ws, static_cast<hipStream_t>(stream)));
+  return hip_rc(moe::launch_place(h->d, cooc, max_swaps, *out, h->ws, begin_call(h, stream)));
 }
 
 namespace {
@@ -339,7 +377,7 @@ extern "C" int moe_plan_dedup_count(moe_plan_t h, const int32_t* slot_key, const
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(
-      moe::launch_dedup(h->d, slot_key, key_rank, n_keys, nullptr, *out, h->ws, static_cast<hipStream_t>(stream)));
+      moe::launch_dedup(h->d, slot_key, key_rank, n_keys, nullptr, *out, h->ws, begin_call(h, stream)));
 }
 
 extern "C" int moe_plan_dedup_dispatch(moe_plan_t h, const int32_t* slot_key, const int32_t* key_rank,
@@ -355,7 +393,7 @@ extern "C" int moe_plan_dedup_dispatch(moe_plan_t h, const int32_t* slot_key, co
   static const uint16_t kNoRows = 0;
   const uint16_t* src = hidden ? hidden : &kNoRows;
   return hip_rc(
-      moe::launch_dedup(h->d, slot_key, key_rank, n_keys, src, *out, h->ws, static_cast<hipStream_t>(stream)));
+      moe::launch_dedup(h->d, slot_key, key_rank, n_keys, src, *out, h->ws, begin_call(h, stream)));
 }
 
 extern "C" int moe_plan_quality(moe_plan_t h, const moe_plan_out* plan, int64_t* out, void* stream) {
@@ -364,7 +402,7 @@ extern "C" int moe_plan_quality(moe_plan_t h, const moe_plan_out* plan, int64_t*
     return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
-  return hip_rc(moe::launch_quality(h->d, *plan, out, h->ws.status, static_cast<hipStream_t>(stream)));
+  return hip_rc(moe::launch_quality(h->d, *plan, out, h->ws.status, begin_call(h, stream)));
 }
 
 extern "C" int moe_plan_predict(moe_plan_t h, const int32_t* topk_cur, const int32_t* trans, const int32_t* count_cur,
@@ -375,7 +413,7 @@ extern "C" int moe_plan_predict(moe_plan_t h, const int32_t* topk_cur, const int
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(moe::launch_predict(h->d, topk_cur, trans, count_cur, key_rank, topk_next, *out, h->ws,
-                                    static_cast<hipStream_t>(stream)));
+                                    begin_call(h, stream)));
 }
 
 extern "C" int moe_plan_slot_map(moe_plan_t h, const moe_plan_out* plan, const moe_slot_out* out, void* stream) {
@@ -384,7 +422,7 @@ extern "C" int moe_plan_slot_map(moe_plan_t h, const moe_plan_out* plan, const m
   if (h->d.n_slot > 0 && (!out->slot_expert || !out->slot_main)) return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
-  return hip_rc(moe::launch_slot_map(h->d, *plan, *out, h->ws.status, static_cast<hipStream_t>(stream)));
+  return hip_rc(moe::launch_slot_map(h->d, *plan, *out, h->ws.status, begin_call(h, stream)));
 }
 
 extern "C" int moe_plan_replica_pull(moe_plan_t h, const int32_t* slot_expert, const uint16_t* main_params,
@@ -395,7 +433,7 @@ extern "C" int moe_plan_replica_pull(moe_plan_t h, const int32_t* slot_expert, c
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(moe::launch_replica_pull(h->d, slot_expert, main_params, param_elems, replica_params, h->ws.status,
-                                         static_cast<hipStream_t>(stream)));
+                                         begin_call(h, stream)));
 }
 
 extern "C" int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, const uint16_t* replica_grads,
@@ -406,7 +444,13 @@ extern "C" int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, c
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
   return hip_rc(moe::launch_replica_push(h->d, slot_expert, replica_grads, param_elems, grad_accum, h->ws.status,
-                                         static_cast<hipStream_t>(stream)));
+                                         begin_call(h, stream)));
+}
+
+extern "C" int moe_plan_set_events(moe_plan_t h, void* gather_begin, void* gather_end) {
+  if (!h || (gather_begin == nullptr) != (gather_end == nullptr)) return MOE_ERR_INVALID_ARG;
+  h->gather_ev = moe::KernelEvents{static_cast<hipEvent_t>(gather_begin), static_cast<hipEvent_t>(gather_end)};
+  return MOE_OK;
 }
 
 extern "C" int moe_plan_device_info(int device, int64_t* out) {
@@ -430,11 +474,13 @@ extern "C" int moe_plan_status(moe_plan_t h, int32_t* host_flags) {
   if (!h || !host_flags) return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
-  if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+  // In order on the last call's stream: read the word, clear it, then wait
+  // for that stream alone (other streams keep running).
+  hipStream_t st = h->last_stream;
   int32_t v = 0;
-  if (hipMemcpy(&v, h->ws.status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
-  if (hipMemset(h->ws.status, 0, sizeof(v)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
-    return MOE_ERR_HIP;
+  if (hipMemcpyAsync(&v, h->ws.status, sizeof(v), hipMemcpyDeviceToHost, st) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_zero(h->ws.status, 1, st) != hipSuccess) return MOE_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_HIP;
   *host_flags = v;
   return MOE_OK;
 }

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(1024) void dedup_scan_kernel(Dims d, const uint64_t
   extern __shared__ int32_t smem_dscan[];
   Dims dr = d;
   dr.E = d.R;  // ranks are the columns
-  tile_scan_block<1024>(dr, mask, base, rank_rows, rank_count, blockIdx.x, smem_dscan);
+  tile_scan_block<1024>(dr, mask, base, rank_rows, rank_count, nullptr, nullptr, blockIdx.x, smem_dscan);
   if (rank_slots) {
     for (int q = threadIdx.x; q < d.R * kScanEB; q += 1024) {
       const int src = q / kScanEB, r = blockIdx.x * kScanEB + (q - src * kScanEB);

@@ -2,10 +2,13 @@
 //
 // [TopoEP] section 5: the plan stays on the device and the receive counts are
 // derived there.  The layout is a stable counting sort of the slots by
-// instance: the plan gives the instance offsets (exclusive prefix of the
-// instance loads) and each slot's position inside its instance (slot_rank),
-// so slot_pos = inst_offset[slot_inst] + slot_rank with no sort, and the
-// whole dispatch is one kernel.
+// instance: the instance offsets are the exclusive prefix of the instance
+// loads (one small workgroup computes them), and the plan gives each slot's
+// position inside its instance (slot_rank), so slot_pos =
+// inst_offset[slot_inst] + slot_rank with no sort, and the row copy is one
+// kernel.  (Scanning the loads inside every gather workgroup instead made the
+// compiler keep the row in scratch memory while the scan ran: the DeepSeek-V3
+// dispatch slowed from 0.83 to 1.34 ms on MI355X.)
 //
 // The copy is source-ordered: each hidden row is read from HBM once and
 // written to its k dispatch rows, so HBM traffic is T*H*2 bytes read plus
@@ -29,6 +32,66 @@ struct AssignIn {
   int32_t* clear;      // zeroed, [0, clear_n) (nullable): a buffer no earlier kernel still reads
   int64_t clear_n;
 };
+
+// The plan's instance loads, for a dispatch that derives its own offsets.
+struct OffsetsIn {
+  const int32_t* n_inst;
+  const int32_t* inst_load;
+  const int32_t* inst_rank;
+  int32_t* inst_offset;  // written by workgroup 0
+  int32_t* rank_offset;  // written by workgroup 0
+};
+
+// Exclusive prefix of the instance loads and each rank's first row (instances
+// are rank-major): one workgroup of 256 threads.  inst_offset gets -1 after
+// entry n_inst; a rank without instances -- impossible in a plan of this
+// library -- takes the next rank's offset.  An n_inst outside [0, cap] sets
+// MOE_STATUS_PLAN_CHECK and is taken as 0.
+__global__ __launch_bounds__(256) void offsets_kernel(Dims d, OffsetsIn in, int32_t* __restrict__ status) {
+  extern __shared__ int32_t pre[];
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int n = in.n_inst[0];
+  if (n < 0 || n > d.cap) {
+    if (tid == 0) atomicOr(status, MOE_STATUS_PLAN_CHECK);
+    n = 0;
+  }
+  const int per = (n + 255) / 256;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int sum = 0;
+  for (int q = lo; q < hi; ++q) sum += in.inst_load[q];
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  for (int r = tid; r < d.R; r += 256) in.rank_offset[r] = -1;
+  __syncthreads();
+  int run = incl - sum;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+  for (int q = lo; q < hi; ++q) {
+    pre[q] = run;
+    run += in.inst_load[q];
+  }
+  if (tid == 0) pre[n] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  for (int i = tid; i <= d.cap; i += 256) in.inst_offset[i] = i <= n ? pre[i] : -1;
+  for (int q = tid; q < n; q += 256) {
+    const int r = in.inst_rank[q];
+    if ((unsigned)r < (unsigned)d.R && (q == 0 || in.inst_rank[q - 1] != r)) in.rank_offset[r] = pre[q];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int next = pre[n];
+    for (int r = d.R - 1; r >= 0; --r) {
+      if (in.rank_offset[r] < 0) in.rank_offset[r] = next;
+      next = in.rank_offset[r];
+    }
+    in.rank_offset[d.R] = pre[n];
+  }
+}
 
 // One workgroup per token.  Threads j < k place slot t*k+j -- reading its
 // instance and rank, or with ASSIGN computing them from the plan
@@ -156,25 +219,31 @@ bool one_round(const Dims& d) { return d.H / 8 <= 256; }
 
 }  // namespace
 
-hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t* slot_rank,
-                         const int32_t* inst_offset, const uint16_t* hidden, int32_t* perm, int32_t* slot_pos,
-                         uint16_t* dispatch, const Workspace& ws, hipStream_t st) {
-  if (d.T == 0) return hipSuccess;
+hipError_t launch_gather(const Dims& d, const moe_plan_out& plan, const uint16_t* hidden, int32_t* perm,
+                         int32_t* slot_pos, int32_t* inst_offset, int32_t* rank_offset, uint16_t* dispatch,
+                         const Workspace& ws, const KernelEvents& ev, hipStream_t st) {
+  const OffsetsIn oi{plan.n_inst, plan.inst_load, plan.inst_rank, inst_offset, rank_offset};
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(256), sizeof(int32_t) * (size_t)(d.cap + 1), st, d, oi, ws.status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || d.T == 0) return e;
+  if (ev.begin && (e = hipEventRecord(ev.begin, st)) != hipSuccess) return e;
   const bool vec = (d.H % 8) == 0 && ((uintptr_t)hidden % 16) == 0 && ((uintptr_t)dispatch % 16) == 0;
   if (vec) {
     if (one_round(d))
-      hipLaunchKernelGGL((gather_vec_kernel<1, false>), dim3(d.T), dim3(256), 0, st, d, slot_inst, slot_rank,
-                         inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+      hipLaunchKernelGGL((gather_vec_kernel<1, false>), dim3(d.T), dim3(256), 0, st, d, plan.slot_inst,
+                         plan.slot_rank, inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
                          reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws);
     else
-      hipLaunchKernelGGL((gather_vec_kernel<4, false>), dim3(d.T), dim3(256), 0, st, d, slot_inst, slot_rank,
-                         inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+      hipLaunchKernelGGL((gather_vec_kernel<4, false>), dim3(d.T), dim3(256), 0, st, d, plan.slot_inst,
+                         plan.slot_rank, inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
                          reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws);
   } else {
-    hipLaunchKernelGGL(gather_u16_kernel, dim3(d.T), dim3(256), 0, st, d, slot_inst, slot_rank, inst_offset, hidden,
-                       perm, slot_pos, dispatch, ws.status);
+    hipLaunchKernelGGL(gather_u16_kernel, dim3(d.T), dim3(256), 0, st, d, plan.slot_inst, plan.slot_rank,
+                       inst_offset, hidden, perm, slot_pos, dispatch, ws.status);
   }
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess && ev.end) e = hipEventRecord(ev.end, st);
+  return e;
 }
 
 bool gather_can_assign(const Dims& d, const uint16_t* hidden, const uint16_t* dispatch) {
@@ -182,21 +251,26 @@ bool gather_can_assign(const Dims& d, const uint16_t* hidden, const uint16_t* di
 }
 
 hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
-                                const int32_t* tile_base, const moe_plan_out& plan, const uint16_t* hidden,
-                                int32_t* perm, int32_t* slot_pos, uint16_t* dispatch, const Workspace& ws,
-                                int32_t* clear, int64_t clear_n, hipStream_t st) {
+                                const int32_t* tile_base, const moe_plan_out& plan, const int32_t* inst_offset,
+                                const uint16_t* hidden, int32_t* perm, int32_t* slot_pos, uint16_t* dispatch,
+                                const Workspace& ws, int32_t* clear, int64_t clear_n, const KernelEvents& ev,
+                                hipStream_t st) {
   if (d.T == 0) return hipSuccess;
+  hipError_t e;
+  if (ev.begin && (e = hipEventRecord(ev.begin, st)) != hipSuccess) return e;
   const AssignIn as{topk_idx, tile_mask, tile_base, plan.quota, plan.slot_inst, plan.slot_rank, clear,
                     clear ? clear_n : 0};
   if (one_round(d))
     hipLaunchKernelGGL((gather_vec_kernel<1, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr,
-                       plan.inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                       inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
                        reinterpret_cast<uint4*>(dispatch), as, ws);
   else
     hipLaunchKernelGGL((gather_vec_kernel<4, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr,
-                       plan.inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                       inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
                        reinterpret_cast<uint4*>(dispatch), as, ws);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess && ev.end) e = hipEventRecord(ev.end, st);
+  return e;
 }
 
 }  // namespace moe

@@ -33,6 +33,9 @@ struct Dims {
 // Device workspace owned by a handle.
 struct Workspace {
   int32_t* status;      // [1]   MOE_STATUS_* bits
+  uint64_t* tile_mask;  // [NT][E] presence masks of the top-k: bit j of [x][e] is set when
+                        // token j of tile x selects e (tile x = s*C + c: tokens s*Tr + 64c ...)
+  int32_t* tile_base;   // [NT][E] assignments of e in all earlier tiles (exclusive prefix)
   uint64_t* prev_mask;  // [NT][E] presence masks of the previous layer's top-k
   int32_t* demand;      // [M][E] domain demand D (Eq. 4) when it does not fit in LDS
   int32_t* einst_off;   // [E+1] per-expert instance lists (rank order) ...
@@ -69,6 +72,19 @@ hipError_t launch_scan_pairs(const Dims& d, const uint64_t* tile_mask, int32_t* 
                              int32_t* count, const uint64_t* prev_mask, int32_t* cooc, int32_t* trans, int32_t* part,
                              hipStream_t st);
 
+// The per-tile histogram scan (tile_scan.h) run by extra workgroups of the
+// solver launch: from the masks, the tile prefix into base and, each when
+// non-null, the routing matrix and expert counts into omega / count, and a
+// comparison of the routing matrix with `check` (MOE_STATUS_BAD_OMEGA on a
+// difference).
+struct ScanJob {
+  const uint64_t* mask;
+  int32_t* base;
+  int32_t* omega;
+  int32_t* count;
+  const int32_t* check;
+};
+
 // Launchers (all asynchronous on `st`).
 // omega_acc (nullable): also add each tile's per-expert counts to this [R][E]
 // accumulator (which must be zero on entry).
@@ -80,30 +96,40 @@ hipError_t launch_build_masks(const Dims& d, const int32_t* topk_idx, const int3
 // omega / count nullable: then only the tile prefix is written.
 hipError_t launch_scan(const Dims& d, const uint64_t* tile_mask, int32_t* tile_base, int32_t* omega,
                        int32_t* count, hipStream_t st);
-// Solver, quotas and dispatch offsets from the routing matrix omega.  When
-// scan_mask is given, extra workgroups of the solver launch also write the
-// tile prefix of those masks to scan_base, the routing matrix and expert
-// counts recomputed from the masks to scan_omega / scan_count, and the pair
-// counts of those masks (and of prev_mask) to cooc / trans, reduced by extra
+// Solver and quotas from the routing matrix omega.  When scan.mask is given,
+// extra workgroups of the solver launch run the scan job, and the pair counts
+// of those masks (and of prev_mask) go to cooc / trans, reduced by extra
 // workgroups of the quota launch (each output nullable; part: workspace).
-hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan_mask, int32_t* scan_base,
-                       int32_t* scan_omega, int32_t* scan_count, const uint64_t* prev_mask, int32_t* cooc,
-                       int32_t* trans, int32_t* part, const moe_plan_out& out, const Workspace& ws, hipStream_t st);
+// With inst_offset / rank_offset non-null the quota launch also writes the
+// dispatch offsets of the plan.
+hipError_t launch_plan(const Dims& d, const int32_t* omega, const ScanJob& scan, const uint64_t* prev_mask,
+                       int32_t* cooc, int32_t* trans, int32_t* part, const moe_plan_out& out, int32_t* inst_offset,
+                       int32_t* rank_offset, const Workspace& ws, hipStream_t st);
+// Zero n int32 words (a fill kernel: safe inside graph capture).
+hipError_t launch_zero(int32_t* p, int64_t n, hipStream_t st);
 // The slot assignment; it also zeroes clear[0, clear_n) (nullable), which no
 // kernel before it on the stream still reads.
 hipError_t launch_assign(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
                          const int32_t* tile_base, const moe_plan_out& out, const Workspace& ws,
                          int32_t* clear, int64_t clear_n, hipStream_t st);
-hipError_t launch_gather(const Dims& d, const int32_t* slot_inst, const int32_t* slot_rank,
-                         const int32_t* inst_offset, const uint16_t* hidden, int32_t* perm, int32_t* slot_pos,
-                         uint16_t* dispatch, const Workspace& ws, hipStream_t st);
+// The dispatch of a plan: its offsets (into inst_offset / rank_offset) and the
+// gather at slot_pos = inst_offset[slot_inst] + slot_rank, in one launch.
+// Events recorded right before and after a gather kernel's launch (both null: none).
+struct KernelEvents {
+  hipEvent_t begin;
+  hipEvent_t end;
+};
+hipError_t launch_gather(const Dims& d, const moe_plan_out& plan, const uint16_t* hidden, int32_t* perm,
+                         int32_t* slot_pos, int32_t* inst_offset, int32_t* rank_offset, uint16_t* dispatch,
+                         const Workspace& ws, const KernelEvents& ev, hipStream_t st);
 // The gather that also assigns the slots (writes plan.slot_inst / slot_rank);
 // only for 16-byte-aligned rows with H a multiple of 8 (gather_can_assign).
 bool gather_can_assign(const Dims& d, const uint16_t* hidden, const uint16_t* dispatch);
 hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
-                                const int32_t* tile_base, const moe_plan_out& plan, const uint16_t* hidden,
-                                int32_t* perm, int32_t* slot_pos, uint16_t* dispatch, const Workspace& ws,
-                                int32_t* clear, int64_t clear_n, hipStream_t st);
+                                const int32_t* tile_base, const moe_plan_out& plan, const int32_t* inst_offset,
+                                const uint16_t* hidden, int32_t* perm, int32_t* slot_pos, uint16_t* dispatch,
+                                const Workspace& ws, int32_t* clear, int64_t clear_n, const KernelEvents& ev,
+                                hipStream_t st);
 
 hipError_t launch_combine(const Dims& d, const float* topk_val, const int32_t* slot_pos, const uint16_t* expert_out,
                           uint16_t* out, int32_t* status, hipStream_t st);

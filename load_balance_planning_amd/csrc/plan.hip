@@ -500,20 +500,18 @@ __device__ void stage2_domain(const Dims& d, const PlanLayout& ly, int m) {
 //   rep_e/rep_U[r][j] expert and load of replica slot j < nrep[r] of rank r
 //   Umain[e]        load of e's main instance;  L[r] rank loads
 // Workgroup 0 is the solver; it reads the routing matrix from omega.
-// Workgroups 1.. (when scan_mask is given) run on the CUs the solver leaves
-// idle: for kScanEB experts each, the tile prefix of the presence masks into
-// scan_base, the routing matrix and expert counts into scan_omega and
-// scan_count (tile_scan.h).
+// Workgroups 1.. (when scan.mask is given) run on the CUs the solver leaves
+// idle: for kScanEB experts each, the scan job of tile_scan.h (the tile
+// prefix of the presence masks; the routing matrix and expert counts, or a
+// comparison of the routing matrix with the solver's input).
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout ly, const int32_t* __restrict__ omega,
-                                                            const uint64_t* __restrict__ scan_mask,
-                                                            int32_t* __restrict__ scan_base,
-                                                            int32_t* __restrict__ scan_omega,
-                                                            int32_t* __restrict__ scan_count, moe_plan_out out,
-                                                            Workspace ws, PairArgs pa, int n_scan) {
+                                                            ScanJob scan, moe_plan_out out, Workspace ws, PairArgs pa,
+                                                            int n_scan) {
   if (blockIdx.x > 0) {
     const int blk = blockIdx.x - 1;
     if (blk < n_scan) {
-      tile_scan_block<kPlanThreads>(d, scan_mask, scan_base, scan_omega, scan_count, blk, plan_lds);
+      tile_scan_block<kPlanThreads>(d, scan.mask, scan.base, scan.omega, scan.count, scan.check, ws.status, blk,
+                                    plan_lds);
       return;
     }
     // pair-count partials (pair_count.h), summed by the quota launch
@@ -806,51 +804,66 @@ __device__ int quota_block_excl_scan(int v, int* wtot) {
 
 // Dispatch offsets: exclusive prefix of the instance loads (the receive
 // counts of every instance) and, since instances are rank-major, each rank's
-// first row.  One workgroup; thread j sums a contiguous run of instances.
-__device__ void offsets_block(const Dims& d, const moe_plan_out& out, int32_t* status) {
+// first row.  One workgroup; thread j sums a contiguous run of instances.  A
+// rank with no instance (impossible in a plan of this library: every rank
+// keeps its main experts) gets the offset of the next rank that has one.
+__device__ void offsets_block(const Dims& d, const moe_plan_out& plan, int32_t* inst_offset, int32_t* rank_offset,
+                              int32_t* status) {
   __shared__ int wtot_o[kQuotaThreads / 64];
   const int tid = threadIdx.x;
-  int n = out.n_inst[0];
+  int n = plan.n_inst[0];
   if (n < 0 || n > d.cap) {
     if (tid == 0) atomicOr(status, MOE_STATUS_PLAN_CHECK);
     n = 0;
   }
+  for (int r = tid; r < d.R; r += kQuotaThreads) rank_offset[r] = -1;
   const int per = (n + kQuotaThreads - 1) / kQuotaThreads;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
   int sum = 0;
-  for (int q = lo; q < hi; ++q) sum += out.inst_load[q];
+  for (int q = lo; q < hi; ++q) sum += plan.inst_load[q];
   const int before = quota_block_excl_scan(sum, wtot_o);
   int total = 0;
   for (int w = 0; w < kQuotaThreads / 64; ++w) total += wtot_o[w];
   int run = before;
   for (int q = lo; q < hi; ++q) {
-    out.inst_offset[q] = run;
-    const int r = out.inst_rank[q];
-    if ((unsigned)r < (unsigned)d.R && (q == 0 || out.inst_rank[q - 1] != r)) out.rank_offset[r] = run;
-    run += out.inst_load[q];
+    inst_offset[q] = run;
+    const int r = plan.inst_rank[q];
+    if ((unsigned)r < (unsigned)d.R && (q == 0 || plan.inst_rank[q - 1] != r)) rank_offset[r] = run;
+    run += plan.inst_load[q];
   }
-  for (int i = n + tid; i <= d.cap; i += kQuotaThreads) out.inst_offset[i] = i == n ? total : -1;
-  if (tid == 0) out.rank_offset[d.R] = total;
+  for (int i = n + tid; i <= d.cap; i += kQuotaThreads) inst_offset[i] = i == n ? total : -1;
+  __syncthreads();
+  if (tid == 0) {
+    int next = total;
+    for (int r = d.R - 1; r >= 0; --r) {
+      if (rank_offset[r] < 0) rank_offset[r] = next;
+      next = rank_offset[r];
+    }
+    rank_offset[d.R] = total;
+  }
 }
 
 // Quotas.  Workgroups [0, n_transport): replicated expert rlist[b]; then
 // n_fill workgroups fill the columns of single-instance experts (all demand
-// on the one instance) and zero the unused columns; the last workgroup
-// computes the dispatch offsets.
+// on the one instance) and zero the unused columns; then, with inst_offset
+// given, one workgroup computes the dispatch offsets; then the pair-count
+// sums.
 __global__ __launch_bounds__(kQuotaThreads) void quota_kernel(Dims d, const int32_t* __restrict__ omega,
-                                                              moe_plan_out out, Workspace ws, int n_transport,
+                                                              moe_plan_out out, int32_t* inst_offset,
+                                                              int32_t* rank_offset, Workspace ws, int n_transport,
                                                               int n_fill, PairArgs pa) {
   const int E = d.E, R = d.R, G = d.G, cap = d.cap;
   const int tid = threadIdx.x;
-  if ((int)blockIdx.x > n_transport + n_fill) {  // the pair counts: sums of the solver launch's partials
+  const int n_off = inst_offset ? 1 : 0;
+  if ((int)blockIdx.x >= n_transport + n_fill + n_off) {  // the pair counts: sums of the solver launch's partials
     constexpr int kChunks = kPairBlock / kQuotaThreads;
-    const int r = (int)blockIdx.x - (n_transport + n_fill + 1), nb = pair_blocks(d);
+    const int r = (int)blockIdx.x - (n_transport + n_fill + n_off), nb = pair_blocks(d);
     const int rest = r / nb;
     pair_reduce_one(d, pa, rest / kChunks + pa.zbase, r % nb, (rest % kChunks) * kQuotaThreads + tid);
     return;
   }
   if ((int)blockIdx.x == n_transport + n_fill) {
-    offsets_block(d, out, ws.status);
+    offsets_block(d, out, inst_offset, rank_offset, ws.status);
     return;
   }
   if ((int)blockIdx.x >= n_transport) {
@@ -1004,17 +1017,17 @@ PlanLayout plan_layout(const Dims& d) {
 
 size_t plan_lds_bytes(const Dims& d) { return sizeof(int32_t) * (size_t)plan_layout(d).total; }
 
-hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan_mask, int32_t* scan_base,
-                       int32_t* scan_omega, int32_t* scan_count, const uint64_t* prev_mask, int32_t* cooc,
-                       int32_t* trans, int32_t* part, const moe_plan_out& out, const Workspace& ws, hipStream_t st) {
+hipError_t launch_plan(const Dims& d, const int32_t* omega, const ScanJob& scan, const uint64_t* prev_mask,
+                       int32_t* cooc, int32_t* trans, int32_t* part, const moe_plan_out& out, int32_t* inst_offset,
+                       int32_t* rank_offset, const Workspace& ws, hipStream_t st) {
   const PlanLayout ly = plan_layout(d);
   size_t lds = sizeof(int32_t) * (size_t)ly.total;
-  const int n_scan = scan_mask ? (d.E + kScanEB - 1) / kScanEB : 0;
+  const int n_scan = scan.mask ? (d.E + kScanEB - 1) / kScanEB : 0;
   if (n_scan > 0) lds = std::max(lds, tile_scan_lds_bytes(d, kPlanThreads));
   // Pair counts from the masks: partials on the CUs the solver leaves idle,
   // their sums in the quota launch (with one split the partials are final).
-  PairArgs pa = pair_args(d, scan_mask, prev_mask, cooc, trans, part, kPlanThreads);
-  if (!scan_mask) pa.nz = 0;
+  PairArgs pa = pair_args(d, scan.mask, prev_mask, cooc, trans, part, kPlanThreads);
+  if (!scan.mask) pa.nz = 0;
   const int64_t n_pair = (int64_t)pair_blocks(d) * pa.splits * pa.nz;
   const int64_t n_reduce = pa.splits > 1 ? (int64_t)pair_blocks(d) * (kPairBlock / kQuotaThreads) * pa.nz : 0;
   if (n_pair > 0) lds = std::max(lds, sizeof(int32_t) * (size_t)kPairBlock);
@@ -1024,13 +1037,29 @@ hipError_t launch_plan(const Dims& d, const int32_t* omega, const uint64_t* scan
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(1 + n_scan + n_pair)), dim3(kPlanThreads), lds, st, d, ly, omega,
-                     scan_mask, scan_base, scan_omega, scan_count, out, ws, pa, n_scan);
+                     scan, out, ws, pa, n_scan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_transport = d.B < d.E ? d.B : d.E;  // each replicated expert owns at least one replica
   const int n_fill = (int)(((int64_t)d.R * d.cap + kFillCells - 1) / kFillCells);
-  hipLaunchKernelGGL(quota_kernel, dim3((unsigned)(n_transport + n_fill + 1 + n_reduce)), dim3(kQuotaThreads), 0, st, d,
-                     omega, out, ws, n_transport, n_fill, pa);
+  const int n_off = inst_offset ? 1 : 0;
+  hipLaunchKernelGGL(quota_kernel, dim3((unsigned)(n_transport + n_fill + n_off + n_reduce)), dim3(kQuotaThreads), 0,
+                     st, d, omega, out, inst_offset, rank_offset, ws, n_transport, n_fill, pa);
+  return hipGetLastError();
+}
+
+namespace {
+
+__global__ __launch_bounds__(256) void zero_kernel(int32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_zero(int32_t* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 

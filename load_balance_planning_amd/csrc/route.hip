@@ -388,7 +388,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(Dims d, const uint64_t* __re
                                                     int32_t* __restrict__ tile_base, int32_t* __restrict__ omega,
                                                     int32_t* __restrict__ count) {
   extern __shared__ int32_t smem_scan[];
-  tile_scan_block<1024>(d, tile_mask, tile_base, omega, count, blockIdx.x, smem_scan);
+  tile_scan_block<1024>(d, tile_mask, tile_base, omega, count, nullptr, nullptr, blockIdx.x, smem_scan);
 }
 
 // Sums of the pair-count partials (pair_count.h), 256 threads per workgroup.
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(1024) void scan_pair_kernel(Dims d, const uint64_t*
                                                          int32_t* __restrict__ count, PairArgs pa, int n_scan) {
   extern __shared__ int32_t smem_scan[];
   if ((int)blockIdx.x < n_scan) {
-    tile_scan_block<1024>(d, tile_mask, tile_base, omega, count, blockIdx.x, smem_scan);
+    tile_scan_block<1024>(d, tile_mask, tile_base, omega, count, nullptr, nullptr, blockIdx.x, smem_scan);
     return;
   }
   const int q = (int)blockIdx.x - n_scan, nb = pair_blocks(d);

@@ -3,7 +3,8 @@
 // For a block of kScanEB experts and every source rank: the routing matrix
 // row sums omega[s][e] = sum of popcount(tile_mask[x][e]) over the tiles x of
 // source s ([TopoEP] Eq. 3), the expert counts, and tile_base[x][e], the
-// exclusive prefix of those popcounts over all tiles in token order.  Thread
+// exclusive prefix of those popcounts over all tiles in token order; or,
+// instead of writing the routing matrix, a comparison with a given one.  Thread
 // (row, e) of the workgroup: NTHR / kScanEB rows; when there are fewer
 // sources than rows each source's tiles are split over several rows.
 // Prefixes go over the rows of a source (chunks of tiles), then over sources.
@@ -22,11 +23,14 @@ inline size_t tile_scan_lds_bytes(const Dims& d, int nthr) {
   return sizeof(int32_t) * ((size_t)d.R * rps * kScanEB + (size_t)d.R * kScanEB);
 }
 
-// Expert block blk (experts blk*kScanEB ...).  omega and count may be null.
+// Expert block blk (experts blk*kScanEB ...).  tile_base, omega, count and
+// check may be null; a routing-matrix entry that differs from check sets
+// MOE_STATUS_BAD_OMEGA in *status.
 template <int NTHR>
 __device__ __forceinline__ void tile_scan_block(const Dims& d, const uint64_t* __restrict__ tile_mask,
                                                 int32_t* __restrict__ tile_base, int32_t* __restrict__ omega,
-                                                int32_t* __restrict__ count, int blk, int32_t* smem) {
+                                                int32_t* __restrict__ count, const int32_t* __restrict__ check,
+                                                int32_t* __restrict__ status, int blk, int32_t* smem) {
   constexpr int kRows = NTHR / kScanEB;
   const int el = threadIdx.x % kScanEB, row = threadIdx.x / kScanEB;
   const int e = blk * kScanEB + el;
@@ -58,7 +62,11 @@ __device__ __forceinline__ void tile_scan_block(const Dims& d, const uint64_t* _
       run += v;
     }
     tot[src * kScanEB + l] = run;
-    if (omega && blk * kScanEB + l < d.E) omega[(int64_t)src * d.E + blk * kScanEB + l] = run;
+    if (blk * kScanEB + l < d.E) {
+      const int64_t at = (int64_t)src * d.E + blk * kScanEB + l;
+      if (omega) omega[at] = run;
+      if (check && check[at] != run) atomicOr(status, MOE_STATUS_BAD_OMEGA);
+    }
   }
   __syncthreads();
   if (threadIdx.x < kScanEB) {
@@ -71,6 +79,7 @@ __device__ __forceinline__ void tile_scan_block(const Dims& d, const uint64_t* _
     if (ok && count) count[e] = run;
   }
   __syncthreads();
+  if (!tile_base) return;
   for (int r = row; r < R * rps; r += kRows) {
     const int src = r / rps, ch = r - src * rps;
     const int c0 = ch * cc, c1 = min(C, c0 + cc);

@@ -1,14 +1,21 @@
 // A caller of the C ABI with no Python and no torch: device buffers from
-// hipMalloc, a stream of its own, the whole pass in one moe_plan_step call.
-// Test helper for tests/test_gpu_c_caller.py.
+// hipMalloc, a stream of its own.  Test helper for tests/test_gpu_c_caller.py.
 //
 //   c_abi_caller <dir>
 // reads  <dir>/cfg.txt     "T E k R G H B" (the other fields: derived defaults)
 //        <dir>/logits.f32  float [T][E]
 //        <dir>/hidden.u16  bf16 bit patterns [T][H]
-// writes <dir>/<name>.bin for every output of the step (raw little-endian
-// arrays, the layouts of include/moe_plan.h) and prints "ok".  Any failing
-// call prints its name and code and exits non-zero.
+//        <dir>/omega.i32   int32 [R][E]  a routing matrix handed to the planner
+//        <dir>/topk.i32    int32 [T][k]  the top-k that matrix counts
+// and runs the path three ways on one handle:
+//   step_*    moe_plan_step (one call)
+//   staged_*  moe_plan_route, moe_plan_plan on the route's omega and topk_idx,
+//             moe_plan_dispatch (three calls)
+//   given_*   moe_plan_plan on omega.i32 / topk.i32, then moe_plan_dispatch
+// writing <dir>/<way>_<name>.bin for every output (raw little-endian arrays,
+// the layouts of include/moe_plan.h), then prints "ok".  Every output buffer
+// is filled with 0xff bytes before each way, so each file holds what that
+// way wrote.  Any failing call prints its name and code and exits non-zero.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -46,27 +53,41 @@ std::vector<char> read_file(const std::string& path, size_t bytes) {
 }
 
 struct DevBuf {
+  const char* name = nullptr;
   void* p = nullptr;
   size_t bytes = 0;
 };
 
-DevBuf alloc(size_t bytes) {
+DevBuf alloc(const char* name, size_t bytes) {
   DevBuf b;
+  b.name = name;
   b.bytes = bytes;
   hip_check(hipMalloc(&b.p, bytes > 0 ? bytes : 1), "hipMalloc");
   return b;
 }
 
-void save(const std::string& dir, const char* name, const DevBuf& b) {
+DevBuf upload(const std::string& path, size_t bytes) {
+  DevBuf b = alloc("input", bytes);
+  const std::vector<char> host = read_file(path, bytes);
+  if (bytes > 0) hip_check(hipMemcpy(b.p, host.data(), bytes, hipMemcpyHostToDevice), "hipMemcpy");
+  return b;
+}
+
+void save(const std::string& dir, const std::string& way, const DevBuf& b) {
   std::vector<char> host(b.bytes);
   if (b.bytes > 0) hip_check(hipMemcpy(host.data(), b.p, b.bytes, hipMemcpyDeviceToHost), "hipMemcpy");
-  const std::string path = dir + "/" + name + ".bin";
+  const std::string path = dir + "/" + way + "_" + b.name + ".bin";
   FILE* f = std::fopen(path.c_str(), "wb");
   if (!f || std::fwrite(host.data(), 1, host.size(), f) != host.size()) {
     std::fprintf(stderr, "cannot write %s\n", path.c_str());
     std::exit(2);
   }
   std::fclose(f);
+}
+
+template <typename T>
+T* as(const DevBuf& b) {
+  return static_cast<T*>(b.p);
 }
 
 }  // namespace
@@ -101,64 +122,72 @@ int main(int argc, char** argv) {
   hip_check(hipStreamCreate(&stream), "hipStreamCreate");
 
   const size_t i4 = sizeof(int32_t);
-  const size_t logits_bytes = (size_t)cfg.T * cfg.E * sizeof(float);
-  const size_t hidden_bytes = (size_t)cfg.T * cfg.H * sizeof(uint16_t);
-  DevBuf logits = alloc(logits_bytes), hidden = alloc(hidden_bytes);
-  {
-    const std::vector<char> lg = read_file(dir + "/logits.f32", logits_bytes);
-    const std::vector<char> hd = read_file(dir + "/hidden.u16", hidden_bytes);
-    hip_check(hipMemcpy(logits.p, lg.data(), logits_bytes, hipMemcpyHostToDevice), "hipMemcpy");
-    hip_check(hipMemcpy(hidden.p, hd.data(), hidden_bytes, hipMemcpyHostToDevice), "hipMemcpy");
-  }
-  DevBuf topk_idx = alloc(sz.topk * i4), topk_val = alloc(sz.topk * sizeof(float)), count = alloc(sz.experts * i4);
-  DevBuf omega = alloc(sz.omega * i4), cooc = alloc(sz.pair * i4);
-  DevBuf tile_mask = alloc(sz.tile_words * sizeof(uint64_t)), tile_base = alloc(sz.tile_words * i4);
-  DevBuf n_inst = alloc(i4), inst_expert = alloc(sz.inst_cap * i4), inst_rank = alloc(sz.inst_cap * i4);
-  DevBuf inst_load = alloc(sz.inst_cap * i4), rank_load = alloc((size_t)cfg.R * i4), quota = alloc(sz.quota * i4);
-  DevBuf slot_inst = alloc(sz.topk * i4), slot_rank = alloc(sz.topk * i4);
-  DevBuf inst_offset = alloc(sz.inst_offset * i4), rank_offset = alloc(sz.rank_offset * i4);
-  DevBuf perm = alloc(sz.topk * i4), slot_pos = alloc(sz.topk * i4);
-  DevBuf dispatch = alloc(sz.dispatch_elems * sizeof(uint16_t));
+  DevBuf logits = upload(dir + "/logits.f32", (size_t)cfg.T * cfg.E * sizeof(float));
+  DevBuf hidden = upload(dir + "/hidden.u16", (size_t)cfg.T * cfg.H * sizeof(uint16_t));
+  DevBuf given_omega = upload(dir + "/omega.i32", (size_t)sz.omega * i4);
+  DevBuf given_topk = upload(dir + "/topk.i32", (size_t)sz.topk * i4);
 
-  moe_route_out route{static_cast<int32_t*>(topk_idx.p), static_cast<float*>(topk_val.p),
-                      static_cast<int32_t*>(count.p),    static_cast<int32_t*>(omega.p),
-                      static_cast<int32_t*>(cooc.p),     nullptr,
-                      static_cast<uint64_t*>(tile_mask.p), static_cast<int32_t*>(tile_base.p)};
-  moe_plan_out plan{static_cast<int32_t*>(n_inst.p),    static_cast<int32_t*>(inst_expert.p),
-                    static_cast<int32_t*>(inst_rank.p), static_cast<int32_t*>(inst_load.p),
-                    static_cast<int32_t*>(rank_load.p), static_cast<int32_t*>(quota.p),
-                    static_cast<int32_t*>(slot_inst.p), static_cast<int32_t*>(slot_rank.p),
-                    static_cast<int32_t*>(inst_offset.p), static_cast<int32_t*>(rank_offset.p)};
-  moe_dispatch_out disp{static_cast<int32_t*>(perm.p), static_cast<int32_t*>(slot_pos.p),
-                        static_cast<uint16_t*>(dispatch.p)};
+  std::vector<DevBuf> outs = {
+      alloc("topk_idx", sz.topk * i4),        alloc("topk_val", sz.topk * sizeof(float)),
+      alloc("count", sz.experts * i4),        alloc("omega", sz.omega * i4),
+      alloc("cooc", sz.pair * i4),            alloc("n_inst", i4),
+      alloc("inst_expert", sz.inst_cap * i4), alloc("inst_rank", sz.inst_cap * i4),
+      alloc("inst_load", sz.inst_cap * i4),   alloc("rank_load", (size_t)cfg.R * i4),
+      alloc("quota", sz.quota * i4),          alloc("slot_inst", sz.topk * i4),
+      alloc("slot_rank", sz.topk * i4),       alloc("perm", sz.topk * i4),
+      alloc("slot_pos", sz.topk * i4),        alloc("inst_offset", sz.inst_offset * i4),
+      alloc("rank_offset", sz.rank_offset * i4), alloc("dispatch", sz.dispatch_elems * sizeof(uint16_t))};
+  auto buf = [&](const char* name) -> const DevBuf& {
+    for (const DevBuf& b : outs)
+      if (std::string(b.name) == name) return b;
+    std::fprintf(stderr, "no buffer %s\n", name);
+    std::exit(2);
+  };
+  const moe_route_out route{as<int32_t>(buf("topk_idx")), as<float>(buf("topk_val")), as<int32_t>(buf("count")),
+                            as<int32_t>(buf("omega")),    as<int32_t>(buf("cooc")),   nullptr};
+  const moe_plan_out plan{as<int32_t>(buf("n_inst")),    as<int32_t>(buf("inst_expert")),
+                          as<int32_t>(buf("inst_rank")), as<int32_t>(buf("inst_load")),
+                          as<int32_t>(buf("rank_load")), as<int32_t>(buf("quota")),
+                          as<int32_t>(buf("slot_inst")), as<int32_t>(buf("slot_rank"))};
+  const moe_dispatch_out disp{as<int32_t>(buf("perm")), as<int32_t>(buf("slot_pos")), as<int32_t>(buf("inst_offset")),
+                              as<int32_t>(buf("rank_offset")), as<uint16_t>(buf("dispatch"))};
 
-  abi_check(moe_plan_step(h, static_cast<const float*>(logits.p), nullptr, static_cast<const uint16_t*>(hidden.p),
-                          &route, &plan, &disp, stream),
+  auto poison = [&]() {
+    for (const DevBuf& b : outs) hip_check(hipMemsetAsync(b.p, 0xff, b.bytes, stream), "hipMemsetAsync");
+  };
+  auto finish = [&](const char* way) {
+    hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize");
+    int32_t flags = -1;
+    abi_check(moe_plan_status(h, &flags), "moe_plan_status");
+    if (flags != 0) {
+      std::fprintf(stderr, "%s: status flags %d\n", way, flags);
+      std::exit(5);
+    }
+    for (const DevBuf& b : outs) save(dir, way, b);
+  };
+
+  poison();
+  abi_check(moe_plan_step(h, as<const float>(logits), nullptr, as<const uint16_t>(hidden), &route, &plan, &disp,
+                          stream),
             "moe_plan_step");
-  hip_check(hipStreamSynchronize(stream), "hipStreamSynchronize");
-  int32_t flags = -1;
-  abi_check(moe_plan_status(h, &flags), "moe_plan_status");
-  if (flags != 0) {
-    std::fprintf(stderr, "status flags %d\n", flags);
-    return 5;
-  }
-  const struct {
-    const char* name;
-    const DevBuf* buf;
-  } outs[] = {{"topk_idx", &topk_idx}, {"topk_val", &topk_val}, {"count", &count},     {"omega", &omega},
-              {"cooc", &cooc},         {"n_inst", &n_inst},     {"inst_expert", &inst_expert},
-              {"inst_rank", &inst_rank}, {"inst_load", &inst_load}, {"rank_load", &rank_load},
-              {"quota", &quota},       {"slot_inst", &slot_inst}, {"slot_rank", &slot_rank},
-              {"inst_offset", &inst_offset}, {"rank_offset", &rank_offset}, {"perm", &perm},
-              {"slot_pos", &slot_pos}, {"dispatch", &dispatch}};
-  for (const auto& o : outs) save(dir, o.name, *o.buf);
+  finish("step");
+
+  poison();
+  abi_check(moe_plan_route(h, as<const float>(logits), nullptr, &route, stream), "moe_plan_route");
+  abi_check(moe_plan_plan(h, route.omega, route.topk_idx, &plan, stream), "moe_plan_plan");
+  abi_check(moe_plan_dispatch(h, &plan, as<const uint16_t>(hidden), &disp, stream), "moe_plan_dispatch");
+  finish("staged");
+
+  poison();
+  abi_check(moe_plan_plan(h, as<const int32_t>(given_omega), as<const int32_t>(given_topk), &plan, stream),
+            "moe_plan_plan (given matrix)");
+  abi_check(moe_plan_dispatch(h, &plan, as<const uint16_t>(hidden), &disp, stream), "moe_plan_dispatch");
+  finish("given");
 
   moe_plan_destroy(h);
   hip_check(hipStreamDestroy(stream), "hipStreamDestroy");
-  for (const DevBuf* b : {&logits, &hidden, &topk_idx, &topk_val, &count, &omega, &cooc, &tile_mask, &tile_base,
-                          &n_inst, &inst_expert, &inst_rank, &inst_load, &rank_load, &quota, &slot_inst,
-                          &slot_rank, &inst_offset, &rank_offset, &perm, &slot_pos, &dispatch})
-    hip_check(hipFree(b->p), "hipFree");
+  for (const DevBuf* b : {&logits, &hidden, &given_omega, &given_topk}) hip_check(hipFree(b->p), "hipFree");
+  for (const DevBuf& b : outs) hip_check(hipFree(b.p), "hipFree");
   std::printf("ok\n");
   return 0;
 }

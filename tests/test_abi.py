@@ -39,13 +39,16 @@ def test_library_exports_every_declared_symbol():
 def test_query_sizes_and_validation():
     import load_balance_planning_amd as m
     s = m.moe_plan_query(m.make_config(32768, 256, 8, 64, 8, 7168, 32))
-    assert (s.topk, s.omega, s.pair, s.tiles, s.inst_cap, s.quota) == (262144, 16384, 65536, 512, 288, 64 * 288)
+    assert (s.topk, s.omega, s.pair, s.inst_cap, s.quota) == (262144, 16384, 65536, 288, 64 * 288)
+    assert (s.inst_offset, s.rank_offset) == (289, 65)
+    # the handle's workspace holds the presence masks and tile prefixes: 512 tiles of 64 tokens, 12 bytes each
+    assert s.workspace_bytes >= 512 * 256 * 12
     assert s.dispatch_elems == 32768 * 8 * 7168 and s.n_slot == 1
     assert s.token_bytes == 2 * 7168 and s.expert_bytes == 9 * 7168 * 7168 // 4
     s = m.moe_plan_query(m.make_config(16384, 128, 8, 8, 4, 2048, 16))
-    assert s.n_slot == 2 and s.tiles == 8 * 32
+    assert s.n_slot == 2
     s = m.moe_plan_query(m.make_config(800, 256, 8, 8, 8, 13, 4))   # 100 tokens per rank: 2 tiles each
-    assert s.tiles == 16
+    assert s.workspace_bytes >= 16 * 256 * 12
     bad = [m.make_config(100, 8, 2, 3, 1, 16, 0),      # T % R
            m.make_config(96, 9, 2, 3, 2, 16, 0),       # R % G
            m.make_config(96, 8, 9, 4, 2, 16, 0),       # k > E
@@ -69,7 +72,7 @@ def test_every_call_rejects_a_null_handle_synchronously():
     calls = {
         "moe_plan_route": (None, None, None, None, None),
         "moe_plan_hist": (None, None, None, None, None),
-        "moe_plan_plan": (None, None, None, None),
+        "moe_plan_plan": (None, None, None, None, None),
         "moe_plan_dispatch": (None, None, None, None, None),
         "moe_plan_step": (None,) * 8,
         "moe_plan_combine": (None,) * 6,
@@ -85,6 +88,7 @@ def test_every_call_rejects_a_null_handle_synchronously():
         "moe_plan_create": (None, None),
         "moe_plan_query": (None, None),
         "moe_plan_device_info": (0, None),
+        "moe_plan_set_events": (None, None, None),
     }
     assert set(calls) | {"moe_plan_destroy"} == set(declared_functions())
     for name, args in calls.items():

@@ -1,7 +1,8 @@
 """The C ABI from a caller with no Python and no torch (tests/c_abi_caller.cpp:
-hipMalloc'd buffers, its own stream, moe_plan_query / create / step / status /
-destroy), run as a child process; every output it writes must equal the
-oracle's byte for byte."""
+hipMalloc'd buffers, its own stream), run as a child process.  It runs the path
+three ways on one handle -- moe_plan_step; route, plan and dispatch as three
+calls; plan and dispatch from a routing matrix and top-k it is handed -- and
+every output of every way must equal the oracle's byte for byte."""
 from __future__ import annotations
 
 import os
@@ -24,6 +25,10 @@ OUTPUTS = {"topk_idx": np.int32, "topk_val": np.float32, "count": np.int32, "ome
            "dispatch": np.uint16}
 
 
+PLAN_DISPATCH = ("n_inst", "inst_expert", "inst_rank", "inst_load", "rank_load", "quota", "slot_inst", "slot_rank",
+                 "inst_offset", "rank_offset", "perm", "slot_pos", "dispatch")
+
+
 @pytest.mark.parametrize("shape", [(4096, 64, 4, 8, 4, 64, 8), (1600, 256, 8, 16, 8, 24, 16)])
 def test_c_caller_matches_the_oracle(tmp_path, shape):
     if not os.path.exists(EXE):  # built by __graft_entry__.build(); built here only when missing
@@ -35,15 +40,19 @@ def test_c_caller_matches_the_oracle(tmp_path, shape):
     print("C caller T=%d E=%d k=%d R=%d G=%d H=%d B=%d" % shape, flush=True)
     lg = inputs.random_logits(T + E, T, E)
     hid = inputs.random_hidden(T + H, T, H)
+    o = oracle.run_all(oracle.make_cfg(T, E, k, R, G, H, B), lg, hid)
     (tmp_path / "cfg.txt").write_text("%d %d %d %d %d %d %d\n" % shape)
     lg.astype(np.float32).tofile(tmp_path / "logits.f32")
     hid.astype(np.uint16).tofile(tmp_path / "hidden.u16")
+    np.ascontiguousarray(o["omega"], np.int32).tofile(tmp_path / "omega.i32")
+    np.ascontiguousarray(o["topk_idx"], np.int32).tofile(tmp_path / "topk.i32")
     r = subprocess.run([EXE, str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
-    o = oracle.run_all(oracle.make_cfg(T, E, k, R, G, H, B), lg, hid)
-    for name, dt in OUTPUTS.items():
-        got = np.fromfile(tmp_path / (name + ".bin"), dtype=dt)
-        want = np.ascontiguousarray(o[name]).astype(dt).reshape(-1)
-        if dt is np.float32:
-            got, want = got.view(np.uint32), want.view(np.uint32)
-        np.testing.assert_array_equal(got, want, err_msg=name)
+    for way, names in (("step", tuple(OUTPUTS)), ("staged", tuple(OUTPUTS)), ("given", PLAN_DISPATCH)):
+        for name in names:
+            dt = OUTPUTS[name]
+            got = np.fromfile(tmp_path / ("%s_%s.bin" % (way, name)), dtype=dt)
+            want = np.ascontiguousarray(o[name]).astype(dt).reshape(-1)
+            if dt is np.float32:
+                got, want = got.view(np.uint32), want.view(np.uint32)
+            np.testing.assert_array_equal(got, want, err_msg="%s %s" % (way, name))

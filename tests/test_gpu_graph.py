@@ -29,10 +29,10 @@ def mp():
 def outputs(layer):
     r, p, d = layer.route_out, layer.plan_out, layer.dispatch_out
     named = dict(topk_idx=r.topk_idx, topk_val=r.topk_val, expert_count=r.expert_count, omega=r.omega,
-                 cooc=r.cooc, trans=r.trans, tile_mask=r.tile_mask, tile_base=r.tile_base, n_inst=p.n_inst,
+                 cooc=r.cooc, trans=r.trans, n_inst=p.n_inst,
                  inst_expert=p.inst_expert, inst_rank=p.inst_rank, inst_load=p.inst_load, rank_load=p.rank_load,
-                 quota=p.quota, slot_inst=p.slot_inst, slot_rank=p.slot_rank, inst_offset=p.inst_offset,
-                 rank_offset=p.rank_offset, perm=d.perm, slot_pos=d.slot_pos, dispatch=d.dispatch)
+                 quota=p.quota, slot_inst=p.slot_inst, slot_rank=p.slot_rank, inst_offset=d.inst_offset,
+                 rank_offset=d.rank_offset, perm=d.perm, slot_pos=d.slot_pos, dispatch=d.dispatch)
     return {k: v for k, v in named.items() if v is not None}
 
 

@@ -56,9 +56,11 @@ def gpu_layer(mp, cfg, logits=None, topk=None, hidden=None, prev_topk=None, tran
     else:
         if logits is not None:
             layer.route(torch.from_numpy(np.ascontiguousarray(logits)).to(dev), prev)
+            layer.plan()
         else:
-            layer.hist(torch.from_numpy(np.ascontiguousarray(topk, np.int32)).to(dev), prev)
-        layer.plan()
+            tk = torch.from_numpy(np.ascontiguousarray(topk, np.int32)).to(dev)
+            layer.hist(tk, prev)
+            layer.plan(topk_idx=tk)  # the route output's routing matrix with the given top-k
         layer.dispatch(hid)
     torch.cuda.synchronize()
     r, p, d = layer.route_out, layer.plan_out, layer.dispatch_out
@@ -66,7 +68,7 @@ def gpu_layer(mp, cfg, logits=None, topk=None, hidden=None, prev_topk=None, tran
                cooc=npy(r.cooc), trans=npy(r.trans), n_inst=npy(p.n_inst), inst_expert=npy(p.inst_expert),
                inst_rank=npy(p.inst_rank), inst_load=npy(p.inst_load), rank_load=npy(p.rank_load),
                quota=npy(p.quota), slot_inst=npy(p.slot_inst), slot_rank=npy(p.slot_rank), perm=npy(d.perm),
-               slot_pos=npy(d.slot_pos), inst_offset=npy(p.inst_offset), rank_offset=npy(p.rank_offset),
+               slot_pos=npy(d.slot_pos), inst_offset=npy(d.inst_offset), rank_offset=npy(d.rank_offset),
                dispatch=npy(d.dispatch).view(np.uint16))
     out["status"] = layer.status()
     layer.close()
@@ -156,8 +158,8 @@ def test_workload_forced_inter_node_stage(mp, name):
 def run_plan_only(mp, cfg, omega):
     """Plan from a given routing matrix (no tokens): T = 0 layers."""
     layer = mp.Layer(cfg, cooc=False, topk_val=False)
-    layer.route_out.omega.copy_(torch.from_numpy(np.asarray(omega, np.int32)))
-    layer.plan()
+    om = torch.from_numpy(np.asarray(omega, np.int32)).to(layer.device)
+    layer.plan(om, torch.zeros((0, cfg.k), dtype=torch.int32, device=layer.device))
     torch.cuda.synchronize()
     p = layer.plan_out
     out = {k: npy(getattr(p, k)) for k in ("n_inst", "inst_expert", "inst_rank", "inst_load", "rank_load", "quota")}
@@ -182,6 +184,28 @@ def test_fig9_example_on_gpu(mp):
     cfg = mp.make_config(c["T"], c["E"], c["k"], c["R"], c["G"], c["H"], c["B"], c["n_slot"], c["W"], c["S"])
     got = run_plan_only(mp, cfg, g["omega"])
     assert list(got["rank_load"]) == ex["rank_load"] and list(got["inst_expert"]) == ex["inst_expert"]
+
+
+@pytest.mark.parametrize("fixture", ["stage1_spread_example.json", "quota_order_example.json"])
+def test_hand_derived_examples_on_gpu(mp, fixture):
+    """The hand-derived stage-1 spreading and quota-order examples, planned on the GPU from their
+    routing matrices (no tokens): equal to the oracle and to the fixture's expected values."""
+    g = json.load(open(os.path.join(GOLDEN, fixture)))
+    c = g["config"]
+    for over in [{}] + [v["override"] for v in g.get("variants", [])]:
+        cc = dict(c, **over)
+        cfg = mp.make_config(cc["T"], cc["E"], cc["k"], cc["R"], cc["G"], cc["H"], cc["B"], cc["n_slot"], cc["W"],
+                             cc["S"], cc["max_iters"])
+        got = run_plan_only(mp, cfg, g["omega"])
+        want = oracle.plan(ocfg(cfg), np.asarray(g["omega"], np.int32), np.zeros((0, cc["k"]), np.int32))
+        for k in ("n_inst", "inst_expert", "inst_rank", "inst_load", "rank_load", "quota"):
+            np.testing.assert_array_equal(got[k].reshape(-1), want[k].reshape(-1), err_msg=str(over) + k)
+        assert got["status"] == 0
+        if not over:
+            ex = g["expected"]
+            assert list(got["rank_load"]) == ex["rank_load"] and list(got["inst_expert"]) == ex["inst_expert"]
+            q = got["quota"]
+            assert [[int(s), int(i), int(q[s, i])] for s, i in zip(*np.nonzero(q))] == ex["quota_nonzero"]
 
 
 def test_even_split_example_on_gpu(mp):
@@ -313,3 +337,91 @@ def test_gpu_runs_are_bitwise_identical(mp):
     for k, v in a.items():
         if isinstance(v, np.ndarray):
             assert np.array_equal(v, b[k]), k
+
+
+# ---------------------------------------------------------------------------
+# The plan call on its own inputs: a routing matrix and the top-k it counts
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["qwen3_layer", "deepseek_v3_layer", "kimi_layer"])
+def test_plan_from_a_given_routing_matrix(mp, name):
+    """moe_plan_plan takes the routing matrix and the top-k from the caller (here the oracle's,
+    as a gathered matrix would arrive), with no route call on the handle: the plan and the
+    dispatch that follows it match the oracle byte for byte."""
+    w = synth.WORKLOADS[name]
+    cfg = workload_cfg(mp, w, expert_bytes=0)
+    cfg.H = 64
+    lg = synth.all_logits(w)[0]
+    hid = synth.hidden(w, H=64)
+    o = oracle_layer(cfg, logits=lg, hidden=hid)
+    print("plan from a given matrix: %s" % name, flush=True)
+    layer = mp.Layer(cfg, cooc=False, topk_val=False)
+    dev = layer.device
+    om = torch.from_numpy(np.ascontiguousarray(o["omega"], np.int32)).to(dev)
+    tk = torch.from_numpy(np.ascontiguousarray(o["topk_idx"], np.int32)).to(dev)
+    layer.plan(om, tk)
+    layer.dispatch(torch.from_numpy(hid.view(np.int16)).to(dev))
+    torch.cuda.synchronize()
+    p, d = layer.plan_out, layer.dispatch_out
+    got = {k: npy(getattr(p, k)) for k in ("n_inst", "inst_expert", "inst_rank", "inst_load", "rank_load", "quota",
+                                            "slot_inst", "slot_rank")}
+    got.update({k: npy(getattr(d, k)) for k in ("perm", "slot_pos", "inst_offset", "rank_offset")})
+    for k, v in got.items():
+        np.testing.assert_array_equal(v.reshape(-1), np.asarray(o[k]).reshape(-1), err_msg=name + " " + k)
+    assert np.array_equal(npy(d.dispatch).view(np.uint16), o["dispatch"]), name + " dispatch rows"
+    assert layer.status() == 0
+    layer.close()
+
+
+def test_plan_flags_a_routing_matrix_that_does_not_match_the_top_k(mp):
+    """A routing matrix that is not the top-k's own sets MOE_STATUS_BAD_OMEGA (the outputs are
+    then unspecified, but every write stays in its buffer); a consistent pair sets nothing."""
+    T, E, k, R, G, H = 1024, 32, 4, 8, 4, 8
+    cfg = mp.make_config(T, E, k, R, G, H, 8, expert_bytes=0)
+    topk = inputs.random_topk(77, T, E, k, skew=1.2)
+    o = oracle_layer(cfg, topk=topk, hidden=inputs.random_hidden(3, T, H))
+    layer = mp.Layer(cfg, cooc=False, topk_val=False)
+    dev = layer.device
+    tk = torch.from_numpy(topk).to(dev)
+    om = torch.from_numpy(np.ascontiguousarray(o["omega"], np.int32)).to(dev)
+    layer.plan(om, tk)
+    torch.cuda.synchronize()
+    assert layer.status() == 0
+    bad = o["omega"].copy()
+    bad[3, 5] += 1
+    bad[3, 6] -= 1 if bad[3, 6] > 0 else -1
+    layer.plan(torch.from_numpy(np.ascontiguousarray(bad, np.int32)).to(dev), tk)
+    torch.cuda.synchronize()
+    assert layer.status() & mp.MOE_STATUS_BAD_OMEGA
+    layer.close()
+
+
+def test_step_after_a_stale_hip_error(mp):
+    """A HIP error left by the caller's own earlier call (here a host-side one: selecting device
+    -1) is not reported by the next step, and the step after it plans from the right routing
+    matrix: the workspace accumulator the step uses is clean before and after."""
+    import ctypes
+    w = synth.WORKLOADS["qwen3_layer"]
+    cfg = workload_cfg(mp, w)
+    cfg.H = 64
+    lg = synth.logits(w)
+    hid = synth.hidden(w, H=64)
+    o = oracle_layer(cfg, logits=lg, hidden=hid)
+    layer = mp.Layer(cfg, cooc=False)
+    dev = layer.device
+    lg_d = torch.from_numpy(lg).to(dev)
+    hid_d = torch.from_numpy(hid.view(np.int16)).to(dev)
+    torch.cuda.synchronize()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    assert hip.hipSetDevice(-1) != 0  # leaves a host-side error behind, touches no device state
+    for rep in range(2):
+        layer.step(lg_d, hid_d)
+        torch.cuda.synchronize()
+        p, d = layer.plan_out, layer.dispatch_out
+        for k in ("n_inst", "inst_expert", "inst_load", "rank_load", "quota", "slot_inst"):
+            np.testing.assert_array_equal(npy(getattr(p, k)).reshape(-1), np.asarray(o[k]).reshape(-1),
+                                          err_msg="step %d %s" % (rep, k))
+        np.testing.assert_array_equal(npy(d.perm), o["perm"], err_msg="step %d perm" % rep)
+        assert layer.status() == 0
+    layer.close()

@@ -40,8 +40,8 @@ def small_outputs(layer):
     r, p, d = layer.route_out, layer.plan_out, layer.dispatch_out
     return dict(topk_idx=r.topk_idx, expert_count=r.expert_count, omega=r.omega, cooc=r.cooc, n_inst=p.n_inst,
                 inst_expert=p.inst_expert, inst_rank=p.inst_rank, inst_load=p.inst_load, rank_load=p.rank_load,
-                quota=p.quota, slot_inst=p.slot_inst, slot_rank=p.slot_rank, inst_offset=p.inst_offset,
-                rank_offset=p.rank_offset, perm=d.perm, slot_pos=d.slot_pos)
+                quota=p.quota, slot_inst=p.slot_inst, slot_rank=p.slot_rank, inst_offset=d.inst_offset,
+                rank_offset=d.rank_offset, perm=d.perm, slot_pos=d.slot_pos)
 
 
 def test_two_stream_pipeline_full_size(mp):
