@@ -386,6 +386,26 @@ int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* prev_topk, c
                   void* stream);
 
 /*
+ * moe_plan_step without a handle and without any allocation, for callers that
+ * cannot call hipMalloc: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It runs the launches of moe_plan_step
+ * (same outputs, bit for bit) on the current HIP device, with the workspace in
+ * a fixed 32 MiB device array of the library (one per GPU, held until the
+ * process ends; the DeepSeek-V3-shaped layer with co-selection counts needs
+ * about 11 MiB).  A configuration whose workspace does not fit returns
+ * MOE_ERR_UNSUPPORTED and enqueues nothing; configuration and argument errors
+ * return as from moe_plan_create / moe_plan_step.
+ *   status  int32 [1] (device, caller-owned): zeroed by the call, then the
+ *           MOE_STATUS_* bits of this call (there is no moe_plan_status here).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (other streams, other threads) race and give unspecified results.
+ * Calls on one stream are ordered and safe.
+ */
+int moe_plan_step_static(const moe_plan_config* cfg, const float* logits, const int32_t* prev_topk,
+                         const uint16_t* hidden, const moe_route_out* route, const moe_plan_out* plan,
+                         const moe_dispatch_out* out, int32_t* status, void* stream);
+
+/*
  * Gate-weighted combine, the return path of the dispatch [TopoEP section 2.1,
  * Fig. 1]: for every token t,
  *   out[t][:] = bf16( sum over j = 0..k-1 of w[t][j] * expert_out[slot_pos[t*k+j]][:] )

@@ -91,7 +91,7 @@ class moe_dedup_out(ctypes.Structure):
 
 
 EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
-           "moe_plan_dispatch", "moe_plan_step", "moe_plan_combine", "moe_plan_place", "moe_plan_dedup_count",
+           "moe_plan_dispatch", "moe_plan_step", "moe_plan_step_static", "moe_plan_combine", "moe_plan_place", "moe_plan_dedup_count",
            "moe_plan_dedup_dispatch", "moe_plan_quality", "moe_plan_predict", "moe_plan_slot_map",
            "moe_plan_replica_pull", "moe_plan_replica_push", "moe_plan_set_events", "moe_plan_device_info",
            "moe_plan_status", "moe_plan_destroy")
@@ -119,6 +119,7 @@ def lib():
         l.moe_plan_plan.argtypes = [vp, vp, vp, vp, vp]
         l.moe_plan_dispatch.argtypes = [vp, vp, vp, vp, vp]
         l.moe_plan_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        l.moe_plan_step_static.argtypes = [vp] * 9
         l.moe_plan_combine.argtypes = [vp, vp, vp, vp, vp, vp]
         l.moe_plan_place.argtypes = [vp, vp, ctypes.c_int32, vp, vp]
         l.moe_plan_dedup_count.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp]
@@ -178,6 +179,13 @@ def moe_plan_step(h, logits: int, prev_topk, hidden: int, route: moe_route_out, 
                   out: moe_dispatch_out, stream: int):
     _check("moe_plan_step", lib().moe_plan_step(h, logits, prev_topk, hidden, ctypes.byref(route), ctypes.byref(plan),
                                                 ctypes.byref(out), stream))
+
+
+def moe_plan_step_static(cfg: moe_plan_config, logits: int, prev_topk, hidden: int, route: moe_route_out,
+                         plan: moe_plan_out, out: moe_dispatch_out, status: int, stream: int):
+    _check("moe_plan_step_static", lib().moe_plan_step_static(ctypes.byref(cfg), logits, prev_topk, hidden,
+                                                              ctypes.byref(route), ctypes.byref(plan),
+                                                              ctypes.byref(out), status, stream))
 
 
 def moe_plan_combine(h, topk_val: int, slot_pos: int, expert_out: int, out: int, stream: int):

@@ -54,8 +54,10 @@ WsLayout ws_layout(const moe::Dims& d) {
   return l;
 }
 
+}  // namespace
+
 // Validates the configuration and derives every dimension the kernels use.
-int derive(const moe_plan_config* c, moe::Dims* d) {
+int moe::derive_dims(const moe_plan_config* c, moe::Dims* d) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->T < 0 || c->E < 1 || c->k < 1 || c->k > c->E || c->R < 1 || c->G < 1 || c->H < 1 ||
       c->replica_budget < 0)
@@ -88,6 +90,8 @@ int derive(const moe_plan_config* c, moe::Dims* d) {
   return MOE_OK;
 }
 
+namespace {
+
 // Makes `device` current for the duration of a call and gives the caller's
 // current device back when the call returns.
 class DeviceScope {
@@ -117,7 +121,7 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 extern "C" int moe_plan_query(const moe_plan_config* cfg, moe_plan_sizes* sz) {
   moe::Dims d;
-  const int rc = derive(cfg, &d);
+  const int rc = moe::derive_dims(cfg, &d);
   if (rc != MOE_OK) return rc;
   if (!sz) return MOE_ERR_INVALID_ARG;
   sz->topk = (int64_t)d.T * d.k;
@@ -141,7 +145,7 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   if (!out) return MOE_ERR_INVALID_ARG;
   *out = nullptr;
   moe::Dims d;
-  const int rc = derive(cfg, &d);
+  const int rc = moe::derive_dims(cfg, &d);
   if (rc != MOE_OK) return rc;
   moe_plan* h = new (std::nothrow) moe_plan();
   if (!h) return MOE_ERR_INTERNAL;
@@ -182,6 +186,9 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   return MOE_OK;
 }
 
+int moe::check_step_args(const moe::Dims& d, const float* logits, const uint16_t* hidden, const moe_route_out* route,
+                         const moe_plan_out* plan, const moe_dispatch_out* out);
+
 namespace {
 
 int check_route_out(const moe::Dims& d, const moe_route_out* out) {
@@ -203,6 +210,18 @@ int check_dispatch_out(const moe::Dims& d, const moe_dispatch_out* out) {
   if (d.T > 0 && (!out->perm || !out->slot_pos || !out->dispatch)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
+
+}  // namespace
+
+int moe::check_step_args(const moe::Dims& d, const float* logits, const uint16_t* hidden, const moe_route_out* route,
+                         const moe_plan_out* plan, const moe_dispatch_out* out) {
+  if (check_route_out(d, route) != MOE_OK || check_plan_out(d, plan) != MOE_OK || check_dispatch_out(d, out) != MOE_OK)
+    return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!logits || !hidden)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+namespace {
 
 // Set-up shared by the calls that enqueue work: clears an error an earlier
 // HIP call of the caller left behind (so that a failure reported by this
@@ -288,15 +307,31 @@ extern "C" int moe_plan_dispatch(moe_plan_t h, const moe_plan_out* plan, const u
 extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* prev_topk, const uint16_t* hidden,
                              const moe_route_out* route, const moe_plan_out* plan, const moe_dispatch_out* out,
                              void* stream) {
-  if (!h || check_route_out(h->d, route) != MOE_OK || check_plan_out(h->d, plan) != MOE_OK ||
-      check_dispatch_out(h->d, out) != MOE_OK)
-    return MOE_ERR_INVALID_ARG;
+  if (!h || moe::check_step_args(h->d, logits, hidden, route, plan, out) != MOE_OK) return MOE_ERR_INVALID_ARG;
   const moe::Dims& d = h->d;
-  if (d.T > 0 && (!logits || !hidden)) return MOE_ERR_INVALID_ARG;
   const DeviceScope on_device(h->device);
   if (!on_device.ok()) return MOE_ERR_HIP;
   hipStream_t st = begin_call(h, stream);
-  const int32_t* prev = (prev_topk && route->trans) ? prev_topk : nullptr;
+  // If a launch fails after the top-k was queued, the accumulator may keep
+  // counts; the next call then clears it first.
+  const int64_t re = (int64_t)d.R * d.E;
+  hipError_t e = hipSuccess;
+  if (h->acc_dirty) {
+    e = moe::launch_zero(h->ws.omega_acc, re, st);
+    if (e != hipSuccess) return hip_rc(e);
+    h->acc_dirty = false;
+  }
+  h->acc_dirty = true;  // until the launch that clears the accumulator is queued
+  e = moe::enqueue_step(d, h->ws, logits, prev_topk, hidden, *route, *plan, *out, h->gather_ev, st);
+  if (e == hipSuccess) h->acc_dirty = false;
+  return hip_rc(e);
+}
+
+hipError_t moe::enqueue_step(const moe::Dims& d, const moe::Workspace& ws, const float* logits,
+                             const int32_t* prev_topk, const uint16_t* hidden, const moe_route_out& route,
+                             const moe_plan_out& plan, const moe_dispatch_out& out, const moe::KernelEvents& ev,
+                             hipStream_t st) {
+  const int32_t* prev = (prev_topk && route.trans) ? prev_topk : nullptr;
   // On `st`: top-k (which also accumulates the routing matrix into the
   // workspace accumulator, zero on entry) -> plan (the solver reads the
   // accumulator; workgroups on the CUs it leaves idle write the tile prefix,
@@ -304,39 +339,27 @@ extern "C" int moe_plan_step(moe_plan_t h, const float* logits, const int32_t* p
   // quotas and dispatch offsets (read the accumulator too; extra workgroups
   // sum the pair-count partials) -> slot instances + gather, which zero the
   // accumulator again: the handle carries no state from one call to the
-  // next, so the call can be captured in a HIP graph and replayed.  If a
-  // launch fails after the top-k was queued, the accumulator may keep counts;
-  // the next call then clears it first.
+  // next, so the call can be captured in a HIP graph and replayed.
   const int64_t re = (int64_t)d.R * d.E;
-  int32_t* acc = h->ws.omega_acc;
-  hipError_t e = hipSuccess;
-  if (h->acc_dirty) {
-    e = moe::launch_zero(acc, re, st);
-    if (e != hipSuccess) return hip_rc(e);
-    h->acc_dirty = false;
-  }
-  h->acc_dirty = true;  // until the launch that clears the accumulator is queued
-  e = moe::launch_route_topk(d, logits, prev, route->topk_idx, route->topk_val, h->ws.tile_mask, h->ws.prev_mask,
-                             acc, h->ws.status, st);
-  const moe::ScanJob scan{h->ws.tile_mask, h->ws.tile_base, route->omega, route->expert_count, nullptr};
+  int32_t* acc = ws.omega_acc;
+  hipError_t e = moe::launch_route_topk(d, logits, prev, route.topk_idx, route.topk_val, ws.tile_mask, ws.prev_mask,
+                                        acc, ws.status, st);
+  const moe::ScanJob scan{ws.tile_mask, ws.tile_base, route.omega, route.expert_count, nullptr};
   if (e == hipSuccess)
-    e = moe::launch_plan(d, acc, scan, h->ws.prev_mask, route->cooc, prev ? route->trans : nullptr, h->ws.pair_part,
-                         *plan, out->inst_offset, out->rank_offset, h->ws, st);
-  if (moe::gather_can_assign(d, hidden, out->dispatch)) {
+    e = moe::launch_plan(d, acc, scan, ws.prev_mask, route.cooc, prev ? route.trans : nullptr, ws.pair_part, plan,
+                         out.inst_offset, out.rank_offset, ws, st);
+  if (moe::gather_can_assign(d, hidden, out.dispatch)) {
     // the gather assigns its token's slots itself, overlapping the row load
     if (e == hipSuccess)
-      e = moe::launch_assign_gather(d, route->topk_idx, h->ws.tile_mask, h->ws.tile_base, *plan, out->inst_offset,
-                                    hidden, out->perm, out->slot_pos, out->dispatch, h->ws, acc, re, h->gather_ev,
-                                    st);
+      e = moe::launch_assign_gather(d, route.topk_idx, ws.tile_mask, ws.tile_base, plan, out.inst_offset, hidden,
+                                    out.perm, out.slot_pos, out.dispatch, ws, acc, re, ev, st);
   } else {
+    if (e == hipSuccess) e = moe::launch_assign(d, route.topk_idx, ws.tile_mask, ws.tile_base, plan, ws, acc, re, st);
     if (e == hipSuccess)
-      e = moe::launch_assign(d, route->topk_idx, h->ws.tile_mask, h->ws.tile_base, *plan, h->ws, acc, re, st);
-    if (e == hipSuccess)
-      e = moe::launch_gather(d, *plan, hidden, out->perm, out->slot_pos, out->inst_offset, out->rank_offset,
-                             out->dispatch, h->ws, h->gather_ev, st);
+      e = moe::launch_gather(d, plan, hidden, out.perm, out.slot_pos, out.inst_offset, out.rank_offset, out.dispatch,
+                             ws, ev, st);
   }
-  if (e == hipSuccess) h->acc_dirty = false;
-  return hip_rc(e);
+  return e;
 }
 
 extern "C" int moe_plan_combine(moe_plan_t h, const float* topk_val, const int32_t* slot_pos,

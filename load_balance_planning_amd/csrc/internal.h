@@ -85,6 +85,18 @@ struct ScanJob {
   const int32_t* check;
 };
 
+// Validates a configuration and derives the dimensions (moe_plan_create's checks).
+int derive_dims(const moe_plan_config* c, Dims* d);
+// Argument checks of moe_plan_step (MOE_OK or MOE_ERR_INVALID_ARG).
+int check_step_args(const Dims& d, const float* logits, const uint16_t* hidden, const moe_route_out* route,
+                    const moe_plan_out* plan, const moe_dispatch_out* out);
+struct KernelEvents;
+// The launches of moe_plan_step on `st` (ws.omega_acc must be zero on entry;
+// it is zero again when the work ends).
+hipError_t enqueue_step(const Dims& d, const Workspace& ws, const float* logits, const int32_t* prev_topk,
+                        const uint16_t* hidden, const moe_route_out& route, const moe_plan_out& plan,
+                        const moe_dispatch_out& out, const KernelEvents& ev, hipStream_t st);
+
 // Launchers (all asynchronous on `st`).
 // omega_acc (nullable): also add each tile's per-expert counts to this [R][E]
 // accumulator (which must be zero on entry).

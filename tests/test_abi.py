@@ -75,6 +75,7 @@ def test_every_call_rejects_a_null_handle_synchronously():
         "moe_plan_plan": (None, None, None, None, None),
         "moe_plan_dispatch": (None, None, None, None, None),
         "moe_plan_step": (None,) * 8,
+        "moe_plan_step_static": (None,) * 9,
         "moe_plan_combine": (None,) * 6,
         "moe_plan_place": (None, None, -1, None, None),
         "moe_plan_dedup_count": (None, None, None, 0, None, None),
@@ -94,3 +95,20 @@ def test_every_call_rejects_a_null_handle_synchronously():
     for name, args in calls.items():
         assert getattr(lib, name)(*args) == m.MOE_ERR_INVALID_ARG, name
     lib.moe_plan_destroy(None)  # a no-op
+
+
+def test_static_step_rejects_a_workspace_beyond_its_array():
+    """moe_plan_step_static checks, on the host and before any device work, that the
+    configuration's workspace fits its fixed 32 MiB array."""
+    import ctypes
+    import load_balance_planning_amd as m
+    lib = m.lib()
+    big = m.make_config(1 << 20, 2048, 1, 256, 8, 8, 0)   # 16 384 tiles x 2048 experts of masks
+    bufs = [ctypes.c_void_p(16)] * 6
+    route = m.moe_route_out(*bufs)
+    plan = m.moe_plan_out(*([ctypes.c_void_p(16)] * 8))
+    disp = m.moe_dispatch_out(*([ctypes.c_void_p(16)] * 5))
+    rc = lib.moe_plan_step_static(ctypes.byref(big), ctypes.c_void_p(16), None, ctypes.c_void_p(16),
+                                  ctypes.byref(route), ctypes.byref(plan), ctypes.byref(disp), ctypes.c_void_p(16),
+                                  None)
+    assert rc == m.MOE_ERR_UNSUPPORTED
