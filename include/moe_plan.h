@@ -558,6 +558,22 @@ int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, const uint16
 int moe_plan_set_events(moe_plan_t h, void* gather_begin, void* gather_end);
 
 /*
+ * Orders the row copies of handles that pipeline batches on separate streams
+ * [TopoEP section 3.3: chunks of a step overlap one another's communication
+ * and computation].  wait_event and done_event are hipEvent_t handles of the
+ * handle's device (each nullable).  While set, every moe_plan_dispatch and
+ * moe_plan_step of this handle makes its stream wait for wait_event (its most
+ * recent record when the call is made) right before the launch of its row
+ * copy, and records done_event right after it.  Chaining two handles A and B
+ * (A waits for B's done event and B for A's) runs their copies one after the
+ * other at full bandwidth while each batch's top-k, plan and quotas run beside
+ * the other batch's copy; without it the two copies tend to run at the same
+ * time, at half the bandwidth each, and the small kernels of both batches
+ * then run with nothing to hide behind.  Host call; enqueues nothing.
+ */
+int moe_plan_set_gather_order(moe_plan_t h, void* wait_event, void* done_event);
+
+/*
  * Figures of a HIP device for roofline reports (host call, no handle):
  * out[0] compute units, out[1] peak shader clock (kHz), out[2] peak memory
  * clock (kHz), out[3] memory bus width (bits), out[4] L2 cache bytes,

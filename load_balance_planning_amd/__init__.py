@@ -93,7 +93,8 @@ class moe_dedup_out(ctypes.Structure):
 EXPORTS = ("moe_plan_query", "moe_plan_create", "moe_plan_route", "moe_plan_hist", "moe_plan_plan",
            "moe_plan_dispatch", "moe_plan_step", "moe_plan_step_static", "moe_plan_combine", "moe_plan_place", "moe_plan_dedup_count",
            "moe_plan_dedup_dispatch", "moe_plan_quality", "moe_plan_predict", "moe_plan_slot_map",
-           "moe_plan_replica_pull", "moe_plan_replica_push", "moe_plan_set_events", "moe_plan_device_info",
+           "moe_plan_replica_pull", "moe_plan_replica_push", "moe_plan_set_events", "moe_plan_set_gather_order",
+           "moe_plan_device_info",
            "moe_plan_status", "moe_plan_destroy")
 
 _LIB = None
@@ -129,6 +130,7 @@ def lib():
         l.moe_plan_slot_map.argtypes = [vp, vp, vp, vp]
         l.moe_plan_device_info.argtypes = [ctypes.c_int, vp]
         l.moe_plan_set_events.argtypes = [vp, vp, vp]
+        l.moe_plan_set_gather_order.argtypes = [vp, vp, vp]
         l.moe_plan_replica_pull.argtypes = [vp, vp, vp, ctypes.c_int64, vp, vp]
         l.moe_plan_replica_push.argtypes = [vp, vp, vp, ctypes.c_int64, vp, vp]
         l.moe_plan_status.argtypes = [vp, vp]
@@ -231,6 +233,10 @@ def moe_plan_replica_push(h, slot_expert: int, replica_grads: int, param_elems: 
 
 def moe_plan_set_events(h, gather_begin, gather_end):
     _check("moe_plan_set_events", lib().moe_plan_set_events(h, gather_begin, gather_end))
+
+
+def moe_plan_set_gather_order(h, wait_event, done_event):
+    _check("moe_plan_set_gather_order", lib().moe_plan_set_gather_order(h, wait_event, done_event))
 
 
 def moe_plan_device_info(device: int = 0) -> dict:
@@ -562,6 +568,13 @@ class Layer:
             moe_plan_set_events(self.handle, None, None)
         else:
             moe_plan_set_events(self.handle, ctypes.c_void_p(begin.cuda_event), ctypes.c_void_p(end.cuda_event))
+
+    def order_gather(self, wait=None, done=None):
+        """moe_plan_set_gather_order with torch.cuda.Events (each None for none): this layer's
+        row copies wait for `wait` and record `done`.  The events must have been recorded once
+        already (torch creates the HIP event on its first record)."""
+        ptr = lambda ev: None if ev is None else ctypes.c_void_p(ev.cuda_event)
+        moe_plan_set_gather_order(self.handle, ptr(wait), ptr(done))
 
     def status(self) -> int:
         return moe_plan_status(self.handle)

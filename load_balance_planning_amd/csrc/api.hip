@@ -12,7 +12,7 @@ struct moe_plan {
   void* ws_base;
   size_t ws_bytes;
   hipStream_t last_stream;  // stream of the last call that enqueued work (moe_plan_status waits for it)
-  moe::KernelEvents gather_ev;  // moe_plan_set_events: recorded around every gather launch
+  moe::KernelEvents gather_ev;  // moe_plan_set_events / moe_plan_set_gather_order: hooks around every gather launch
   bool acc_dirty;           // a step failed after its top-k was queued: the accumulator may hold counts
 };
 
@@ -152,7 +152,7 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   h->d = d;
   h->cfg = *cfg;
   h->last_stream = nullptr;
-  h->gather_ev = moe::KernelEvents{nullptr, nullptr};
+  h->gather_ev = moe::KernelEvents{nullptr, nullptr, nullptr, nullptr};
   h->acc_dirty = false;
   if (hipGetDevice(&h->device) != hipSuccess) { delete h; return MOE_ERR_HIP; }
   const WsLayout l = ws_layout(d);
@@ -345,9 +345,10 @@ hipError_t moe::enqueue_step(const moe::Dims& d, const moe::Workspace& ws, const
   hipError_t e = moe::launch_route_topk(d, logits, prev, route.topk_idx, route.topk_val, ws.tile_mask, ws.prev_mask,
                                         acc, ws.status, st);
   const moe::ScanJob scan{ws.tile_mask, ws.tile_base, route.omega, route.expert_count, nullptr};
+  int32_t* trans = prev ? route.trans : nullptr;
   if (e == hipSuccess)
-    e = moe::launch_plan(d, acc, scan, ws.prev_mask, route.cooc, prev ? route.trans : nullptr, ws.pair_part, plan,
-                         out.inst_offset, out.rank_offset, ws, st);
+    e = moe::launch_plan(d, acc, scan, ws.prev_mask, route.cooc, trans, ws.pair_part, plan, out.inst_offset,
+                         out.rank_offset, ws, st);
   if (moe::gather_can_assign(d, hidden, out.dispatch)) {
     // the gather assigns its token's slots itself, overlapping the row load
     if (e == hipSuccess)
@@ -472,7 +473,15 @@ extern "C" int moe_plan_replica_push(moe_plan_t h, const int32_t* slot_expert, c
 
 extern "C" int moe_plan_set_events(moe_plan_t h, void* gather_begin, void* gather_end) {
   if (!h || (gather_begin == nullptr) != (gather_end == nullptr)) return MOE_ERR_INVALID_ARG;
-  h->gather_ev = moe::KernelEvents{static_cast<hipEvent_t>(gather_begin), static_cast<hipEvent_t>(gather_end)};
+  h->gather_ev.begin = static_cast<hipEvent_t>(gather_begin);
+  h->gather_ev.end = static_cast<hipEvent_t>(gather_end);
+  return MOE_OK;
+}
+
+extern "C" int moe_plan_set_gather_order(moe_plan_t h, void* wait_event, void* done_event) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  h->gather_ev.wait = static_cast<hipEvent_t>(wait_event);
+  h->gather_ev.done = static_cast<hipEvent_t>(done_event);
   return MOE_OK;
 }
 

@@ -20,6 +20,7 @@
 //           token's distinct ranks.  HBM traffic T*H*2 read plus
 //           n_rows*H*2 written, n_rows = sum of the distinct-rank counts.
 #include "internal.h"
+#include "row_stage.h"
 #include "tile_scan.h"
 
 namespace moe {
@@ -135,15 +136,9 @@ __global__ __launch_bounds__(256) void dedup_gather_kernel(Dims d, KeyMap km, co
   const bool live = t < d.T;
   const int64_t N = (int64_t)d.T * d.k;
   const int vpr = VEC ? d.H / 8 : d.H;
-  uint4 v[VPT];
-  if (VEC && live) {
-    const uint4* src = reinterpret_cast<const uint4*>(hidden) + t * vpr;
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int c = tid + u * 256;
-      if (c < vpr) v[u] = src[c];
-    }
-  }
+  __shared__ uint4 stage_s[VPT * 256];
+  RowStage<VPT> v{stage_s};
+  if (VEC && live) v.load(reinterpret_cast<const uint4*>(hidden) + t * vpr, tid, vpr);
   // Exclusive prefix of the per-rank row counts (R <= 256: one per thread).
   int cntv = tid < d.R ? rank_count[tid] : 0;
   int inc = cntv;
@@ -200,21 +195,8 @@ __global__ __launch_bounds__(256) void dedup_gather_kernel(Dims d, KeyMap km, co
   if (VEC) {
     const uint4* src = reinterpret_cast<const uint4*>(hidden) + t * vpr;
     for (int b0 = 0; b0 < vpr; b0 += 256 * VPT) {
-      if (b0 > 0) {
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-          const int c = b0 + tid + u * 256;
-          if (c < vpr) v[u] = src[c];
-        }
-      }
-      for (int j = 0; j < nd; ++j) {
-        uint4* dst = reinterpret_cast<uint4*>(out) + (int64_t)row_s[j] * vpr;
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-          const int c = b0 + tid + u * 256;
-          if (c < vpr) dst[c] = v[u];
-        }
-      }
+      if (b0 > 0) v.load(src, b0 + tid, vpr);
+      for (int j = 0; j < nd; ++j) v.store(reinterpret_cast<uint4*>(out) + (int64_t)row_s[j] * vpr, b0 + tid, vpr);
     }
   } else {
     const uint16_t* src = hidden + t * d.H;

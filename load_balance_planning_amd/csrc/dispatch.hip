@@ -16,6 +16,7 @@
 // k times (and measured slower on MI355X).  Plain stores: on MI355X they beat
 // non-temporal ones for this write pattern.
 #include "internal.h"
+#include "row_stage.h"
 #include "slot_assign.h"
 
 namespace moe {
@@ -96,8 +97,8 @@ __global__ __launch_bounds__(256) void offsets_kernel(Dims d, OffsetsIn in, int3
 // One workgroup per token.  Threads j < k place slot t*k+j -- reading its
 // instance and rank, or with ASSIGN computing them from the plan
 // (slot_assign.h) and writing them; the workgroup loads its hidden row (the
-// first 256*VPT vectors) and writes it to its k destinations (16-byte
-// vectors, plain stores).
+// first 256*VPT vectors, staged through LDS: row_stage.h) and writes it to its
+// k destinations (16-byte vectors, plain stores).
 template <int VPT, bool ASSIGN>
 __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* __restrict__ slot_inst,
                                                          const int32_t* __restrict__ slot_rank,
@@ -115,14 +116,9 @@ __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* 
   // row loads first and overlapping them pays; with the two loads of a plain
   // placement, loading after the positions is faster.
   constexpr bool kLoadFirst = ASSIGN;
-  uint4 v[VPT];
-  if (kLoadFirst) {
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int c = tid + u * 256;
-      if (c < vpr) v[u] = src[c];
-    }
-  }
+  __shared__ uint4 stage_s[VPT * 256];
+  RowStage<VPT> v{stage_s};
+  if (kLoadFirst) v.load(src, tid, vpr);
   if (ASSIGN)
     for (int64_t q = t * 256 + tid; q < as.clear_n; q += (int64_t)gridDim.x * 256) as.clear[q] = 0;
   if (tid < d.k) {
@@ -147,31 +143,13 @@ __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* 
     slot_pos[sigma] = (int32_t)p;
     pos_s[tid] = (int32_t)p;
   }
-  if (!kLoadFirst) {
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int c = tid + u * 256;
-      if (c < vpr) v[u] = src[c];
-    }
-  }
+  if (!kLoadFirst) v.load(src, tid, vpr);
   __syncthreads();
   for (int base = 0; base < vpr; base += 256 * VPT) {
-    if (base > 0) {
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int c = base + tid + u * 256;
-        if (c < vpr) v[u] = src[c];
-      }
-    }
+    if (base > 0) v.load(src, base + tid, vpr);
     for (int j = 0; j < d.k; ++j) {
       const int p = pos_s[j];
-      if (p < 0) continue;
-      uint4* dst = dispatch + (int64_t)p * vpr;
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int c = base + tid + u * 256;
-        if (c < vpr) dst[c] = v[u];
-      }
+      if (p >= 0) v.store(dispatch + (int64_t)p * vpr, base + tid, vpr);
     }
   }
 }
@@ -226,7 +204,7 @@ hipError_t launch_gather(const Dims& d, const moe_plan_out& plan, const uint16_t
   hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(256), sizeof(int32_t) * (size_t)(d.cap + 1), st, d, oi, ws.status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || d.T == 0) return e;
-  if (ev.begin && (e = hipEventRecord(ev.begin, st)) != hipSuccess) return e;
+  if ((e = gather_hooks_before(ev, st)) != hipSuccess) return e;
   const bool vec = (d.H % 8) == 0 && ((uintptr_t)hidden % 16) == 0 && ((uintptr_t)dispatch % 16) == 0;
   if (vec) {
     if (one_round(d))
@@ -242,7 +220,21 @@ hipError_t launch_gather(const Dims& d, const moe_plan_out& plan, const uint16_t
                        inst_offset, hidden, perm, slot_pos, dispatch, ws.status);
   }
   e = hipGetLastError();
-  if (e == hipSuccess && ev.end) e = hipEventRecord(ev.end, st);
+  if (e == hipSuccess) e = gather_hooks_after(ev, st);
+  return e;
+}
+
+hipError_t gather_hooks_before(const KernelEvents& ev, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (ev.wait) e = hipStreamWaitEvent(st, ev.wait, 0);
+  if (e == hipSuccess && ev.begin) e = hipEventRecord(ev.begin, st);
+  return e;
+}
+
+hipError_t gather_hooks_after(const KernelEvents& ev, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (ev.end) e = hipEventRecord(ev.end, st);
+  if (e == hipSuccess && ev.done) e = hipEventRecord(ev.done, st);
   return e;
 }
 
@@ -257,7 +249,7 @@ hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const ui
                                 hipStream_t st) {
   if (d.T == 0) return hipSuccess;
   hipError_t e;
-  if (ev.begin && (e = hipEventRecord(ev.begin, st)) != hipSuccess) return e;
+  if ((e = gather_hooks_before(ev, st)) != hipSuccess) return e;
   const AssignIn as{topk_idx, tile_mask, tile_base, plan.quota, plan.slot_inst, plan.slot_rank, clear,
                     clear ? clear_n : 0};
   if (one_round(d))
@@ -269,7 +261,7 @@ hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const ui
                        inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
                        reinterpret_cast<uint4*>(dispatch), as, ws);
   e = hipGetLastError();
-  if (e == hipSuccess && ev.end) e = hipEventRecord(ev.end, st);
+  if (e == hipSuccess) e = gather_hooks_after(ev, st);
   return e;
 }
 

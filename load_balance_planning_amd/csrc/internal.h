@@ -126,11 +126,18 @@ hipError_t launch_assign(const Dims& d, const int32_t* topk_idx, const uint64_t*
                          int32_t* clear, int64_t clear_n, hipStream_t st);
 // The dispatch of a plan: its offsets (into inst_offset / rank_offset) and the
 // gather at slot_pos = inst_offset[slot_inst] + slot_rank, in one launch.
-// Events recorded right before and after a gather kernel's launch (both null: none).
+// Events around a gather kernel's launch (each nullable): `wait` is waited
+// for on the stream right before the launch, `begin` / `end` are recorded
+// right before and after it (timing), `done` right after it (ordering).
 struct KernelEvents {
   hipEvent_t begin;
   hipEvent_t end;
+  hipEvent_t wait;
+  hipEvent_t done;
 };
+// The launch of a gather kernel between the hooks of `ev`.
+hipError_t gather_hooks_before(const KernelEvents& ev, hipStream_t st);
+hipError_t gather_hooks_after(const KernelEvents& ev, hipStream_t st);
 hipError_t launch_gather(const Dims& d, const moe_plan_out& plan, const uint16_t* hidden, int32_t* perm,
                          int32_t* slot_pos, int32_t* inst_offset, int32_t* rank_offset, uint16_t* dispatch,
                          const Workspace& ws, const KernelEvents& ev, hipStream_t st);

@@ -30,7 +30,7 @@ namespace {
 // of PlanLayout so that every access compiles to an LDS instruction.
 extern __shared__ int32_t plan_lds[];
 
-constexpr int kPlanThreads = 512;
+constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kDemandLdsMax = 16384;  // M*E int32 entries kept in LDS when they fit
 constexpr int kQuotaThreads = 256;     // >= kMaxR: one source (and one instance) per thread

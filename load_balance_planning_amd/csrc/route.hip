@@ -132,15 +132,22 @@ __device__ __forceinline__ uint32_t group_sort_desc_u32(uint32_t v, int lig) {
   return v;
 }
 
-// Workgroup size of the top-k kernel: the waves walk the tile's tokens in
-// groups of P lanes, two tokens per group (the second one's row is
-// prefetched while the first is ranked), so a tile has 32P threads (at most
-// 1024); many waves per SIMD hide the latency of the cross-lane steps.  32
-// keys per lane need more than the 128 VGPRs a 1024-thread workgroup allows:
-// those take 512 threads.
-template <int P, int VPL>
+// Tokens per top-k workgroup: one token per group of P lanes, every token of
+// the workgroup in a single round (no loop, no prefetch registers).  A 64-token
+// tile is split over 64 / TPW workgroups, each of which stores its TPW-bit
+// slice (8 bits at least) of every presence mask.  Workgroups are 256 threads
+// (512 for 64 lanes per token): the size of a gather workgroup, so that with
+// two batches in flight the top-k of one takes the slots the other batch's
+// gather frees one workgroup at a time (1024-thread workgroups waited there
+// for the whole gather: 755 us instead of 22 on MI355X; alone the two sizes
+// run the same).
+template <int P, int V>
+constexpr int topk_tpw() {
+  return 256 / P < 8 ? 8 : (256 / P > 64 ? 64 : 256 / P);
+}
+template <int P, int V>
 constexpr int topk_threads() {
-  return (P * 32 < 128 ? 128 : (P * 32 > 1024 ? 1024 : P * 32)) / (VPL >= 32 ? 2 : 1);
+  return topk_tpw<P, V>() * P;
 }
 
 // Expert held in key slot v of lane l: 16-byte loads give lane l the experts
@@ -150,32 +157,20 @@ __device__ __forceinline__ int slot_expert(int l, int v) {
   return VEC4 ? 4 * (l + P * (v >> 2)) + (v & 3) : l + P * v;
 }
 
-// Issue the loads of one logit row for lane l of its group (raw IEEE bits);
-// slots past the row re-read its start (their keys are masked later).
-template <int P, int VPL, bool VEC4>
-__device__ __forceinline__ void load_logit_row(const float* __restrict__ row, int l, int E, uint32_t (&u)[VPL]) {
-  if (VEC4) {
-#pragma unroll
-    for (int w = 0; w < VPL / 4; ++w) {
-      const int e0 = slot_expert<P, VEC4>(l, 4 * w);
-      const float4 f = *reinterpret_cast<const float4*>(row + (e0 < E ? e0 : 0));
-      u[4 * w + 0] = __float_as_uint(f.x);
-      u[4 * w + 1] = __float_as_uint(f.y);
-      u[4 * w + 2] = __float_as_uint(f.z);
-      u[4 * w + 3] = __float_as_uint(f.w);
-    }
-  } else {
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = slot_expert<P, VEC4>(l, v);
-      u[v] = __float_as_uint(row[e < E ? e : 0]);
-    }
-  }
+// Order key of IEEE bits u: the IEEE total order as unsigned integers.
+__device__ __forceinline__ uint32_t order_key(uint32_t u) {
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-// One workgroup per tile; a group of P lanes handles one token, lane l holding
-// VPL logits as 32-bit order keys (the IEEE total order as unsigned integers).
-// Selection:
+// Order keys of the IEEE total order: +inf and -inf.  A NaN's key lies above
+// the first (positive NaNs) or below the second (negative NaNs).
+constexpr uint32_t kKeyPosInf = 0xFF800000u;
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;
+constexpr uint32_t kKeyNegZero = 0x7FFFFFFFu;
+constexpr uint32_t kKeyPosZero = 0x80000000u;
+
+// A group of P lanes handles one token, lane l holding V logits as order
+// keys.  Selection:
 //   1. tau = the k-th largest of the P lane maxima.  k keys reach tau, so
 //      every key of the top-k does; the keys >= tau are the candidates.
 //   2. The candidates (about k + 2 on average when P >= 2k) are compacted to
@@ -186,22 +181,28 @@ __device__ __forceinline__ void load_logit_row(const float* __restrict__ row, in
 // do not express, and more than P candidates do not fit the group: such tokens
 // take k rounds of a group max over 64-bit keys that fold -0.0 onto +0.0 and
 // keep the sign in bit 0.
-template <int P, int VPL, bool VEC4>
-__global__ __launch_bounds__((topk_threads<P, VPL>())) void route_topk_kernel(Dims d, const float* __restrict__ logits,
-                                                                          const int32_t* __restrict__ prev_topk,
-                                                                          int32_t* __restrict__ topk_idx,
-                                                                          float* __restrict__ topk_val,
-                                                                          uint64_t* __restrict__ tile_mask,
-                                                                          uint64_t* __restrict__ prev_mask,
-                                                                          int32_t* __restrict__ omega_acc,
-                                                                          int32_t* __restrict__ status) {
+// A NaN shows as a lane maximum above the key of +inf or a lane minimum below
+// the key of -inf.  With `full` (P*V == E, 16-byte loads) every slot holds an
+// expert and no slot needs masking.
+template <int P, int V, bool VEC4>
+__global__ __launch_bounds__((topk_threads<P, V>())) void route_topk_kernel(Dims d, bool full,
+                                                                        const float* __restrict__ logits,
+                                                                        const int32_t* __restrict__ prev_topk,
+                                                                        int32_t* __restrict__ topk_idx,
+                                                                        float* __restrict__ topk_val,
+                                                                        uint64_t* __restrict__ tile_mask,
+                                                                        uint64_t* __restrict__ prev_mask,
+                                                                        int32_t* __restrict__ omega_acc,
+                                                                        int32_t* __restrict__ status) {
+  constexpr int TPW = topk_tpw<P, V>();
+  constexpr int SLICES = 64 / TPW;
   extern __shared__ unsigned long long smem_masks[];
   unsigned long long* smask = smem_masks;
   unsigned long long* pmask = smem_masks + d.E;
-  const int x = blockIdx.x;
+  const int x = blockIdx.x / SLICES, h = blockIdx.x - x * SLICES;
   const int s = x / d.C, c = x - s * d.C;
-  const int64_t t0 = (int64_t)s * d.Tr + (int64_t)c * kTile;
-  const int nt = min(kTile, d.Tr - c * kTile);
+  const int64_t t0 = (int64_t)s * d.Tr + (int64_t)c * kTile + h * TPW;
+  const int nt = max(0, min(TPW, d.Tr - c * kTile - h * TPW));
   const int tid = threadIdx.x, nthr = blockDim.x;
   const bool want_prev = prev_topk != nullptr;
   for (int e = tid; e < d.E; e += nthr) {
@@ -214,52 +215,74 @@ __global__ __launch_bounds__((topk_threads<P, VPL>())) void route_topk_kernel(Di
   const int grp_base = (tid & 63) - lane;  // wave lane of the group's first lane
   const uint64_t grp_bits = (P == 64 ? ~0ull : ((1ull << P) - 1ull)) << grp_base;
   uint64_t* cand = reinterpret_cast<uint64_t*>(smem_masks + (want_prev ? 2 : 1) * d.E) + (tid & ~63) + grp_base;
-  const int ngrp = nthr / P;
+  const int i = tid / P;  // token of this group
   bool bad = false;
-  const int i0 = tid / P;
-  uint32_t nxt[VPL];
-  load_logit_row<P, VPL, VEC4>(logits + (t0 + (i0 < nt ? i0 : nt - 1)) * d.E, lane, d.E, nxt);
-  for (int i = i0; i < nt; i += ngrp) {
+  if (i < nt) {
     const int64_t t = t0 + i;
-    uint32_t key[VPL];
-    {
-      uint32_t u[VPL];
+    const float* __restrict__ row = logits + t * d.E;
+    uint32_t key[V];
+    if (VEC4) {
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) u[v] = nxt[v];
-      // prefetch the group's next token (the last one re-reads its own row)
-      const int in = i + ngrp < nt ? i + ngrp : i;
-      load_logit_row<P, VPL, VEC4>(logits + (t0 + in) * d.E, lane, d.E, nxt);
+      for (int w = 0; w < V / 4; ++w) {
+        const int e0 = slot_expert<P, VEC4>(lane, 4 * w);
+        const float4 f = *reinterpret_cast<const float4*>(row + (full || e0 < d.E ? e0 : 0));
+        key[4 * w + 0] = __float_as_uint(f.x);
+        key[4 * w + 1] = __float_as_uint(f.y);
+        key[4 * w + 2] = __float_as_uint(f.z);
+        key[4 * w + 3] = __float_as_uint(f.w);
+      }
+    } else {
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        // with 16-byte loads E is a multiple of 4: a vector is valid as a whole
-        const bool ok = VEC4 ? 4 * (lane + P * (v >> 2)) < d.E : slot_expert<P, VEC4>(lane, v) < d.E;
-        bad |= ok && __builtin_isnan(__uint_as_float(u[v]));
-        key[v] = ok ? (u[v] ^ ((uint32_t)((int32_t)u[v] >> 31) | 0x80000000u)) : 0u;  // 0: below every logit
+      for (int v = 0; v < V; ++v) {
+        const int e = slot_expert<P, VEC4>(lane, v);
+        key[v] = __float_as_uint(row[e < d.E ? e : 0]);
       }
     }
-    uint32_t lmax = key[0];
+    uint32_t lmax, lmin;
+    if (full) {
 #pragma unroll
-    for (int v = 1; v < VPL; ++v) lmax = max(lmax, key[v]);
+      for (int v = 0; v < V; ++v) key[v] = order_key(key[v]);
+      lmax = key[0];
+      lmin = key[0];
+#pragma unroll
+      for (int v = 1; v < V; ++v) {
+        lmax = max(lmax, key[v]);
+        lmin = min(lmin, key[v]);
+      }
+    } else {
+      lmax = 0u;
+      lmin = ~0u;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        // with 16-byte loads E is a multiple of 4: a vector is valid as a whole
+        const bool ok = VEC4 ? 4 * (lane + P * (v >> 2)) < d.E : slot_expert<P, VEC4>(lane, v) < d.E;
+        const uint32_t kv = order_key(key[v]);
+        key[v] = ok ? kv : 0u;  // 0: below every logit
+        lmax = max(lmax, key[v]);
+        lmin = min(lmin, ok ? kv : ~0u);
+      }
+    }
+    bad = lmax > kKeyPosInf || lmin < kKeyNegInf;
     bool fast = d.k <= P;
     if (fast) {
       const uint32_t tau = (uint32_t)__shfl((int)group_sort_desc_u32<P>(lmax, lane), grp_base + d.k - 1);
-      if ((__ballot(tau <= 0x80000000u) & grp_bits) != 0ull) {
-        // threshold at or below +0.0: a -0.0 (order key 0x7fffffff) may tie with a candidate
+      if ((__ballot(tau <= kKeyPosZero) & grp_bits) != 0ull) {
+        // threshold at or below +0.0: a -0.0 may tie with a candidate
         bool nz = false;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) nz |= key[v] == 0x7fffffffu;
+        for (int v = 0; v < V; ++v) nz |= key[v] == kKeyNegZero;
         fast = (__ballot(nz) & grp_bits) == 0ull;
       }
       int mine = 0;
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) mine += key[v] >= tau ? 1 : 0;
+      for (int v = 0; v < V; ++v) mine += key[v] >= tau ? 1 : 0;
       const int incl = group_incl_scan<P>(mine, lane);
       const int total = group_last<P>(incl);
       fast = fast && total <= P;
       if (fast) {
         int w = incl - mine;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) {
+        for (int v = 0; v < V; ++v) {
           if (key[v] >= tau) {
             const uint32_t e = (uint32_t)slot_expert<P, VEC4>(lane, v);
             cand[w++] = ((uint64_t)key[v] << 32) | (uint64_t)((0x7fffffffu - e) << 1);
@@ -283,28 +306,34 @@ __global__ __launch_bounds__((topk_threads<P, VPL>())) void route_topk_kernel(Di
       }
     }
     if (!fast) {
-      uint64_t k64[VPL];
+      // k rounds of a group max.  -0.0 ranks as +0.0: its key is folded onto
+      // +0.0's (the output value is read back from the row, which keeps the
+      // sign).  Each round every lane takes its largest key (ties to the
+      // lower slot, i.e. the lower expert), the group the largest (key, lower
+      // expert) pair, and the lane holding it clears that key.
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const uint32_t e = (uint32_t)slot_expert<P, VEC4>(lane, v);
-        const bool nz = key[v] == 0x7fffffffu;  // the order key of -0.0
-        const uint32_t hi = nz ? 0x80000000u : key[v];
-        k64[v] = key[v] == 0u ? 0ull : ((uint64_t)hi << 32) | (uint64_t)(((0x7fffffffu - e) << 1) | (nz ? 1u : 0u));
-      }
+      for (int v = 0; v < V; ++v) key[v] = key[v] == kKeyNegZero ? kKeyPosZero : key[v];
       for (int j = 0; j < d.k; ++j) {
-        uint64_t best = k64[0];
+        uint32_t kb = key[0];
+        int vb = 0;
 #pragma unroll
-        for (int v = 1; v < VPL; ++v) best = max_u64(best, k64[v]);
-        best = group_max_u64<P>(best);
+        for (int v = 1; v < V; ++v) {
+          const bool gt = key[v] > kb;
+          kb = gt ? key[v] : kb;
+          vb = gt ? v : vb;
+        }
+        const uint32_t eb = (uint32_t)slot_expert<P, VEC4>(lane, vb);
+        const uint64_t mine64 = kb == 0u ? 0ull : ((uint64_t)kb << 32) | (uint64_t)(0x7fffffffu - eb);
+        const uint64_t gbest = group_max_u64<P>(mine64);
+        if (gbest != 0ull && mine64 == gbest) {
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) k64[v] = k64[v] == best ? 0ull : k64[v];
+          for (int v = 0; v < V; ++v) key[v] = v == vb ? 0u : key[v];
+        }
         if (lane == 0) {
-          const uint32_t lo = (uint32_t)best;
-          const int e = (int)(0x7fffffffu - (lo >> 1));
-          if ((unsigned)e < (unsigned)d.E) {
-            const uint32_t ub = (lo & 1u) ? 0x80000000u : float_from_order_key((uint32_t)(best >> 32));
+          const int e = (int)(0x7fffffffu - (uint32_t)gbest);
+          if (gbest != 0ull && (unsigned)e < (unsigned)d.E) {
             topk_idx[t * d.k + j] = e;
-            if (topk_val) topk_val[t * d.k + j] = __uint_as_float(ub);
+            if (topk_val) topk_val[t * d.k + j] = row[e];
             atomicOr(&smask[e], 1ull << i);
           } else {
             bad = true;
@@ -315,11 +344,11 @@ __global__ __launch_bounds__((topk_threads<P, VPL>())) void route_topk_kernel(Di
   }
   if (want_prev) {
     for (int q = tid; q < nt * d.k; q += nthr) {
-      const int i = q / d.k;
-      const int e = prev_topk[(t0 + i) * d.k + (q - i * d.k)];
+      const int ip = q / d.k;
+      const int e = prev_topk[(t0 + ip) * d.k + (q - ip * d.k)];
       if ((unsigned)e < (unsigned)d.E) {
-        const unsigned long long old = atomicOr(&pmask[e], 1ull << i);
-        if (old & (1ull << i)) atomicOr(status, MOE_STATUS_BAD_TOPK);
+        const unsigned long long old = atomicOr(&pmask[e], 1ull << ip);
+        if (old & (1ull << ip)) atomicOr(status, MOE_STATUS_BAD_TOPK);
       } else {
         atomicOr(status, MOE_STATUS_BAD_TOPK);
       }
@@ -327,10 +356,22 @@ __global__ __launch_bounds__((topk_threads<P, VPL>())) void route_topk_kernel(Di
   }
   if (bad) atomicOr(status, MOE_STATUS_NAN_LOGIT);
   __syncthreads();
+  // This workgroup's TPW-bit slice of every mask word of the tile.
   for (int e = tid; e < d.E; e += nthr) {
     const unsigned long long mk = smask[e];
-    tile_mask[(int64_t)x * d.E + e] = mk;
-    if (want_prev) prev_mask[(int64_t)x * d.E + e] = pmask[e];
+    uint64_t* word = tile_mask + (int64_t)x * d.E + e;
+    if (TPW == 64) *word = mk;
+    else if (TPW == 32) reinterpret_cast<uint32_t*>(word)[h] = (uint32_t)mk;
+    else if (TPW == 16) reinterpret_cast<uint16_t*>(word)[h] = (uint16_t)mk;
+    else reinterpret_cast<uint8_t*>(word)[h] = (uint8_t)mk;
+    if (want_prev) {
+      const unsigned long long pk = pmask[e];
+      uint64_t* pw = prev_mask + (int64_t)x * d.E + e;
+      if (TPW == 64) *pw = pk;
+      else if (TPW == 32) reinterpret_cast<uint32_t*>(pw)[h] = (uint32_t)pk;
+      else if (TPW == 16) reinterpret_cast<uint16_t*>(pw)[h] = (uint16_t)pk;
+      else reinterpret_cast<uint8_t*>(pw)[h] = (uint8_t)pk;
+    }
     if (omega_acc && mk != 0ull) atomicAdd(&omega_acc[(int64_t)s * d.E + e], __popcll(mk));  // Eq. 3
   }
 }
@@ -413,57 +454,53 @@ __global__ __launch_bounds__(kPairThreads) void pair_reduce_kernel(Dims d, PairA
   pair_reduce_one(d, pa, (int)blockIdx.z + pa.zbase, blockIdx.x, blockIdx.y * kPairThreads + threadIdx.x);
 }
 
-template <int P, int VPL>
-hipError_t launch_topk_pv(const Dims& d, const float* logits, const int32_t* prev_topk, int32_t* topk_idx,
+template <int P, int V, bool VEC4>
+hipError_t launch_topk_pv(const Dims& d, bool full, const float* logits, const int32_t* prev_topk, int32_t* topk_idx,
                           float* topk_val, uint64_t* tile_mask, uint64_t* prev_mask, int32_t* omega_acc,
                           int32_t* status, hipStream_t st) {
-  const int threads = topk_threads<P, VPL>();
+  constexpr int threads = topk_threads<P, V>();
+  constexpr int slices = 64 / topk_tpw<P, V>();
   const size_t lds = sizeof(unsigned long long) * ((size_t)d.E * (prev_topk ? 2 : 1) + threads);
-  const bool vec4 = (d.E % 4) == 0 && (VPL % 4) == 0 && ((uintptr_t)logits % 16) == 0;
-  if (vec4) {
-    hipLaunchKernelGGL((route_topk_kernel<P, VPL, true>), dim3(d.NT), dim3(threads), lds, st, d, logits, prev_topk,
-                       topk_idx, topk_val, tile_mask, prev_mask, omega_acc, status);
-  } else {
-    hipLaunchKernelGGL((route_topk_kernel<P, VPL, false>), dim3(d.NT), dim3(threads), lds, st, d, logits, prev_topk,
-                       topk_idx, topk_val, tile_mask, prev_mask, omega_acc, status);
-  }
+  hipLaunchKernelGGL((route_topk_kernel<P, V, VEC4>), dim3((unsigned)(d.NT * slices)), dim3(threads), lds, st, d, full,
+                     logits, prev_topk, topk_idx, topk_val, tile_mask, prev_mask, omega_acc, status);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Lanes per token P: the smallest power of two (>= 4) that leaves at most 16
-// logits per lane and is at least 2k, so that the threshold of the selection
-// (the k-th largest lane maximum) rarely admits more than P candidates; VPL:
-// logits per lane rounded up to a power of two (>= 4).
+// Lanes per token P: the smallest power of two (>= 4) that is at least 2k, so
+// that the threshold of the selection (the k-th largest lane maximum) rarely
+// admits more than P candidates, and leaves at most 32 logits per lane; V:
+// logits per lane, a multiple of 4 (16-byte loads) when E is.
 hipError_t launch_route_topk(const Dims& d, const float* logits, const int32_t* prev_topk, int32_t* topk_idx,
                              float* topk_val, uint64_t* tile_mask, uint64_t* prev_mask, int32_t* omega_acc,
                              int32_t* status, hipStream_t st) {
   if (d.NT == 0) return hipSuccess;
+  const bool vec4 = (d.E % 4) == 0 && ((uintptr_t)logits % 16) == 0;
   int P = 4;
-  while (P < 64 && (P * 16 < d.E || P < 2 * d.k)) P *= 2;
-  int V = 4;
-  while (P * V < d.E) V *= 2;
-#define MOE_TOPK_CASE(P_, V_)                                                                             \
-  if (P == (P_) && V == (V_))                                                                             \
-    return launch_topk_pv<P_, V_>(d, logits, prev_topk, topk_idx, topk_val, tile_mask, prev_mask, omega_acc, \
-                                  status, st);
-  MOE_TOPK_CASE(4, 4)
-  MOE_TOPK_CASE(4, 8)
-  MOE_TOPK_CASE(4, 16)
-  MOE_TOPK_CASE(8, 4)
-  MOE_TOPK_CASE(8, 8)
-  MOE_TOPK_CASE(8, 16)
-  MOE_TOPK_CASE(16, 4)
-  MOE_TOPK_CASE(16, 8)
-  MOE_TOPK_CASE(16, 16)
-  MOE_TOPK_CASE(32, 4)
-  MOE_TOPK_CASE(32, 8)
-  MOE_TOPK_CASE(32, 16)
-  MOE_TOPK_CASE(64, 4)
-  MOE_TOPK_CASE(64, 8)
-  MOE_TOPK_CASE(64, 16)
-  MOE_TOPK_CASE(64, 32)
+  while (P < 64 && (P < 2 * d.k || P * 32 < d.E)) P *= 2;
+  int V;
+  if (vec4) {
+    V = (d.E + 4 * P - 1) / (4 * P) * 4;
+  } else {
+    V = 8;
+    while (P * V < d.E) V *= 4;  // 8 or 32
+  }
+  const bool full = vec4 && P * V == d.E;
+#define MOE_TOPK_CASE(P_, V_, VEC_)                                                                          \
+  if (P == (P_) && V == (V_) && vec4 == (VEC_))                                                             \
+    return launch_topk_pv<P_, V_, VEC_>(d, full, logits, prev_topk, topk_idx, topk_val, tile_mask, prev_mask, \
+                                        omega_acc, status, st);
+#define MOE_TOPK_VEC(P_)                                                                                     \
+  MOE_TOPK_CASE(P_, 4, true) MOE_TOPK_CASE(P_, 8, true) MOE_TOPK_CASE(P_, 12, true) MOE_TOPK_CASE(P_, 16, true) \
+  MOE_TOPK_CASE(P_, 20, true) MOE_TOPK_CASE(P_, 24, true) MOE_TOPK_CASE(P_, 28, true) MOE_TOPK_CASE(P_, 32, true) \
+  MOE_TOPK_CASE(P_, 8, false) MOE_TOPK_CASE(P_, 32, false)
+  MOE_TOPK_VEC(4)
+  MOE_TOPK_VEC(8)
+  MOE_TOPK_VEC(16)
+  MOE_TOPK_VEC(32)
+  MOE_TOPK_VEC(64)
+#undef MOE_TOPK_VEC
 #undef MOE_TOPK_CASE
   return hipErrorInvalidValue;
 }

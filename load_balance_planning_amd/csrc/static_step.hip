@@ -88,6 +88,6 @@ extern "C" int moe_plan_step_static(const moe_plan_config* cfg, const float* log
   if (e == hipSuccess) e = moe::launch_zero(ws.omega_acc, (int64_t)d.R * d.E, st);
   if (e == hipSuccess)
     e = moe::enqueue_step(d, ws, logits, with_prev ? prev_topk : nullptr, hidden, *route, *plan, *out,
-                          moe::KernelEvents{nullptr, nullptr}, st);
+                          moe::KernelEvents{nullptr, nullptr, nullptr, nullptr}, st);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -90,6 +90,7 @@ def test_every_call_rejects_a_null_handle_synchronously():
         "moe_plan_query": (None, None),
         "moe_plan_device_info": (0, None),
         "moe_plan_set_events": (None, None, None),
+        "moe_plan_set_gather_order": (None, None, None),
     }
     assert set(calls) | {"moe_plan_destroy"} == set(declared_functions())
     for name, args in calls.items():
