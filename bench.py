@@ -111,9 +111,14 @@ def inputs_sha(w) -> dict:
     return out
 
 
+def batch_of(w, i: int):
+    """The batch of handle i of a pipeline: the workload's recipe with the i-th next seed."""
+    return dataclasses.replace(w, seed=w.seed + i)
+
+
 def second_batch(w):
-    """The batch of the second handle: the workload's recipe with the next seed."""
-    return dataclasses.replace(w, seed=w.seed + 1)
+    """The batch of the second handle."""
+    return batch_of(w, 1)
 
 
 def dedup_bytes(w, n_rows: int) -> int:
@@ -206,10 +211,10 @@ def cpu_baseline(w, budget_s: float) -> dict:
             "stage_ms_median_of_3": {k: float(np.median(v)) * 1e3 for k, v in stages.items()}}
 
 
-def time_path(w, steps: int, warmup: int, dev, keep: bool = False) -> dict:
-    """The timed passes of one workload: `steps` steps with two batches in flight (the headline
-    configuration), the same steps one at a time on one stream with the gather kernel of every
-    moe_plan_step bracketed by HIP events (moe_plan_set_events), and the same steps as three
+def time_path(w, steps: int, warmup: int, dev, keep: bool = False, flight: int = 2) -> dict:
+    """The timed passes of one workload: `steps` steps with `flight` batches in flight (the
+    headline configuration), the same steps one at a time on one stream with the gather kernel of
+    every moe_plan_step bracketed by HIP events (moe_plan_set_events), and the same steps as three
     calls per layer with events around each call and around the gather kernel of
     moe_plan_dispatch.  With keep, the first batch's layers and inputs stay open for further
     measurements (else everything is freed)."""
@@ -218,18 +223,20 @@ def time_path(w, steps: int, warmup: int, dev, keep: bool = False) -> dict:
     cfg = mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
     hidden = torch.from_numpy(synth.hidden(w).view(np.int16)).to(dev)
     logits = [torch.from_numpy(lg).to(dev) for lg in synth.all_logits(w)]
-    # The second handle's batch: the same recipe with the next seed, so that no
+    # The other handles' batches: the same recipe with the next seeds, so that no
     # step re-reads the inputs the step before it read.
-    w2 = second_batch(w)
-    batches = [(logits, hidden), ([torch.from_numpy(lg).to(dev) for lg in synth.all_logits(w2)],
-                                  torch.from_numpy(synth.hidden(w2).view(np.int16)).to(dev))]
-    # Two batches in flight: consecutive steps alternate between two handles (each
-    # with its own buffers and batch) on two streams, so the latency-bound route +
-    # plan of one batch overlaps the HBM-bound gather of the other.
-    sets = [[mp.Layer(cfg, device=dev, cooc=True, trans=(l > 0)) for l in range(w.L)] for _ in range(2)]
+    batches = [(logits, hidden)]
+    for i in range(1, flight):
+        wi = batch_of(w, i)
+        batches.append(([torch.from_numpy(lg).to(dev) for lg in synth.all_logits(wi)],
+                        torch.from_numpy(synth.hidden(wi).view(np.int16)).to(dev)))
+    # Batches in flight: consecutive steps rotate over `flight` handles (each with
+    # its own buffers and batch) on as many streams, so the latency-bound route +
+    # plan of one batch overlaps the HBM-bound gather of another.
+    sets = [[mp.Layer(cfg, device=dev, cooc=True, trans=(l > 0)) for l in range(w.L)] for _ in range(flight)]
     layers = sets[0]
     stream = torch.cuda.current_stream(dev)
-    streams = [stream, torch.cuda.Stream(dev)]
+    streams = [stream] + [torch.cuda.Stream(dev) for _ in range(flight - 1)]
 
     def step(i=0):
         # one pass of the whole path per layer: moe_plan_step (route + plan + dispatch in one call)
@@ -239,50 +246,51 @@ def time_path(w, steps: int, warmup: int, dev, keep: bool = False) -> dict:
                 prev = sets[i][l - 1].route_out.topk_idx if l > 0 else None
                 layer.step(lgs[l], hid, prev)
 
-    # When the row copies are HBM-bound, the two batches' copies take turns
-    # (moe_plan_set_gather_order): each handle's copy waits for the other
-    # handle's latest one, so the copies run one after the other at full
-    # bandwidth while each batch's top-k, plan and quotas run beside the other
-    # batch's copy.  The calls are enqueued layer by layer, alternating
-    # batches, so that every wait refers to the copy enqueued just before it.
-    # A layer whose rows stay in the Infinity Cache lets the copies overlap.
-    order = working_set(w) >= CACHE_BYTES
-    turn = [torch.cuda.Event(), torch.cuda.Event()]
+    # When the row copies are HBM-bound, the handles' copies take turns
+    # (moe_plan_set_gather_order): each handle's copy waits for the latest copy
+    # of the handle before it in the rotation, so the copies run one after the
+    # other at full bandwidth while the other batches' top-k, plan and quotas
+    # run beside them.  The calls are enqueued layer by layer, rotating over
+    # the batches, so that every wait refers to the copy enqueued just before
+    # it.  A layer whose rows stay in the Infinity Cache lets the copies overlap.
+    order = working_set(w) >= CACHE_BYTES and flight > 1
+    turn = [torch.cuda.Event() for _ in range(flight)]
     for ev in turn:
         ev.record(stream)  # creates the HIP events; the first copy then waits for nothing
 
-    def two_batch(n):
+    def pipelined(n):  # n steps, rotating over the handles
         if order:
-            for layer in sets[0]:
-                layer.order_gather(wait=turn[1], done=turn[0])
-            for layer in sets[1]:
-                layer.order_gather(wait=turn[0], done=turn[1])
-        for s_ in range(0, n, 2):
+            for i in range(flight):
+                for layer in sets[i]:
+                    layer.order_gather(wait=turn[(i - 1) % flight], done=turn[i])
+        for s_ in range(0, n, flight):
             for l in range(w.L):
-                for i in ((0, 1) if s_ + 1 < n else (0,)):
+                for i in range(min(flight, n - s_)):
                     lgs, hid = batches[i]
                     with torch.cuda.stream(streams[i]):
                         prev = sets[i][l - 1].route_out.topk_idx if l > 0 else None
                         sets[i][l].step(lgs[l], hid, prev)
-        for layer in sets[0] + sets[1]:
+        for layer in [x for st_ in sets for x in st_]:
             layer.order_gather()
 
-    two_batch(warmup)
+    pipelined(warmup)
     torch.cuda.synchronize()
-    for layer in sets[0] + sets[1]:
+    for layer in [x for st_ in sets for x in st_]:
         if layer.status() != 0:
             raise RuntimeError("device status word set during warm-up")
     # Timed region: exactly `steps` steps, synchronised on both sides; the end
-    # event waits for both streams.
+    # event waits for every stream.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    t_side = torch.cuda.Event()
+    t_side = [torch.cuda.Event() for _ in streams[1:]]
     torch.cuda.synchronize()
     t_start.record(stream)
-    streams[1].wait_event(t_start)
-    two_batch(steps)
-    t_side.record(streams[1])
-    stream.wait_event(t_side)
+    for st_ in streams[1:]:
+        st_.wait_event(t_start)
+    pipelined(steps)
+    for ev, st_ in zip(t_side, streams[1:]):
+        ev.record(st_)
+        stream.wait_event(ev)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
@@ -319,9 +327,9 @@ def time_path(w, steps: int, warmup: int, dev, keep: bool = False) -> dict:
     for layer in layers:
         layer.time_gather()
     step_gather_ms = [a.elapsed_time(b) for a, b in gev]
-    for layer in sets[1]:
+    for layer in [x for st_ in sets[1:] for x in st_]:
         if layer.status() != 0:
-            raise RuntimeError("device status word set on the second handle")
+            raise RuntimeError("device status word set on another handle")
         layer.close()
     # Per-call durations from events around each call, in a third pass of the same
     # steps as three calls, and the gather kernel of moe_plan_dispatch alone.

@@ -107,6 +107,7 @@ __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* 
                                                          int32_t* __restrict__ slot_pos, uint4* __restrict__ dispatch,
                                                          AssignIn as, Workspace ws) {
   __shared__ int32_t pos_s[kMaxK];
+  static_assert(sizeof(uint4) * VPT * 256 + sizeof(pos_s) <= kGatherWgLds, "the row copy's LDS");
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t N = (int64_t)d.T * d.k;

@@ -35,7 +35,6 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kDemandLdsMax = 16384;  // M*E int32 entries kept in LDS when they fit
 constexpr int kQuotaThreads = 256;     // >= kMaxR: one source (and one instance) per thread
 constexpr int kFillCells = 1024;       // quota cells per fill workgroup
-constexpr size_t kPlanLdsBudget = 160 * 1024 - 512;  // room for the static LDS copies of the dims
 
 // Offsets (int32 units) of the plan kernel's LDS arrays.
 struct PlanLayout {
@@ -1006,8 +1005,11 @@ PlanLayout plan_layout(const Dims& d) {
   ly.rep_U = take(d.R * ly.NS);
   ly.rep_id = take(d.R * ly.NS);
   ly.wave_tot = take(kPlanWaves + 1);
-  // The domain demand lives in LDS when it is small and still fits.
-  const bool d_fits = d.M * d.E <= kDemandLdsMax && (size_t)(o + d.M * d.E) * 4 <= kPlanLdsBudget;
+  // The domain demand lives in LDS when the whole layout then still fits
+  // beside another batch's resident row copy (measured on the Kimi-K2-sized
+  // layer: with D in LDS, 48 KB, the solver launch waited for the other
+  // copy's end; with D in global memory the solver takes ~10 us more alone).
+  const bool d_fits = d.M * d.E <= kDemandLdsMax && (size_t)(o + d.M * d.E) * 4 <= kBesideGatherLds;
   ly.D = d_fits ? take(d.M * d.E) : -1;
   ly.total = o;
   return ly;
