@@ -211,15 +211,37 @@ def cpu_baseline(w, budget_s: float) -> dict:
             "stage_ms_median_of_3": {k: float(np.median(v)) * 1e3 for k, v in stages.items()}}
 
 
+_STREAMS = []
+
+
+def pipeline_streams(dev, n: int):
+    """n streams for the batches in flight, created once per process and reused, so that every
+    measurement puts its batches on the same streams (HIP maps each stream to one of a few
+    hardware queues at creation; two batches on one queue run one after the other)."""
+    import torch
+    while len(_STREAMS) < n:
+        _STREAMS.append(torch.cuda.Stream(dev))
+    return _STREAMS[:n]
+
+
 def time_path(w, steps: int, warmup: int, dev, keep: bool = False, flight: int = 2) -> dict:
-    """The timed passes of one workload: `steps` steps with `flight` batches in flight (the
+    """time_path_on with the pipeline's streams, the first one current."""
+    import torch
+    streams = pipeline_streams(dev, flight)
+    with torch.cuda.stream(streams[0]):
+        return time_path_on(w, steps, warmup, dev, streams, keep)
+
+
+def time_path_on(w, steps: int, warmup: int, dev, streams, keep: bool = False) -> dict:
+    """The timed passes of one workload: `steps` steps with len(streams) batches in flight (the
     headline configuration), the same steps one at a time on one stream with the gather kernel of
     every moe_plan_step bracketed by HIP events (moe_plan_set_events), and the same steps as three
     calls per layer with events around each call and around the gather kernel of
     moe_plan_dispatch.  With keep, the first batch's layers and inputs stay open for further
-    measurements (else everything is freed)."""
+    measurements (else everything is freed).  streams[0] is the current stream."""
     import torch
     import load_balance_planning_amd as mp
+    flight = len(streams)
     cfg = mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
     hidden = torch.from_numpy(synth.hidden(w).view(np.int16)).to(dev)
     logits = [torch.from_numpy(lg).to(dev) for lg in synth.all_logits(w)]
@@ -235,16 +257,7 @@ def time_path(w, steps: int, warmup: int, dev, keep: bool = False, flight: int =
     # plan of one batch overlaps the HBM-bound gather of another.
     sets = [[mp.Layer(cfg, device=dev, cooc=True, trans=(l > 0)) for l in range(w.L)] for _ in range(flight)]
     layers = sets[0]
-    stream = torch.cuda.current_stream(dev)
-    streams = [stream] + [torch.cuda.Stream(dev) for _ in range(flight - 1)]
-
-    def step(i=0):
-        # one pass of the whole path per layer: moe_plan_step (route + plan + dispatch in one call)
-        lgs, hid = batches[i]
-        with torch.cuda.stream(streams[i]):
-            for l, layer in enumerate(sets[i]):
-                prev = sets[i][l - 1].route_out.topk_idx if l > 0 else None
-                layer.step(lgs[l], hid, prev)
+    stream = streams[0]
 
     # When the row copies are HBM-bound, the handles' copies take turns
     # (moe_plan_set_gather_order): each handle's copy waits for the latest copy
@@ -266,6 +279,7 @@ def time_path(w, steps: int, warmup: int, dev, keep: bool = False, flight: int =
         for s_ in range(0, n, flight):
             for l in range(w.L):
                 for i in range(min(flight, n - s_)):
+                    # one pass of the whole path: moe_plan_step (route + plan + dispatch in one call)
                     lgs, hid = batches[i]
                     with torch.cuda.stream(streams[i]):
                         prev = sets[i][l - 1].route_out.topk_idx if l > 0 else None
