@@ -693,6 +693,77 @@ def copy_reference(nbytes: int, steps: int) -> dict:
             "GBps": 2 * nbytes / (ms / 1e3) / 1e9}
 
 
+def ceilings(w, steps: int) -> dict:
+    """Device reference rates for the gather's traffic, from torch's own kernels on the
+    workload's shapes (HIP-event timed, `steps` launches each after one untimed): the k-fold
+    dispatch buffer written sequentially (fill), the same rows written at the plan's positions in
+    slot order (index_fill on 16-byte elements: the gather's write pattern without its reads), the
+    buffer read (sum), a plain copy of it, and torch's destination-ordered equivalent of the
+    gather (index_select: sequential writes, each hidden row read k times); beside them the
+    library's own row copies."""
+    import torch
+    import load_balance_planning_amd as mp
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    N, H = w.T * w.k, w.H
+    hidden = torch.from_numpy(synth.hidden(w).view(np.int16)).to(dev)
+    layer = mp.Layer(mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B), device=dev, cooc=True)
+    layer.step(torch.from_numpy(synth.logits(w)).to(dev), hidden)
+    torch.cuda.synchronize()
+    if layer.status() != 0:
+        raise RuntimeError("device status word set")
+    slot_pos = layer.dispatch_out.slot_pos.to(torch.int64)         # position of slot t*k+j
+    token_of_row = layer.dispatch_out.perm.to(torch.int64) // w.k  # token of each dispatch row
+    disp = layer.dispatch_out.dispatch
+    vecs = disp.view(torch.complex128).view(N, H // 8)  # 16-byte elements, as the gather stores them
+    other = torch.empty_like(disp)
+    row_bytes = H * 2
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    out = {}
+
+    def put(name, us, read, written, what):
+        out[name] = {"us": us, "bytes_read": read, "bytes_written": written,
+                     "GBps": (read + written) / (us / 1e6) / 1e9,
+                     "frac": (read + written) / (us / 1e6) / 1e9 / HBM_PEAK_GBS, "what": what}
+
+    put("write_sequential", timed(lambda: disp.zero_()), 0, N * row_bytes, "torch fill of the dispatch buffer")
+    put("write_at_plan_positions", timed(lambda: vecs.index_fill_(0, slot_pos, 0)), N * 8, N * row_bytes,
+        "torch index_fill of the rows at the plan's positions in slot order, 16-byte elements (reads the indices)")
+    put("read_sequential", timed(lambda: disp.view(torch.int64).sum()), N * row_bytes, 0,
+        "torch sum of the dispatch buffer")
+    put("copy", timed(lambda: other.copy_(disp)), N * row_bytes, N * row_bytes, "torch copy of the dispatch buffer")
+    put("gather_destination_order", timed(lambda: torch.index_select(hidden, 0, token_of_row, out=other)),
+        N * row_bytes, N * row_bytes + N * 8,
+        "torch index_select of the hidden rows in dispatch-row order (bytes as if every read came from HBM)")
+    ab = algorithmic_bytes(w)
+    gev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    gev[0].record()
+    gev[1].record()
+    layer.time_gather(*gev)
+    us = []
+    for _ in range(steps):
+        layer.dispatch(hidden)
+        torch.cuda.synchronize()
+        us.append(gev[0].elapsed_time(gev[1]) * 1e3)
+    layer.time_gather()
+    put("library_dispatch_gather", float(np.mean(us)), w.T * row_bytes, N * row_bytes,
+        "gather_vec_kernel of moe_plan_dispatch (event-timed; algorithmic bytes %d)" % ab["gather"])
+    layer.close()
+    return {"workload": w.name, "rows": N, "row_bytes": row_bytes, "steps": steps, "peak_GBps": HBM_PEAK_GBS,
+            "rates": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -705,6 +776,9 @@ def main():
                     help="print TopoEP's plan-quality or solver-scaling study instead of the path benchmark")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the path, time a plain copy of this many bytes (counter calibration)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the path, time torch's own fill, scattered fill, read, copy and "
+                         "index_select on the workload's gather shapes (device reference rates)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the step timings of the other four workloads (the line's `configs` object)")
     ap.add_argument("--config-steps", type=int, default=20)
@@ -721,6 +795,9 @@ def main():
         print(json.dumps(copy_reference(args.copy_bytes, args.steps)), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
+    if args.ceilings:
+        print(json.dumps(ceilings(w, args.steps)), flush=True)
+        return
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
     g = run_gpu(w, args.steps, args.warmup)
     ms_per_step = g["ms_total"] / args.steps
