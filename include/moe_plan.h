@@ -569,7 +569,11 @@ int moe_plan_set_events(moe_plan_t h, void* gather_begin, void* gather_end);
  * other at full bandwidth while each batch's top-k, plan and quotas run beside
  * the other batch's copy; without it the two copies tend to run at the same
  * time, at half the bandwidth each, and the small kernels of both batches
- * then run with nothing to hide behind.  Host call; enqueues nothing.
+ * then run with nothing to hide behind.  While either event is set, the
+ * handle's solver launch is also sized to be placed beside the other
+ * handle's running copy (256-thread workgroups within the LDS that copy
+ * leaves free) instead of for running alone (512-thread workgroups); the
+ * outputs are the same either way.  Host call; enqueues nothing.
  */
 int moe_plan_set_gather_order(moe_plan_t h, void* wait_event, void* done_event);
 

@@ -285,7 +285,8 @@ extern "C" int moe_plan_plan(moe_plan_t h, const int32_t* omega, const int32_t* 
   hipError_t e = moe::launch_build_masks(d, topk_idx, nullptr, h->ws.tile_mask, nullptr, h->ws.status, st);
   const moe::ScanJob scan{d.T > 0 ? h->ws.tile_mask : nullptr, h->ws.tile_base, nullptr, nullptr, omega};
   if (e == hipSuccess)
-    e = moe::launch_plan(d, omega, scan, nullptr, nullptr, nullptr, nullptr, *out, nullptr, nullptr, h->ws, st);
+    e = moe::launch_plan(d, omega, scan, nullptr, nullptr, nullptr, nullptr, *out, nullptr, nullptr, h->ws,
+                         moe::pipelined(h->gather_ev), st);
   if (e == hipSuccess)
     e = moe::launch_assign(d, topk_idx, h->ws.tile_mask, h->ws.tile_base, *out, h->ws, nullptr, 0, st);
   return hip_rc(e);
@@ -348,7 +349,7 @@ hipError_t moe::enqueue_step(const moe::Dims& d, const moe::Workspace& ws, const
   int32_t* trans = prev ? route.trans : nullptr;
   if (e == hipSuccess)
     e = moe::launch_plan(d, acc, scan, ws.prev_mask, route.cooc, trans, ws.pair_part, plan, out.inst_offset,
-                         out.rank_offset, ws, st);
+                         out.rank_offset, ws, moe::pipelined(ev), st);
   if (moe::gather_can_assign(d, hidden, out.dispatch)) {
     // the gather assigns its token's slots itself, overlapping the row load
     if (e == hipSuccess)

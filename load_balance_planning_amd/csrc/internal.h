@@ -123,10 +123,12 @@ hipError_t launch_scan(const Dims& d, const uint64_t* tile_mask, int32_t* tile_b
 // of those masks (and of prev_mask) go to cooc / trans, reduced by extra
 // workgroups of the quota launch (each output nullable; part: workspace).
 // With inst_offset / rank_offset non-null the quota launch also writes the
-// dispatch offsets of the plan.
+// dispatch offsets of the plan.  beside: the solver launch is to run beside
+// another batch's row copy (256-thread workgroups within kBesideGatherLds of
+// LDS) rather than alone (512-thread workgroups); the outputs are the same.
 hipError_t launch_plan(const Dims& d, const int32_t* omega, const ScanJob& scan, const uint64_t* prev_mask,
                        int32_t* cooc, int32_t* trans, int32_t* part, const moe_plan_out& out, int32_t* inst_offset,
-                       int32_t* rank_offset, const Workspace& ws, hipStream_t st);
+                       int32_t* rank_offset, const Workspace& ws, bool beside, hipStream_t st);
 // Zero n int32 words (a fill kernel: safe inside graph capture).
 hipError_t launch_zero(int32_t* p, int64_t n, hipStream_t st);
 // The slot assignment; it also zeroes clear[0, clear_n) (nullable), which no
@@ -145,6 +147,10 @@ struct KernelEvents {
   hipEvent_t wait;
   hipEvent_t done;
 };
+// Whether these hooks order the row copy with another handle's (a batch
+// pipelined beside another): the solver launch is then sized to be placed
+// beside that handle's running copy.
+inline bool pipelined(const KernelEvents& ev) { return ev.wait != nullptr || ev.done != nullptr; }
 // The launch of a gather kernel between the hooks of `ev`.
 hipError_t gather_hooks_before(const KernelEvents& ev, hipStream_t st);
 hipError_t gather_hooks_after(const KernelEvents& ev, hipStream_t st);

@@ -30,8 +30,13 @@ namespace {
 // of PlanLayout so that every access compiles to an LDS instruction.
 extern __shared__ int32_t plan_lds[];
 
-constexpr int kPlanThreads = 256;
-constexpr int kPlanWaves = kPlanThreads / 64;
+// Solver launch workgroups: 512 threads (one wave per domain of up to eight
+// in both stages) when the launch runs alone, 256 -- the row copy's size --
+// when it must be placed beside another batch's running copy, which frees
+// one 256-thread slot at a time.
+constexpr int kPlanThreadsAlone = 512;
+constexpr int kPlanThreadsBeside = 256;
+constexpr int kPlanMaxWaves = kPlanThreadsAlone / 64;
 constexpr int kDemandLdsMax = 16384;  // M*E int32 entries kept in LDS when they fit
 constexpr int kQuotaThreads = 256;     // >= kMaxR: one source (and one instance) per thread
 constexpr int kFillCells = 1024;       // quota cells per fill workgroup
@@ -128,11 +133,14 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// In-place exclusive scan of a[0..n) in LDS by the whole plan workgroup; returns the total.
+// In-place exclusive scan of a[0..n) in LDS by the whole plan workgroup (NT
+// threads); returns the total.
+template <int NT>
 __device__ int block_excl_scan(int* a, int n, int* wave_tot) {
+  constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __syncthreads();
-  const int per = (n + kPlanThreads - 1) / kPlanThreads;
+  const int per = (n + NT - 1) / NT;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
   int sum = 0;
   for (int q = lo; q < hi; ++q) sum += a[q];
@@ -141,12 +149,12 @@ __device__ int block_excl_scan(int* a, int n, int* wave_tot) {
   __syncthreads();
   if (tid == 0) {
     int run = 0;
-    for (int w = 0; w < kPlanWaves; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const int v = wave_tot[w];
       wave_tot[w] = run;
       run += v;
     }
-    wave_tot[kPlanWaves] = run;
+    wave_tot[kWaves] = run;
   }
   __syncthreads();
   int run = wave_tot[wave] + incl - sum;
@@ -155,7 +163,7 @@ __device__ int block_excl_scan(int* a, int n, int* wave_tot) {
     a[q] = run;
     run += v;
   }
-  const int total = wave_tot[kPlanWaves];
+  const int total = wave_tot[kWaves];
   __syncthreads();
   return total;
 }
@@ -503,19 +511,20 @@ __device__ void stage2_domain(const Dims& d, const PlanLayout& ly, int m) {
 // idle: for kScanEB experts each, the scan job of tile_scan.h (the tile
 // prefix of the presence masks; the routing matrix and expert counts, or a
 // comparison of the routing matrix with the solver's input).
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout ly, const int32_t* __restrict__ omega,
+template <int NT>
+__global__ __launch_bounds__(NT) void plan_kernel(Dims d, PlanLayout ly, const int32_t* __restrict__ omega,
                                                             ScanJob scan, moe_plan_out out, Workspace ws, PairArgs pa,
                                                             int n_scan) {
   if (blockIdx.x > 0) {
     const int blk = blockIdx.x - 1;
     if (blk < n_scan) {
-      tile_scan_block<kPlanThreads>(d, scan.mask, scan.base, scan.omega, scan.count, scan.check, ws.status, blk,
+      tile_scan_block<NT>(d, scan.mask, scan.base, scan.omega, scan.count, scan.check, ws.status, blk,
                                     plan_lds);
       return;
     }
     // pair-count partials (pair_count.h), summed by the quota launch
     const int q = blk - n_scan, nb = pair_blocks(d);
-    pair_partial_block<kPlanThreads>(d, pa, (q / nb) / pa.splits + pa.zbase, q % nb, (q / nb) % pa.splits, plan_lds);
+    pair_partial_block<NT>(d, pa, (q / nb) / pa.splits + pa.zbase, q % nb, (q / nb) % pa.splits, plan_lds);
     return;
   }
   int32_t* lds = plan_lds;
@@ -549,7 +558,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
   };
 
   // ---- domain demand D[m][e] (Eq. 4), expert loads, main placement (C5) ----
-  for (int idx = tid; idx < M * E; idx += kPlanThreads) {
+  for (int idx = tid; idx < M * E; idx += NT) {
     const int m = idx / E, e = idx - m * E;
     const int32_t* o = omega + (int64_t)m * G * E + e;
     int sum = 0;
@@ -557,22 +566,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
     for (int g = 0; g < G; ++g) sum += o[(int64_t)g * E];
     D[idx] = sum;
   }
-  for (int q = tid; q < E * RW; q += kPlanThreads) {
+  for (int q = tid; q < E * RW; q += NT) {
     const int e = q / RW, w = q - e * RW;
     const int rm = e / Er;
     hm[q] = (rm >> 6) == w ? (1ull << (rm & 63)) : 0ull;
   }
-  for (int r = tid; r < R; r += kPlanThreads) nrep[r] = 0;
+  for (int r = tid; r < R; r += NT) nrep[r] = 0;
   if (tid == 0) { misc[0] = 0; misc[1] = 0; misc[2] = 0; misc[3] = 0; }
   __syncthreads();
-  for (int e = tid; e < E; e += kPlanThreads) {
+  for (int e = tid; e < E; e += NT) {
     int cnt = 0;
     for (int m = 0; m < M; ++m) cnt += D[m * E + e];
     Umain[e] = cnt;  // every assignment on the main instance until replicas exist
   }
 
   // ---- stage 1: inter-node placement (Eq. 9), one wave per domain ----------
-  for (int m = wave; m < M; m += kPlanWaves) {
+  for (int m = wave; m < M; m += (NT / 64)) {
     if (E <= 64 * 2) stage1_domain<2>(m, ws.demand);
     else if (E <= 64 * 4) stage1_domain<4>(m, ws.demand);
     else if (E <= 64 * 16) stage1_domain<16>(m, ws.demand);
@@ -585,7 +594,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
   // Replicated experts are routed per source: to the instance in the source's
   // domain if there is one (at most one after stage 1), else split evenly over
   // all instances in rank order.
-  for (int e = tid; e < E; e += kPlanThreads) {
+  for (int e = tid; e < E; e += NT) {
     int n = 0;
     for (int w = 0; w < RW; ++w) n += __popcll(hm[e * RW + w]);
     if (n > 1) {
@@ -595,7 +604,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
   }
   __syncthreads();
   const int nr1 = misc[1];
-  for (int idx = tid; idx < nr1 * R; idx += kPlanThreads) {
+  for (int idx = tid; idx < nr1 * R; idx += NT) {
     const int q = idx / R, s = idx - q * R;
     const int e = rl[q];
     const int w = omega[(int64_t)s * E + e];
@@ -634,7 +643,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
     }
   }
   __syncthreads();
-  for (int r = tid; r < R; r += kPlanThreads) {
+  for (int r = tid; r < R; r += NT) {
     int sum = 0;
     for (int h = 0; h < Er; ++h) sum += Umain[r * Er + h];
     for (int j = 0; j < nrep[r]; ++j) sum += rep_U[r * NS + j];
@@ -648,14 +657,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
   // busiest rank, and applies its own side of the chosen move.
   const bool grouped = G <= 16;
   if (grouped) {
-    for (int m = wave; m < M; m += kPlanWaves) {
+    for (int m = wave; m < M; m += (NT / 64)) {
       if (G <= 2) stage2_domain<2>(d, ly, m);
       else if (G <= 4) stage2_domain<4>(d, ly, m);
       else if (G <= 8) stage2_domain<8>(d, ly, m);
       else stage2_domain<16>(d, ly, m);
     }
   } else
-  for (int m = wave; m < M; m += kPlanWaves) {
+  for (int m = wave; m < M; m += (NT / 64)) {
     const int Bd = domain_budget(d, m);
     const int r0 = m * G;
     const bool in_dom = lane < G;
@@ -737,11 +746,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
   __syncthreads();
 
   // ---- instance table -------------------------------------------------------
-  for (int q = tid; q < R; q += kPlanThreads) inst_base[q] = Er + nrep[q];
-  const int n_inst = block_excl_scan(inst_base, R, wave_tot);
+  for (int q = tid; q < R; q += NT) inst_base[q] = Er + nrep[q];
+  const int n_inst = block_excl_scan<NT>(inst_base, R, wave_tot);
   if (tid == 0) inst_base[R] = n_inst;
   // Replicas of rank q: ids after its mains, ordered by expert.
-  for (int q = tid; q < R; q += kPlanThreads) {
+  for (int q = tid; q < R; q += NT) {
     const int n = nrep[q];
     for (int j = 0; j < n; ++j) {
       const int e = rep_e[q * NS + j];
@@ -752,7 +761,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
       out.inst_expert[id] = e; out.inst_rank[id] = q; out.inst_load[id] = rep_U[q * NS + j];
     }
   }
-  for (int e = tid; e < E; e += kPlanThreads) {
+  for (int e = tid; e < E; e += NT) {
     const int q = e / Er;
     const int id = inst_base[q] + (e - q * Er);
     out.inst_expert[id] = e; out.inst_rank[id] = q; out.inst_load[id] = Umain[e];
@@ -760,18 +769,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(Dims d, PlanLayout l
     for (int w = 0; w < RW; ++w) n += __popcll(hm[e * RW + w]);
     eoff[e] = n;
   }
-  for (int i = n_inst + tid; i < d.cap; i += kPlanThreads) {
+  for (int i = n_inst + tid; i < d.cap; i += NT) {
     out.inst_expert[i] = -1; out.inst_rank[i] = -1; out.inst_load[i] = -1;
   }
-  for (int q = tid; q < R; q += kPlanThreads) out.rank_load[q] = L[q];
+  for (int q = tid; q < R; q += NT) out.rank_load[q] = L[q];
   if (tid == 0) out.n_inst[0] = n_inst;
-  const int total_inst = block_excl_scan(eoff, E, wave_tot);
+  const int total_inst = block_excl_scan<NT>(eoff, E, wave_tot);
   if (tid == 0) eoff[E] = total_inst;
   __syncthreads();
-  for (int e = tid; e <= E; e += kPlanThreads) ws.einst_off[e] = eoff[e];
+  for (int e = tid; e <= E; e += NT) ws.einst_off[e] = eoff[e];
   // Per-expert instance lists in rank order (the set bits of the host mask),
   // and the experts with more than one instance.
-  for (int e = tid; e < E; e += kPlanThreads) {
+  for (int e = tid; e < E; e += NT) {
     const int rm = e / Er;
     int pos = eoff[e];
     if (eoff[e + 1] - pos > 1) ws.rlist[atomicAdd(&misc[2], 1)] = e;
@@ -984,7 +993,8 @@ __global__ __launch_bounds__(256) void assign_kernel(Dims d, const int32_t* __re
   slot_rank[sigma] = rank;
 }
 
-PlanLayout plan_layout(const Dims& d) {
+// beside: the launch must fit beside another batch's resident row copy.
+PlanLayout plan_layout(const Dims& d, bool beside) {
   PlanLayout ly;
   int o = 0;
   auto take = [&](int n) { const int at = o; o += (n + 3) & ~3; return at; };
@@ -1004,12 +1014,14 @@ PlanLayout plan_layout(const Dims& d) {
   ly.rep_e = take(d.R * ly.NS);
   ly.rep_U = take(d.R * ly.NS);
   ly.rep_id = take(d.R * ly.NS);
-  ly.wave_tot = take(kPlanWaves + 1);
-  // The domain demand lives in LDS when the whole layout then still fits
-  // beside another batch's resident row copy (measured on the Kimi-K2-sized
-  // layer: with D in LDS, 48 KB, the solver launch waited for the other
-  // copy's end; with D in global memory the solver takes ~10 us more alone).
-  const bool d_fits = d.M * d.E <= kDemandLdsMax && (size_t)(o + d.M * d.E) * 4 <= kBesideGatherLds;
+  ly.wave_tot = take(kPlanMaxWaves + 1);
+  // The domain demand lives in LDS when the whole layout then still fits --
+  // beside another batch's resident row copy, within what that copy leaves
+  // free (measured on the Kimi-K2-sized layer: with D in LDS, 48 KB, the
+  // solver launch waited for the other copy's end; with D in global memory
+  // the solver takes ~10 us more alone).
+  const size_t budget = beside ? kBesideGatherLds : kCuLdsBytes - 512;  // 512: the static LDS of the kernel
+  const bool d_fits = d.M * d.E <= kDemandLdsMax && (size_t)(o + d.M * d.E) * 4 <= budget;
   ly.D = d_fits ? take(d.M * d.E) : -1;
   ly.total = o;
   return ly;
@@ -1017,31 +1029,47 @@ PlanLayout plan_layout(const Dims& d) {
 
 }  // namespace
 
-size_t plan_lds_bytes(const Dims& d) { return sizeof(int32_t) * (size_t)plan_layout(d).total; }
+size_t plan_lds_bytes(const Dims& d) { return sizeof(int32_t) * (size_t)plan_layout(d, false).total; }
 
-hipError_t launch_plan(const Dims& d, const int32_t* omega, const ScanJob& scan, const uint64_t* prev_mask,
-                       int32_t* cooc, int32_t* trans, int32_t* part, const moe_plan_out& out, int32_t* inst_offset,
-                       int32_t* rank_offset, const Workspace& ws, hipStream_t st) {
-  const PlanLayout ly = plan_layout(d);
+namespace {
+
+template <int NT>
+hipError_t launch_plan_nt(const Dims& d, const int32_t* omega, const ScanJob& scan, const uint64_t* prev_mask,
+                          int32_t* cooc, int32_t* trans, int32_t* part, const moe_plan_out& out, const Workspace& ws,
+                          bool beside, PairArgs* pa_out, hipStream_t st) {
+  const PlanLayout ly = plan_layout(d, beside);
   size_t lds = sizeof(int32_t) * (size_t)ly.total;
   const int n_scan = scan.mask ? (d.E + kScanEB - 1) / kScanEB : 0;
-  if (n_scan > 0) lds = std::max(lds, tile_scan_lds_bytes(d, kPlanThreads));
+  if (n_scan > 0) lds = std::max(lds, tile_scan_lds_bytes(d, NT));
   // Pair counts from the masks: partials on the CUs the solver leaves idle,
   // their sums in the quota launch (with one split the partials are final).
-  PairArgs pa = pair_args(d, scan.mask, prev_mask, cooc, trans, part, kPlanThreads);
+  PairArgs pa = pair_args(d, scan.mask, prev_mask, cooc, trans, part, NT);
   if (!scan.mask) pa.nz = 0;
   const int64_t n_pair = (int64_t)pair_blocks(d) * pa.splits * pa.nz;
-  const int64_t n_reduce = pa.splits > 1 ? (int64_t)pair_blocks(d) * (kPairBlock / kQuotaThreads) * pa.nz : 0;
   if (n_pair > 0) lds = std::max(lds, sizeof(int32_t) * (size_t)kPairBlock);
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_kernel),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_kernel<NT>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(plan_kernel, dim3((unsigned)(1 + n_scan + n_pair)), dim3(kPlanThreads), lds, st, d, ly, omega,
-                     scan, out, ws, pa, n_scan);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL(plan_kernel<NT>, dim3((unsigned)(1 + n_scan + n_pair)), dim3(NT), lds, st, d, ly, omega, scan,
+                     out, ws, pa, n_scan);
+  *pa_out = pa;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_plan(const Dims& d, const int32_t* omega, const ScanJob& scan, const uint64_t* prev_mask,
+                       int32_t* cooc, int32_t* trans, int32_t* part, const moe_plan_out& out, int32_t* inst_offset,
+                       int32_t* rank_offset, const Workspace& ws, bool beside, hipStream_t st) {
+  PairArgs pa;
+  hipError_t e = beside ? launch_plan_nt<kPlanThreadsBeside>(d, omega, scan, prev_mask, cooc, trans, part, out, ws,
+                                                            true, &pa, st)
+                        : launch_plan_nt<kPlanThreadsAlone>(d, omega, scan, prev_mask, cooc, trans, part, out, ws,
+                                                           false, &pa, st);
   if (e != hipSuccess) return e;
+  const int64_t n_reduce = pa.splits > 1 ? (int64_t)pair_blocks(d) * (kPairBlock / kQuotaThreads) * pa.nz : 0;
   const int n_transport = d.B < d.E ? d.B : d.E;  // each replicated expert owns at least one replica
   const int n_fill = (int)(((int64_t)d.R * d.cap + kFillCells - 1) / kFillCells);
   const int n_off = inst_offset ? 1 : 0;

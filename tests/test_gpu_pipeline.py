@@ -1,6 +1,7 @@
 """Parity in the launch configuration bench.py times: two handles on two
 streams, consecutive steps alternating between them with no synchronisation
-in between, at the full DeepSeek-V3-shaped size.
+in between, at full size (the DeepSeek-V3-shaped layer with and without the
+copies taking turns, the Kimi-K2-shaped one with them).
 
 The two handles plan two different batches (the workload's logits and those
 of the same recipe with another seed), so a handle that read the other's
@@ -44,30 +45,51 @@ def small_outputs(layer):
                 rank_offset=d.rank_offset, perm=d.perm, slot_pos=d.slot_pos)
 
 
-def test_two_stream_pipeline_full_size(mp):
-    w = synth.WORKLOADS["deepseek_v3_layer"]
+_EXPECTED = {}
+
+
+def expected(name):
+    if name in _EXPECTED:
+        return _EXPECTED[name]
+    w = synth.WORKLOADS[name]
     batches = [w, dataclasses.replace(w, seed=1)]
-    cfg = mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
     ocfg = oracle.make_cfg(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
     logits = [synth.logits(b) for b in batches]
-    hidden = synth.hidden(w)
     want = []
     for i, lg in enumerate(logits):
         print("pipeline: oracle for batch %d" % i, flush=True)
         want.append(oracle.run_all(ocfg, lg, None, want_cooc=True))
     assert not np.array_equal(want[0]["slot_pos"], want[1]["slot_pos"])
+    _EXPECTED[name] = (w, logits, synth.hidden(w), want)
+    return _EXPECTED[name]
 
+
+@pytest.mark.parametrize("name,ordered", [("deepseek_v3_layer", False), ("deepseek_v3_layer", True),
+                                          ("kimi_layer", True)])
+def test_two_stream_pipeline_full_size(mp, name, ordered):
+    """With ordered, the two handles' row copies take turns (moe_plan_set_gather_order), as
+    bench.py runs them, and their solver launches take the workgroup size and LDS budget meant
+    for running beside the other handle's copy (on the Kimi-K2-shaped layer the domain demand
+    then lives in global memory)."""
+    w, logits, hidden, want = expected(name)
+    cfg = mp.make_config(w.T, w.E, w.k, w.R, w.G, w.H, w.B)
     dev = torch.device("cuda", torch.cuda.current_device())
     hid = torch.from_numpy(hidden.view(np.int16)).to(dev)
     lgs = [torch.from_numpy(lg).to(dev) for lg in logits]
     layers = [mp.Layer(cfg, device=dev, cooc=True) for _ in range(2)]
     streams = [torch.cuda.current_stream(dev), torch.cuda.Stream(dev)]
+    turn = [torch.cuda.Event(), torch.cuda.Event()]
+    for ev in turn:
+        ev.record(streams[0])
+    if ordered:
+        layers[0].order_gather(wait=turn[1], done=turn[0])
+        layers[1].order_gather(wait=turn[0], done=turn[1])
     rng = np.random.default_rng(11)
     rows = torch.from_numpy(rng.choice(w.T * w.k, 4096, replace=False).astype(np.int64)).to(dev)
     torch.cuda.synchronize()
     copies = []
     n_steps = 6
-    print("pipeline: %d alternating steps on two streams" % n_steps, flush=True)
+    print("pipeline: %d alternating steps on two streams (ordered copies: %s)" % (n_steps, ordered), flush=True)
     for s in range(n_steps):
         i = s % 2
         with torch.cuda.stream(streams[i]):
@@ -77,6 +99,7 @@ def test_two_stream_pipeline_full_size(mp):
             copies.append((i, snap))
     torch.cuda.synchronize()
     for layer in layers:
+        layer.order_gather()
         assert layer.status() == 0
     rows_np = rows.cpu().numpy()
     for s, (i, snap) in enumerate(copies):
