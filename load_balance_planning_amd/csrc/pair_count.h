@@ -4,9 +4,14 @@
 //   out[a][b] = sum_x popcount(A[x][a] & B[x][b])      ([Coupling])
 //
 // Output blocks of 64 a x kPairB b.  Lane l of a wave holds A[x][a0 + l]; the
-// kPairB masks B[x][b0 ..] are wave-uniform and arrive through scalar loads,
-// so one b costs two AND and two popcount-accumulate VALU operations for 64
-// experts a and 64 tokens.  The tiles of a block are split over `splits`
+// kPairB masks B[x][b0 ..] are wave-uniform: the workgroup stages them in LDS
+// for a chunk of tiles at a time (one vector load per mask, all in flight)
+// and every wave reads them back as LDS broadcasts, so one b costs two AND
+// and two popcount-accumulate VALU operations for 64 experts a and 64
+// tokens.  (Fetched with scalar loads, one per mask and tile, they made the
+// pair workgroups the longest part of the solver launch: measured on MI355X,
+// DeepSeek-V3-shaped launch 31.5 -> 24.9 us, Kimi-K2-shaped 98.8 -> 59.6 us.)
+// The tiles of a block are split over `splits`
 // workgroups (and over the waves of each) so that a launch fills the chip;
 // the waves meet in LDS and each workgroup stores its partial block, which
 // pair_reduce_one adds up in split order (with one split the block is
@@ -54,9 +59,17 @@ __device__ __forceinline__ void pair_store(const Dims& d, int32_t* __restrict__ 
   }
 }
 
+// Tiles per LDS chunk of B masks, for workgroups of nthr threads (four per wave).
+__host__ __device__ constexpr int pair_chunk(int nthr) { return 4 * (nthr / 64); }
+// LDS bytes of pair_partial_block for workgroups of nthr threads.
+__host__ __device__ constexpr size_t pair_lds_bytes(int nthr) {
+  return sizeof(int32_t) * kPairBlock + sizeof(uint64_t) * kPairB * pair_chunk(nthr);
+}
+
 // Split `split` of block blk of slice z, by a workgroup of NTHR threads;
-// acc_s: kPairBlock ints of LDS.
-template <int NTHR>
+// acc_s: pair_lds_bytes(NTHR) bytes of LDS (the block's sums, then a chunk
+// of B masks).
+template <int NTHR, int KCHUNK = pair_chunk(NTHR)>
 __device__ __forceinline__ void pair_partial_block(const Dims& d, const PairArgs& pa, int z, int blk, int split,
                                                    int32_t* acc_s) {
   if (pair_block_skipped(d, z, blk)) return;  // strictly below the diagonal: written as mirrors
@@ -75,25 +88,32 @@ __device__ __forceinline__ void pair_partial_block(const Dims& d, const PairArgs
   uint32_t acc[kPairB];
 #pragma unroll
   for (int bb = 0; bb < kPairB; ++bb) acc[bb] = 0;
-  constexpr int kBatch = 2;
   constexpr int kWaves = NTHR / 64;
-  for (int xb = x0 + wave * kBatch; xb < x1; xb += kWaves * kBatch) {
-    uint64_t am[kBatch];
+  constexpr int kPer = KCHUNK / kWaves;  // tiles of a chunk per wave
+  uint64_t* bst = reinterpret_cast<uint64_t*>(acc_s + kPairBlock);
+  for (int c0 = x0; c0 < x1; c0 += KCHUNK) {
+    const int cn = min(KCHUNK, x1 - c0);
+    __syncthreads();
+    for (int q = threadIdx.x; q < cn * kPairB; q += NTHR) {
+      const int u = q / kPairB, bb = q - u * kPairB;
+      bst[q] = b0 + bb < d.E ? pa.cur[(int64_t)(c0 + u) * d.E + b0 + bb] : 0ull;
+    }
+    __syncthreads();
+    uint64_t am[kPer];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const bool in = xb + u < x1;
-      const int x = in ? xb + u : xb;
-      am[u] = A[(int64_t)x * d.E + (a_ok ? a : 0)];
-      am[u] = (a_ok && in) ? am[u] : 0ull;
+    for (int j = 0; j < kPer; ++j) {
+      const int u = wave + j * kWaves;
+      am[j] = (a_ok && u < cn) ? A[(int64_t)(c0 + u) * d.E + a] : 0ull;
     }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int x = xb + u < x1 ? xb + u : xb;
-      const uint64_t* brow = pa.cur + (int64_t)x * d.E;
-      const uint32_t alo = (uint32_t)am[u], ahi = (uint32_t)(am[u] >> 32);
+    for (int j = 0; j < kPer; ++j) {
+      const int u = wave + j * kWaves;
+      if (u >= cn) break;
+      const uint64_t* brow = bst + u * kPairB;
+      const uint32_t alo = (uint32_t)am[j], ahi = (uint32_t)(am[j] >> 32);
 #pragma unroll
       for (int bb = 0; bb < kPairB; ++bb) {
-        const uint64_t bv = brow[b0 + bb < d.E ? b0 + bb : 0];
+        const uint64_t bv = brow[bb];
         acc[bb] += __popc(alo & (uint32_t)bv) + __popc(ahi & (uint32_t)(bv >> 32));
       }
     }

@@ -1046,7 +1046,7 @@ hipError_t launch_plan_nt(const Dims& d, const int32_t* omega, const ScanJob& sc
   PairArgs pa = pair_args(d, scan.mask, prev_mask, cooc, trans, part, NT);
   if (!scan.mask) pa.nz = 0;
   const int64_t n_pair = (int64_t)pair_blocks(d) * pa.splits * pa.nz;
-  if (n_pair > 0) lds = std::max(lds, sizeof(int32_t) * (size_t)kPairBlock);
+  if (n_pair > 0) lds = std::max(lds, pair_lds_bytes(NT));
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_kernel<NT>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

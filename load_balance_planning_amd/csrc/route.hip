@@ -556,7 +556,7 @@ hipError_t launch_scan_pairs(const Dims& d, const uint64_t* tile_mask, int32_t* 
   const int n_scan = (d.E + kScanEB - 1) / kScanEB;
   const int64_t n_pair = (int64_t)pair_blocks(d) * pa.splits * pa.nz;
   size_t lds = scan_lds_bytes(d);
-  if (lds < sizeof(int32_t) * kPairBlock) lds = sizeof(int32_t) * kPairBlock;
+  if (lds < pair_lds_bytes(1024)) lds = pair_lds_bytes(1024);
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_pair_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
