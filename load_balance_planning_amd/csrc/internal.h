@@ -16,14 +16,17 @@ constexpr int kMaxG = 64;
 constexpr int kMaxB = 1024;
 constexpr int kTile = 64;  // tokens per tile: one bit per token in a 64-bit presence mask
 
-// LDS of one CU, and of one workgroup of the row copy (its row staged as four
-// 16-byte vectors per thread of 256, plus the k slot positions).  The copy
-// keeps eight workgroups resident per CU; a workgroup of another launch is
-// placed beside them only when it asks for at most what they leave free, so
-// the launches meant to run beside another batch's row copy (top-k, solver,
-// quotas) keep each workgroup within kBesideGatherLds.
+// LDS of one CU, the block size in which it is given to a workgroup, and the
+// LDS of one workgroup of the row copy (its row staged as four 16-byte
+// vectors per thread of 256, plus the k slot positions, in whole blocks).
+// The copy keeps eight workgroups resident per CU; a workgroup of another
+// launch is placed beside them only when it asks for at most what they leave
+// free, so the launches meant to run beside another batch's row copy (top-k,
+// solver, quotas) keep each workgroup's whole LDS, static and dynamic,
+// within kBesideGatherLds.
 constexpr size_t kCuLdsBytes = 160 * 1024;
-constexpr size_t kGatherWgLds = 4 * 256 * 16 + 4 * kMaxK;
+constexpr size_t kLdsBlock = 512;
+constexpr size_t kGatherWgLds = (4 * 256 * 16 + 4 * kMaxK + kLdsBlock - 1) / kLdsBlock * kLdsBlock;
 constexpr size_t kBesideGatherLds = kCuLdsBytes - 8 * kGatherWgLds;
 
 // Everything a kernel needs to know about the layer, derived once at create time.

@@ -28,7 +28,9 @@ namespace {
 
 // Dynamic LDS of the plan kernel; the solver helpers index it by the offsets
 // of PlanLayout so that every access compiles to an LDS instruction.
-extern __shared__ int32_t plan_lds[];
+// 16-byte aligned: parts of it are read as 64- and 128-bit words, and the
+// dynamic region starts after the static LDS, whatever its size.
+extern __shared__ __align__(16) int32_t plan_lds[];
 
 // Solver launch workgroups: 512 threads (one wave per domain of up to eight
 // in both stages) when the launch runs alone, 256 -- the row copy's size --
@@ -1020,7 +1022,8 @@ PlanLayout plan_layout(const Dims& d, bool beside) {
   // free (measured on the Kimi-K2-sized layer: with D in LDS, 48 KB, the
   // solver launch waited for the other copy's end; with D in global memory
   // the solver takes ~10 us more alone).
-  const size_t budget = beside ? kBesideGatherLds : kCuLdsBytes - 512;  // 512: the static LDS of the kernel
+  // (one LDS block is left for the kernel's static LDS, the layer dimensions)
+  const size_t budget = (beside ? kBesideGatherLds : kCuLdsBytes) - kLdsBlock;
   const bool d_fits = d.M * d.E <= kDemandLdsMax && (size_t)(o + d.M * d.E) * 4 <= budget;
   ly.D = d_fits ? take(d.M * d.E) : -1;
   ly.total = o;

@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void build_masks_kernel(Dims d, const int32_t*
 __global__ __launch_bounds__(1024) void scan_kernel(Dims d, const uint64_t* __restrict__ tile_mask,
                                                     int32_t* __restrict__ tile_base, int32_t* __restrict__ omega,
                                                     int32_t* __restrict__ count) {
-  extern __shared__ int32_t smem_scan[];
+  extern __shared__ __align__(16) int32_t smem_scan[];  // the pair blocks read 64-bit words
   tile_scan_block<1024>(d, tile_mask, tile_base, omega, count, nullptr, nullptr, blockIdx.x, smem_scan);
 }
 
@@ -440,7 +440,7 @@ constexpr int kPairThreads = 256;
 __global__ __launch_bounds__(1024) void scan_pair_kernel(Dims d, const uint64_t* __restrict__ tile_mask,
                                                          int32_t* __restrict__ tile_base, int32_t* __restrict__ omega,
                                                          int32_t* __restrict__ count, PairArgs pa, int n_scan) {
-  extern __shared__ int32_t smem_scan[];
+  extern __shared__ __align__(16) int32_t smem_scan[];  // the pair blocks read 64-bit words
   if ((int)blockIdx.x < n_scan) {
     tile_scan_block<1024>(d, tile_mask, tile_base, omega, count, nullptr, nullptr, blockIdx.x, smem_scan);
     return;
