@@ -560,13 +560,26 @@ __global__ __launch_bounds__(NT) void plan_kernel(Dims d, PlanLayout ly, const i
   };
 
   // ---- domain demand D[m][e] (Eq. 4), expert loads, main placement (C5) ----
-  for (int idx = tid; idx < M * E; idx += NT) {
-    const int m = idx / E, e = idx - m * E;
-    const int32_t* o = omega + (int64_t)m * G * E + e;
-    int sum = 0;
+  // Four entries per thread at a time, so that their G loads each are in
+  // flight together (the routing matrix comes from L2 or HBM: one entry at a
+  // time left the Kimi-K2-shaped solver ~10 us in this loop).
+  for (int i0 = tid; i0 < M * E; i0 += 4 * NT) {
+    const int32_t* o[4];
+    int sum[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = min(i0 + u * NT, M * E - 1);
+      const int m = idx / E, e = idx - m * E;
+      o[u] = omega + (int64_t)m * G * E + e;
+      sum[u] = 0;
+    }
 #pragma unroll 8
-    for (int g = 0; g < G; ++g) sum += o[(int64_t)g * E];
-    D[idx] = sum;
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sum[u] += o[u][(int64_t)g * E];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * NT < M * E) D[i0 + u * NT] = sum[u];
   }
   for (int q = tid; q < E * RW; q += NT) {
     const int e = q / RW, w = q - e * RW;
