@@ -9,6 +9,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -107,21 +108,39 @@ MUTANTS = [
 ]
 
 
-@pytest.mark.slow
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_reject_mutant(tmp_path, name, old, new):
+PIN_SUITES = ["test_oracle_pins.py", "test_oracle_combine.py", "test_oracle_placement.py", "test_oracle_quality.py",
+              "test_oracle_predict.py", "test_oracle_slots.py"]
+
+
+def judge_mutant(workdir, name, old, new):
+    """Build the oracle with one planted mistake and run the pin suites against it in a
+    process of their own; returns the suites' exit status (0: every pin accepted it)."""
     text = open(SRC).read()
     assert text.count(old) == 1, "mutation site not found: " + name
-    src = tmp_path / "moe_oracle.cpp"
-    src.write_text(text.replace(old, new))
-    lib = obuild.build(out=str(tmp_path / "libmutant.so"), src=str(src))
+    os.makedirs(workdir, exist_ok=True)
+    src = os.path.join(workdir, "moe_oracle.cpp")
+    with open(src, "w") as fh:
+        fh.write(text.replace(old, new))
+    lib = obuild.build(out=os.path.join(workdir, "libmutant.so"), src=src)
     env = dict(os.environ, MOE_ORACLE_LIB=lib)
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_combine.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_placement.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_quality.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_predict.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_slots.py")],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
-    assert r.returncode != 0, "the pins accept the mutant '%s'" % name
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] +
+                       [os.path.join(ROOT, "tests", f) for f in PIN_SUITES],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return r.returncode
+
+
+@pytest.fixture(scope="module")
+def verdicts(tmp_path_factory):
+    """Every mutant judged once, several at a time (each build and pin run is a process of
+    its own), so the whole self-test takes about a minute instead of several."""
+    base = tmp_path_factory.mktemp("mutants")
+    workers = max(1, min(8, (os.cpu_count() or 2) - 1))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        futs = {m[0]: pool.submit(judge_mutant, str(base / ("m%02d" % i)), *m) for i, m in enumerate(MUTANTS)}
+        return {k: f.result() for k, f in futs.items()}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", [m[0] for m in MUTANTS])
+def test_pins_reject_mutant(verdicts, name):
+    assert verdicts[name] != 0, "the pins accept the mutant '%s'" % name
