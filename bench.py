@@ -699,8 +699,9 @@ def ceilings(w, steps: int) -> dict:
     dispatch buffer written sequentially (fill), the same rows written at the plan's positions in
     slot order (index_fill on 16-byte elements: the gather's write pattern without its reads), the
     buffer read (sum), a plain copy of it, and torch's destination-ordered equivalent of the
-    gather (index_select: sequential writes, each hidden row read k times); beside them the
-    library's own row copies."""
+    gather (index_select: sequential writes, each hidden row read k times), a read of a cold
+    logits-sized tensor right after a step (the memory state of the next step's top-k); beside
+    them the library's own row copies."""
     import torch
     import load_balance_planning_amd as mp
     dev = torch.device("cuda", 0)
@@ -746,6 +747,27 @@ def ceilings(w, steps: int) -> dict:
     put("gather_destination_order", timed(lambda: torch.index_select(hidden, 0, token_of_row, out=other)),
         N * row_bytes, N * row_bytes + N * 8,
         "torch index_select of the hidden rows in dispatch-row order (bytes as if every read came from HBM)")
+    # The top-k's reference: a read of a logits-sized tensor that is not in any cache,
+    # right after a step (whose row copy leaves the caches full of its dirty rows) -- the
+    # memory state in which the next step's top-k reads its logits.
+    lg = torch.from_numpy(synth.logits(w)).to(dev)
+    cold = [torch.from_numpy(synth.logits(batch_of(w, i))).to(dev) for i in (1, 2, 3)]
+    rd = []
+    for i in range(steps + 1):
+        layer.step(lg, hidden)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        cold[i % 3].sum()
+        b.record()
+        torch.cuda.synchronize()
+        if i > 0:
+            rd.append(a.elapsed_time(b) * 1e3)
+    if layer.status() != 0:
+        raise RuntimeError("device status word set")
+    put("read_logits_after_step", float(np.median(rd)), w.T * w.E * 4, 0,
+        "torch sum of a logits-sized tensor in no cache, right after a step (the next top-k's memory state; "
+        "median of %d)" % steps)
+    del cold
     ab = algorithmic_bytes(w)
     gev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     gev[0].record()
