@@ -289,7 +289,8 @@ int moe_plan_query(const moe_plan_config* cfg, moe_plan_sizes* sizes);
 /*
  * Validate cfg, bind the current HIP device and allocate the handle's
  * workspace (it may synchronise).  Limits of the library: E <= 2048, k <= 32,
- * R <= 256, G <= 64, B <= 1024, E/R + N_slot <= 1024, T*k < 2^31, H >= 1.
+ * R <= 256, G <= 64, B <= 1024, E/R + N_slot <= 1024, T < 2^22, T*k < 2^31,
+ * H >= 1.
  * On success *out is a new handle; on error *out is NULL.
  */
 int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out);

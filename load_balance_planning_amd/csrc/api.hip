@@ -67,6 +67,9 @@ int moe::derive_dims(const moe_plan_config* c, moe::Dims* d) {
       c->replica_budget > moe::kMaxB)
     return MOE_ERR_UNSUPPORTED;
   if ((int64_t)c->T * c->k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  // The row copy launches up to four 256-thread workgroups per token, and a
+  // dispatch holds fewer than 2^32 work-items.
+  if (c->T >= 1 << 22) return MOE_ERR_UNSUPPORTED;
   if (c->token_bytes > ((int64_t)1 << 30) || c->expert_bytes > ((int64_t)1 << 62)) return MOE_ERR_UNSUPPORTED;
   moe::Dims x;
   x.T = c->T; x.E = c->E; x.k = c->k; x.R = c->R; x.G = c->G; x.H = c->H; x.B = c->replica_budget;

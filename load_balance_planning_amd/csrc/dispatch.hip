@@ -94,21 +94,24 @@ __global__ __launch_bounds__(256) void offsets_kernel(Dims d, OffsetsIn in, int3
   }
 }
 
-// One workgroup per token.  Threads j < k place slot t*k+j -- reading its
-// instance and rank, or with ASSIGN computing them from the plan
-// (slot_assign.h) and writing them; the workgroup loads its hidden row (the
-// first 256*VPT vectors, staged through LDS: row_stage.h) and writes it to its
-// k destinations (16-byte vectors, plain stores).
+// `split` adjacent workgroups per token, workgroup `part` taking the token's
+// slots j in [part*k/split, (part+1)*k/split).  Its first threads place those
+// slots -- reading instance and rank, or with ASSIGN computing them from the
+// plan (slot_assign.h) and writing them; the workgroup loads the hidden row
+// (the first 256*VPT vectors, staged through LDS: row_stage.h) and writes it
+// to those destinations (16-byte vectors, plain stores).
 template <int VPT, bool ASSIGN>
 __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* __restrict__ slot_inst,
                                                          const int32_t* __restrict__ slot_rank,
                                                          const int32_t* __restrict__ inst_offset,
                                                          const uint4* __restrict__ hidden, int32_t* __restrict__ perm,
                                                          int32_t* __restrict__ slot_pos, uint4* __restrict__ dispatch,
-                                                         AssignIn as, Workspace ws) {
+                                                         AssignIn as, Workspace ws, int split) {
   __shared__ int32_t pos_s[kMaxK];
   static_assert(sizeof(uint4) * VPT * 256 + sizeof(pos_s) <= kGatherWgLds, "the row copy's LDS");
-  const int64_t t = blockIdx.x;
+  const int64_t t = blockIdx.x / split;
+  const int part = (int)(blockIdx.x - t * split);
+  const int j0 = part * d.k / split, kp = (part + 1) * d.k / split - j0;
   const int tid = threadIdx.x;
   const int64_t N = (int64_t)d.T * d.k;
   const int vpr = d.H / 8;
@@ -121,9 +124,9 @@ __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* 
   RowStage<VPT> v{stage_s};
   if (kLoadFirst) v.load(src, tid, vpr);
   if (ASSIGN)
-    for (int64_t q = t * 256 + tid; q < as.clear_n; q += (int64_t)gridDim.x * 256) as.clear[q] = 0;
-  if (tid < d.k) {
-    const int64_t sigma = t * d.k + tid;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + tid; q < as.clear_n; q += (int64_t)gridDim.x * 256) as.clear[q] = 0;
+  if (tid < kp) {
+    const int64_t sigma = t * d.k + j0 + tid;
     int i, r;
     if (ASSIGN) {
       assign_slot(d, sigma, as.topk, as.tile_mask, as.tile_base, as.quota, ws, i, r);
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* 
   __syncthreads();
   for (int base = 0; base < vpr; base += 256 * VPT) {
     if (base > 0) v.load(src, base + tid, vpr);
-    for (int j = 0; j < d.k; ++j) {
+    for (int j = 0; j < kp; ++j) {
       const int p = pos_s[j];
       if (p >= 0) v.store(dispatch + (int64_t)p * vpr, base + tid, vpr);
     }
@@ -196,6 +199,17 @@ __global__ __launch_bounds__(256) void gather_u16_kernel(Dims d, const int32_t* 
 // (measured on MI355X: Qwen3-shaped step 160 -> 154 us, Mixtral-shaped 45 -> 32 us).
 bool one_round(const Dims& d) { return d.H / 8 <= 256; }
 
+// Workgroups per token of the row copy, measured on MI355X.  The assigning
+// copy runs best with about eight destinations per workgroup: a Kimi-K2-shaped
+// layer (k = 16, 7168-wide rows) takes 770 -> 735 us in two, while k = 8 in
+// two exposes the assignment's chain of dependent loads in every half
+// (DeepSeek-V3-shaped 804 -> 860 us, Qwen3-shaped 118 -> 133 us).  The plain
+// copy of a row longer than one store round gains from halving any k >= 8
+// (DeepSeek-V3-shaped 828 -> 777 us, Kimi-K2-shaped 790 -> 740 us; four parts:
+// 750-770 us); 2048-wide rows lose (118 -> 137 us).
+int assign_split(const Dims& d) { return (d.k + 7) / 8; }
+int plain_split(const Dims& d) { return !one_round(d) && d.k >= 8 ? 2 : 1; }
+
 }  // namespace
 
 hipError_t launch_gather(const Dims& d, const moe_plan_out& plan, const uint16_t* hidden, int32_t* perm,
@@ -209,13 +223,13 @@ hipError_t launch_gather(const Dims& d, const moe_plan_out& plan, const uint16_t
   const bool vec = (d.H % 8) == 0 && ((uintptr_t)hidden % 16) == 0 && ((uintptr_t)dispatch % 16) == 0;
   if (vec) {
     if (one_round(d))
-      hipLaunchKernelGGL((gather_vec_kernel<1, false>), dim3(d.T), dim3(256), 0, st, d, plan.slot_inst,
-                         plan.slot_rank, inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
-                         reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws);
+      hipLaunchKernelGGL((gather_vec_kernel<1, false>), dim3(d.T * plain_split(d)), dim3(256), 0, st, d,
+                         plan.slot_inst, plan.slot_rank, inst_offset, reinterpret_cast<const uint4*>(hidden), perm,
+                         slot_pos, reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws, plain_split(d));
     else
-      hipLaunchKernelGGL((gather_vec_kernel<4, false>), dim3(d.T), dim3(256), 0, st, d, plan.slot_inst,
-                         plan.slot_rank, inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
-                         reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws);
+      hipLaunchKernelGGL((gather_vec_kernel<4, false>), dim3(d.T * plain_split(d)), dim3(256), 0, st, d,
+                         plan.slot_inst, plan.slot_rank, inst_offset, reinterpret_cast<const uint4*>(hidden), perm,
+                         slot_pos, reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws, plain_split(d));
   } else {
     hipLaunchKernelGGL(gather_u16_kernel, dim3(d.T), dim3(256), 0, st, d, plan.slot_inst, plan.slot_rank,
                        inst_offset, hidden, perm, slot_pos, dispatch, ws.status);
@@ -254,13 +268,13 @@ hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const ui
   const AssignIn as{topk_idx, tile_mask, tile_base, plan.quota, plan.slot_inst, plan.slot_rank, clear,
                     clear ? clear_n : 0};
   if (one_round(d))
-    hipLaunchKernelGGL((gather_vec_kernel<1, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr,
-                       inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
-                       reinterpret_cast<uint4*>(dispatch), as, ws);
+    hipLaunchKernelGGL((gather_vec_kernel<1, true>), dim3(d.T * assign_split(d)), dim3(256), 0, st, d, nullptr,
+                       nullptr, inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                       reinterpret_cast<uint4*>(dispatch), as, ws, assign_split(d));
   else
-    hipLaunchKernelGGL((gather_vec_kernel<4, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr,
-                       inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
-                       reinterpret_cast<uint4*>(dispatch), as, ws);
+    hipLaunchKernelGGL((gather_vec_kernel<4, true>), dim3(d.T * assign_split(d)), dim3(256), 0, st, d, nullptr,
+                       nullptr, inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                       reinterpret_cast<uint4*>(dispatch), as, ws, assign_split(d));
   e = hipGetLastError();
   if (e == hipSuccess) e = gather_hooks_after(ev, st);
   return e;

@@ -59,7 +59,7 @@ def test_query_sizes_and_validation():
             m.moe_plan_query(c)
         assert ei.value.code == m.MOE_ERR_INVALID_ARG
     for c in [m.make_config(1024, 4096, 2, 4, 2, 16, 0), m.make_config(1024, 64, 33, 4, 2, 16, 0),
-              m.make_config(1024, 512, 2, 512, 2, 16, 0)]:
+              m.make_config(1024, 512, 2, 512, 2, 16, 0), m.make_config(1 << 22, 8, 1, 4, 2, 16, 0)]:
         with pytest.raises(m.MoePlanError) as ei:
             m.moe_plan_query(c)
         assert ei.value.code == m.MOE_ERR_UNSUPPORTED

@@ -270,6 +270,22 @@ def test_row_rounds_of_the_gather(mp, H, fused):
             "H=%d fused=%s" % (H, fused))
 
 
+@pytest.mark.parametrize("k,H,fused", [(12, 2056, True), (12, 2056, False), (16, 2056, True), (24, 2056, True),
+                                       (32, 2056, True), (32, 2056, False), (16, 2048, True), (9, 8200, True)])
+def test_row_copy_split_over_workgroups(mp, k, H, fused):
+    """A token's destinations shared by several workgroups of the gather: the assigning
+    copy of the step takes about eight per workgroup (k = 9..16 in two parts, possibly
+    uneven, 24 in three, 32 in four), the staged dispatch halves k >= 8 for rows longer
+    than one store round."""
+    T, E, R, G = 640, 64, 8, 4
+    cfg = mp.make_config(T, E, k, R, G, H, 8)
+    lg = inputs.random_logits(k * 100 + H, T, E)
+    hid = inputs.random_hidden(k, T, H)
+    print("row copy split k=%d H=%d fused=%s" % (k, H, fused), flush=True)
+    compare(gpu_layer(mp, cfg, logits=lg, hidden=hid, fused=fused), oracle_layer(cfg, logits=lg, hidden=hid),
+            "k=%d H=%d fused=%s" % (k, H, fused))
+
+
 def test_ties_signed_zero_and_infinities(mp):
     T, E, k, R, G = 256, 64, 8, 4, 2
     lg = inputs.random_logits(9, T, E, ties=True)
