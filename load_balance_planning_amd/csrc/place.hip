@@ -360,31 +360,81 @@ __global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds l
 
   // Degrees (column sums, equal to the row sums of a symmetric matrix) and
   // input checks: zero diagonal, no negative count, sums below 2^31
-  // (symmetry itself is the caller's contract).
-  int64_t my_max_deg = 0;
-  uint32_t my_max_entry = 0;  // a negative count reads as a large one here
+  // (symmetry itself is the caller's contract).  Every thread reads: with E a
+  // multiple of 4 and C 16-byte aligned, thread t takes the 16-byte column
+  // group t mod (E/4) of the rows congruent to t / (E/4), otherwise one column
+  // of the rows congruent to t / E (up to E = 512) or whole columns, and adds
+  // its partial sums into 64-bit totals kept in the member and slot tables'
+  // space (unused until the growth).
   uint16_t* c16 = reinterpret_cast<uint16_t*>(smem_place + ly.c16);
-  for (int e = tid; e < E; e += kPlaceThreads) {
-    int64_t s = 0;
-    bool bad = false;
+  int64_t* deg64 = reinterpret_cast<int64_t*>(smem_place + ly.mem);  // spans mem and pos
+  const int Es = c16_stride(E);
+  for (int e = tid; e < E; e += kPlaceThreads) deg64[e] = 0;
+  __syncthreads();
+  uint32_t my_max_entry = 0;  // a negative count reads as a large one here
+  bool bad = false;
+  auto add_deg = [&](int e, int64_t v) {
+    atomicAdd(reinterpret_cast<unsigned long long*>(&deg64[e]), (unsigned long long)v);
+  };
+  if (E % 4 == 0 && ((uintptr_t)C & 15) == 0) {
+    const int Q = E / 4, G = kPlaceThreads / Q;  // G >= 2: E <= 2048
+    if (tid < G * Q) {
+      const int c4 = tid % Q, g = tid / Q, e0 = 4 * c4;
+      const int4* C4 = reinterpret_cast<const int4*>(C);
+      int64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
 #pragma unroll 8
-    for (int x = 0; x < E; ++x) {
-      const int32_t v = C[(int64_t)x * E + e];
-      bad |= v < 0 || (x == e && v != 0);
-      s += v;
-      if constexpr (C_LDS) {
-        my_max_entry = max(my_max_entry, (uint32_t)v);
-        c16[x * c16_stride(E) + e] = (uint16_t)v;  // used only when every entry fits
+      for (int x = g; x < E; x += G) {
+        const int4 v = C4[(int64_t)x * Q + c4];
+        bad |= v.x < 0 || v.y < 0 || v.z < 0 || v.w < 0;
+        if (x >= e0 && x < e0 + 4) bad |= (x == e0 ? v.x : x == e0 + 1 ? v.y : x == e0 + 2 ? v.z : v.w) != 0;
+        s0 += v.x;
+        s1 += v.y;
+        s2 += v.z;
+        s3 += v.w;
+        if constexpr (C_LDS) {
+          my_max_entry = max(my_max_entry, max(max((uint32_t)v.x, (uint32_t)v.y), max((uint32_t)v.z, (uint32_t)v.w)));
+          uint2 h;  // used only when every entry fits; Es = E here, so 8-byte aligned
+          h.x = ((uint32_t)v.x & 0xffffu) | ((uint32_t)v.y << 16);
+          h.y = ((uint32_t)v.z & 0xffffu) | ((uint32_t)v.w << 16);
+          *reinterpret_cast<uint2*>(c16 + x * Es + e0) = h;
+        }
       }
+      add_deg(e0, s0);
+      add_deg(e0 + 1, s1);
+      add_deg(e0 + 2, s2);
+      add_deg(e0 + 3, s3);
     }
-    if (bad || s > INT32_MAX) atomicOr(pa.status, MOE_STATUS_BAD_PAIRS);
+  } else {
+    const int G = E <= kPlaceThreads / 2 ? kPlaceThreads / E : 1;
+    for (int t = tid; t < G * E; t += kPlaceThreads) {
+      const int e = t % E, g = t / E;
+      int64_t s = 0;
+#pragma unroll 8
+      for (int x = g; x < E; x += G) {
+        const int32_t v = C[(int64_t)x * E + e];
+        bad |= v < 0 || (x == e && v != 0);
+        s += v;
+        if constexpr (C_LDS) {
+          my_max_entry = max(my_max_entry, (uint32_t)v);
+          c16[x * Es + e] = (uint16_t)v;  // used only when every entry fits
+        }
+      }
+      add_deg(e, s);
+    }
+  }
+  if (bad) atomicOr(pa.status, MOE_STATUS_BAD_PAIRS);
+  bool use_c16 = false;
+  if constexpr (C_LDS) use_c16 = block_max((uint64_t)my_max_entry, red) <= 0xffffu;
+  else __syncthreads();
+  int64_t my_max_deg = 0;
+  for (int e = tid; e < E; e += kPlaceThreads) {
+    const int64_t s = deg64[e];
+    if (s > INT32_MAX) atomicOr(pa.status, MOE_STATUS_BAD_PAIRS);
     const int32_t dg = (int32_t)(s < 0 ? 0 : s > INT32_MAX ? INT32_MAX : s);
     deg[e] = dg;
     my_max_deg = max(my_max_deg, (int64_t)dg);
   }
-  const uint64_t max_deg = block_max((uint64_t)my_max_deg, red);  // also publishes deg[] and c16
-  bool use_c16 = false;
-  if constexpr (C_LDS) use_c16 = block_max((uint64_t)my_max_entry, red) <= 0xffffu;
+  const uint64_t max_deg = block_max((uint64_t)my_max_deg, red);  // also publishes deg[]; deg64 is free after
 
   // Greedy growth.  Scores are sums of counts, so never above the largest
   // degree: when that is below 2^20 a 32-bit key (score, then 4095 - e) suffices.
