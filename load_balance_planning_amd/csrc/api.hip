@@ -353,16 +353,17 @@ hipError_t moe::enqueue_step(const moe::Dims& d, const moe::Workspace& ws, const
   if (e == hipSuccess)
     e = moe::launch_plan(d, acc, scan, ws.prev_mask, route.cooc, trans, ws.pair_part, plan, out.inst_offset,
                          out.rank_offset, ws, moe::pipelined(ev), st);
-  if (moe::gather_can_assign(d, hidden, out.dispatch)) {
+  if (moe::gather_can_assign(d, hidden, out.dispatch) && moe::copy_in_one_part(d)) {
     // the gather assigns its token's slots itself, overlapping the row load
     if (e == hipSuccess)
       e = moe::launch_assign_gather(d, route.topk_idx, ws.tile_mask, ws.tile_base, plan, out.inst_offset, hidden,
                                     out.perm, out.slot_pos, out.dispatch, ws, acc, re, ev, st);
   } else {
+    // a copy in several parts per token: the slots first (before the copy's
+    // ordering hooks, so beside another batch's copy), then the parts
     if (e == hipSuccess) e = moe::launch_assign(d, route.topk_idx, ws.tile_mask, ws.tile_base, plan, ws, acc, re, st);
     if (e == hipSuccess)
-      e = moe::launch_gather(d, plan, hidden, out.perm, out.slot_pos, out.inst_offset, out.rank_offset, out.dispatch,
-                             ws, ev, st);
+      e = moe::launch_gather_rows(d, plan, hidden, out.perm, out.slot_pos, out.inst_offset, out.dispatch, ws, ev, st);
   }
   return e;
 }

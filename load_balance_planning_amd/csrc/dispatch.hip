@@ -94,35 +94,38 @@ __global__ __launch_bounds__(256) void offsets_kernel(Dims d, OffsetsIn in, int3
   }
 }
 
-// `split` adjacent workgroups per token, workgroup `part` taking the token's
-// slots j in [part*k/split, (part+1)*k/split).  Its first threads place those
-// slots -- reading instance and rank, or with ASSIGN computing them from the
-// plan (slot_assign.h) and writing them; the workgroup loads the hidden row
-// (the first 256*VPT vectors, staged through LDS: row_stage.h) and writes it
-// to those destinations (16-byte vectors, plain stores).
+// split * csplit adjacent workgroups per token: workgroup (part, half) takes
+// the token's slots j in [part*k/split, (part+1)*k/split) and the half-th of
+// csplit equal column ranges of the row.  Its first threads place those slots
+// -- reading instance and rank, or with ASSIGN computing them from the plan
+// (slot_assign.h) and writing them; the workgroup loads its range of the
+// hidden row (256*VPT vectors at a time, staged through LDS: row_stage.h) and
+// writes it to those destinations (16-byte vectors, plain stores).  Every
+// column part writes the same perm / slot_pos entries with the same values.
 template <int VPT, bool ASSIGN>
 __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* __restrict__ slot_inst,
                                                          const int32_t* __restrict__ slot_rank,
                                                          const int32_t* __restrict__ inst_offset,
                                                          const uint4* __restrict__ hidden, int32_t* __restrict__ perm,
                                                          int32_t* __restrict__ slot_pos, uint4* __restrict__ dispatch,
-                                                         AssignIn as, Workspace ws, int split) {
+                                                         AssignIn as, Workspace ws, int split, int csplit) {
   __shared__ int32_t pos_s[kMaxK];
   static_assert(sizeof(uint4) * VPT * 256 + sizeof(pos_s) <= kGatherWgLds, "the row copy's LDS");
-  const int64_t t = blockIdx.x / split;
-  const int part = (int)(blockIdx.x - t * split);
+  const int64_t t = blockIdx.x / (split * csplit);
+  const int rem = (int)(blockIdx.x - t * (split * csplit)), part = rem / csplit, half = rem - part * csplit;
   const int j0 = part * d.k / split, kp = (part + 1) * d.k / split - j0;
   const int tid = threadIdx.x;
   const int64_t N = (int64_t)d.T * d.k;
   const int vpr = d.H / 8;
   const uint4* src = hidden + t * vpr;
+  const int chunk = (vpr + csplit - 1) / csplit, cbeg = half * chunk, cend = min(vpr, cbeg + chunk);
   // Measured on MI355X: with the long chain of the assignment, issuing the
   // row loads first and overlapping them pays; with the two loads of a plain
   // placement, loading after the positions is faster.
   constexpr bool kLoadFirst = ASSIGN;
   __shared__ uint4 stage_s[VPT * 256];
   RowStage<VPT> v{stage_s};
-  if (kLoadFirst) v.load(src, tid, vpr);
+  if (kLoadFirst) v.load(src, cbeg + tid, cend);
   if (ASSIGN)
     for (int64_t q = (int64_t)blockIdx.x * 256 + tid; q < as.clear_n; q += (int64_t)gridDim.x * 256) as.clear[q] = 0;
   if (tid < kp) {
@@ -147,13 +150,13 @@ __global__ __launch_bounds__(256) void gather_vec_kernel(Dims d, const int32_t* 
     slot_pos[sigma] = (int32_t)p;
     pos_s[tid] = (int32_t)p;
   }
-  if (!kLoadFirst) v.load(src, tid, vpr);
+  if (!kLoadFirst) v.load(src, cbeg + tid, cend);
   __syncthreads();
-  for (int base = 0; base < vpr; base += 256 * VPT) {
-    if (base > 0) v.load(src, base + tid, vpr);
+  for (int base = cbeg; base < cend; base += 256 * VPT) {
+    if (base > cbeg) v.load(src, base + tid, cend);
     for (int j = 0; j < kp; ++j) {
       const int p = pos_s[j];
-      if (p >= 0) v.store(dispatch + (int64_t)p * vpr, base + tid, vpr);
+      if (p >= 0) v.store(dispatch + (int64_t)p * vpr, base + tid, cend);
     }
   }
 }
@@ -199,16 +202,27 @@ __global__ __launch_bounds__(256) void gather_u16_kernel(Dims d, const int32_t* 
 // (measured on MI355X: Qwen3-shaped step 160 -> 154 us, Mixtral-shaped 45 -> 32 us).
 bool one_round(const Dims& d) { return d.H / 8 <= 256; }
 
-// Workgroups per token of the row copy, measured on MI355X.  The assigning
-// copy runs best with about eight destinations per workgroup: a Kimi-K2-shaped
-// layer (k = 16, 7168-wide rows) takes 770 -> 735 us in two, while k = 8 in
-// two exposes the assignment's chain of dependent loads in every half
-// (DeepSeek-V3-shaped 804 -> 860 us, Qwen3-shaped 118 -> 133 us).  The plain
-// copy of a row longer than one store round gains from halving any k >= 8
-// (DeepSeek-V3-shaped 828 -> 777 us, Kimi-K2-shaped 790 -> 740 us; four parts:
-// 750-770 us); 2048-wide rows lose (118 -> 137 us).
-int assign_split(const Dims& d) { return (d.k + 7) / 8; }
-int plain_split(const Dims& d) { return !one_round(d) && d.k >= 8 ? 2 : 1; }
+// Parts per token of the row copy, measured on MI355X: the copy runs fastest
+// when each workgroup writes about 56 KiB (3584 16-byte vectors), so a token
+// writing k rows of vpr vectors takes floor(k * vpr / 3584) parts (at least
+// one, at most four), split by columns first (each hidden row is then read
+// once) and by destinations after.  DeepSeek-V3-shaped (k 8, 896 vectors):
+// one part 780-797 us, two column parts 771-776, two destination parts
+// 771-775 (reading each row twice), four parts 837; Kimi-K2-shaped (k 16):
+// one part 783-790 us, two destination parts 735-740, two column parts 771,
+// two of each 721; Qwen3-shaped (k 8, 256 vectors): one part 118 us, two
+// 127-137.
+constexpr int kCopyVectorsPerPart = 3584;
+struct CopyParts {
+  int split;   // destination parts
+  int csplit;  // column parts
+};
+CopyParts copy_parts(const Dims& d) {
+  const int vpr = d.H / 8;
+  const int64_t n = std::min<int64_t>(4, std::max<int64_t>(1, (int64_t)d.k * vpr / kCopyVectorsPerPart));
+  const int cs = n >= 2 && vpr >= 512 ? 2 : 1;
+  return CopyParts{std::min(d.k, (int)n / cs), cs};
+}
 
 }  // namespace
 
@@ -217,19 +231,28 @@ hipError_t launch_gather(const Dims& d, const moe_plan_out& plan, const uint16_t
                          const Workspace& ws, const KernelEvents& ev, hipStream_t st) {
   const OffsetsIn oi{plan.n_inst, plan.inst_load, plan.inst_rank, inst_offset, rank_offset};
   hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(256), sizeof(int32_t) * (size_t)(d.cap + 1), st, d, oi, ws.status);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || d.T == 0) return e;
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_gather_rows(d, plan, hidden, perm, slot_pos, inst_offset, dispatch, ws, ev, st);
+}
+
+hipError_t launch_gather_rows(const Dims& d, const moe_plan_out& plan, const uint16_t* hidden, int32_t* perm,
+                              int32_t* slot_pos, const int32_t* inst_offset, uint16_t* dispatch, const Workspace& ws,
+                              const KernelEvents& ev, hipStream_t st) {
+  if (d.T == 0) return hipSuccess;
+  hipError_t e;
   if ((e = gather_hooks_before(ev, st)) != hipSuccess) return e;
-  const bool vec = (d.H % 8) == 0 && ((uintptr_t)hidden % 16) == 0 && ((uintptr_t)dispatch % 16) == 0;
-  if (vec) {
+  if (gather_can_assign(d, hidden, dispatch)) {
+    const CopyParts cp = copy_parts(d);
+    const dim3 grid((unsigned)(d.T * cp.split * cp.csplit));
     if (one_round(d))
-      hipLaunchKernelGGL((gather_vec_kernel<1, false>), dim3(d.T * plain_split(d)), dim3(256), 0, st, d,
-                         plan.slot_inst, plan.slot_rank, inst_offset, reinterpret_cast<const uint4*>(hidden), perm,
-                         slot_pos, reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws, plain_split(d));
+      hipLaunchKernelGGL((gather_vec_kernel<1, false>), grid, dim3(256), 0, st, d, plan.slot_inst, plan.slot_rank,
+                         inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                         reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws, cp.split, cp.csplit);
     else
-      hipLaunchKernelGGL((gather_vec_kernel<4, false>), dim3(d.T * plain_split(d)), dim3(256), 0, st, d,
-                         plan.slot_inst, plan.slot_rank, inst_offset, reinterpret_cast<const uint4*>(hidden), perm,
-                         slot_pos, reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws, plain_split(d));
+      hipLaunchKernelGGL((gather_vec_kernel<4, false>), grid, dim3(256), 0, st, d, plan.slot_inst, plan.slot_rank,
+                         inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
+                         reinterpret_cast<uint4*>(dispatch), AssignIn{}, ws, cp.split, cp.csplit);
   } else {
     hipLaunchKernelGGL(gather_u16_kernel, dim3(d.T), dim3(256), 0, st, d, plan.slot_inst, plan.slot_rank,
                        inst_offset, hidden, perm, slot_pos, dispatch, ws.status);
@@ -257,6 +280,11 @@ bool gather_can_assign(const Dims& d, const uint16_t* hidden, const uint16_t* di
   return (d.H % 8) == 0 && ((uintptr_t)hidden % 16) == 0 && ((uintptr_t)dispatch % 16) == 0;
 }
 
+bool copy_in_one_part(const Dims& d) {
+  const CopyParts cp = copy_parts(d);
+  return cp.split * cp.csplit == 1;
+}
+
 hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
                                 const int32_t* tile_base, const moe_plan_out& plan, const int32_t* inst_offset,
                                 const uint16_t* hidden, int32_t* perm, int32_t* slot_pos, uint16_t* dispatch,
@@ -268,13 +296,13 @@ hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const ui
   const AssignIn as{topk_idx, tile_mask, tile_base, plan.quota, plan.slot_inst, plan.slot_rank, clear,
                     clear ? clear_n : 0};
   if (one_round(d))
-    hipLaunchKernelGGL((gather_vec_kernel<1, true>), dim3(d.T * assign_split(d)), dim3(256), 0, st, d, nullptr,
-                       nullptr, inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
-                       reinterpret_cast<uint4*>(dispatch), as, ws, assign_split(d));
+    hipLaunchKernelGGL((gather_vec_kernel<1, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr, inst_offset,
+                       reinterpret_cast<const uint4*>(hidden), perm, slot_pos, reinterpret_cast<uint4*>(dispatch), as,
+                       ws, 1, 1);
   else
-    hipLaunchKernelGGL((gather_vec_kernel<4, true>), dim3(d.T * assign_split(d)), dim3(256), 0, st, d, nullptr,
-                       nullptr, inst_offset, reinterpret_cast<const uint4*>(hidden), perm, slot_pos,
-                       reinterpret_cast<uint4*>(dispatch), as, ws, assign_split(d));
+    hipLaunchKernelGGL((gather_vec_kernel<4, true>), dim3(d.T), dim3(256), 0, st, d, nullptr, nullptr, inst_offset,
+                       reinterpret_cast<const uint4*>(hidden), perm, slot_pos, reinterpret_cast<uint4*>(dispatch), as,
+                       ws, 1, 1);
   e = hipGetLastError();
   if (e == hipSuccess) e = gather_hooks_after(ev, st);
   return e;

@@ -160,9 +160,17 @@ hipError_t gather_hooks_after(const KernelEvents& ev, hipStream_t st);
 hipError_t launch_gather(const Dims& d, const moe_plan_out& plan, const uint16_t* hidden, int32_t* perm,
                          int32_t* slot_pos, int32_t* inst_offset, int32_t* rank_offset, uint16_t* dispatch,
                          const Workspace& ws, const KernelEvents& ev, hipStream_t st);
-// The gather that also assigns the slots (writes plan.slot_inst / slot_rank);
-// only for 16-byte-aligned rows with H a multiple of 8 (gather_can_assign).
+// The row copy alone (no dispatch offsets) from the plan's slot_inst / slot_rank.
+hipError_t launch_gather_rows(const Dims& d, const moe_plan_out& plan, const uint16_t* hidden, int32_t* perm,
+                              int32_t* slot_pos, const int32_t* inst_offset, uint16_t* dispatch, const Workspace& ws,
+                              const KernelEvents& ev, hipStream_t st);
+// The gather that also assigns the slots (writes plan.slot_inst / slot_rank),
+// one workgroup per token; only for 16-byte-aligned rows with H a multiple of
+// 8 (gather_can_assign).  The single call uses it where the copy runs in one
+// part per token (copy_in_one_part); elsewhere it assigns first and copies in
+// parts, since each part would repeat the assignment's dependent loads.
 bool gather_can_assign(const Dims& d, const uint16_t* hidden, const uint16_t* dispatch);
+bool copy_in_one_part(const Dims& d);
 hipError_t launch_assign_gather(const Dims& d, const int32_t* topk_idx, const uint64_t* tile_mask,
                                 const int32_t* tile_base, const moe_plan_out& plan, const int32_t* inst_offset,
                                 const uint16_t* hidden, int32_t* perm, int32_t* slot_pos, uint16_t* dispatch,

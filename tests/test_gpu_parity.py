@@ -270,18 +270,21 @@ def test_row_rounds_of_the_gather(mp, H, fused):
             "H=%d fused=%s" % (H, fused))
 
 
-@pytest.mark.parametrize("k,H,fused", [(12, 2056, True), (12, 2056, False), (16, 2056, True), (24, 2056, True),
-                                       (32, 2056, True), (32, 2056, False), (16, 2048, True), (9, 8200, True)])
-def test_row_copy_split_over_workgroups(mp, k, H, fused):
-    """A token's destinations shared by several workgroups of the gather: the assigning
-    copy of the step takes about eight per workgroup (k = 9..16 in two parts, possibly
-    uneven, 24 in three, 32 in four), the staged dispatch halves k >= 8 for rows longer
-    than one store round."""
+@pytest.mark.parametrize("k,H,fused", [(8, 7168, True), (8, 7168, False), (16, 7168, True), (12, 2056, True),
+                                       (12, 2056, False), (32, 2056, True), (9, 8200, True), (32, 8200, True),
+                                       (8, 16400, False), (16, 2048, True)])
+def test_row_copy_in_parts(mp, k, H, fused):
+    """The row copy in one to four parts per token (about 3584 16-byte vectors written per
+    workgroup): column halves of 7168- and 8200-wide rows (an odd 1025 vectors), destination
+    halves of short rows at k = 32, both at k >= 16 with long rows (and the four-part cap at
+    k = 32), two load rounds per column half at H = 16400; through the staged dispatch and
+    the single call, which assigns the slots in a kernel of its own before a copy in parts
+    and inside the copy otherwise."""
     T, E, R, G = 640, 64, 8, 4
     cfg = mp.make_config(T, E, k, R, G, H, 8)
     lg = inputs.random_logits(k * 100 + H, T, E)
     hid = inputs.random_hidden(k, T, H)
-    print("row copy split k=%d H=%d fused=%s" % (k, H, fused), flush=True)
+    print("row copy parts k=%d H=%d fused=%s" % (k, H, fused), flush=True)
     compare(gpu_layer(mp, cfg, logits=lg, hidden=hid, fused=fused), oracle_layer(cfg, logits=lg, hidden=hid),
             "k=%d H=%d fused=%s" % (k, H, fused))
 
