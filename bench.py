@@ -139,6 +139,19 @@ def source_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
+def step_copy_kernel(w) -> str:
+    """The row-copy kernel moe_plan_step launches for this shape, by the library's rule: a
+    part per 3584 16-byte vectors a token writes (k rows of H/8 vectors; one to four parts).
+    With one part the copy assigns the slots itself; with more, assign_kernel runs first."""
+    vpr = w.H // 8
+    vpt = 1 if vpr <= 256 else 4
+    parts = min(4, max(1, w.k * vpr // 3584))
+    if parts == 1:
+        return "gather_vec_kernel<%d, true> (the row copy of moe_plan_step, with the slot assignment)" % vpt
+    return ("gather_vec_kernel<%d, false> (the row copy of moe_plan_step, %d parts per token, after the slot "
+            "assignment's own kernel)" % (vpt, parts))
+
+
 def gather_traffic(w):
     """HBM bytes per gather launch as measured by the committed rocprofv3 counter runs
     (FETCH_SIZE and WRITE_SIZE, each in a run of its own, scaled by a plain copy), if they
@@ -856,7 +869,7 @@ def main():
                    "inputs_sha256_16": inputs_sha(w), "second_batch_seed": second_batch(w).seed,
                    "second_batch_sha256_16": inputs_sha(second_batch(w))},
         "roofline": {"bound": "hbm",
-                     "kernel": "gather_vec_kernel<4, true> (the row copy of moe_plan_step, with the slot assignment)",
+                     "kernel": step_copy_kernel(w),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "traffic_source": traffic_source,
                      "algorithmic_bytes_per_launch": ab["gather"], "launch_ms": gather_ms,
