@@ -25,7 +25,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
   size_t status, tile_mask, tile_base, prev_mask, demand, einst_off, einst_list, rlist, colpre, pair_part, omega_acc;
-  size_t place_aff, place_key, dd_mask, dd_cnt, dd_base, dd_count, pred_vote, total;
+  size_t place_aff, place_key, place_int, place_mem, place_c16, dd_mask, dd_cnt, dd_base, dd_count, pred_vote, total;
 };
 
 WsLayout ws_layout(const moe::Dims& d) {
@@ -45,6 +45,9 @@ WsLayout ws_layout(const moe::Dims& d) {
   l.omega_acc = take(sizeof(int32_t) * (size_t)d.R * d.E);
   l.place_aff = take(sizeof(int32_t) * (size_t)d.R * d.E);
   l.place_key = take(sizeof(uint64_t) * (size_t)d.R * d.R);
+  l.place_int = take(sizeof(int32_t) * 4 * (size_t)d.E);
+  l.place_mem = take(sizeof(int32_t) * (size_t)d.E);
+  l.place_c16 = take(sizeof(uint16_t) * moe::place_c16_elems(d));
   l.dd_mask = take(sizeof(uint64_t) * (size_t)d.NT * d.R);
   l.dd_cnt = take(sizeof(int32_t) * (size_t)d.NT * d.R);
   l.dd_base = take(sizeof(int32_t) * (size_t)d.NT * d.R);
@@ -175,6 +178,9 @@ extern "C" int moe_plan_create(const moe_plan_config* cfg, moe_plan_t* out) {
   h->ws.omega_acc = reinterpret_cast<int32_t*>(b + l.omega_acc);
   h->ws.place_aff = reinterpret_cast<int32_t*>(b + l.place_aff);
   h->ws.place_key = reinterpret_cast<uint64_t*>(b + l.place_key);
+  h->ws.place_int = reinterpret_cast<int32_t*>(b + l.place_int);
+  h->ws.place_mem = reinterpret_cast<int32_t*>(b + l.place_mem);
+  h->ws.place_c16 = reinterpret_cast<uint16_t*>(b + l.place_c16);
   h->ws.dd_mask = reinterpret_cast<uint64_t*>(b + l.dd_mask);
   h->ws.dd_cnt = reinterpret_cast<int32_t*>(b + l.dd_cnt);
   h->ws.dd_base = reinterpret_cast<int32_t*>(b + l.dd_base);

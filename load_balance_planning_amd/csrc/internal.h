@@ -58,8 +58,11 @@ struct Workspace {
   int32_t* pair_part;   // partial pair-count blocks of the tile splits (pair_part_words)
   int32_t* omega_acc;   // [R][E] routing matrix accumulated by the top-k kernel of
                         // moe_plan_step; zero between calls (the slot assignment clears it)
-  int32_t* place_aff;   // [R][E] placement affinities when they do not fit in LDS
-  uint64_t* place_key;  // [R][R] best swap key per rank pair when it does not fit in LDS
+  int32_t* place_aff;   // [R][E] placement affinities
+  uint64_t* place_key;  // [R][R] best swap key per rank pair
+  int32_t* place_int;   // [4][E] placement: degrees, largest entry per row, rank of each expert, own affinity
+  int32_t* place_mem;   // [E] placement: the experts of each rank, E/R per rank
+  uint16_t* place_c16;  // [place_c16_elems] 16-bit copy of the co-selection counts
   uint64_t* dd_mask;    // [NT][R] deduplication: tokens of each tile with a slot on each rank
   int32_t* dd_cnt;      // [NT][R] slots of each tile on each rank
   int32_t* dd_base;     // [NT][R] rows of each rank before each tile
@@ -208,6 +211,7 @@ hipError_t launch_replica_push(const Dims& d, const int32_t* slot_expert, const 
 size_t plan_lds_bytes(const Dims& d);
 size_t scan_lds_bytes(const Dims& d);
 size_t place_lds_bytes(const Dims& d);
+size_t place_c16_elems(const Dims& d);
 size_t dedup_scan_lds_bytes(const Dims& d);
 // Workspace words of the pair kernel.
 size_t pair_part_words(const Dims& d);

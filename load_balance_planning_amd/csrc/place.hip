@@ -16,19 +16,24 @@
 //               (aff[r][x] = sum over y on rank r of C[x][y]; ties to the lower
 //               a, then b) while the gain is positive, at most max_swaps times.
 //
-// One workgroup of 1024 threads; the problem is tiny and sequential.  Growth
-// takes E steps of one argmax each: every thread holds the affinities of its
-// E/1024 experts in registers, a wave's maximum comes from a DPP butterfly
-// inside each 16-lane row and four lane reads, and the workgroup's from an LDS
-// atomic max into one of three rotating slots -- one barrier per step.  When
-// the counts fit 16 bits and E*E*2 bytes fit in LDS (E up to ~270), C is
-// copied to LDS during the degree pass and one wave runs the whole growth
-// (wave-uniform argmax, no atomic, no barrier per step).
-// Refinement keeps, for every rank pair (r1 < r2), the best swap key of the
-// pairs between them; a swap between ra and rb changes only the gains of pairs
-// with an expert on ra or rb, so an iteration re-evaluates 2R-3 rank pairs
-// (about 2*E*E/R expert pairs) instead of all E*E/2.  aff and the rank-pair
-// keys live in LDS when they fit, else in the handle's workspace.
+// Four launches.  The passes over all of C run on the whole chip; the two
+// sequential phases run in one workgroup each:
+//   prep   one wave per row: the degree (row sum), the input checks, the row's
+//          largest entry and a 16-bit copy of the row;
+//   grow   one workgroup.  When every count fits 16 bits one wave grows alone
+//          -- each step a wave-uniform argmax (DPP and lane reads, no atomic,
+//          no barrier) and one 16-bit row read, from LDS when the copy fits
+//          there, else from the L2-resident copy; otherwise the whole
+//          workgroup holds the affinities, one LDS atomic max and one barrier
+//          per step.  It leaves the ranks, aff and own[e] = aff[rank(e)][e];
+//   pass   one wave per expert x: the swap keys of its pairs (x, y > x),
+//          folded per rank in LDS, then one device atomic max per rank pair;
+//   swap   one workgroup: the refinement.  A swap between ra and rb changes
+//          only the gains of pairs with an expert on ra or rb, so an iteration
+//          re-evaluates 2R-3 rank pairs (about 2*E*E/R expert pairs) instead
+//          of all E*E/2.  aff and the rank-pair keys live in LDS when they fit.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace moe {
@@ -36,64 +41,40 @@ namespace {
 
 constexpr int kPlaceThreads = 1024;
 constexpr int kPlaceWaves = kPlaceThreads / 64;
+constexpr int kPassWaves = 4;               // waves per workgroup of the prep and pair passes
+constexpr int kGrowThreads = 256;           // the growth's workgroup
+constexpr int kGrowWaves = kGrowThreads / 64;
 constexpr uint64_t kGainBias = 1ull << 40;  // |gain| < 2^34 for valid counts
 constexpr int kPairBits = 22;               // pair index a*E+b < 2048^2
 constexpr uint64_t kPairMask = (1ull << kPairBits) - 1;
 
-struct PlaceArgs {
-  const int32_t* C;    // [E][E] co-selection counts
-  int32_t max_swaps;
-  int32_t* expert_rank;
-  int32_t* rank_experts;
-  int64_t* intra;
-  int32_t* n_swaps;
-  int32_t* aff_ws;     // [R][E] when aff does not fit in LDS
-  uint64_t* key_ws;    // [R][R] when the rank-pair keys do not fit in LDS
-  int32_t* status;
-};
-
-struct PlaceLds {
-  size_t rank_of, mem, pos, deg, own, col, red, aff, key, c16, total;
-  bool aff_in_lds, key_in_lds, c_in_lds;
-};
-
 constexpr size_t kPlaceAffLds = 64 * 1024;
-constexpr size_t kPlaceKeyLds = 32 * 1024;
-
+constexpr size_t kPlaceKeyLds = 34 * 1024;  // R up to 64, rows padded by one key
 constexpr size_t kPlaceLdsBudget = 160 * 1024;
-constexpr int kWaveGrowMaxE = 384;  // the one-wave growth holds up to 6 experts per lane
+constexpr int kMaxU = 16;  // 32-bit words of a 16-bit row per lane: E <= 2048
+constexpr size_t kGrowRedBytes = 16 * (kGrowWaves + 2);  // the reduction slots and a sink word
 
-// Row stride (16-bit elements) of the LDS copy of C: even, so that a lane's
+// Row stride (16-bit elements) of the 16-bit copy of C: even, so that a lane's
 // two experts 2l, 2l + 1 are one aligned 32-bit word.  A tail pad of 128
 // elements covers the last row's reads past E.
 __host__ __device__ inline int c16_stride(int E) { return E + (E & 1); }
+__host__ __device__ inline size_t c16_count(int E) { return (size_t)E * c16_stride(E) + 128; }
 
-// LDS: the arrays of the whole kernel first; then a region that the growth
-// uses for a 16-bit copy of the co-selection counts (when it fits) and the
-// refinement for own, the per-wave columns, aff and the rank-pair keys.
-PlaceLds place_lds(const Dims& d) {
-  PlaceLds l;
-  size_t o = 0;
-  auto take = [&](size_t b) { const size_t at = o; o += (b + 15) / 16 * 16; return at; };
-  l.rank_of = take(sizeof(int32_t) * d.E);
-  l.mem = take(sizeof(int32_t) * d.E);
-  l.pos = take(sizeof(int32_t) * d.E);
-  l.deg = take(sizeof(int32_t) * d.E);
-  l.red = take(sizeof(uint64_t) * (kPlaceWaves + 1));  // also the growth's three argmax slots
-  const size_t shared_at = o;
-  l.own = take(sizeof(int32_t) * d.E);
-  l.col = take(sizeof(int32_t) * kPlaceWaves * (size_t)d.R);
-  const size_t aff_b = sizeof(int32_t) * (size_t)d.R * d.E;
-  const size_t key_b = sizeof(uint64_t) * (size_t)d.R * d.R;
-  l.aff_in_lds = aff_b <= kPlaceAffLds;
-  l.key_in_lds = key_b <= kPlaceKeyLds;
-  l.aff = l.aff_in_lds ? take(aff_b) : 0;
-  l.key = l.key_in_lds ? take(key_b) : 0;
-  const size_t c16_b = sizeof(uint16_t) * ((size_t)d.E * c16_stride(d.E) + 128);
-  l.c16 = shared_at;
-  l.c_in_lds = shared_at + c16_b <= kPlaceLdsBudget && d.E <= kWaveGrowMaxE;
-  l.total = l.c_in_lds && shared_at + c16_b > o ? shared_at + c16_b : o;
-  return l;
+// The workspace parts of the placement.
+struct PlaceState {
+  int32_t* deg;      // [E] row sums, clamped to [0, 2^31)
+  int32_t* rowmax;   // [E] largest entry of each row, as unsigned (a negative entry reads as a large one)
+  int32_t* rank_of;  // [E]
+  int32_t* own;      // [E] aff[rank_of[e]][e]
+  int32_t* mem;      // [R][Er] the experts of each rank
+  int32_t* aff;      // [R][E]
+  uint64_t* key;     // [R][R] best swap key of each rank pair (r1 < r2)
+  uint16_t* c16;     // [E][c16_stride(E)] + pad
+};
+
+PlaceState place_state(const Dims& d, const Workspace& ws) {
+  return PlaceState{ws.place_int,         ws.place_int + d.E, ws.place_int + 2 * d.E, ws.place_int + 3 * d.E,
+                    ws.place_mem,         ws.place_aff,       ws.place_key,           ws.place_c16};
 }
 
 // DPP moves inside a 16-lane row (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
@@ -142,109 +123,154 @@ __device__ __forceinline__ int64_t wave_sum(int64_t v) {
   return v;
 }
 
-// Maximum of v over the workgroup, returned to every thread.
+// Maximum of v over a workgroup of NW waves, returned to every thread
+// (red: NW + 1 entries; the next call may follow at once, as it writes
+// entries [0, NW) and reads entry NW only after a barrier).
+template <int NW>
 __device__ __forceinline__ uint64_t block_max(uint64_t v, uint64_t* red) {
   v = wave_max(v);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (lane == 0) red[w] = v;
   __syncthreads();
   if (w == 0) {
-    uint64_t x = lane < kPlaceWaves ? red[lane] : 0;
+    uint64_t x = lane < NW ? red[lane] : 0;
     x = wave_max(x);
-    if (lane == 0) red[kPlaceWaves] = x;
+    if (lane == 0) red[NW] = x;
   }
   __syncthreads();
-  return red[kPlaceWaves];
+  return red[NW];
 }
 
-// Rank-pair swap keys live in LDS (ds atomics) or in global memory (device
-// atomics at L2; reads bypass the L1).
-template <bool LDS>
-__device__ __forceinline__ uint64_t key_load(const uint64_t* p) {
-  if constexpr (LDS) return *p;
-  else return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Swap key of experts x on rank rx and y on rank ry != rx: the gain
+//   aff[ry][x] - own[x] + aff[rx][y] - own[y] - 2 C[x][y]
+// biased to be positive, then the pair (lower id first) preferring lower ids.
+__device__ __forceinline__ uint64_t swap_key(int64_t gain, int x, int y, int E) {
+  const uint64_t pair = (uint64_t)min(x, y) * E + max(x, y);
+  return ((uint64_t)(gain + (int64_t)kGainBias) << kPairBits) | (kPairMask - pair);
 }
 
-// Swap keys of the pairs (x, y), y on another rank than x, folded into
-// key[min(rx, ry)][max(rx, ry)] by atomic max.  A key is the gain, then the
-// pair (lower id first) preferring lower ids:
-//   gain = aff[ry][x] - own[x] + aff[rx][y] - own[y] - 2 C[x][y],
-// own[e] = aff[rank(e)][e].  ALL: every x, with y > x.  Otherwise x runs over
-// the experts of ranks ra and rb and y over all experts.  One wave per x:
-// the C row and the aff[rx] row are read along y (coalesced); the column
-// aff[*][x] goes to the wave's LDS buffer col.
-template <bool ALL, bool KEY_LDS>
-__device__ __forceinline__ void eval_rows(const Dims& d, const int32_t* __restrict__ C, const int32_t* aff,
-                                          const int32_t* own, const int32_t* rank_of, const int32_t* mem,
-                                          uint64_t* key, int32_t* col, int ra, int rb) {
-  const int E = d.E, R = d.R, Er = d.Er;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nx = ALL ? E : 2 * Er;
-  for (int i = wave; i < nx; i += kPlaceWaves) {
-    const int x = ALL ? i : (i < Er ? mem[ra * Er + i] : mem[rb * Er + i - Er]);
-    const int rx = rank_of[x];
-    const int64_t ox = own[x];
-    for (int r = lane; r < R; r += 64) col[r] = aff[(int64_t)r * E + x];
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    const int32_t* crow = C + (int64_t)x * E;
-    const int32_t* arow = aff + (int64_t)rx * E;
-#pragma unroll 2
-    for (int y = (ALL ? x + 1 : 0) + lane; y < E; y += 64) {
-      const int ry = rank_of[y];
-      if (ry == rx) continue;
-      const int64_t g = (int64_t)col[ry] - ox + arow[y] - own[y] - 2 * (int64_t)crow[y];
-      const uint64_t pair = (uint64_t)min(x, y) * E + max(x, y);
-      const uint64_t kk = ((uint64_t)(g + (int64_t)kGainBias) << kPairBits) | (kPairMask - pair);
-      atomicMax(&key[min(rx, ry) * R + max(rx, ry)], kk);
+// Brings [p, p + bytes) into this CU's L2 (one dword per 128-byte line, eight
+// lines in flight per thread) so that the sequential phase after it reads its
+// rows at L2 latency.  The loaded words are folded into *sink (LDS) only to
+// keep the loads; the value is meaningless.
+template <int NT>
+__device__ __forceinline__ void warm_l2(const void* p, size_t bytes, uint32_t* sink) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+  const int64_t lines = (int64_t)(bytes / 128);
+  uint32_t acc = 0;
+  for (int64_t l0 = threadIdx.x; l0 < lines; l0 += 8 * NT) {
+    uint32_t t[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) t[b] = l0 + b * NT < lines ? w[(l0 + b * NT) * 32] : 0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc ^= t[b];
+  }
+  if (acc == 0x9e3779b9u) *sink = acc;
+}
+
+// ---------------------------------------------------------------------------
+// prep: one wave per row e of C.  deg[e] = sum_x C[e][x], the checks (no
+// negative count, zero diagonal, row sum below 2^31; symmetry is the caller's
+// contract), the row's largest entry and its 16-bit copy (meaningful only
+// when every entry fits 16 bits, which the growth checks).
+__global__ __launch_bounds__(64 * kPassWaves) void place_prep_kernel(Dims d, const int32_t* __restrict__ C,
+                                                                     PlaceState s, int32_t* __restrict__ status) {
+  const int E = d.E, Es = c16_stride(E);
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * kPassWaves + (threadIdx.x >> 6);
+  if (e >= E) return;  // no barrier below
+  const int32_t* row = C + (int64_t)e * E;
+  uint16_t* out = s.c16 + (size_t)e * Es;
+  int64_t sum = 0;
+  uint32_t mx = 0;
+  bool bad = false;
+  if (E % 4 == 0 && ((uintptr_t)C & 15) == 0) {
+    const int4* r4 = reinterpret_cast<const int4*>(row);
+#pragma unroll 4
+    for (int q = lane; q < E / 4; q += 64) {
+      const int4 v = r4[q];
+      const int y = 4 * q;
+      bad |= v.x < 0 || v.y < 0 || v.z < 0 || v.w < 0;
+      if (e >= y && e < y + 4) bad |= (e == y ? v.x : e == y + 1 ? v.y : e == y + 2 ? v.z : v.w) != 0;
+      sum += (int64_t)v.x + v.y + v.z + v.w;
+      mx = max(mx, max(max((uint32_t)v.x, (uint32_t)v.y), max((uint32_t)v.z, (uint32_t)v.w)));
+      uint2 h;  // Es = E here: 8-byte aligned
+      h.x = ((uint32_t)v.x & 0xffffu) | ((uint32_t)v.y << 16);
+      h.y = ((uint32_t)v.z & 0xffffu) | ((uint32_t)v.w << 16);
+      *reinterpret_cast<uint2*>(out + y) = h;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // col is rewritten for the next x
+  } else {
+    for (int y = lane; y < E; y += 64) {
+      const int32_t v = row[y];
+      bad |= v < 0 || (y == e && v != 0);
+      sum += v;
+      mx = max(mx, (uint32_t)v);
+      out[y] = (uint16_t)v;
+    }
+  }
+  if (bad) atomicOr(status, MOE_STATUS_BAD_PAIRS);
+  sum = wave_sum(sum);
+  mx = wave_max(mx);
+  if (lane == 0) {
+    if (sum > INT32_MAX) atomicOr(status, MOE_STATUS_BAD_PAIRS);
+    s.deg[e] = (int32_t)(sum < 0 ? 0 : sum > INT32_MAX ? INT32_MAX : sum);
+    s.rowmax[e] = (int32_t)mx;
   }
 }
 
-// Greedy growth in one wave, with C's rows in LDS (16-bit, row stride
-// c16_stride(E), even): lane l holds the affinities of experts 2l + 128u and
-// 2l + 128u + 1 (u < U), read as one 32-bit word per u and step with no
-// bounds branch -- lanes past E read the next row (or the tail pad) into
-// experts that are never alive.  The argmax is wave-uniform (DPP and lane
-// reads), so a step needs no atomic and no barrier; the picks are kept one
-// per lane and written out every 64 steps and at the end of each rank.
+// ---------------------------------------------------------------------------
+// grow: the greedy growth.
+
+// One wave, with C's rows as 16-bit counts (row stride c16_stride(E), even):
+// lane l holds the affinities of experts 2l + 128u and 2l + 128u + 1 (u < U),
+// read as one 32-bit word per u and step with no bounds branch -- lanes past E
+// read the next row (or the tail pad) into experts that are never alive.  A
+// key is (score, then 4095 - e), masked to 0 once e is placed; the argmax is
+// wave-uniform (DPP and lane reads), so a step needs no atomic and no barrier.
+// The picks are kept one per lane and written out every 64 steps and at the
+// end of each rank.  c16 points to LDS or to global memory.
 template <class K, int U>
 __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, const int32_t* deg, int32_t* rank_of,
-                                          int32_t* mem, int32_t* pos, int32_t* aff) {
+                                          int32_t* mem, int32_t* aff) {
   const int E = d.E, R = d.R, Er = d.Er, Es = c16_stride(E);
   const int lane = threadIdx.x & 63;
   constexpr int J = 2 * U;
   constexpr int kShift = 12;
   constexpr K kIdx = ((K)1 << kShift) - 1;
-  int32_t dg[J], a[J];
-  uint32_t alive = 0;
+  int32_t live[J], dg[J], a[J];  // live: 0 once placed, else -1 (a key mask)
+  uint32_t ik[J];                 // 4095 - e
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = 2 * lane + 128 * (j >> 1) + (j & 1);
-    dg[j] = e < E ? deg[e] : 0;
-    if (e < E) alive |= 1u << j;
+    ik[j] = (uint32_t)(kIdx - (K)e);
+    live[j] = e < E ? -1 : 0;
+    dg[j] = deg[min(e, E - 1)];  // unguarded: a guarded load waits alone
+    a[j] = 0;
   }
   int32_t pk = 0;  // lane i: the pick of step (m - m % 64 + i) of the current rank
   for (int r = 0; r < R; ++r) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) a[j] = 0;
     for (int m = 0; m < Er; ++m) {
       K best = 0;
+      if (m == 0) {
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int e = 2 * lane + 128 * (j >> 1) + (j & 1);
-        const K kk = ((K)(m == 0 ? dg[j] : a[j]) << kShift) | (K)(kIdx - e);
-        best = ((alive >> j) & 1u) && kk > best ? kk : best;
+        for (int j = 0; j < J; ++j) best = max(best, (((K)(uint32_t)dg[j] << kShift) | ik[j]) & (K)(int64_t)live[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) best = max(best, (((K)(uint32_t)a[j] << kShift) | ik[j]) & (K)(int64_t)live[j]);
       }
       best = wave_max(best);
-      const int pick = (int)(kIdx - (best & kIdx));
+      // A live expert always has a key above 0, so the pick is below E; the
+      // clamp only keeps the row read inside the copy whatever the input.
+      const int pick = min((int)(kIdx - (best & kIdx)), E - 1);
       const uint32_t* row = reinterpret_cast<const uint32_t*>(c16 + pick * Es) + lane;
       uint32_t v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) v[u] = row[64 * u];
+      const int jj = 2 * (pick >> 7) + (pick & 1);
+      const bool mine = lane == ((pick & 127) >> 1);
 #pragma unroll
       for (int j = 0; j < J; ++j)
-        if (2 * lane + 128 * (j >> 1) + (j & 1) == pick) alive &= ~(1u << j);
+        if (j == jj && mine) live[j] = 0;
       const int q = m & 63;
       if (lane == q) pk = pick;
       if (q == 63 || m == Er - 1) {
@@ -252,13 +278,20 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
         if (lane <= q) {
           mem[base + lane] = pk;
           rank_of[pk] = r;
-          pos[pk] = base + lane;
         }
       }
+      if (m == 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        a[2 * u] += (int32_t)(v[u] & 0xffffu);
-        a[2 * u + 1] += (int32_t)(v[u] >> 16);
+        for (int u = 0; u < U; ++u) {
+          a[2 * u] = (int32_t)(v[u] & 0xffffu);
+          a[2 * u + 1] = (int32_t)(v[u] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          a[2 * u] += (int32_t)(v[u] & 0xffffu);
+          a[2 * u + 1] += (int32_t)(v[u] >> 16);
+        }
       }
     }
 #pragma unroll
@@ -269,21 +302,28 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
   }
 }
 
-template <class K>
-__device__ __forceinline__ void grow_wave_any(const Dims& d, const uint16_t* c16, const int32_t* deg, int32_t* rank_of,
-                                              int32_t* mem, int32_t* pos, int32_t* aff) {
-  if (d.E <= 128) grow_wave<K, 1>(d, c16, deg, rank_of, mem, pos, aff);
-  else if (d.E <= 256) grow_wave<K, 2>(d, c16, deg, rank_of, mem, pos, aff);
-  else grow_wave<K, 3>(d, c16, deg, rank_of, mem, pos, aff);
+// grow_wave for U = ceil(E / 128) words per lane (rounded up to an
+// instantiated size); UMAX bounds the sizes instantiated.
+template <class K, int UMAX>
+__device__ __forceinline__ void grow_wave_u(int U, const Dims& d, const uint16_t* c16, const int32_t* deg,
+                                            int32_t* rank_of, int32_t* mem, int32_t* aff) {
+  if (U <= 1) grow_wave<K, 1>(d, c16, deg, rank_of, mem, aff);
+  else if (UMAX <= 2 || U <= 2) grow_wave<K, (UMAX < 2 ? UMAX : 2)>(d, c16, deg, rank_of, mem, aff);
+  else if (UMAX <= 3 || U <= 3) grow_wave<K, (UMAX < 3 ? UMAX : 3)>(d, c16, deg, rank_of, mem, aff);
+  else if (UMAX <= 4 || U <= 4) grow_wave<K, (UMAX < 4 ? UMAX : 4)>(d, c16, deg, rank_of, mem, aff);
+  else if (UMAX <= 6 || U <= 6) grow_wave<K, (UMAX < 6 ? UMAX : 6)>(d, c16, deg, rank_of, mem, aff);
+  else if (UMAX <= 8 || U <= 8) grow_wave<K, (UMAX < 8 ? UMAX : 8)>(d, c16, deg, rank_of, mem, aff);
+  else if (UMAX <= 12 || U <= 12) grow_wave<K, (UMAX < 12 ? UMAX : 12)>(d, c16, deg, rank_of, mem, aff);
+  else grow_wave<K, UMAX>(d, c16, deg, rank_of, mem, aff);
 }
 
-// Greedy growth, one expert per step for E steps; thread t holds the
-// affinities to the rank being filled of experts t, t + 1024, ... (NPL of
+// The whole workgroup, with the int32 counts (any entry size): thread t holds
+// the affinities to the rank being filled of experts t, t + 256, ... (NPL of
 // them).  The step's argmax goes through slot[g % 3]: step g clears the slot
 // of step g + 1, whose last readers (step g - 2) all passed barrier g - 1.
 template <class K, int NPL>
-__device__ __forceinline__ void grow(const Dims& d, const int32_t* __restrict__ C, const int32_t* deg, int32_t* rank_of,
-                                     int32_t* mem, int32_t* pos, int32_t* aff, uint64_t* red) {
+__device__ __forceinline__ void grow_block(const Dims& d, const int32_t* __restrict__ C, const int32_t* deg,
+                                           int32_t* rank_of, int32_t* mem, int32_t* aff, uint64_t* red) {
   const int E = d.E, R = d.R, Er = d.Er;
   const int tid = threadIdx.x, lane = tid & 63;
   constexpr int kShift = 12;  // kIdx - e >= 2048: a candidate's key is never 0
@@ -292,9 +332,13 @@ __device__ __forceinline__ void grow(const Dims& d, const int32_t* __restrict__ 
   if (tid < 3) slot[tid] = 0;
   __syncthreads();
   bool placed[NPL];
-  int32_t a[NPL];
+  int32_t a[NPL], dg[NPL];
 #pragma unroll
-  for (int u = 0; u < NPL; ++u) placed[u] = false;
+  for (int u = 0; u < NPL; ++u) {
+    const int e = tid + kGrowThreads * u;
+    placed[u] = false;
+    dg[u] = deg[min(e, E - 1)];  // unguarded: a guarded load waits alone
+  }
   int g = 0;
   for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -303,9 +347,9 @@ __device__ __forceinline__ void grow(const Dims& d, const int32_t* __restrict__ 
       K best = 0;
 #pragma unroll
       for (int u = 0; u < NPL; ++u) {
-        const int e = tid + kPlaceThreads * u;
+        const int e = tid + kGrowThreads * u;
         if (e < E && !placed[u]) {
-          const int32_t sc = m == 0 ? deg[e] : max(a[u], 0);
+          const int32_t sc = m == 0 ? dg[u] : max(a[u], 0);
           const K kk = ((K)sc << kShift) | (K)(kIdx - e);
           best = kk > best ? kk : best;
         }
@@ -314,163 +358,238 @@ __device__ __forceinline__ void grow(const Dims& d, const int32_t* __restrict__ 
       if (lane == 0 && best != 0) atomicMax(&slot[g % 3], best);
       if (tid == 0) slot[(g + 1) % 3] = 0;
       __syncthreads();
-      const int pick = (int)(kIdx - (slot[g % 3] & kIdx));
+      const int pick = min((int)(kIdx - (slot[g % 3] & kIdx)), E - 1);  // below E for any live expert
 #pragma unroll
       for (int u = 0; u < NPL; ++u)
-        if (tid + kPlaceThreads * u == pick) placed[u] = true;
+        if (tid + kGrowThreads * u == pick) placed[u] = true;
       if (tid == 0) {
         rank_of[pick] = r;
         mem[r * Er + m] = pick;
-        pos[pick] = r * Er + m;
       }
       const int32_t* row = C + (int64_t)pick * E;  // C[pick][e] = C[e][pick]
 #pragma unroll
       for (int u = 0; u < NPL; ++u) {
-        const int e = tid + kPlaceThreads * u;
+        const int e = tid + kGrowThreads * u;
         if (e < E) a[u] += row[e];
       }
     }
 #pragma unroll
     for (int u = 0; u < NPL; ++u) {
-      const int e = tid + kPlaceThreads * u;
+      const int e = tid + kGrowThreads * u;
       if (e < E) aff[(int64_t)r * E + e] = a[u];
     }
   }
 }
 
-template <int NPL, bool AFF_LDS, bool KEY_LDS, bool C_LDS>
-__global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds ly, PlaceArgs pa) {
-  extern __shared__ __align__(16) char smem_place[];
-  int32_t* rank_of = reinterpret_cast<int32_t*>(smem_place + ly.rank_of);
-  int32_t* mem = reinterpret_cast<int32_t*>(smem_place + ly.mem);  // [R][Er] experts of each rank
-  int32_t* pos = reinterpret_cast<int32_t*>(smem_place + ly.pos);  // slot of each expert in mem
-  int32_t* deg = reinterpret_cast<int32_t*>(smem_place + ly.deg);
-  int32_t* own = reinterpret_cast<int32_t*>(smem_place + ly.own);
-  int32_t* col = reinterpret_cast<int32_t*>(smem_place + ly.col) + (threadIdx.x >> 6) * d.R;
-  uint64_t* red = reinterpret_cast<uint64_t*>(smem_place + ly.red);
-  int32_t* aff;
-  uint64_t* key;
-  if constexpr (AFF_LDS) aff = reinterpret_cast<int32_t*>(smem_place + ly.aff);
-  else aff = pa.aff_ws;
-  if constexpr (KEY_LDS) key = reinterpret_cast<uint64_t*>(smem_place + ly.key);
-  else key = pa.key_ws;
-  const int E = d.E, R = d.R, Er = d.Er;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t* __restrict__ C = pa.C;
-
-  // Degrees (column sums, equal to the row sums of a symmetric matrix) and
-  // input checks: zero diagonal, no negative count, sums below 2^31
-  // (symmetry itself is the caller's contract).  Every thread reads: with E a
-  // multiple of 4 and C 16-byte aligned, thread t takes the 16-byte column
-  // group t mod (E/4) of the rows congruent to t / (E/4), otherwise one column
-  // of the rows congruent to t / E (up to E = 512) or whole columns, and adds
-  // its partial sums into 64-bit totals kept in the member and slot tables'
-  // space (unused until the growth).
-  uint16_t* c16 = reinterpret_cast<uint16_t*>(smem_place + ly.c16);
-  int64_t* deg64 = reinterpret_cast<int64_t*>(smem_place + ly.mem);  // spans mem and pos
-  const int Es = c16_stride(E);
-  for (int e = tid; e < E; e += kPlaceThreads) deg64[e] = 0;
-  __syncthreads();
-  uint32_t my_max_entry = 0;  // a negative count reads as a large one here
-  bool bad = false;
-  auto add_deg = [&](int e, int64_t v) {
-    atomicAdd(reinterpret_cast<unsigned long long*>(&deg64[e]), (unsigned long long)v);
-  };
-  if (E % 4 == 0 && ((uintptr_t)C & 15) == 0) {
-    const int Q = E / 4, G = kPlaceThreads / Q;  // G >= 2: E <= 2048
-    if (tid < G * Q) {
-      const int c4 = tid % Q, g = tid / Q, e0 = 4 * c4;
-      const int4* C4 = reinterpret_cast<const int4*>(C);
-      int64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-#pragma unroll 8
-      for (int x = g; x < E; x += G) {
-        const int4 v = C4[(int64_t)x * Q + c4];
-        bad |= v.x < 0 || v.y < 0 || v.z < 0 || v.w < 0;
-        if (x >= e0 && x < e0 + 4) bad |= (x == e0 ? v.x : x == e0 + 1 ? v.y : x == e0 + 2 ? v.z : v.w) != 0;
-        s0 += v.x;
-        s1 += v.y;
-        s2 += v.z;
-        s3 += v.w;
-        if constexpr (C_LDS) {
-          my_max_entry = max(my_max_entry, max(max((uint32_t)v.x, (uint32_t)v.y), max((uint32_t)v.z, (uint32_t)v.w)));
-          uint2 h;  // used only when every entry fits; Es = E here, so 8-byte aligned
-          h.x = ((uint32_t)v.x & 0xffffu) | ((uint32_t)v.y << 16);
-          h.y = ((uint32_t)v.z & 0xffffu) | ((uint32_t)v.w << 16);
-          *reinterpret_cast<uint2*>(c16 + x * Es + e0) = h;
-        }
-      }
-      add_deg(e0, s0);
-      add_deg(e0 + 1, s1);
-      add_deg(e0 + 2, s2);
-      add_deg(e0 + 3, s3);
-    }
-  } else {
-    const int G = E <= kPlaceThreads / 2 ? kPlaceThreads / E : 1;
-    for (int t = tid; t < G * E; t += kPlaceThreads) {
-      const int e = t % E, g = t / E;
-      int64_t s = 0;
-#pragma unroll 8
-      for (int x = g; x < E; x += G) {
-        const int32_t v = C[(int64_t)x * E + e];
-        bad |= v < 0 || (x == e && v != 0);
-        s += v;
-        if constexpr (C_LDS) {
-          my_max_entry = max(my_max_entry, (uint32_t)v);
-          c16[x * Es + e] = (uint16_t)v;  // used only when every entry fits
-        }
-      }
-      add_deg(e, s);
-    }
+// One workgroup of 256.  Reads the prep results; with every count within 16
+// bits the first wave grows alone (from an LDS copy of the 16-bit rows when
+// C_LDS, else from the copy in global memory), otherwise the workgroup does.
+// Also clears the rank-pair keys for the pair pass and writes own.
+template <bool C_LDS, int NPL>
+__global__ __launch_bounds__(kGrowThreads) void place_grow_kernel(Dims d, const int32_t* __restrict__ C,
+                                                                  PlaceState s) {
+  extern __shared__ __align__(16) char smem_grow[];
+  uint64_t* red = reinterpret_cast<uint64_t*>(smem_grow);  // kGrowWaves + 1 entries
+  const int E = d.E, R = d.R;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  uint32_t mx = 0, md = 0;
+  for (int e = tid; e < E; e += kGrowThreads) {
+    mx = max(mx, (uint32_t)s.rowmax[e]);
+    md = max(md, (uint32_t)s.deg[e]);
   }
-  if (bad) atomicOr(pa.status, MOE_STATUS_BAD_PAIRS);
-  bool use_c16 = false;
-  if constexpr (C_LDS) use_c16 = block_max((uint64_t)my_max_entry, red) <= 0xffffu;
-  else __syncthreads();
-  int64_t my_max_deg = 0;
-  for (int e = tid; e < E; e += kPlaceThreads) {
-    const int64_t s = deg64[e];
-    if (s > INT32_MAX) atomicOr(pa.status, MOE_STATUS_BAD_PAIRS);
-    const int32_t dg = (int32_t)(s < 0 ? 0 : s > INT32_MAX ? INT32_MAX : s);
-    deg[e] = dg;
-    my_max_deg = max(my_max_deg, (int64_t)dg);
-  }
-  const uint64_t max_deg = block_max((uint64_t)my_max_deg, red);  // also publishes deg[]; deg64 is free after
-
-  // Greedy growth.  Scores are sums of counts, so never above the largest
-  // degree: when that is below 2^20 a 32-bit key (score, then 4095 - e) suffices.
-  // With the LDS copy of C the first wave grows alone; as the refinement
-  // reuses that LDS space, aff goes to the workspace first and into LDS after.
-  if (use_c16) {
-    if (wave == 0) {
-      if (max_deg < (1u << 20)) grow_wave_any<uint32_t>(d, c16, deg, rank_of, mem, pos, pa.aff_ws);
-      else grow_wave_any<uint64_t>(d, c16, deg, rank_of, mem, pos, pa.aff_ws);
+  for (int64_t q = tid; q < (int64_t)R * R; q += kGrowThreads) s.key[q] = 0;
+  const bool fit16 = block_max<kGrowWaves>(mx, red) <= 0xffffu;
+  const bool key32 = block_max<kGrowWaves>(md, red) < (1u << 20);  // scores never exceed the largest degree
+  const int U = (E + 127) / 128;
+  if (fit16) {
+    const uint16_t* c16 = s.c16;
+    if constexpr (C_LDS) {
+      // The 16-bit rows into LDS, sixteen 16-byte loads in flight per thread.
+      uint16_t* c16l = reinterpret_cast<uint16_t*>(smem_grow + kGrowRedBytes);
+      const int nvec = (int)((size_t)E * c16_stride(E) * 2 / 16) + 1;  // within the pad
+      const uint4* src = reinterpret_cast<const uint4*>(s.c16);
+      uint4* dst = reinterpret_cast<uint4*>(c16l);
+      for (int q0 = tid; q0 < nvec; q0 += 16 * kGrowThreads) {
+        uint4 t[16];
+#pragma unroll
+        for (int b = 0; b < 16; ++b) t[b] = q0 + b * kGrowThreads < nvec ? src[q0 + b * kGrowThreads] : uint4{};
+#pragma unroll
+        for (int b = 0; b < 16; ++b)
+          if (q0 + b * kGrowThreads < nvec) dst[q0 + b * kGrowThreads] = t[b];
+      }
+      c16 = c16l;
+    } else {
+      warm_l2<kGrowThreads>(s.c16, c16_count(E) * sizeof(uint16_t), reinterpret_cast<uint32_t*>(red + kGrowWaves + 1));
     }
     __syncthreads();
-    if constexpr (AFF_LDS)
-      for (int q = tid; q < R * E; q += kPlaceThreads) aff[q] = pa.aff_ws[q];
-  } else if (max_deg < (1u << 20)) {
-    grow<uint32_t, NPL>(d, C, deg, rank_of, mem, pos, aff, red);
+    // An LDS copy holds at most 282 rows: three words per lane.
+    constexpr int UMAX = C_LDS ? 3 : kMaxU;
+    if (wave == 0) {
+      if (key32) grow_wave_u<uint32_t, UMAX>(U, d, c16, s.deg, s.rank_of, s.mem, s.aff);
+      else grow_wave_u<uint64_t, UMAX>(U, d, c16, s.deg, s.rank_of, s.mem, s.aff);
+    }
+  } else if (key32) {
+    grow_block<uint32_t, NPL>(d, C, s.deg, s.rank_of, s.mem, s.aff, red);
   } else {
-    grow<uint64_t, NPL>(d, C, deg, rank_of, mem, pos, aff, red);
+    grow_block<uint64_t, NPL>(d, C, s.deg, s.rank_of, s.mem, s.aff, red);
   }
-  for (int64_t q = tid; q < (int64_t)R * R; q += kPlaceThreads) key[q] = 0;
   __syncthreads();
-  for (int e = tid; e < E; e += kPlaceThreads) own[e] = aff[(int64_t)rank_of[e] * E + e];
-  __syncthreads();
+  for (int e = tid; e < E; e += kGrowThreads) s.own[e] = s.aff[(int64_t)s.rank_of[e] * E + e];
+}
 
-  // Best swap of every rank pair.
-  eval_rows<true, KEY_LDS>(d, C, aff, own, rank_of, mem, key, col, 0, 0);
+// ---------------------------------------------------------------------------
+// pass: one wave per expert x, the keys of its pairs (x, y > x) with y on
+// another rank; each wave folds them per rank ry in LDS (atomic max), then
+// adds one device atomic max per rank into key[min(rx, ry)][max(rx, ry)].
+// rank_of and own are staged in LDS by the workgroup.
+__global__ __launch_bounds__(64 * kPassWaves) void place_pass_kernel(Dims d, const int32_t* __restrict__ C,
+                                                                     PlaceState s) {
+  extern __shared__ __align__(16) char smem_pass[];
+  const int E = d.E, R = d.R;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t* kb = reinterpret_cast<uint64_t*>(smem_pass) + (size_t)wave * R;
+  int32_t* col = reinterpret_cast<int32_t*>(smem_pass + sizeof(uint64_t) * kPassWaves * R) + (size_t)wave * R;
+  int32_t* rk = reinterpret_cast<int32_t*>(smem_pass + (sizeof(uint64_t) + sizeof(int32_t)) * kPassWaves * R);
+  int32_t* ow = rk + E;
+  for (int e = threadIdx.x; e < E; e += 64 * kPassWaves) {
+    rk[e] = s.rank_of[e];
+    ow[e] = s.own[e];
+  }
   __syncthreads();
+  const int x = blockIdx.x * kPassWaves + wave;
+  if (x >= E) return;  // no barrier below
+  const int rx = rk[x];
+  const int64_t ox = ow[x];
+  for (int r = lane; r < R; r += 64) {
+    col[r] = s.aff[(int64_t)r * E + x];
+    kb[r] = 0;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const int32_t* crow = C + (int64_t)x * E;
+  const int32_t* arow = s.aff + (int64_t)rx * E;
+  constexpr int kB = 8;  // entries per lane with their loads in flight together (unguarded, clamped)
+  for (int y0 = x + 1 + lane; y0 < E; y0 += 64 * kB) {
+    int32_t av[kB], cv[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int y = min(y0 + 64 * b, E - 1);
+      av[b] = arow[y];
+      cv[b] = crow[y];
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int y = y0 + 64 * b;
+      if (y >= E) break;
+      const int ry = rk[y];
+      if (ry == rx) continue;
+      const int64_t g = (int64_t)col[ry] - ox + av[b] - ow[y] - 2 * (int64_t)cv[b];
+      atomicMax(&kb[ry], swap_key(g, x, y, E));
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  for (int r = lane; r < R; r += 64) {
+    const uint64_t v = kb[r];
+    if (v != 0) atomicMax(reinterpret_cast<unsigned long long*>(&s.key[min(rx, r) * R + max(rx, r)]),
+                          (unsigned long long)v);
+  }
+}
 
-  const int cap = pa.max_swaps < 0 ? 4096 : pa.max_swaps;
+// ---------------------------------------------------------------------------
+// swap: the refinement, one workgroup of 1024.
+
+struct SwapLds {
+  size_t rank_of, mem, own, red, col, aff, key, total;
+  bool aff_in_lds, key_in_lds;
+};
+
+SwapLds swap_lds(const Dims& d) {
+  SwapLds l;
+  size_t o = 0;
+  auto take = [&](size_t b) { const size_t at = o; o += (b + 15) / 16 * 16; return at; };
+  l.rank_of = take(sizeof(int32_t) * d.E);
+  l.mem = take(sizeof(int32_t) * d.E);
+  l.own = take(sizeof(int32_t) * d.E);
+  l.red = take(sizeof(uint64_t) * (kPlaceWaves + 1));
+  l.col = take(sizeof(int32_t) * kPlaceWaves * (size_t)d.R);
+  const size_t aff_b = sizeof(int32_t) * (size_t)d.R * d.E;
+  const size_t key_b = sizeof(uint64_t) * (size_t)d.R * (d.R + 1);
+  l.aff_in_lds = aff_b <= kPlaceAffLds;
+  l.key_in_lds = key_b <= kPlaceKeyLds;
+  l.aff = l.aff_in_lds ? take(aff_b) : 0;
+  l.key = l.key_in_lds ? take(key_b) : 0;
+  l.total = o;
+  return l;
+}
+
+// Rank-pair swap keys live in LDS (ds atomics) or in global memory (device
+// atomics at L2; reads bypass the L1).
+template <bool LDS>
+__device__ __forceinline__ uint64_t key_load(const uint64_t* p) {
+  if constexpr (LDS) return *p;
+  else return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Keys of the pairs (x, y) with x on rank ra or rb and y on another rank than
+// x, folded into key[min(rx, ry) * ks + max(rx, ry)] by atomic max.  One wave per
+// x: the column aff[*][x] goes to the wave's LDS buffer col; the C row and
+// the aff[rx] row are read along y (coalesced), eight entries per lane at a
+// time with all their loads issued before the first is used (unguarded, at
+// clamped indices: a guarded load gets a basic block and a wait of its own).
+template <bool C16>
+__device__ __forceinline__ void eval_rows(const Dims& d, const int32_t* __restrict__ C, const uint16_t* __restrict__ c16,
+                                          const int32_t* aff, const int32_t* own, const int32_t* rank_of,
+                                          const int32_t* mem, uint64_t* key, int ks, int32_t* col, int ra, int rb) {
+  const int E = d.E, R = d.R, Er = d.Er, Es = c16_stride(E);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kB = 8;
+  for (int i = wave; i < 2 * Er; i += kPlaceWaves) {
+    const int x = i < Er ? mem[ra * Er + i] : mem[rb * Er + i - Er];
+    const int rx = rank_of[x];
+    const int64_t ox = own[x];
+    for (int r = lane; r < R; r += 64) col[r] = aff[(int64_t)r * E + x];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const int32_t* crow = C + (int64_t)x * E;
+    const uint16_t* hrow = c16 + (int64_t)x * Es;
+    const int32_t* arow = aff + (int64_t)rx * E;
+    for (int y0 = lane; y0 < E; y0 += 64 * kB) {
+      int32_t av[kB], cv[kB];
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const int y = min(y0 + 64 * b, E - 1);
+        av[b] = arow[y];
+        cv[b] = C16 ? (int32_t)hrow[y] : crow[y];
+      }
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const int y = y0 + 64 * b;
+        if (y >= E) break;
+        const int ry = rank_of[y];
+        if (ry == rx) continue;
+        const int64_t g = (int64_t)col[ry] - ox + av[b] - own[y] - 2 * (int64_t)cv[b];
+        atomicMax(&key[min(rx, ry) * ks + max(rx, ry)], swap_key(g, x, y, E));
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // col is rewritten for the next x
+  }
+}
+
+// The pair swaps, at most max_swaps (< 0: 4096) while the best gain is
+// positive; returns their number.  C16: the counts are read from the 16-bit rows.
+template <bool C16, bool KEY_LDS>
+__device__ __forceinline__ int swap_loop(const Dims& d, const int32_t* __restrict__ C, const uint16_t* __restrict__ c16,
+                                         int32_t max_swaps, int32_t* aff, int32_t* own, int32_t* rank_of, int32_t* mem,
+                                         uint64_t* key, int ks, int32_t* col, uint64_t* red) {
+  const int E = d.E, R = d.R, Er = d.Er, Es = c16_stride(E);
+  const int tid = threadIdx.x;
+  const int cap = max_swaps < 0 ? 4096 : max_swaps;
   int swaps = 0;
   for (;;) {
     uint64_t best = 0;
-    for (int q = tid; q < R * R; q += kPlaceThreads) {
+    for (int q = tid; q < R * ks; q += kPlaceThreads) {
       const uint64_t v = key_load<KEY_LDS>(&key[q]);
       best = v > best ? v : best;
     }
-    best = block_max(best, red);
+    best = block_max<kPlaceWaves>(best, red);
     const int64_t gain = (int64_t)(best >> kPairBits) - (int64_t)kGainBias;
     if (best == 0 || gain <= 0 || swaps >= cap) break;
     const int64_t pair = (int64_t)(kPairMask - (best & kPairMask));
@@ -478,31 +597,80 @@ __global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds l
     const int ra = rank_of[xa], rb = rank_of[xb];
     // aff of ranks ra and rb; clear the keys of every rank pair with ra or rb.
     for (int x = tid; x < E; x += kPlaceThreads) {
-      const int32_t ca = C[(int64_t)xa * E + x], cb = C[(int64_t)xb * E + x];
+      const int32_t ca = C16 ? (int32_t)c16[(int64_t)xa * Es + x] : C[(int64_t)xa * E + x];
+      const int32_t cb = C16 ? (int32_t)c16[(int64_t)xb * Es + x] : C[(int64_t)xb * E + x];
       aff[(int64_t)ra * E + x] += cb - ca;
       aff[(int64_t)rb * E + x] += ca - cb;
     }
     for (int q = tid; q < 2 * R; q += kPlaceThreads) {
       const int c = q < R ? ra : rb, o = q < R ? q : q - R;
-      if (o != c) key[min(c, o) * R + max(c, o)] = 0;
+      if (o != c) key[min(c, o) * ks + max(c, o)] = 0;
     }
     __syncthreads();  // every thread has read rank_of[xa], rank_of[xb]
     // The swap: each of the 2*Er slots of ranks ra and rb is rewritten by one
-    // thread (xa and xb trade places), with its expert's rank, slot and own.
+    // thread (xa and xb trade places), with its expert's rank and own.
     for (int q = tid; q < 2 * Er; q += kPlaceThreads) {
       const int r = q < Er ? ra : rb, slot = r * Er + (q < Er ? q : q - Er);
       int e = mem[slot];
       e = e == xa ? xb : e == xb ? xa : e;
       mem[slot] = e;
       rank_of[e] = r;
-      pos[e] = slot;
       own[e] = aff[(int64_t)r * E + e];
     }
     __syncthreads();
-    eval_rows<false, KEY_LDS>(d, C, aff, own, rank_of, mem, key, col, ra, rb);
+    eval_rows<C16>(d, C, c16, aff, own, rank_of, mem, key, ks, col, ra, rb);
     __syncthreads();
     ++swaps;
   }
+
+  return swaps;
+}
+
+template <bool AFF_LDS, bool KEY_LDS>
+__global__ __launch_bounds__(kPlaceThreads) void place_swap_kernel(Dims d, SwapLds ly, const int32_t* __restrict__ C,
+                                                                   int32_t max_swaps, PlaceState s, moe_place_out out) {
+  extern __shared__ __align__(16) char smem_swap[];
+  int32_t* rank_of = reinterpret_cast<int32_t*>(smem_swap + ly.rank_of);
+  int32_t* mem = reinterpret_cast<int32_t*>(smem_swap + ly.mem);  // [R][Er] experts of each rank
+  int32_t* own = reinterpret_cast<int32_t*>(smem_swap + ly.own);
+  int32_t* col = reinterpret_cast<int32_t*>(smem_swap + ly.col) + (threadIdx.x >> 6) * d.R;
+  uint64_t* red = reinterpret_cast<uint64_t*>(smem_swap + ly.red);
+  int32_t* aff;
+  uint64_t* key;
+  const int E = d.E, R = d.R, Er = d.Er;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (AFF_LDS) {
+    aff = reinterpret_cast<int32_t*>(smem_swap + ly.aff);
+    for (int64_t q = tid; q < (int64_t)R * E; q += kPlaceThreads) aff[q] = s.aff[q];
+  } else {
+    aff = s.aff;
+  }
+  // In LDS the key table's rows are R + 1 words apart: the entries
+  // key[r][rx] of one column then fall in different banks (with R words
+  // apart every lane's atomic on a rank below rx hit one bank).
+  const int ks = KEY_LDS ? R + 1 : R;
+  if constexpr (KEY_LDS) {
+    key = reinterpret_cast<uint64_t*>(smem_swap + ly.key);
+    for (int q = tid; q < R * ks; q += kPlaceThreads) {
+      const int r = q / ks, c = q - r * ks;
+      key[q] = c < R ? s.key[r * R + c] : 0;
+    }
+  } else {
+    key = s.key;
+  }
+  for (int e = tid; e < E; e += kPlaceThreads) {
+    rank_of[e] = s.rank_of[e];
+    mem[e] = s.mem[e];
+    own[e] = s.own[e];
+  }
+  __syncthreads();
+
+  // The counts as 16-bit rows when they fit (half the bytes).
+  uint32_t mx = 0;
+  for (int e = tid; e < E; e += kPlaceThreads) mx = max(mx, (uint32_t)s.rowmax[e]);
+  const bool fit16 = block_max<kPlaceWaves>(mx, red) <= 0xffffu;
+  const int swaps = fit16 ? swap_loop<true, KEY_LDS>(d, C, s.c16, max_swaps, aff, own, rank_of, mem, key, ks, col, red)
+                          : swap_loop<false, KEY_LDS>(d, C, s.c16, max_swaps, aff, own, rank_of, mem, key, ks, col, red);
 
   // Outputs: ranks, the experts of each rank in ascending order, the kept weight.
   int64_t w = 0;
@@ -510,54 +678,84 @@ __global__ __launch_bounds__(kPlaceThreads) void place_kernel(Dims d, PlaceLds l
     const int r = rank_of[e];
     int before = 0;
     for (int i = 0; i < Er; ++i) before += mem[r * Er + i] < e;
-    pa.expert_rank[e] = r;
-    pa.rank_experts[r * Er + before] = e;
+    out.expert_rank[e] = r;
+    out.rank_experts[r * Er + before] = e;
     w += own[e];
   }
   w = wave_sum(w);
-  __syncthreads();
   if (lane == 0) reinterpret_cast<int64_t*>(red)[wave] = w;
   __syncthreads();
   if (tid == 0) {
-    int64_t s = 0;
-    for (int i = 0; i < kPlaceWaves; ++i) s += reinterpret_cast<int64_t*>(red)[i];
-    *pa.intra = s / 2;  // each pair counted from both sides
-    *pa.n_swaps = swaps;
+    int64_t t = 0;
+    for (int i = 0; i < kPlaceWaves; ++i) t += reinterpret_cast<int64_t*>(red)[i];
+    *out.intra = t / 2;  // each pair counted from both sides
+    *out.n_swaps = swaps;
   }
 }
 
-template <int NPL, bool AFF_LDS, bool KEY_LDS, bool C_LDS>
-hipError_t launch_place_n(const Dims& d, const PlaceLds& ly, const PlaceArgs& pa, hipStream_t st) {
-  auto kern = place_kernel<NPL, AFF_LDS, KEY_LDS, C_LDS>;
-  if (ly.total > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ly.total);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kern, dim3(1), dim3(kPlaceThreads), ly.total, st, d, ly, pa);
+// ---------------------------------------------------------------------------
+// Launch shapes.
+
+size_t grow_c16_lds_bytes(const Dims& d) { return c16_count(d.E) * sizeof(uint16_t); }
+bool grow_c_in_lds(const Dims& d) { return kGrowRedBytes + grow_c16_lds_bytes(d) <= kPlaceLdsBudget; }
+size_t grow_lds_bytes(const Dims& d) { return kGrowRedBytes + (grow_c_in_lds(d) ? grow_c16_lds_bytes(d) : 0); }
+size_t pass_lds_bytes(const Dims& d) {
+  return (sizeof(uint64_t) + sizeof(int32_t)) * kPassWaves * (size_t)d.R + 2 * sizeof(int32_t) * (size_t)d.E;
+}
+
+// Dynamic LDS above 64 KiB must be allowed per kernel.
+hipError_t allow_lds(const void* kern, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <bool C_LDS, int NPL>
+hipError_t launch_grow(const Dims& d, const int32_t* C, const PlaceState& s, hipStream_t st) {
+  auto kern = place_grow_kernel<C_LDS, NPL>;
+  const size_t lds = grow_lds_bytes(d);
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern), lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(1), dim3(kGrowThreads), lds, st, d, C, s);
   return hipGetLastError();
 }
 
-template <int NPL, bool C_LDS>
-hipError_t launch_place_lds(const Dims& d, const PlaceLds& ly, const PlaceArgs& pa, hipStream_t st) {
-  if (ly.aff_in_lds && ly.key_in_lds) return launch_place_n<NPL, true, true, C_LDS>(d, ly, pa, st);
-  if (ly.aff_in_lds) return launch_place_n<NPL, true, false, C_LDS>(d, ly, pa, st);
-  if (ly.key_in_lds) return launch_place_n<NPL, false, true, C_LDS>(d, ly, pa, st);
-  return launch_place_n<NPL, false, false, C_LDS>(d, ly, pa, st);
+template <bool AFF_LDS, bool KEY_LDS>
+hipError_t launch_swap(const Dims& d, const SwapLds& ly, const int32_t* C, int32_t max_swaps, const PlaceState& s,
+                       const moe_place_out& out, hipStream_t st) {
+  auto kern = place_swap_kernel<AFF_LDS, KEY_LDS>;
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern), ly.total);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(1), dim3(kPlaceThreads), ly.total, st, d, ly, C, max_swaps, s, out);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-size_t place_lds_bytes(const Dims& d) { return place_lds(d).total; }
+size_t place_c16_elems(const Dims& d) { return c16_count(d.E); }
+
+size_t place_lds_bytes(const Dims& d) {
+  return std::max(std::max(grow_lds_bytes(d), pass_lds_bytes(d)), swap_lds(d).total);
+}
 
 hipError_t launch_place(const Dims& d, const int32_t* cooc, int32_t max_swaps, const moe_place_out& out,
                         const Workspace& ws, hipStream_t st) {
-  const PlaceLds ly = place_lds(d);
-  const PlaceArgs pa{cooc, max_swaps, out.expert_rank, out.rank_experts, out.intra, out.n_swaps,
-                     ws.place_aff, ws.place_key, ws.status};
-  if (ly.c_in_lds) return launch_place_lds<1, true>(d, ly, pa, st);  // E <= 384 here
-  if (d.E <= kPlaceThreads) return launch_place_lds<1, false>(d, ly, pa, st);
-  return launch_place_lds<2, false>(d, ly, pa, st);
+  const PlaceState s = place_state(d, ws);
+  const unsigned pass_grid = (unsigned)((d.E + kPassWaves - 1) / kPassWaves);
+  hipLaunchKernelGGL(place_prep_kernel, dim3(pass_grid), dim3(64 * kPassWaves), 0, st, d, cooc, s, ws.status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (grow_c_in_lds(d)) e = launch_grow<true, 2>(d, cooc, s, st);  // E <= 282 here
+  else if (d.E <= 2 * kGrowThreads) e = launch_grow<false, 2>(d, cooc, s, st);
+  else if (d.E <= 4 * kGrowThreads) e = launch_grow<false, 4>(d, cooc, s, st);
+  else e = launch_grow<false, 8>(d, cooc, s, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(place_pass_kernel, dim3(pass_grid), dim3(64 * kPassWaves), pass_lds_bytes(d), st, d, cooc, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const SwapLds ly = swap_lds(d);
+  if (ly.aff_in_lds && ly.key_in_lds) return launch_swap<true, true>(d, ly, cooc, max_swaps, s, out, st);
+  if (ly.aff_in_lds) return launch_swap<true, false>(d, ly, cooc, max_swaps, s, out, st);
+  if (ly.key_in_lds) return launch_swap<false, true>(d, ly, cooc, max_swaps, s, out, st);
+  return launch_swap<false, false>(d, ly, cooc, max_swaps, s, out, st);
 }
 
 }  // namespace moe
