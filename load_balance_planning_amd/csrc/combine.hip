@@ -11,7 +11,9 @@
 // k row positions into LDS; every thread then owns 32 columns (four 16-byte
 // vectors) and streams the k rows through them, eight rows' loads in flight.
 // HBM traffic is k rows read and one written per token -- the mirror of the
-// gather.
+// gather.  The expert rows are read once, with non-temporal loads (measured
+// on MI355X: DeepSeek-V3-shaped layer 798 -> 777 us, Kimi-K2-shaped 757 ->
+// 712 us).
 #include "internal.h"
 
 namespace moe {
@@ -19,6 +21,7 @@ namespace {
 
 constexpr int kCombThreads = 256;
 constexpr int kRowsInFlight = 8;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -107,7 +110,9 @@ __global__ __launch_bounds__(kCombThreads) void combine_vec_kernel(Dims d, const
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
           const int c = base + threadIdx.x + u * kCombThreads;
-          x[q][u] = c < vpr && pj[q] >= 0 ? row[c] : make_uint4(0, 0, 0, 0);  // a skipped slot adds 0 * 0
+          const v4u y = c < vpr && pj[q] >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(row) + c)
+                                              : v4u{0, 0, 0, 0};  // a skipped slot adds 0 * 0
+          x[q][u] = make_uint4(y.x, y.y, y.z, y.w);
         }
       }
 #pragma unroll
