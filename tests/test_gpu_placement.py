@@ -90,6 +90,17 @@ def test_place_large_counts(mp, lo, hi):
         check_place(gpu_place(mp, E, R, C), oracle.place(c, C), "E=%d R=%d lo=%d" % (E, R, lo))
 
 
+@pytest.mark.parametrize("E,R", [(1024, 16), (2048, 64)])
+def test_place_large_counts_many_experts(mp, E, R):
+    """Counts past 16 bits with many experts: the workgroup growth with four and eight experts
+    per thread, the refinement on the 32-bit counts (swaps capped to keep the oracle quick)."""
+    print("place large E=%d R=%d" % (E, R), flush=True)
+    C = sym(inputs.rng(E + R).integers(30000, 70000, (E, E)))
+    c = oracle.make_cfg(R, E, 1, R, 1, 8, 0)
+    for cap in (0, 6):
+        check_place(gpu_place(mp, E, R, C, cap), oracle.place(c, C, cap), "E=%d R=%d cap=%d" % (E, R, cap))
+
+
 def test_place_flags_invalid_counts(mp):
     E, R = 32, 4
     C = sym(inputs.rng(3).integers(0, 9, (E, E)))
