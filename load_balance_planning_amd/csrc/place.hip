@@ -117,6 +117,32 @@ __device__ __forceinline__ K wave_max(K v) {
   return x > y ? x : y;
 }
 
+// Maximum over the wave, wave-uniform, for the growth's per-step argmax: the
+// 16-lane row maxima, then row_bcast:15 (rows 1 and 3 take the last lane of
+// the row before) and row_bcast:31 (rows 2 and 3 take lane 31), so lane 63
+// holds the maximum: one lane read instead of four and their scalar maxima.
+// Keys are unsigned, so the 0 that disabled rows read leaves them unchanged.
+__device__ __forceinline__ uint32_t bcast_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+}
+
+__device__ __forceinline__ uint64_t bcast_max(uint64_t v) {
+  auto step = [](uint64_t x, uint32_t lo, uint32_t hi) {
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > x ? o : x;
+  };
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x142, 0xa, 0xf, false),
+           (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x142, 0xa, 0xf, false));
+  return step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x143, 0xc, 0xf, false),
+              (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x143, 0xc, 0xf, false));
+}
+
+template <class K>
+__device__ __forceinline__ K wave_max63(K v) {
+  return lane_read(bcast_max(row_max(v)), 63);
+}
+
 __device__ __forceinline__ int64_t wave_sum(int64_t v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -226,9 +252,8 @@ __global__ __launch_bounds__(64 * kPassWaves) void place_prep_kernel(Dims d, con
 // read as one 32-bit word per u and step with no bounds branch -- lanes past E
 // read the next row (or the tail pad) into experts that are never alive.  A
 // key is (score, then 4095 - e), masked to 0 once e is placed; the argmax is
-// wave-uniform (DPP and lane reads), so a step needs no atomic and no barrier.
-// The picks are kept one per lane and written out every 64 steps and at the
-// end of each rank.  c16 points to LDS or to global memory.
+// wave-uniform (DPP and one lane read), so a step needs no atomic and no
+// barrier; lane 0 records each pick.  c16 points to LDS or to global memory.
 template <class K, int U>
 __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, const int32_t* deg, int32_t* rank_of,
                                           int32_t* mem, int32_t* aff) {
@@ -247,7 +272,6 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
     dg[j] = deg[min(e, E - 1)];  // unguarded: a guarded load waits alone
     a[j] = 0;
   }
-  int32_t pk = 0;  // lane i: the pick of step (m - m % 64 + i) of the current rank
   for (int r = 0; r < R; ++r) {
     for (int m = 0; m < Er; ++m) {
       K best = 0;
@@ -258,7 +282,7 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
 #pragma unroll
         for (int j = 0; j < J; ++j) best = max(best, (((K)(uint32_t)a[j] << kShift) | ik[j]) & (K)(int64_t)live[j]);
       }
-      best = wave_max(best);
+      best = wave_max63(best);
       // A live expert always has a key above 0, so the pick is below E; the
       // clamp only keeps the row read inside the copy whatever the input.
       const int pick = min((int)(kIdx - (best & kIdx)), E - 1);
@@ -266,19 +290,13 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
       uint32_t v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) v[u] = row[64 * u];
-      const int jj = 2 * (pick >> 7) + (pick & 1);
-      const bool mine = lane == ((pick & 127) >> 1);
+      // placed: the one (lane, j) whose id part matches (experts past E never do)
+      const uint32_t ikp = (uint32_t)(kIdx - (K)pick);
 #pragma unroll
-      for (int j = 0; j < J; ++j)
-        if (j == jj && mine) live[j] = 0;
-      const int q = m & 63;
-      if (lane == q) pk = pick;
-      if (q == 63 || m == Er - 1) {
-        const int base = r * Er + m - q;
-        if (lane <= q) {
-          mem[base + lane] = pk;
-          rank_of[pk] = r;
-        }
+      for (int j = 0; j < J; ++j) live[j] = ik[j] == ikp ? 0 : live[j];
+      if (lane == 0) {
+        mem[r * Er + m] = pick;
+        rank_of[pick] = r;
       }
       if (m == 0) {
 #pragma unroll
