@@ -442,8 +442,11 @@ int moe_plan_combine(moe_plan_t h, const float* topk_val, const int32_t* slot_po
  * diagonal, entries >= 0, row sums < 2^31.  A negative entry, a non-zero
  * diagonal or a row sum >= 2^31 sets MOE_STATUS_BAD_PAIRS (the result is
  * then a valid partition but otherwise unspecified); asymmetric input is not
- * detected and gives an unspecified partition.  One workgroup; time grows
- * with E (a sequential greedy step per expert).
+ * detected and gives an unspecified partition.  Four launches: the passes
+ * over all of cooc run on the whole chip, the growth and the refinement in
+ * one workgroup each; time grows with E (a sequential greedy step per
+ * expert).  Uses the handle's workspace, so calls on one handle run in
+ * stream order.
  */
 int moe_plan_place(moe_plan_t h, const int32_t* cooc, int32_t max_swaps, const moe_place_out* out,
                    void* stream);
