@@ -211,7 +211,10 @@ bool one_round(const Dims& d) { return d.H / 8 <= 256; }
 // 771-775 (reading each row twice), four parts 837; Kimi-K2-shaped (k 16):
 // one part 783-790 us, two destination parts 735-740, two column parts 771,
 // two of each 721; Qwen3-shaped (k 8, 256 vectors): one part 118 us, two
-// 127-137.
+// 127-137.  Narrower column parts write shorter pieces of each row and run
+// slower: four column parts (3.5 KiB pieces) 793 us on the DeepSeek-V3 shape
+// and 747 us on the Kimi-K2 one, eight 1 000 and 791 us, four by two
+// destination parts 954 and 784 us (against 777 and 727 us, same box).
 constexpr int kCopyVectorsPerPart = 3584;
 struct CopyParts {
   int split;   // destination parts
