@@ -550,16 +550,17 @@ __device__ __forceinline__ uint64_t key_load(const uint64_t* p) {
 // Keys of the pairs (x, y) with x on rank ra or rb and y on another rank than
 // x, folded into key[min(rx, ry) * ks + max(rx, ry)] by atomic max.  One wave per
 // x: the column aff[*][x] goes to the wave's LDS buffer col; the C row and
-// the aff[rx] row are read along y (coalesced), eight entries per lane at a
-// time with all their loads issued before the first is used (unguarded, at
-// clamped indices: a guarded load gets a basic block and a wait of its own).
-template <bool C16>
+// the aff[rx] row are read along y (coalesced), kB entries per lane at a time:
+// every read of a batch (C, aff, rank, own; then the column entries of those
+// ranks) is issued before its first key is formed and its atomics go out
+// (the loads unguarded, at clamped indices: a guarded load gets a basic block
+// and a wait of its own).
+template <bool C16, int kB>
 __device__ __forceinline__ void eval_rows(const Dims& d, const int32_t* __restrict__ C, const uint16_t* __restrict__ c16,
                                           const int32_t* aff, const int32_t* own, const int32_t* rank_of,
                                           const int32_t* mem, uint64_t* key, int ks, int32_t* col, int ra, int rb) {
   const int E = d.E, R = d.R, Er = d.Er, Es = c16_stride(E);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kB = 8;
   for (int i = wave; i < 2 * Er; i += kPlaceWaves) {
     const int x = i < Er ? mem[ra * Er + i] : mem[rb * Er + i - Er];
     const int rx = rank_of[x];
@@ -570,21 +571,26 @@ __device__ __forceinline__ void eval_rows(const Dims& d, const int32_t* __restri
     const uint16_t* hrow = c16 + (int64_t)x * Es;
     const int32_t* arow = aff + (int64_t)rx * E;
     for (int y0 = lane; y0 < E; y0 += 64 * kB) {
-      int32_t av[kB], cv[kB];
+      // every read of the batch before any atomic: the reads, then the
+      // column entries of the ranks just read, then the keys
+      int32_t av[kB], cv[kB], ryv[kB], owv[kB], cov[kB];
 #pragma unroll
       for (int b = 0; b < kB; ++b) {
         const int y = min(y0 + 64 * b, E - 1);
         av[b] = arow[y];
         cv[b] = C16 ? (int32_t)hrow[y] : crow[y];
+        ryv[b] = rank_of[y];
+        owv[b] = own[y];
       }
 #pragma unroll
+      for (int b = 0; b < kB; ++b) cov[b] = col[ryv[b]];
+#pragma unroll
       for (int b = 0; b < kB; ++b) {
-        const int y = y0 + 64 * b;
-        if (y >= E) break;
-        const int ry = rank_of[y];
-        if (ry == rx) continue;
-        const int64_t g = (int64_t)col[ry] - ox + av[b] - own[y] - 2 * (int64_t)cv[b];
-        atomicMax(&key[min(rx, ry) * ks + max(rx, ry)], swap_key(g, x, y, E));
+        const int y = y0 + 64 * b, ry = ryv[b];
+        if (y < E && ry != rx) {
+          const int64_t g = (int64_t)cov[b] - ox + av[b] - owv[b] - 2 * (int64_t)cv[b];
+          atomicMax(&key[min(rx, ry) * ks + max(rx, ry)], swap_key(g, x, y, E));
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // col is rewritten for the next x
@@ -636,7 +642,10 @@ __device__ __forceinline__ int swap_loop(const Dims& d, const int32_t* __restric
       own[e] = aff[(int64_t)r * E + e];
     }
     __syncthreads();
-    eval_rows<C16>(d, C, c16, aff, own, rank_of, mem, key, ks, col, ra, rb);
+    // entries per lane and batch: E / 64, at most eight (no clamped duplicates when E is small)
+    if (E <= 128) eval_rows<C16, 2>(d, C, c16, aff, own, rank_of, mem, key, ks, col, ra, rb);
+    else if (E <= 256) eval_rows<C16, 4>(d, C, c16, aff, own, rank_of, mem, key, ks, col, ra, rb);
+    else eval_rows<C16, 8>(d, C, c16, aff, own, rank_of, mem, key, ks, col, ra, rb);
     __syncthreads();
     ++swaps;
   }
