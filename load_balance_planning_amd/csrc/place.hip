@@ -329,8 +329,11 @@ __device__ __forceinline__ void grow_wave_u(int U, const Dims& d, const uint16_t
   else if (UMAX <= 2 || U <= 2) grow_wave<K, (UMAX < 2 ? UMAX : 2)>(d, c16, deg, rank_of, mem, aff);
   else if (UMAX <= 3 || U <= 3) grow_wave<K, (UMAX < 3 ? UMAX : 3)>(d, c16, deg, rank_of, mem, aff);
   else if (UMAX <= 4 || U <= 4) grow_wave<K, (UMAX < 4 ? UMAX : 4)>(d, c16, deg, rank_of, mem, aff);
+  else if (UMAX <= 5 || U <= 5) grow_wave<K, (UMAX < 5 ? UMAX : 5)>(d, c16, deg, rank_of, mem, aff);
   else if (UMAX <= 6 || U <= 6) grow_wave<K, (UMAX < 6 ? UMAX : 6)>(d, c16, deg, rank_of, mem, aff);
+  else if (UMAX <= 7 || U <= 7) grow_wave<K, (UMAX < 7 ? UMAX : 7)>(d, c16, deg, rank_of, mem, aff);
   else if (UMAX <= 8 || U <= 8) grow_wave<K, (UMAX < 8 ? UMAX : 8)>(d, c16, deg, rank_of, mem, aff);
+  else if (UMAX <= 10 || U <= 10) grow_wave<K, (UMAX < 10 ? UMAX : 10)>(d, c16, deg, rank_of, mem, aff);
   else if (UMAX <= 12 || U <= 12) grow_wave<K, (UMAX < 12 ? UMAX : 12)>(d, c16, deg, rank_of, mem, aff);
   else grow_wave<K, UMAX>(d, c16, deg, rank_of, mem, aff);
 }
