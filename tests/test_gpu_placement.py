@@ -70,7 +70,7 @@ def test_place_on_each_workload(mp, name):
 @pytest.mark.parametrize("E,R,hi", [(8, 4, 3), (12, 3, 2), (64, 8, 5), (96, 32, 4), (130, 10, 50), (256, 64, 9),
                                     (512, 16, 3), (1024, 128, 6), (2048, 256, 4), (2048, 8, 1000), (40, 40, 9),
                                     (40, 1, 9), (99, 9, 7), (255, 5, 4), (270, 10, 6), (200, 2, 5), (128, 1, 3),
-                                    (384, 12, 5)])
+                                    (384, 12, 5), (1280, 64, 5), (1536, 128, 3)])
 def test_place_random_coselection_with_ties(mp, E, R, hi):
     """Small integer weights: many equal gains and scores, so the tie rules decide."""
     print("place random E=%d R=%d" % (E, R), flush=True)
