@@ -253,7 +253,8 @@ __global__ __launch_bounds__(64 * kPassWaves) void place_prep_kernel(Dims d, con
 // read the next row (or the tail pad) into experts that are never alive.  A
 // key is (score, then 4095 - e), masked to 0 once e is placed; the argmax is
 // wave-uniform (DPP and one lane read), so a step needs no atomic and no
-// barrier; lane 0 records each pick.  c16 points to LDS or to global memory.
+// barrier.  Step g's pick goes into lane g % 64 of a register, stored with
+// its rank every 64 steps.  c16 points to LDS or to global memory.
 template <class K, int U>
 __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, const int32_t* deg, int32_t* rank_of,
                                           int32_t* mem, int32_t* aff) {
@@ -272,8 +273,16 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
     dg[j] = deg[min(e, E - 1)];  // unguarded: a guarded load waits alone
     a[j] = 0;
   }
+  // picks of steps g0 .. g0 + n - 1 in lanes 0 .. n - 1: mem and rank_of
+  auto flush = [&](int held, int g0, int n) {
+    if (lane < n) {
+      mem[g0 + lane] = held;
+      rank_of[held] = (g0 + lane) / Er;
+    }
+  };
+  int held = 0, g = 0;
   for (int r = 0; r < R; ++r) {
-    for (int m = 0; m < Er; ++m) {
+    for (int m = 0; m < Er; ++m, ++g) {
       K best = 0;
       if (m == 0) {
 #pragma unroll
@@ -294,10 +303,8 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
       const uint32_t ikp = (uint32_t)(kIdx - (K)pick);
 #pragma unroll
       for (int j = 0; j < J; ++j) live[j] = ik[j] == ikp ? 0 : live[j];
-      if (lane == 0) {
-        mem[r * Er + m] = pick;
-        rank_of[pick] = r;
-      }
+      held = lane == (g & 63) ? pick : held;
+      if ((g & 63) == 63) flush(held, g - 63, 64);
       if (m == 0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -318,6 +325,7 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
       if (e < E) aff[(int64_t)r * E + e] = a[j];
     }
   }
+  if (g & 63) flush(held, g & ~63, g & 63);
 }
 
 // grow_wave for U = ceil(E / 128) words per lane (rounded up to an
