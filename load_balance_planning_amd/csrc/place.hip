@@ -32,6 +32,7 @@
 //          only the gains of pairs with an expert on ra or rb, so an iteration
 //          re-evaluates 2R-3 rank pairs (about 2*E*E/R expert pairs) instead
 //          of all E*E/2.  aff and the rank-pair keys live in LDS when they fit.
+#include <type_traits>
 #include <algorithm>
 
 #include "internal.h"
@@ -263,8 +264,13 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
   constexpr int J = 2 * U;
   constexpr int kShift = 12;
   constexpr K kIdx = ((K)1 << kShift) - 1;
-  int32_t live[J], dg[J], a[J];  // live: 0 once placed, else -1 (a key mask)
-  uint32_t ik[J];                 // 4095 - e
+  // live: 0 once placed, else -1 (a key mask); with more than eight slots a
+  // vector, so that the slot a step kills is written by a wave-uniform index
+  // in registers
+  typedef int32_t LiveVec __attribute__((ext_vector_type(J <= 16 ? 16 : 32)));
+  std::conditional_t<(J > 8), LiveVec, int32_t[J]> live;
+  int32_t dg[J], a[J];
+  uint32_t ik[J];  // 4095 - e
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = 2 * lane + 128 * (j >> 1) + (j & 1);
@@ -299,10 +305,18 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
       uint32_t v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) v[u] = row[64 * u];
-      // placed: the one (lane, j) whose id part matches (experts past E never do)
-      const uint32_t ikp = (uint32_t)(kIdx - (K)pick);
+      // placed: slot 2 (pick / 128) + pick % 2 of lane (pick / 2) % 64.  The
+      // slot index is wave-uniform: with many slots per lane the one register
+      // is read and written by index (four instructions); with few, every slot
+      // compares its id with the pick's.
+      if constexpr (J > 8) {
+        const int jp = 2 * (pick >> 7) + (pick & 1);
+        live[jp] = lane == ((pick >> 1) & 63) ? 0 : live[jp];
+      } else {
+        const uint32_t ikp = (uint32_t)(kIdx - (K)pick);
 #pragma unroll
-      for (int j = 0; j < J; ++j) live[j] = ik[j] == ikp ? 0 : live[j];
+        for (int j = 0; j < J; ++j) live[j] = ik[j] == ikp ? 0 : live[j];
+      }
       held = lane == (g & 63) ? pick : held;
       if ((g & 63) == 63) flush(held, g - 63, 64);
       if (m == 0) {
