@@ -360,6 +360,99 @@ __device__ __forceinline__ void grow_wave_u(int U, const Dims& d, const uint16_t
   else grow_wave<K, UMAX>(d, c16, deg, rank_of, mem, aff);
 }
 
+// One wave, from the int32 rows of C (L2-resident), when every degree is
+// below 2^19: lane l holds experts l + 64 j (j < J), each as one 32-bit key
+//   live << 31 | score << 12 | (4095 - e),
+// the score (the co-selection with the rank so far, at most the expert's
+// degree) never reaching bit 31.  A step adds each row entry << 12 to its key
+// (one shift-and-add, no mask): a placed expert's cleared live bit keeps it
+// below every live key.  The rank's first step keys the live experts by
+// degree instead.  The placed slot is cleared by its wave-uniform index.
+template <int J>
+__device__ __forceinline__ void grow_wave_c32(const Dims& d, const int32_t* __restrict__ C, const int32_t* deg,
+                                              int32_t* rank_of, int32_t* mem, int32_t* aff) {
+  const int E = d.E, R = d.R, Er = d.Er;
+  const int lane = threadIdx.x & 63;
+  constexpr uint32_t kLive = 0x80000000u, kIdx = 0xfffu;
+  typedef uint32_t KeyVec __attribute__((ext_vector_type(J <= 16 ? 16 : 32)));
+  KeyVec key;
+  uint32_t dk[J];  // deg << 12 | (4095 - e)
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = lane + 64 * j;
+    const uint32_t ik = kIdx - (uint32_t)e;
+    key[j] = (e < E ? kLive : 0u) | ik;
+    dk[j] = ((uint32_t)deg[min(e, E - 1)] << 12) | ik;  // unguarded: a guarded load waits alone
+  }
+  // picks of steps g0 .. g0 + n - 1 in lanes 0 .. n - 1: mem and rank_of
+  auto flush = [&](int held, int g0, int n) {
+    if (lane < n) {
+      mem[g0 + lane] = held;
+      rank_of[held] = (g0 + lane) / Er;
+    }
+  };
+  int held = 0, g = 0;
+  for (int r = 0; r < R; ++r) {
+    for (int m = 0; m < Er; ++m, ++g) {
+      uint32_t best = 0;
+      if (m == 0) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) best = max(best, (key[j] & kLive) | dk[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) best = max(best, (uint32_t)key[j]);
+      }
+      best = wave_max63(best);
+      // A live expert always has a key at or above 2^31 (its degree key above
+      // 0), so the pick is below E; the clamp only keeps the row read inside C.
+      const int pick = min((int)(kIdx - (best & kIdx)), E - 1);
+      const int32_t* row = C + (int64_t)pick * E;
+      uint32_t v[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) v[j] = (uint32_t)row[min(64 * j + lane, E - 1)];
+      const int jp = pick >> 6;
+      key[jp] = lane == (pick & 63) ? key[jp] & ~kLive : key[jp];
+      held = lane == (g & 63) ? pick : held;
+      if ((g & 63) == 63) flush(held, g - 63, 64);
+      if (m == 0) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) key[j] = (key[j] & (kLive | kIdx)) + (v[j] << 12);
+      } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) key[j] += v[j] << 12;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) aff[(int64_t)r * E + e] = (int32_t)((key[j] >> 12) & 0x7ffffu);
+    }
+  }
+  if (g & 63) flush(held, g & ~63, g & 63);
+}
+
+// grow_wave_c32 with J >= ceil(E / 64) slots per lane, from the sizes
+// instantiated for a workgroup of 256 threads holding NPL experts each.
+template <int NPL>
+__device__ __forceinline__ void grow_wave_c32_e(const Dims& d, const int32_t* C, const int32_t* deg,
+                                                int32_t* rank_of, int32_t* mem, int32_t* aff) {
+  const int J = (d.E + 63) / 64;
+  if constexpr (NPL <= 2) {
+    if (J <= 6) grow_wave_c32<6>(d, C, deg, rank_of, mem, aff);
+    else grow_wave_c32<8>(d, C, deg, rank_of, mem, aff);
+  } else if constexpr (NPL <= 4) {
+    if (J <= 10) grow_wave_c32<10>(d, C, deg, rank_of, mem, aff);
+    else if (J <= 12) grow_wave_c32<12>(d, C, deg, rank_of, mem, aff);
+    else if (J <= 14) grow_wave_c32<14>(d, C, deg, rank_of, mem, aff);
+    else grow_wave_c32<16>(d, C, deg, rank_of, mem, aff);
+  } else {
+    if (J <= 20) grow_wave_c32<20>(d, C, deg, rank_of, mem, aff);
+    else if (J <= 24) grow_wave_c32<24>(d, C, deg, rank_of, mem, aff);
+    else if (J <= 28) grow_wave_c32<28>(d, C, deg, rank_of, mem, aff);
+    else grow_wave_c32<32>(d, C, deg, rank_of, mem, aff);
+  }
+}
+
 // The whole workgroup, with the int32 counts (any entry size): thread t holds
 // the affinities to the rank being filled of experts t, t + 256, ... (NPL of
 // them).  The step's argmax goes through slot[g % 3]: step g clears the slot
@@ -442,9 +535,16 @@ __global__ __launch_bounds__(kGrowThreads) void place_grow_kernel(Dims d, const 
   }
   for (int64_t q = tid; q < (int64_t)R * R; q += kGrowThreads) s.key[q] = 0;
   const bool fit16 = block_max<kGrowWaves>(mx, red) <= 0xffffu;
-  const bool key32 = block_max<kGrowWaves>(md, red) < (1u << 20);  // scores never exceed the largest degree
+  const uint32_t mdeg = block_max<kGrowWaves>(md, red);
+  const bool key32 = mdeg < (1u << 20);  // scores never exceed the largest degree
   const int U = (E + 127) / 128;
-  if (fit16) {
+  if (!C_LDS && mdeg < (1u << 19)) {
+    // rows too many for LDS, degrees small enough for the live-bit keys: the
+    // int32 rows, warmed into this CU's L2
+    warm_l2<kGrowThreads>(C, (size_t)E * E * sizeof(int32_t), reinterpret_cast<uint32_t*>(red + kGrowWaves + 1));
+    __syncthreads();
+    if (wave == 0) grow_wave_c32_e<NPL>(d, C, s.deg, s.rank_of, s.mem, s.aff);
+  } else if (fit16) {
     const uint16_t* c16 = s.c16;
     if constexpr (C_LDS) {
       // The 16-bit rows into LDS, sixteen 16-byte loads in flight per thread.

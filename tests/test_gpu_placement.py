@@ -80,6 +80,33 @@ def test_place_random_coselection_with_ties(mp, E, R, hi):
         check_place(gpu_place(mp, E, R, C, cap), oracle.place(c, C, cap), "E=%d R=%d cap=%d" % (E, R, cap))
 
 
+def sparse_large(E, seed, big, per_row):
+    """Small counts plus a few large ones (up to per_row per row, each below big)."""
+    g = inputs.rng(seed)
+    C = g.integers(0, 3, (E, E))
+    for _ in range(E * per_row // 2):
+        a, b = g.integers(0, E, 2)
+        C[a, b] = g.integers(big // 2, big)
+    return sym(C)
+
+
+@pytest.mark.parametrize("case", ["sparse_past_16_bits", "degrees_past_2^19", "ragged_E", "one_slot_per_lane"])
+def test_place_growth_paths_many_experts(mp, case):
+    """More experts than an LDS copy holds: the one-wave growth from the int32 rows (degrees below
+    2^19, also with single counts past 16 bits and E not a multiple of 64), the one from the 16-bit
+    copy (degrees past 2^19, counts within 16 bits), and ranks of three experts."""
+    E, R, C = {
+        "sparse_past_16_bits": lambda: (384, 12, sparse_large(384, 11, 200000, 1)),
+        "degrees_past_2^19": lambda: (512, 16, sym(inputs.rng(12).integers(0, 3000, (512, 512)))),
+        "ragged_E": lambda: (1000, 8, sym(inputs.rng(13).integers(0, 20, (1000, 1000)))),
+        "one_slot_per_lane": lambda: (768, 256, sym(inputs.rng(14).integers(0, 50, (768, 768)))),
+    }[case]()
+    print("place paths %s E=%d R=%d max deg %d max count %d" % (case, E, R, C.sum(1).max(), C.max()), flush=True)
+    c = oracle.make_cfg(R, E, 1, R, 1, 8, 0)
+    for cap in (0, 4):
+        check_place(gpu_place(mp, E, R, C, cap), oracle.place(c, C, cap), "%s cap=%d" % (case, cap))
+
+
 @pytest.mark.parametrize("lo,hi", [(10000, 30000), (60000, 70000), (0, 1 << 20)])
 def test_place_large_counts(mp, lo, hi):
     """Counts near and past 16 bits, degrees past 2^20 (the 64-bit growth keys)."""
