@@ -20,12 +20,16 @@
 // sequential phases run in one workgroup each:
 //   prep   one wave per row: the degree (row sum), the input checks, the row's
 //          largest entry and a 16-bit copy of the row;
-//   grow   one workgroup.  When every count fits 16 bits one wave grows alone
-//          -- each step a wave-uniform argmax (DPP and lane reads, no atomic,
-//          no barrier) and one 16-bit row read, from LDS when the copy fits
-//          there, else from the L2-resident copy; otherwise the whole
-//          workgroup holds the affinities, one LDS atomic max and one barrier
-//          per step.  It leaves the ranks, aff and own[e] = aff[rank(e)][e];
+//   grow   one workgroup.  One wave grows alone -- each step a wave-uniform
+//          argmax (DPP and one lane read, no atomic, no barrier) and one row
+//          read: the 16-bit rows from LDS when every count fits 16 bits and
+//          the copy fits there (E <= 282); else, with every degree below
+//          2^19, the int32 rows of C from L2 with keys that carry a live bit
+//          (one shift-and-add per expert and step); else the 16-bit copy from
+//          L2.  The rest (counts past 16 bits with E <= 282, or with a
+//          degree of 2^19 or more) takes the whole workgroup: affinities in
+//          registers, one LDS atomic max and one barrier per step.  It
+//          leaves the ranks, aff and own[e] = aff[rank(e)][e];
 //   pass   one wave per expert x: the swap keys of its pairs (x, y > x),
 //          folded per rank in LDS, then one device atomic max per rank pair;
 //   swap   one workgroup: the refinement.  A swap between ra and rb changes
