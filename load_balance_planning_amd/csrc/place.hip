@@ -24,9 +24,9 @@
 //          argmax (DPP and one lane read, no atomic, no barrier) and one row
 //          read: the 16-bit rows from LDS when every count fits 16 bits and
 //          the copy fits there (E <= 282); else, with every degree below
-//          2^19, the int32 rows of C from L2 with keys that carry a live bit
-//          (one shift-and-add per expert and step); else the 16-bit copy from
-//          L2.  The rest (counts past 16 bits with E <= 282, or with a
+//          2^19, the int32 rows of C from L2; else the 16-bit copy from L2.
+//          With degrees below 2^19 a key carries a live bit (a step adds the
+//          count << 12, no mask), else a per-slot mask.  The rest (counts past 16 bits with E <= 282, or with a
 //          degree of 2^19 or more) takes the whole workgroup: affinities in
 //          registers, one LDS atomic max and one barrier per step.  It
 //          leaves the ranks, aff and own[e] = aff[rank(e)][e];
@@ -346,6 +346,76 @@ __device__ __forceinline__ void grow_wave(const Dims& d, const uint16_t* c16, co
   if (g & 63) flush(held, g & ~63, g & 63);
 }
 
+// grow_wave with the 32-bit live-bit keys of grow_wave_c32 (every degree below
+// 2^19): a step adds each 16-bit count << 12 to its key with no mask.
+template <int U>
+__device__ __forceinline__ void grow_wave_live(const Dims& d, const uint16_t* c16, const int32_t* deg,
+                                               int32_t* rank_of, int32_t* mem, int32_t* aff) {
+  const int E = d.E, R = d.R, Er = d.Er, Es = c16_stride(E);
+  const int lane = threadIdx.x & 63;
+  constexpr int J = 2 * U;
+  constexpr uint32_t kLive = 0x80000000u, kIdx = 0xfffu;
+  uint32_t key[J], dk[J], ik[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = 2 * lane + 128 * (j >> 1) + (j & 1);
+    ik[j] = kIdx - (uint32_t)e;
+    key[j] = (e < E ? kLive : 0u) | ik[j];
+    dk[j] = ((uint32_t)deg[min(e, E - 1)] << 12) | ik[j];  // unguarded: a guarded load waits alone
+  }
+  // picks of steps g0 .. g0 + n - 1 in lanes 0 .. n - 1: mem and rank_of
+  auto flush = [&](int held, int g0, int n) {
+    if (lane < n) {
+      mem[g0 + lane] = held;
+      rank_of[held] = (g0 + lane) / Er;
+    }
+  };
+  int held = 0, g = 0;
+  for (int r = 0; r < R; ++r) {
+    for (int m = 0; m < Er; ++m, ++g) {
+      uint32_t best = 0;
+      if (m == 0) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) best = max(best, (key[j] & kLive) | dk[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) best = max(best, key[j]);
+      }
+      best = wave_max63(best);
+      // A live expert always has a key at or above 2^31, so the pick is below
+      // E; the clamp only keeps the row read inside the copy whatever the input.
+      const int pick = min((int)(kIdx - (best & kIdx)), E - 1);
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(c16 + pick * Es) + lane;
+      uint32_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = row[64 * u];
+      // placed: the one (lane, j) whose id part matches (experts past E never do)
+      const uint32_t ikp = kIdx - (uint32_t)pick;
+#pragma unroll
+      for (int j = 0; j < J; ++j) key[j] = ik[j] == ikp ? key[j] & ~kLive : key[j];
+      held = lane == (g & 63) ? pick : held;
+      if ((g & 63) == 63) flush(held, g - 63, 64);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t lo = (v[u] & 0xffffu) << 12, hi = (v[u] >> 16) << 12;
+        if (m == 0) {
+          key[2 * u] = (key[2 * u] & (kLive | kIdx)) + lo;
+          key[2 * u + 1] = (key[2 * u + 1] & (kLive | kIdx)) + hi;
+        } else {
+          key[2 * u] += lo;
+          key[2 * u + 1] += hi;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = 2 * lane + 128 * (j >> 1) + (j & 1);
+      if (e < E) aff[(int64_t)r * E + e] = (int32_t)((key[j] >> 12) & 0x7ffffu);
+    }
+  }
+  if (g & 63) flush(held, g & ~63, g & 63);
+}
+
 // grow_wave for U = ceil(E / 128) words per lane (rounded up to an
 // instantiated size); UMAX bounds the sizes instantiated.
 template <class K, int UMAX>
@@ -572,8 +642,15 @@ __global__ __launch_bounds__(kGrowThreads) void place_grow_kernel(Dims d, const 
     // An LDS copy holds at most 282 rows: three words per lane.
     constexpr int UMAX = C_LDS ? 3 : kMaxU;
     if (wave == 0) {
-      if (key32) grow_wave_u<uint32_t, UMAX>(U, d, c16, s.deg, s.rank_of, s.mem, s.aff);
-      else grow_wave_u<uint64_t, UMAX>(U, d, c16, s.deg, s.rank_of, s.mem, s.aff);
+      if (C_LDS && mdeg < (1u << 19)) {
+        if (U <= 1) grow_wave_live<1>(d, c16, s.deg, s.rank_of, s.mem, s.aff);
+        else if (U <= 2) grow_wave_live<2>(d, c16, s.deg, s.rank_of, s.mem, s.aff);
+        else grow_wave_live<3>(d, c16, s.deg, s.rank_of, s.mem, s.aff);
+      } else if (key32) {
+        grow_wave_u<uint32_t, UMAX>(U, d, c16, s.deg, s.rank_of, s.mem, s.aff);
+      } else {
+        grow_wave_u<uint64_t, UMAX>(U, d, c16, s.deg, s.rank_of, s.mem, s.aff);
+      }
     }
   } else if (key32) {
     grow_block<uint32_t, NPL>(d, C, s.deg, s.rank_of, s.mem, s.aff, red);

@@ -90,12 +90,15 @@ def sparse_large(E, seed, big, per_row):
     return sym(C)
 
 
-@pytest.mark.parametrize("case", ["sparse_past_16_bits", "degrees_past_2^19", "ragged_E", "one_slot_per_lane"])
+@pytest.mark.parametrize("case", ["sparse_past_16_bits", "degrees_past_2^19", "ragged_E", "one_slot_per_lane",
+                                  "lds_degrees_past_2^19"])
 def test_place_growth_paths_many_experts(mp, case):
     """More experts than an LDS copy holds: the one-wave growth from the int32 rows (degrees below
     2^19, also with single counts past 16 bits and E not a multiple of 64), the one from the 16-bit
-    copy (degrees past 2^19, counts within 16 bits), and ranks of three experts."""
+    copy (degrees past 2^19, counts within 16 bits), and ranks of three experts; with the rows in
+    LDS, degrees between 2^19 and 2^20 (the masked 32-bit keys)."""
     E, R, C = {
+        "lds_degrees_past_2^19": lambda: (200, 8, sym(inputs.rng(15).integers(3000, 5000, (200, 200)))),
         "sparse_past_16_bits": lambda: (384, 12, sparse_large(384, 11, 200000, 1)),
         "degrees_past_2^19": lambda: (512, 16, sym(inputs.rng(12).integers(0, 3000, (512, 512)))),
         "ragged_E": lambda: (1000, 8, sym(inputs.rng(13).integers(0, 20, (1000, 1000)))),
