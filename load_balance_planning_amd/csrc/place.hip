@@ -733,7 +733,7 @@ SwapLds swap_lds(const Dims& d) {
   l.rank_of = take(sizeof(int32_t) * d.E);
   l.mem = take(sizeof(int32_t) * d.E);
   l.own = take(sizeof(int32_t) * d.E);
-  l.red = take(sizeof(uint64_t) * (kPlaceWaves + 1));
+  l.red = take(sizeof(uint64_t) * (kPlaceWaves + 3));  // wave partials, a result, two swap-loop maxima
   l.col = take(sizeof(int32_t) * kPlaceWaves * (size_t)d.R);
   const size_t aff_b = sizeof(int32_t) * (size_t)d.R * d.E;
   const size_t key_b = sizeof(uint64_t) * (size_t)d.R * (d.R + 1);
@@ -812,19 +812,30 @@ __device__ __forceinline__ int swap_loop(const Dims& d, const int32_t* __restric
   const int E = d.E, R = d.R, Er = d.Er, Es = c16_stride(E);
   const int tid = threadIdx.x;
   const int cap = max_swaps < 0 ? 4096 : max_swaps;
+  // The largest key of iteration i: each wave's maximum into top[i % 2] by an
+  // LDS atomic, one barrier, then read by all.  top[(i + 1) % 2] is cleared
+  // in iteration i after that barrier: its last reads (iteration i - 1) were
+  // before the barriers that ended iteration i - 1.
+  uint64_t* top = red + kPlaceWaves + 1;
+  if (tid == 0) top[0] = top[1] = 0;
+  __syncthreads();
   int swaps = 0;
-  for (;;) {
+  for (int it = 0;; ++it) {
     uint64_t best = 0;
     for (int q = tid; q < R * ks; q += kPlaceThreads) {
       const uint64_t v = key_load<KEY_LDS>(&key[q]);
       best = v > best ? v : best;
     }
-    best = block_max<kPlaceWaves>(best, red);
+    best = wave_max(best);
+    if ((tid & 63) == 0) atomicMax(&top[it & 1], best);
+    __syncthreads();
+    best = top[it & 1];
     const int64_t gain = (int64_t)(best >> kPairBits) - (int64_t)kGainBias;
     if (best == 0 || gain <= 0 || swaps >= cap) break;
     const int64_t pair = (int64_t)(kPairMask - (best & kPairMask));
     const int xa = (int)(pair / E), xb = (int)(pair - (int64_t)xa * E);
     const int ra = rank_of[xa], rb = rank_of[xb];
+    if (tid == 0) top[(it + 1) & 1] = 0;
     // aff of ranks ra and rb; clear the keys of every rank pair with ra or rb.
     for (int x = tid; x < E; x += kPlaceThreads) {
       const int32_t ca = C16 ? (int32_t)c16[(int64_t)xa * Es + x] : C[(int64_t)xa * E + x];
